@@ -1,0 +1,104 @@
+"""Seeded synthetic inputs shared by the tests, the benchmark and the smoke check.
+
+This module holds no part of the W12 method: it draws Gaussian weights and
+activations, rounds them to BF16 and sprinkles exact zeros.  Bringing raw
+weights into a group's encodable exponent range is format arithmetic and is
+done by the callers (through a pack/unpack round trip), not here.
+
+The workloads stand in for the checkpoints of the 8-30B dense models the
+pages measure on (AI Radar summary of SpecPilot, English edition, "Reasons":
+8-30B dense models; HotRepo digest of StargazerX0/SpecPilot, project
+introduction: batch 1-32), which are not available: shapes are those of the
+linear layers of a ~27B dense decoder, values are N(0, sigma) draws.
+
+Recipe (numpy PCG64 via ``default_rng``):
+  * weights: fp32 standard normal * sigma, rounded to BF16 (round to nearest
+    even), then a Bernoulli(p_zero) mask drawn from its own seed replaces an
+    element by a zero that keeps the drawn sign (so +0 and -0 both occur);
+  * activations: fp32 standard normal * sigma_x, rounded to BF16.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+
+def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """Round fp32 to the nearest BF16 (ties to even); NaN stays a quiet NaN."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    u = a.view(np.uint32).astype(np.uint64)
+    rounded = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+    nan = np.isnan(a)
+    if nan.any():
+        rounded[nan] = ((u[nan] >> 16).astype(np.uint16) | 0x0040)
+    return rounded
+
+
+def bf16_bits_to_f32(a: np.ndarray) -> np.ndarray:
+    a = np.asarray(a, dtype=np.uint16)
+    return (a.astype(np.uint32) << 16).view(np.float32)
+
+
+def gaussian_bf16(shape, sigma: float, seed: int) -> np.ndarray:
+    rng = np.random.default_rng(seed)
+    a = rng.standard_normal(shape, dtype=np.float32)
+    a *= np.float32(sigma)
+    return f32_to_bf16_bits(a)
+
+
+def inject_zeros(w: np.ndarray, p_zero: float, seed: int) -> np.ndarray:
+    """Replace a Bernoulli(p_zero) subset by signed zeros (sign of the draw)."""
+    rng = np.random.default_rng(seed)
+    mask = rng.random(w.shape, dtype=np.float32) < np.float32(p_zero)
+    out = w.copy()
+    out[mask] &= np.uint16(0x8000)
+    return out
+
+
+@dataclass(frozen=True)
+class GemmCase:
+    """One GEMM workload: W [N, K] ~ N(0, sigma_w), x [M, K] ~ N(0, sigma_x)."""
+    name: str
+    N: int
+    K: int
+    M: int
+    sigma_w: float
+    sigma_x: float
+    seed_w: int
+    seed_x: int
+    seed_zero: int
+    p_zero: float = 0.001
+
+    def weights_raw(self) -> np.ndarray:
+        w = gaussian_bf16((self.N, self.K), self.sigma_w, self.seed_w)
+        return inject_zeros(w, self.p_zero, self.seed_zero)
+
+    def activations(self, M: int | None = None) -> np.ndarray:
+        M = self.M if M is None else M
+        return gaussian_bf16((M, self.K), self.sigma_x, self.seed_x + 1000 * M)
+
+    @property
+    def weight_elems(self) -> int:
+        return self.N * self.K
+
+
+# The five workloads: a tiny case, then linear layers of a ~27B dense decoder
+# (hidden 5120, QKV out 7168, fused gate+up 34816, down in 17408).
+TINY = GemmCase("tiny 1024x512", 1024, 512, 1, 0.02, 1.0, 101, 102, 103)
+QKV = GemmCase("qkv 7168x5120", 7168, 5120, 1, 0.02, 1.0, 201, 202, 203)
+GATE_UP = GemmCase("gate_up 34816x5120", 34816, 5120, 16, 0.02, 1.0, 301, 302, 303)
+DOWN = GemmCase("down 5120x17408", 5120, 17408, 32, 0.015, 0.5, 401, 402, 403)
+
+CASES = {c.name.split()[0]: c for c in (TINY, QKV, GATE_UP, DOWN)}
+
+# 64-layer stack: per layer QKV, O, gate+up, down (N, K).
+STACK_LAYERS = 64
+STACK_SHAPES = ((7168, 5120), (5120, 5120), (34816, 5120), (5120, 17408))
+
+
+def stack_case(layer: int, j: int) -> GemmCase:
+    N, K = STACK_SHAPES[j]
+    s = 10000 + 10 * layer + j
+    return GemmCase("stack L%d.%d %dx%d" % (layer, j, N, K), N, K, 1, 0.02, 1.0,
+                    s, 20000, s + 500000)

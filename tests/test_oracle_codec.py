@@ -1,0 +1,181 @@
+"""Pins for the oracle's W12 codec, independent of the oracle's own formulas.
+
+The pages fix three things about W12 (AI Radar summary of SpecPilot, English
+edition, "Reasons"; HotRepo digest of StargazerX0/SpecPilot, project
+introduction): it is 12 bits per BF16 weight in three 4-bit planes, it is
+lossless, and the GEMM rebuilds the BF16 bits exactly.  Each test below
+checks one of those facts (or a consequence that a plausible slip in the
+oracle would break) by brute force, counting, or a hand-derived example.
+"""
+import os
+
+import numpy as np
+import pytest
+
+ALL_BF16 = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+EXP = (ALL_BF16.astype(np.int32) >> 7) & 0xFF
+
+
+@pytest.mark.parametrize("beta", list(range(0, 121)))
+def test_exhaustive_bijection_per_beta(oracle, beta):
+    """For every base, exactly 2^12 BF16 patterns are stored exactly, and the
+    12-bit codes of those patterns are a bijection onto 0..4095 whose decode
+    gives the pattern back (lossless 12-bit code, brute force over all
+    65536 BF16 words)."""
+    code, ok = oracle.encode_many(ALL_BF16, beta)
+    assert code.max() < 4096                          # 12 bits per weight
+    assert int(ok.sum()) == 4096                      # a 12-bit code's capacity, used fully
+    enc = code[ok]
+    assert np.array_equal(np.sort(enc), np.arange(4096, dtype=np.uint16))
+    assert np.array_equal(oracle.decode_many(enc, beta), ALL_BF16[ok])
+    # Every code decodes to a stored pattern: decode is the inverse map.
+    dec_all = oracle.decode_many(np.arange(4096, dtype=np.uint16), beta)
+    assert len(np.unique(dec_all)) == 4096
+    assert set(dec_all.tolist()) == set(ALL_BF16[ok].tolist())
+    # The stored set is sign-symmetric and closed under every mantissa for a
+    # given exponent (only the exponent decides encodability).
+    stored_exps = set(EXP[ok].tolist())
+    assert len(stored_exps) == 16
+    for e in stored_exps:
+        assert int(ok[EXP == e].sum()) == 256
+    # Zero, the subnormals and the smallest normal binade are always stored.
+    assert {0, 1} <= stored_exps
+    # The stored normal exponents above 1 form one contiguous run of 14.
+    upper = sorted(e for e in stored_exps if e > 1)
+    assert upper == list(range(upper[0], upper[0] + 14))
+
+
+def test_beta_rule_bruteforce(oracle):
+    """The group base is the smallest base for which the group's largest
+    element survives the round trip (checked by trying every base), and the
+    oracle's base keeps every smaller stored exponent down to its floor."""
+    rng = np.random.default_rng(7)
+    for emax in range(256):
+        for _ in range(3):
+            s = int(rng.integers(0, 2))
+            m = int(rng.integers(0, 128))
+            v = (s << 15) | (emax << 7) | m
+            smallest = next(b for b in range(0, 128)
+                            if oracle.decode(oracle.encode(v, b)[0], b) == v)
+            assert oracle.beta_for_emax(emax) == smallest
+        beta = oracle.beta_for_emax(emax)
+        assert 0 <= beta <= 120
+        # no byte carry: the largest rebuilt exponent field fits 7 bits
+        assert beta + 7 <= 127
+
+
+def test_clamp_is_window_floor(oracle):
+    """An element below its group's window is written as the smallest stored
+    normal magnitude of that window, with its sign (documented clamp)."""
+    for beta in (0, 1, 5, 56, 120):
+        code, ok = oracle.encode_many(ALL_BF16, beta)
+        dec = oracle.decode_many(code, beta)
+        stored = ALL_BF16[ok]
+        stored_exp = EXP[ok]
+        floor_mag = int(stored[(stored_exp > 1) & (stored < 0x8000)].min())
+        below = (~ok) & (EXP > 1) & (EXP < (floor_mag >> 7))
+        if beta == 0:
+            assert not below.any()
+            continue
+        assert below.any()
+        expect = (ALL_BF16[below] & 0x8000) | floor_mag
+        assert np.array_equal(dec[below], expect.astype(np.uint16))
+
+
+def _read_golden():
+    path = os.path.join(os.path.dirname(__file__), "golden", "w12_layout_example.txt")
+    rec = {}
+    with open(path) as f:
+        for line in f:
+            if line.startswith("#") or ":" not in line:
+                continue
+            k, v = line.split(":", 1)
+            rec[k.strip()] = [int(t, 16) for t in v.split()]
+    return rec
+
+
+@pytest.mark.parametrize("variant,k7", [("GAP", 0x3800), ("IN", 0x3980)])
+def test_layout_worked_example(oracle, variant, k7):
+    """Hand-derived worked example: plane bytes in split-nibble order, meta
+    byte, unencodable flag and count, and the unpacked words."""
+    g = _read_golden()
+    w = np.zeros((1, 128), np.uint16)
+    w[0, :8] = [0x3F80, 0xBF00, 0x3C01, 0x8000, 0x3A5B, 0x0001, 0xB9C7, k7]
+    p0, p1, p2, meta, bad = oracle.pack(w)
+    for name, plane in (("p0", p0), ("p1", p1), ("p2", p2)):
+        assert plane.shape == (1, 64)
+        assert list(plane[0, :4]) == g[variant + "." + name]
+        assert not plane[0, 4:].any()
+    assert list(meta[0]) == g[variant + ".meta"]
+    assert bad == g[variant + ".bad"][0]
+    out = oracle.unpack(p0, p1, p2, meta, 1, 128)
+    assert list(out[0, :8]) == g[variant + ".unpacked"]
+    assert not out[0, 8:].any()
+
+
+def test_container_bytes_are_three_quarters(oracle):
+    """Packed planes are exactly 0.75x the BF16 bytes (12 of 16 bits), plus
+    one metadata byte per 128-weight group."""
+    for N, K in ((1, 128), (3, 256), (1024, 512), (7, 17408)):
+        w = np.zeros((N, K), np.uint16)
+        p0, p1, p2, meta, _ = oracle.pack(w)
+        assert p0.nbytes + p1.nbytes + p2.nbytes == 0.75 * (2 * N * K)
+        assert meta.nbytes == N * K // 128
+        assert oracle.plane_bytes(N, K) * 3 == 3 * N * K // 2
+        assert oracle.meta_bytes(N, K) == meta.nbytes
+
+
+def _groups_random(rng, rows, gap_rows):
+    """BF16 rows of one group each; rows in gap_rows get one element pushed
+    far below the row maximum."""
+    w = rng.standard_normal((rows, 128)).astype(np.float32) * np.float32(0.02)
+    from lossless_bit_weight_amd.inputs import f32_to_bf16_bits
+    b = f32_to_bf16_bits(w)
+    for r in gap_rows:
+        b[r, int(rng.integers(0, 128))] = np.uint16(0x3000 | int(rng.integers(0, 128)))
+    return b
+
+
+def test_flag_iff_not_lossless(oracle):
+    """A group is flagged exactly when its round trip is not the identity,
+    and the count equals the number of flagged groups."""
+    rng = np.random.default_rng(11)
+    b = _groups_random(rng, 400, gap_rows=range(0, 400, 7))
+    p0, p1, p2, meta, bad = oracle.pack(b)
+    back = oracle.unpack(p0, p1, p2, meta, 400, 128)
+    changed = np.any(back != b, axis=1)
+    flagged = (meta[:, 0] & 0x80) != 0
+    assert np.array_equal(changed, flagged)
+    assert bad == int(flagged.sum())
+    assert flagged[::7].all()
+
+
+def test_clamped_tensor_round_trips(oracle):
+    """unpack(pack(.)) projects onto the stored set: packing the projection
+    raises no flag and reproduces it bit for bit, with identical planes."""
+    from lossless_bit_weight_amd.inputs import TINY
+    w_raw = TINY.weights_raw()
+    p0, p1, p2, meta, bad = oracle.pack(w_raw)
+    w = oracle.unpack(p0, p1, p2, meta, TINY.N, TINY.K)
+    q0, q1, q2, qmeta, bad2 = oracle.pack(w)
+    assert bad2 == 0
+    assert np.array_equal(oracle.unpack(q0, q1, q2, qmeta, TINY.N, TINY.K), w)
+    assert np.array_equal(q0, p0) and np.array_equal(q1, p1) and np.array_equal(q2, p2)
+    assert np.array_equal(qmeta, meta & 0x7F)
+    # Elements already stored exactly are untouched by the projection.
+    same = w == w_raw
+    assert same.mean() > 0.999
+
+
+def test_special_values_round_trip(oracle):
+    """+-0, subnormals, the smallest normals, +-Inf and NaN payloads survive
+    when they share a group with compatible neighbours."""
+    rows = []
+    rows.append([0x0000, 0x8000, 0x0001, 0x807F, 0x0080, 0x80FF] + [0] * 122)
+    rows.append([0x7F80, 0xFF80, 0x7FC1, 0xFFFF, 0x7F81, 0x7900] + [0x7F00] * 122)
+    rows.append([0x7F7F, 0xFF7F] + [0x0000] * 126)
+    w = np.array(rows, dtype=np.uint16)
+    p0, p1, p2, meta, bad = oracle.pack(w)
+    assert bad == 0
+    assert np.array_equal(oracle.unpack(p0, p1, p2, meta, 3, 128), w)
+    assert list(meta[:, 0]) == [0, 120, 120]
