@@ -1,0 +1,286 @@
+"""Benchmark of the W12 decode GEMM on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-sweep] [--no-cpu-baseline]
+
+Prints ONE JSON line.  The headline workload is the attention QKV projection
+of a ~27B dense decoder at single-request decode: W [7168, 5120] packed to
+W12 (group 128), x [1, 5120], y fp32.  One step = one w12_gemm launch over
+that weight (x staged in LDS, the three planes streamed, BF16 rebuilt in
+registers, fp32 dot products, epilogue).  `value` is the effective weight
+stream rate: stored W12 bytes (planes + meta) per launch x launches / time.
+
+Timing protocol (the pages warm up before timing and tune kernels against
+the memory-bandwidth limit: HotRepo digest of StargazerX0/SpecPilot, quick
+start; AI Radar summary of SpecPilot, English edition, opening paragraph):
+  * inputs are resident in HBM before the timed region;
+  * R distinct copies of the weight (>= 1 GB in total, above the 256 MB
+    last-level cache) are used in rotation, so every launch streams from HBM;
+  * the R launches are captured once in a HIP graph; W warm-up launches run,
+    then the graph is replayed until K launches are done, bracketed by
+    synchronize + HIP events recorded on the launch stream.
+The same protocol times the same-tiling BF16 control; `speedup_vs_bf16` is
+the ratio of the two.  `cpu_baseline` times the CPU oracle (decode + fp64
+GEMM, all host threads) on the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+if HERE not in sys.path:
+    sys.path.insert(0, HERE)
+
+HBM_PEAK_GBPS = 8000.0           # MI355X HBM3E, published
+ROTATE_BYTES = 1 << 30           # >= 1 GiB of distinct weights per rotation
+METRIC = "w12_gemm effective weight GB/s & % HBM peak; speedup vs BF16 GEMM, M=1–32"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--no-sweep", action="store_true", help="headline workload only")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="approximate CPU-oracle work to time")
+    ap.add_argument("--sweep-ms", type=str, default="1,2,4,8,16,32")
+    return ap.parse_args()
+
+
+def source_sha() -> str:
+    """Hash of the kernel sources, to tie stored counter readings to code."""
+    h = hashlib.sha256()
+    csrc = os.path.join(HERE, "lossless_bit_weight_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+class Workload:
+    """One weight on the GPU in R rotated copies, W12 and BF16."""
+
+    def __init__(self, case, torch, w12):
+        from lossless_bit_weight_amd.inputs import GemmCase  # noqa: F401
+        self.case = case
+        self.N, self.K = case.N, case.K
+        raw = case.weights_raw()
+        wd = torch.from_numpy(raw.view(np.int16)).cuda()
+        # project onto the encodable set with the library itself, then repack
+        first, self.raw_bad = w12.pack(wd)
+        self.w_bf16 = w12.w12_unpack(first)
+        wt, bad = w12.pack(self.w_bf16)
+        if bad:
+            raise RuntimeError("projected weights still have unencodable groups")
+        del wd, first
+        self.w12_bytes = wt.nbytes
+        self.bf16_bytes = 2 * self.N * self.K
+        r12 = max(2, math.ceil(ROTATE_BYTES / self.w12_bytes))
+        r16 = max(2, math.ceil(ROTATE_BYTES / self.bf16_bytes))
+        self.w12_copies = [wt] + [w12.W12Weight(wt.p0.clone(), wt.p1.clone(), wt.p2.clone(),
+                                                wt.meta.clone(), self.N, self.K)
+                                  for _ in range(r12 - 1)]
+        self.bf16_copies = [self.w_bf16] + [self.w_bf16.clone() for _ in range(r16 - 1)]
+        torch.cuda.synchronize()
+
+
+def time_graph(torch, launches, steps, warmup):
+    """Capture `launches` (callables, in rotation) into one graph, replay it
+    until `steps` launches ran; return average ms per launch measured with
+    events on the launch stream."""
+    R = len(launches)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for i in range(max(warmup, R)):
+            launches[i % R]()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for f in launches:
+            f()
+    reps = max(1, math.ceil(steps / R))
+    g.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / (reps * R), reps * R
+
+
+def gemm_bytes(N, K, M, out_bytes, w_bytes):
+    return w_bytes + 2 * M * K + out_bytes * M * N
+
+
+def measure(torch, w12, wl: Workload, M, steps, warmup, out_dtype):
+    x = torch.from_numpy(wl.case.activations(M).view(np.int16)).cuda()
+    y = torch.empty((M, wl.N), dtype=out_dtype, device="cuda")
+    out_b = 4 if out_dtype == torch.float32 else 2
+    l12 = [(lambda c=c: w12.w12_gemm(x, c, y=y)) for c in wl.w12_copies]
+    l16 = [(lambda c=c: w12.bf16_gemm(x, c, y=y)) for c in wl.bf16_copies]
+    ms12, n12 = time_graph(torch, l12, steps, warmup)
+    ms16, n16 = time_graph(torch, l16, steps, warmup)
+    b12 = gemm_bytes(wl.N, wl.K, M, out_b, wl.w12_bytes)
+    b16 = gemm_bytes(wl.N, wl.K, M, out_b, wl.bf16_bytes)
+    return {
+        "workload": wl.case.name, "M": M,
+        "w12_kernel": w12.w12_gemm_variant(M, wl.N, wl.K, True),
+        "bf16_kernel": w12.w12_gemm_variant(M, wl.N, wl.K, False),
+        "w12_us": ms12 * 1e3, "bf16_us": ms16 * 1e3,
+        "w12_weight_gbps": wl.w12_bytes / (ms12 * 1e-3) / 1e9,
+        "w12_bf16_equiv_gbps": wl.bf16_bytes / (ms12 * 1e-3) / 1e9,
+        "bf16_weight_gbps": wl.bf16_bytes / (ms16 * 1e-3) / 1e9,
+        "w12_alg_gbps": b12 / (ms12 * 1e-3) / 1e9,
+        "bf16_alg_gbps": b16 / (ms16 * 1e-3) / 1e9,
+        "w12_alg_bytes": b12, "bf16_alg_bytes": b16,
+        "speedup_vs_bf16": ms16 / ms12,
+        "launches": n12,
+    }
+
+
+def stored_traffic(kernel: str):
+    """HBM bytes per launch from committed rocprofv3 counter readings, if
+    they were taken on the current kernel sources; else None."""
+    path = os.path.join(HERE, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_sha") != source_sha():
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    if not k:
+        return None
+    return k.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(case, M, seconds):
+    """The CPU oracle as it stands: container decode + fp64 GEMM on all host
+    threads, on a row sample of the headline workload sized to ~`seconds`."""
+    import oracle
+    nthreads = len(os.sched_getaffinity(0))
+    raw = case.weights_raw()
+    x = case.activations(M)
+    # Oracle-side projection and container (no input from the HIP path).
+    rows = case.N
+    probe = 256
+    p0, p1, p2, meta, _ = oracle.pack(np.ascontiguousarray(raw[:probe]))
+    w = oracle.unpack(p0, p1, p2, meta, probe, case.K)
+    q = oracle.pack(w)
+    t0 = time.perf_counter()
+    oracle.gemm_w12_f64(x, *q[:4], probe, nthreads=nthreads)
+    per_row = (time.perf_counter() - t0) / probe
+    rows = int(min(case.N, max(probe, seconds / max(per_row, 1e-9))))
+    sub = np.ascontiguousarray(raw[:rows])
+    p0, p1, p2, meta, _ = oracle.pack(sub)
+    w = oracle.unpack(p0, p1, p2, meta, rows, case.K)
+    q = oracle.pack(w)
+    t0 = time.perf_counter()
+    oracle.gemm_w12_f64(x, *q[:4], rows, nthreads=nthreads)
+    dt = time.perf_counter() - t0
+    wbytes = 1.5 * rows * case.K + rows * case.K / 128
+    return {
+        "value": wbytes / dt / 1e9, "unit": "GB/s", "cores": nthreads, "kind": "oracle",
+        "sample": "%d of %d rows of %s, M=%d (decode + fp64 GEMM), %.1f s"
+                  % (rows, case.N, case.name, M, dt),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: the W12 decode GEMM of one weight on "
+              "one MI355X; --gpus %d is not supported" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from lossless_bit_weight_amd import inputs, w12
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    w12.lib()
+    props = torch.cuda.get_device_properties(0)
+    print("device: %s, %d CUs" % (props.name, props.multi_processor_count), file=sys.stderr,
+          flush=True)
+
+    head_case = inputs.QKV
+    wl = Workload(head_case, torch, w12)
+    print("headline workload ready (%s, raw unencodable groups %d)" % (head_case.name, wl.raw_bad),
+          file=sys.stderr, flush=True)
+    head = measure(torch, w12, wl, 1, args.steps, args.warmup, torch.float32)
+    print("headline: %s" % json.dumps(head), file=sys.stderr, flush=True)
+
+    sweep = []
+    if not args.no_sweep:
+        ms = [int(m) for m in args.sweep_ms.split(",") if m]
+        for name in ("qkv", "gate_up", "down"):
+            case = inputs.CASES[name]
+            wlc = wl if name == "qkv" else Workload(case, torch, w12)
+            for M in ms:
+                r = measure(torch, w12, wlc, M, args.steps, args.warmup, torch.float32)
+                sweep.append(r)
+                print("sweep: %s M=%d w12 %.2f us (%.0f GB/s) bf16 %.2f us speedup %.3f"
+                      % (name, M, r["w12_us"], r["w12_weight_gbps"], r["bf16_us"],
+                         r["speedup_vs_bf16"]), file=sys.stderr, flush=True)
+            if wlc is not wl:
+                del wlc
+                torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(head_case, 1, args.cpu_seconds)
+        print("cpu baseline: %s" % json.dumps(cpu), file=sys.stderr, flush=True)
+
+    kernel = head["w12_kernel"]
+    achieved = head["w12_alg_gbps"]
+    traffic = stored_traffic(kernel)
+    out = {
+        "metric": METRIC,
+        "value": round(head["w12_weight_gbps"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": head["launches"],
+        "warmup": args.warmup,
+        "ms_per_step": head["w12_us"] / 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "QKV projection W[7168,5120] as W12 (group 128), x[1,5120] "
+                               "BF16, y fp32; single-request decode GEMV",
+                   "N": head_case.N, "K": head_case.K, "M": 1, "group": 128,
+                   "rotation_copies": len(wl.w12_copies)},
+        "pct_hbm_peak": round(100.0 * head["w12_weight_gbps"] / HBM_PEAK_GBPS, 2),
+        "w12_us": round(head["w12_us"], 3),
+        "bf16_us": round(head["bf16_us"], 3),
+        "speedup_vs_bf16": round(head["speedup_vs_bf16"], 4),
+        "roofline": {"bound": "hbm", "kernel": kernel, "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic, "alg_bytes_per_launch": head["w12_alg_bytes"]},
+        "cpu_baseline": cpu,
+        "sweep": [{k: (round(v, 3) if isinstance(v, float) else v) for k, v in r.items()}
+                  for r in sweep],
+        "source_sha": source_sha(),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,147 @@
+/*
+ * w12.h -- C ABI of libw12.so: the W12 lossless 12-bit BF16 weight format and
+ * small-M decode GEMMs for AMD MI355X (gfx950).
+ *
+ * The operation.  W12 stores each BF16 weight in 12 bits spread over three
+ * 4-bit planes and rebuilds the exact BF16 bits in registers inside the GEMM
+ * (AI Radar paper summary of SpecPilot, English edition, "Reasons", item on
+ * the discovered mechanisms; HotRepo digest "StargazerX0/SpecPilot",
+ * project introduction, second paragraph: decoded bit-exactly inside the
+ * GEMM, batch 1-32).  The pages give no bit allocation; this library uses
+ * format W12-v1:
+ *
+ *   group    = 128 consecutive weights along K of one row (K % 128 == 0);
+ *   beta     = smallest beta >= 0 with 2*beta+15 >= the group's largest
+ *              biased exponent E (0 <= beta <= 120);
+ *   stored   = exponents {0, 1} and [2*beta+2, 2*beta+15] (4096 values);
+ *   nibbles  = P0 = v[3:0], P1 = v[7:4], P2 = sign<<3 | h with h = 0 for
+ *              E <= 1, else h = (E >> 1) - beta (1..7);
+ *   layout   = plane p is u8[N][K/2]; element k of row n is in byte
+ *              n*K/2 + 4*(k/8) + (k%8)%4, low nibble if k%8 < 4, else high;
+ *   meta     = u8[N][K/128]: beta | 0x80 if the group is unencodable.
+ *
+ * A group holding an exponent in [2, 2*beta+1] cannot be stored exactly: the
+ * packer flags it (meta bit 7), counts it, and stores that element as the
+ * window floor +-2^(2*beta+2-127).  Unpack and GEMM ignore the flag and use
+ * the stored (clamped) value.
+ *
+ * Conventions for every call below:
+ *   - all tensor pointers are DEVICE memory owned by the caller; the library
+ *     allocates, frees and keeps nothing, and never synchronises;
+ *   - BF16 tensors are passed as their 16-bit patterns;
+ *   - `stream` is a hipStream_t (NULL = the default stream); work is enqueued
+ *     on it and the call returns without waiting;
+ *   - arguments are checked on the host before any launch; on error nothing
+ *     is enqueued and a negative w12_status_t is returned;
+ *   - launch failures return W12_ERR_HIP;
+ *   - calls on different streams are independent (the library is stateless
+ *     and thread-safe); outputs must not alias inputs.
+ */
+#ifndef W12_H
+#define W12_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define W12_ABI_VERSION 1
+#define W12_GROUP 128
+#define W12_MAX_M 32
+
+typedef enum {
+    W12_OK = 0,
+    W12_ERR_NULL = -1,        /* a required pointer is NULL                  */
+    W12_ERR_SHAPE = -2,       /* N < 1, K < 128, K % 128 != 0, M < 1, ld < K/N */
+    W12_ERR_ALIGN = -3,       /* pointer or leading dimension misaligned     */
+    W12_ERR_DTYPE = -4,       /* unknown output type                         */
+    W12_ERR_UNSUPPORTED = -6, /* M > 32                                      */
+    W12_ERR_HIP = -7          /* the HIP launch reported an error            */
+} w12_status_t;
+
+typedef enum {
+    W12_OUT_BF16 = 0,         /* y stored as BF16 bits, round to nearest even */
+    W12_OUT_F32 = 1           /* y stored as fp32                             */
+} w12_out_t;
+
+/* ABI version of the loaded library (W12_ABI_VERSION at build time). */
+int w12_abi_version(void);
+
+/* Static, never-NULL description of a status code. */
+const char *w12_status_string(int status);
+
+/* Bytes of ONE nibble plane for an [N, K] weight: N*K/2 (0 on bad shape). */
+size_t w12_plane_bytes(int64_t N, int64_t K);
+
+/* Bytes of the metadata array: N*K/128 (0 on bad shape). */
+size_t w12_meta_bytes(int64_t N, int64_t K);
+
+/*
+ * w12_pack -- BF16 [N, K] (row-major, contiguous) -> three planes + meta.
+ * The format's encoder (a1): one 128-weight group at a time, integer only.
+ *   w          : device, N*K BF16 words, 16-byte aligned.
+ *   p0, p1, p2 : device outputs, w12_plane_bytes(N, K) bytes each, 16-byte aligned.
+ *   meta       : device output, w12_meta_bytes(N, K) bytes.
+ *   bad_groups : device uint32 counter or NULL; the number of unencodable
+ *                groups is ADDED to it (the caller zeroes it beforehand).
+ * Errors: W12_ERR_NULL, W12_ERR_SHAPE, W12_ERR_ALIGN, W12_ERR_HIP.
+ */
+int w12_pack(const uint16_t *w, int64_t N, int64_t K,
+             void *p0, void *p1, void *p2, uint8_t *meta,
+             uint32_t *bad_groups, void *stream);
+
+/*
+ * w12_unpack -- planes + meta -> BF16 [N, K] (a7, the inverse of w12_pack on
+ * every unflagged group; same in-register decode as the GEMMs).
+ *   p0, p1, p2 : device, w12_plane_bytes(N, K) bytes each, 16-byte aligned.
+ *   meta       : device, w12_meta_bytes(N, K) bytes.
+ *   w_out      : device output, N*K BF16 words, 16-byte aligned.
+ * Errors: W12_ERR_NULL, W12_ERR_SHAPE, W12_ERR_ALIGN, W12_ERR_HIP.
+ */
+int w12_unpack(const void *p0, const void *p1, const void *p2,
+               const uint8_t *meta, int64_t N, int64_t K,
+               uint16_t *w_out, void *stream);
+
+/*
+ * w12_gemm -- y[m, n] = sum_k x[m, k] * W[n, k] with W read from a W12
+ * container and rebuilt in registers (a2-a6), fp32 accumulation.
+ *   x      : device BF16 [M, K], row stride ldx elements (ldx >= K,
+ *            ldx % 8 == 0), 16-byte aligned.  1 <= M <= 32.
+ *   p0..meta: the container of an [N, K] weight as written by w12_pack.
+ *   y      : device output [M, N], row stride ldy elements (ldy >= N),
+ *            BF16 bits (2-byte aligned) or fp32 (4-byte aligned) per y_type.
+ * M <= 8 runs a wavefront-reduction GEMV; 9 <= M <= 32 runs bf16 MFMA with
+ * x padded to 16 or 32 rows.
+ * Errors: W12_ERR_NULL, W12_ERR_SHAPE, W12_ERR_ALIGN, W12_ERR_DTYPE,
+ *         W12_ERR_UNSUPPORTED (M > 32), W12_ERR_HIP.
+ */
+int w12_gemm(const uint16_t *x, int64_t M, int64_t ldx,
+             const void *p0, const void *p1, const void *p2,
+             const uint8_t *meta, int64_t N, int64_t K,
+             void *y, int64_t ldy, int y_type, void *stream);
+
+/*
+ * bf16_gemm -- the control: the same kernels, tiling and summation order as
+ * w12_gemm, with W read as plain BF16 (a8).  For W = unpack(pack(W)) the two
+ * calls return bitwise identical y.
+ *   w : device BF16 [N, K], row-major contiguous, 16-byte aligned.
+ *   other arguments and errors as w12_gemm.
+ */
+int bf16_gemm(const uint16_t *x, int64_t M, int64_t ldx,
+              const uint16_t *w, int64_t N, int64_t K,
+              void *y, int64_t ldy, int y_type, void *stream);
+
+/*
+ * Name of the kernel variant w12_gemm / bf16_gemm launch for this shape
+ * (static string, for reports and profiles), or NULL if the shape is
+ * rejected.  `is_w12` selects the weight fetch.
+ */
+const char *w12_gemm_variant(int64_t M, int64_t N, int64_t K, int is_w12);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W12_H */

@@ -1,0 +1,132 @@
+// w12_api.hip -- the C ABI declared in include/w12.h: host-side argument
+// checks, tiling choice, and launches on the caller's stream.  Nothing here
+// allocates, synchronises or keeps state.
+#include <stdint.h>
+
+#include "../../include/w12.h"
+#include "w12_internal.hpp"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Largest element count a launch accepts: keeps every grid below 2^31 blocks
+// and every byte offset far inside int64.
+constexpr int64_t kMaxElems = (int64_t)1 << 40;
+
+int check_weight_shape(int64_t N, int64_t K) {
+    if (N < 1 || K < W12_GROUP || K % W12_GROUP != 0) return W12_ERR_SHAPE;
+    if (N > kMaxElems / K) return W12_ERR_SHAPE;
+    return W12_OK;
+}
+
+int check_gemm_common(const uint16_t* x, int64_t M, int64_t ldx, int64_t N, int64_t K, void* y,
+                      int64_t ldy, int y_type) {
+    if (x == nullptr || y == nullptr) return W12_ERR_NULL;
+    if (int rc = check_weight_shape(N, K)) return rc;
+    if (M < 1) return W12_ERR_SHAPE;
+    if (M > W12_MAX_M) return W12_ERR_UNSUPPORTED;
+    if (ldx < K || ldy < N) return W12_ERR_SHAPE;
+    if (y_type != W12_OUT_BF16 && y_type != W12_OUT_F32) return W12_ERR_DTYPE;
+    if (!aligned16(x) || ldx % 8 != 0) return W12_ERR_ALIGN;
+    const uintptr_t ya = reinterpret_cast<uintptr_t>(y);
+    if (y_type == W12_OUT_F32 ? (ya & 3u) : (ya & 1u)) return W12_ERR_ALIGN;
+    return W12_OK;
+}
+
+int status_of(hipError_t e) { return e == hipSuccess ? W12_OK : W12_ERR_HIP; }
+
+w12::GemmArgs make_args(const uint16_t* x, int64_t M, int64_t ldx, int64_t N, int64_t K, void* y,
+                        int64_t ldy, int y_type) {
+    w12::GemmArgs a{};
+    a.x = x;
+    a.ldx = ldx;
+    a.M = (int)M;
+    a.N = N;
+    a.K = K;
+    a.y = y;
+    a.ldy = ldy;
+    a.y_f32 = y_type == W12_OUT_F32;
+    return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+int w12_abi_version(void) { return W12_ABI_VERSION; }
+
+const char* w12_status_string(int status) {
+    switch (status) {
+        case W12_OK: return "ok";
+        case W12_ERR_NULL: return "a required pointer is NULL";
+        case W12_ERR_SHAPE: return "bad shape (need N >= 1, K a positive multiple of 128, M >= 1, ldx >= K, ldy >= N)";
+        case W12_ERR_ALIGN: return "misaligned pointer or leading dimension (16-byte tensors, ldx % 8 == 0)";
+        case W12_ERR_DTYPE: return "unknown output type";
+        case W12_ERR_UNSUPPORTED: return "unsupported size (M > 32)";
+        case W12_ERR_HIP: return "HIP launch failed";
+        default: return "unknown status";
+    }
+}
+
+size_t w12_plane_bytes(int64_t N, int64_t K) {
+    if (check_weight_shape(N, K) != W12_OK) return 0;
+    return (size_t)(N * K / 2);
+}
+
+size_t w12_meta_bytes(int64_t N, int64_t K) {
+    if (check_weight_shape(N, K) != W12_OK) return 0;
+    return (size_t)(N * (K / W12_GROUP));
+}
+
+int w12_pack(const uint16_t* w, int64_t N, int64_t K, void* p0, void* p1, void* p2, uint8_t* meta,
+             uint32_t* bad_groups, void* stream) {
+    if (!w || !p0 || !p1 || !p2 || !meta) return W12_ERR_NULL;
+    if (int rc = check_weight_shape(N, K)) return rc;
+    if (!aligned16(w) || !aligned16(p0) || !aligned16(p1) || !aligned16(p2)) return W12_ERR_ALIGN;
+    if (bad_groups && (reinterpret_cast<uintptr_t>(bad_groups) & 3u)) return W12_ERR_ALIGN;
+    return status_of(w12::launch_pack(w, N, K, p0, p1, p2, meta, bad_groups,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+int w12_unpack(const void* p0, const void* p1, const void* p2, const uint8_t* meta, int64_t N,
+               int64_t K, uint16_t* w_out, void* stream) {
+    if (!p0 || !p1 || !p2 || !meta || !w_out) return W12_ERR_NULL;
+    if (int rc = check_weight_shape(N, K)) return rc;
+    if (!aligned16(p0) || !aligned16(p1) || !aligned16(p2) || !aligned16(w_out)) return W12_ERR_ALIGN;
+    return status_of(w12::launch_unpack(p0, p1, p2, meta, N, K, w_out,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+int w12_gemm(const uint16_t* x, int64_t M, int64_t ldx, const void* p0, const void* p1,
+             const void* p2, const uint8_t* meta, int64_t N, int64_t K, void* y, int64_t ldy,
+             int y_type, void* stream) {
+    if (!p0 || !p1 || !p2 || !meta) return W12_ERR_NULL;
+    if (int rc = check_gemm_common(x, M, ldx, N, K, y, ldy, y_type)) return rc;
+    if (!aligned16(p0) || !aligned16(p1) || !aligned16(p2)) return W12_ERR_ALIGN;
+    w12::GemmArgs a = make_args(x, M, ldx, N, K, y, ldy, y_type);
+    a.p0 = static_cast<const uint8_t*>(p0);
+    a.p1 = static_cast<const uint8_t*>(p1);
+    a.p2 = static_cast<const uint8_t*>(p2);
+    a.meta = meta;
+    const w12::Tiling t = w12::choose_tiling((int)M, N, K);
+    return status_of(w12::launch_gemm(a, t, true, static_cast<hipStream_t>(stream)));
+}
+
+int bf16_gemm(const uint16_t* x, int64_t M, int64_t ldx, const uint16_t* w, int64_t N, int64_t K,
+              void* y, int64_t ldy, int y_type, void* stream) {
+    if (!w) return W12_ERR_NULL;
+    if (int rc = check_gemm_common(x, M, ldx, N, K, y, ldy, y_type)) return rc;
+    if (!aligned16(w)) return W12_ERR_ALIGN;
+    w12::GemmArgs a = make_args(x, M, ldx, N, K, y, ldy, y_type);
+    a.w = w;
+    const w12::Tiling t = w12::choose_tiling((int)M, N, K);
+    return status_of(w12::launch_gemm(a, t, false, static_cast<hipStream_t>(stream)));
+}
+
+const char* w12_gemm_variant(int64_t M, int64_t N, int64_t K, int is_w12) {
+    if (check_weight_shape(N, K) != W12_OK || M < 1 || M > W12_MAX_M) return nullptr;
+    return w12::tiling_name(w12::choose_tiling((int)M, N, K), is_w12 != 0);
+}
+
+}  // extern "C"

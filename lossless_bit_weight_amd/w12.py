@@ -1,0 +1,260 @@
+"""Python binding of libw12.so (include/w12.h): argument marshalling only.
+
+Every function here hands torch tensors' device pointers and torch's current
+HIP stream to the C ABI; all arithmetic runs in the library's HIP kernels.
+There is no fallback: if the library is missing or the tensors are not on
+the GPU, the call raises.
+
+BF16 tensors may be passed as torch.bfloat16, torch.int16 or torch.uint16
+(the bit pattern is what crosses the boundary).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libw12.so")
+HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "w12.h")
+
+GROUP = 128
+MAX_M = 32
+OUT_BF16 = 0
+OUT_F32 = 1
+
+STATUS = {
+    0: "W12_OK", -1: "W12_ERR_NULL", -2: "W12_ERR_SHAPE", -3: "W12_ERR_ALIGN",
+    -4: "W12_ERR_DTYPE", -6: "W12_ERR_UNSUPPORTED", -7: "W12_ERR_HIP",
+}
+
+
+class W12Error(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__("%s: %s (%s)" % (what, STATUS.get(status, status),
+                                          w12_status_string(status)))
+
+
+class W12UnencodableError(ValueError):
+    """Raised by pack(..., strict=True) when some group cannot round-trip."""
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libw12.so (after torch, so the library binds to torch's HIP runtime)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            "libw12.so is not built (%s); run `python -m lossless_bit_weight_amd.build`" % LIB_PATH)
+    L = ctypes.CDLL(LIB_PATH)
+    i64, i32, p = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
+    L.w12_abi_version.argtypes = []
+    L.w12_abi_version.restype = i32
+    L.w12_status_string.argtypes = [i32]
+    L.w12_status_string.restype = ctypes.c_char_p
+    L.w12_plane_bytes.argtypes = [i64, i64]
+    L.w12_plane_bytes.restype = ctypes.c_size_t
+    L.w12_meta_bytes.argtypes = [i64, i64]
+    L.w12_meta_bytes.restype = ctypes.c_size_t
+    L.w12_pack.argtypes = [p, i64, i64, p, p, p, p, p, p]
+    L.w12_pack.restype = i32
+    L.w12_unpack.argtypes = [p, p, p, p, i64, i64, p, p]
+    L.w12_unpack.restype = i32
+    L.w12_gemm.argtypes = [p, i64, i64, p, p, p, p, i64, i64, p, i64, i32, p]
+    L.w12_gemm.restype = i32
+    L.bf16_gemm.argtypes = [p, i64, i64, p, i64, i64, p, i64, i32, p]
+    L.bf16_gemm.restype = i32
+    L.w12_gemm_variant.argtypes = [i64, i64, i64, i32]
+    L.w12_gemm_variant.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def header_functions() -> list[str]:
+    """Names of the functions include/w12.h declares."""
+    with open(HEADER_PATH) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)
+
+
+# ---- marshalling helpers ---------------------------------------------------
+
+_BF16_TYPES = (torch.bfloat16, torch.int16, torch.uint16)
+
+
+def _dev_ptr(t: torch.Tensor, what: str) -> int:
+    if not t.is_cuda:
+        raise ValueError("%s must be a GPU tensor" % what)
+    return t.data_ptr()
+
+
+def _stream() -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _check(status: int, what: str) -> None:
+    if status != 0:
+        raise W12Error(status, what)
+
+
+def _bf16_2d(t: torch.Tensor, what: str) -> torch.Tensor:
+    if t.dtype not in _BF16_TYPES:
+        raise TypeError("%s must hold BF16 bits (bfloat16/int16/uint16), got %s" % (what, t.dtype))
+    if t.dim() != 2:
+        raise ValueError("%s must be 2-D" % what)
+    return t
+
+
+# ---- the C ABI, by name ----------------------------------------------------
+
+def w12_abi_version() -> int:
+    return int(lib().w12_abi_version())
+
+
+def w12_status_string(status: int) -> str:
+    return lib().w12_status_string(int(status)).decode()
+
+
+def w12_plane_bytes(N: int, K: int) -> int:
+    return int(lib().w12_plane_bytes(int(N), int(K)))
+
+
+def w12_meta_bytes(N: int, K: int) -> int:
+    return int(lib().w12_meta_bytes(int(N), int(K)))
+
+
+def w12_gemm_variant(M: int, N: int, K: int, is_w12: bool = True) -> str | None:
+    r = lib().w12_gemm_variant(int(M), int(N), int(K), int(bool(is_w12)))
+    return None if r is None else r.decode()
+
+
+@dataclass
+class W12Weight:
+    """A packed [N, K] weight: three uint8 planes [N, K/2] and meta [N, K/128]."""
+    p0: torch.Tensor
+    p1: torch.Tensor
+    p2: torch.Tensor
+    meta: torch.Tensor
+    N: int
+    K: int
+
+    @property
+    def nbytes(self) -> int:
+        return 3 * self.p0.numel() + self.meta.numel()
+
+
+def empty_weight(N: int, K: int, device="cuda") -> W12Weight:
+    pb, mb = w12_plane_bytes(N, K), w12_meta_bytes(N, K)
+    if pb == 0:
+        raise W12Error(-2, "empty_weight(%d, %d)" % (N, K))
+    mk = lambda: torch.empty((N, K // 2), dtype=torch.uint8, device=device)
+    return W12Weight(mk(), mk(), mk(), torch.empty((N, K // GROUP), dtype=torch.uint8,
+                                                   device=device), N, K)
+
+
+def w12_pack(w: torch.Tensor, out: W12Weight | None = None,
+             bad_groups: torch.Tensor | None = None) -> W12Weight:
+    """Pack BF16 [N, K] (contiguous) into W12.  If `bad_groups` (int32/uint32
+    GPU tensor with one element) is given, the count of unencodable groups is
+    added to it on the stream."""
+    w = _bf16_2d(w, "w")
+    if not w.is_contiguous():
+        raise ValueError("w must be contiguous")
+    N, K = w.shape
+    if out is None:
+        out = empty_weight(N, K, w.device)
+    bad_ptr = None
+    if bad_groups is not None:
+        if bad_groups.dtype not in (torch.int32, torch.uint32) or bad_groups.numel() < 1:
+            raise TypeError("bad_groups must be a 32-bit integer GPU tensor")
+        bad_ptr = _dev_ptr(bad_groups, "bad_groups")
+    _check(lib().w12_pack(_dev_ptr(w, "w"), N, K, _dev_ptr(out.p0, "p0"), _dev_ptr(out.p1, "p1"),
+                          _dev_ptr(out.p2, "p2"), _dev_ptr(out.meta, "meta"), bad_ptr, _stream()),
+           "w12_pack")
+    return out
+
+
+def pack(w: torch.Tensor, strict: bool = False) -> tuple[W12Weight, int]:
+    """Pack and return (container, number of unencodable groups).  Reading the
+    count synchronises the stream; with strict=True a non-zero count raises."""
+    bad = torch.zeros(1, dtype=torch.int32, device=w.device)
+    out = w12_pack(w, bad_groups=bad)
+    n_bad = int(bad.item())
+    if strict and n_bad:
+        raise W12UnencodableError("%d of %d groups cannot be stored losslessly"
+                                  % (n_bad, w.numel() // GROUP))
+    return out, n_bad
+
+
+def w12_unpack(wt: W12Weight, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Decode a container back to BF16 [N, K] (torch.bfloat16)."""
+    if out is None:
+        out = torch.empty((wt.N, wt.K), dtype=torch.bfloat16, device=wt.p0.device)
+    _bf16_2d(out, "out")
+    _check(lib().w12_unpack(_dev_ptr(wt.p0, "p0"), _dev_ptr(wt.p1, "p1"), _dev_ptr(wt.p2, "p2"),
+                            _dev_ptr(wt.meta, "meta"), wt.N, wt.K, _dev_ptr(out, "out"), _stream()),
+           "w12_unpack")
+    return out
+
+
+def _out_tensor(M: int, N: int, out_dtype: torch.dtype, device) -> tuple[torch.Tensor, int]:
+    if out_dtype == torch.float32:
+        return torch.empty((M, N), dtype=torch.float32, device=device), OUT_F32
+    if out_dtype == torch.bfloat16:
+        return torch.empty((M, N), dtype=torch.bfloat16, device=device), OUT_BF16
+    raise TypeError("out_dtype must be torch.float32 or torch.bfloat16")
+
+
+def _y_args(y: torch.Tensor) -> tuple[int, int]:
+    if y.dim() != 2 or y.stride(1) != 1:
+        raise ValueError("y must be 2-D with unit column stride")
+    if y.dtype == torch.float32:
+        return y.stride(0), OUT_F32
+    if y.dtype in _BF16_TYPES:
+        return y.stride(0), OUT_BF16
+    raise TypeError("y must be float32 or BF16")
+
+
+def _x_args(x: torch.Tensor) -> tuple[int, int]:
+    x = _bf16_2d(x, "x")
+    if x.stride(1) != 1:
+        raise ValueError("x must have unit column stride")
+    return x.shape[0], x.stride(0)
+
+
+def w12_gemm(x: torch.Tensor, wt: W12Weight, out_dtype: torch.dtype = torch.float32,
+             y: torch.Tensor | None = None) -> torch.Tensor:
+    """y[m, n] = sum_k x[m, k] W[n, k] with W rebuilt from the container."""
+    M, ldx = _x_args(x)
+    if y is None:
+        y, _ = _out_tensor(M, wt.N, out_dtype, x.device)
+    ldy, yt = _y_args(y)
+    _check(lib().w12_gemm(_dev_ptr(x, "x"), M, ldx, _dev_ptr(wt.p0, "p0"), _dev_ptr(wt.p1, "p1"),
+                          _dev_ptr(wt.p2, "p2"), _dev_ptr(wt.meta, "meta"), wt.N, wt.K,
+                          _dev_ptr(y, "y"), ldy, yt, _stream()), "w12_gemm")
+    return y
+
+
+def bf16_gemm(x: torch.Tensor, w: torch.Tensor, out_dtype: torch.dtype = torch.float32,
+              y: torch.Tensor | None = None) -> torch.Tensor:
+    """The same-tiling control: y = x . W^T with W read as plain BF16 [N, K]."""
+    M, ldx = _x_args(x)
+    w = _bf16_2d(w, "w")
+    if not w.is_contiguous():
+        raise ValueError("w must be contiguous")
+    N, K = w.shape
+    if y is None:
+        y, _ = _out_tensor(M, N, out_dtype, x.device)
+    ldy, yt = _y_args(y)
+    _check(lib().bf16_gemm(_dev_ptr(x, "x"), M, ldx, _dev_ptr(w, "w"), N, K, _dev_ptr(y, "y"),
+                           ldy, yt, _stream()), "bf16_gemm")
+    return y

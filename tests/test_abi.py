@@ -1,0 +1,83 @@
+"""The C-ABI library without a GPU: it loads, exports every function the
+header declares, and rejects bad arguments on the host before any launch."""
+import ctypes
+
+import pytest
+
+from lossless_bit_weight_amd import w12
+
+P = ctypes.c_void_p
+A16 = P(4096)       # a non-null, 16-byte aligned stand-in (never dereferenced:
+MIS = P(4098)       # every call below fails validation before any launch)
+
+
+def test_loads_and_exports_every_declared_symbol():
+    L = w12.lib()
+    names = w12.header_functions()
+    assert set(names) >= {"w12_pack", "w12_unpack", "w12_gemm", "bf16_gemm",
+                          "w12_plane_bytes", "w12_meta_bytes", "w12_status_string",
+                          "w12_abi_version", "w12_gemm_variant"}
+    for n in names:
+        assert hasattr(L, n), n
+    assert w12.w12_abi_version() == 1
+
+
+def test_sizes():
+    assert w12.w12_plane_bytes(7168, 5120) == 7168 * 5120 // 2
+    assert w12.w12_meta_bytes(7168, 5120) == 7168 * 40
+    assert w12.w12_plane_bytes(3, 100) == 0
+    assert w12.w12_meta_bytes(0, 128) == 0
+
+
+def test_status_strings():
+    for s in (0, -1, -2, -3, -4, -6, -7, 99):
+        assert isinstance(w12.w12_status_string(s), str) and w12.w12_status_string(s)
+
+
+def _gemm(**kw):
+    a = dict(x=A16, M=1, ldx=512, p0=A16, p1=A16, p2=A16, meta=A16, N=64, K=512, y=A16,
+             ldy=64, yt=0)
+    a.update(kw)
+    return w12.lib().w12_gemm(a["x"], a["M"], a["ldx"], a["p0"], a["p1"], a["p2"], a["meta"],
+                              a["N"], a["K"], a["y"], a["ldy"], a["yt"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), -1), (dict(p1=None), -1), (dict(meta=None), -1), (dict(y=None), -1),
+    (dict(K=500), -2), (dict(K=0), -2), (dict(N=0), -2), (dict(M=0), -2),
+    (dict(ldx=256), -2), (dict(ldy=63), -2),
+    (dict(M=33), -6), (dict(yt=2), -4),
+    (dict(x=MIS), -3), (dict(ldx=516), -3), (dict(p2=MIS), -3),
+    (dict(yt=1, y=P(4098)), -3),
+])
+def test_gemm_rejects(kw, status):
+    assert _gemm(**kw) == status
+
+
+def test_bf16_gemm_rejects():
+    L = w12.lib()
+    assert L.bf16_gemm(A16, 1, 512, None, 64, 512, A16, 64, 0, None) == -1
+    assert L.bf16_gemm(A16, 1, 512, MIS, 64, 512, A16, 64, 0, None) == -3
+    assert L.bf16_gemm(A16, 40, 512, A16, 64, 512, A16, 64, 0, None) == -6
+    assert L.bf16_gemm(A16, 1, 512, A16, 64, 384 + 1, A16, 64, 0, None) == -2
+
+
+def test_pack_unpack_reject():
+    L = w12.lib()
+    assert L.w12_pack(None, 4, 128, A16, A16, A16, A16, None, None) == -1
+    assert L.w12_pack(A16, 4, 130, A16, A16, A16, A16, None, None) == -2
+    assert L.w12_pack(MIS, 4, 128, A16, A16, A16, A16, None, None) == -3
+    assert L.w12_pack(A16, 4, 128, A16, A16, A16, A16, P(4097), None) == -3
+    assert L.w12_unpack(A16, A16, A16, None, 4, 128, A16, None) == -1
+    assert L.w12_unpack(A16, A16, A16, A16, -1, 128, A16, None) == -2
+    assert L.w12_unpack(A16, A16, A16, A16, 4, 128, MIS, None) == -3
+
+
+def test_variant_selection():
+    assert w12.w12_gemm_variant(1, 7168, 5120).startswith("w12_gemv_m1_")
+    assert w12.w12_gemm_variant(8, 7168, 5120, False).startswith("bf16_gemv_m8_")
+    assert w12.w12_gemm_variant(9, 7168, 5120).startswith("w12_mfma_mt16_")
+    assert w12.w12_gemm_variant(16, 34816, 5120).startswith("w12_mfma_mt16_")
+    assert w12.w12_gemm_variant(17, 5120, 17408).startswith("w12_mfma_mt32_")
+    assert w12.w12_gemm_variant(33, 5120, 17408) is None
+    assert w12.w12_gemm_variant(1, 5120, 100) is None

@@ -1,0 +1,174 @@
+"""GPU parity for w12_gemm and the bf16_gemm control.
+
+Reference: the oracle's fp64 y = x . W^T on the oracle's own pack/unpack of
+the same raw weights (the GEMM the pages describe rebuilds W bit-exactly
+inside the kernel: HotRepo digest of StargazerX0/SpecPilot, project
+introduction, batch 1-32).  Pass rule for fp32 outputs, per element:
+|y_gpu - y_ref| <= 1e-3 ||x_m||_2 ||w_n||_2 + 1e-6.  BF16 outputs must equal
+the round-to-nearest-even of the same kernel's fp32 output bit for bit, and
+w12_gemm must equal bf16_gemm on the unpacked weights bit for bit (same
+kernels, same summation order; only the weight fetch differs).
+"""
+import numpy as np
+import pytest
+import torch
+
+from lossless_bit_weight_amd import inputs, w12
+from tests.gpu_util import assert_gemm_close, require_gpu, to_dev, to_host_u16
+
+pytestmark = pytest.mark.gpu
+
+M_SWEEP = [1, 2, 3, 4, 5, 7, 8, 9, 12, 15, 16, 17, 24, 31, 32]
+
+
+class Prepared:
+    """Raw weights on the host; the GPU container packed from them and its
+    unpacked BF16 tensor (the control's operand)."""
+
+    def __init__(self, raw: np.ndarray):
+        require_gpu()
+        self.raw = raw
+        self.N, self.K = raw.shape
+        self.wt = w12.w12_pack(to_dev(raw))
+        self.w_bf16 = w12.w12_unpack(self.wt)
+        torch.cuda.synchronize()
+
+    def ref_rows(self, oracle, rows):
+        """Oracle projection of the raw rows (groups never span rows)."""
+        sub = np.ascontiguousarray(self.raw[rows])
+        p0, p1, p2, meta, _ = oracle.pack(sub)
+        return oracle.unpack(p0, p1, p2, meta, sub.shape[0], self.K)
+
+
+_cache = {}
+
+
+def prepared(name_or_shape) -> Prepared:
+    if name_or_shape not in _cache:
+        if isinstance(name_or_shape, str):
+            raw = inputs.CASES[name_or_shape].weights_raw()
+        else:
+            N, K = name_or_shape
+            raw = inputs.gaussian_bf16((N, K), 0.02, 7 * N + K)
+        _cache[name_or_shape] = Prepared(raw)
+    return _cache[name_or_shape]
+
+
+def _sample_rows(N, n=384, seed=0):
+    rng = np.random.default_rng(seed)
+    rows = set(range(min(64, N))) | set(range(max(0, N - 64), N))
+    rows |= set(rng.choice(N, size=min(n, N), replace=False).tolist())
+    return np.array(sorted(rows))
+
+
+def _run_both(x_bits, P: Prepared, out=torch.float32):
+    xd = to_dev(x_bits)
+    y12 = w12.w12_gemm(xd, P.wt, out)
+    y16 = w12.bf16_gemm(xd, P.w_bf16, out)
+    torch.cuda.synchronize()
+    return y12, y16
+
+
+def _check(oracle, P: Prepared, x_bits, rows, what):
+    print("gemm parity:", what, flush=True)
+    y12, y16 = _run_both(x_bits, P)
+    y12h = y12.cpu().numpy()
+    y16h = y16.cpu().numpy()
+    assert np.array_equal(y12h.view(np.uint32), y16h.view(np.uint32)), what + ": w12 != bf16 bitwise"
+    w_ref = P.ref_rows(oracle, rows)
+    y_ref = oracle.gemm_bf16_f64(x_bits, w_ref)
+    tol = oracle.tolerance(x_bits, w_ref)
+    assert_gemm_close(y12h[:, rows], y_ref, tol, what)
+    return y12
+
+
+@pytest.mark.parametrize("M", list(range(1, 33)))
+def test_tiny_every_m(oracle, M):
+    P = prepared("tiny")
+    x = inputs.TINY.activations(M)
+    _check(oracle, P, x, np.arange(P.N), "tiny M=%d" % M)
+
+
+@pytest.mark.parametrize("shape", [(1000, 640), (37, 128), (4099, 384), (130, 1152), (17, 2560)])
+@pytest.mark.parametrize("M", [1, 3, 8, 9, 16, 17, 32])
+def test_ragged_shapes(oracle, shape, M):
+    P = prepared(shape)
+    x = inputs.gaussian_bf16((M, shape[1]), 1.0, 11 * M + shape[1])
+    _check(oracle, P, x, np.arange(P.N), "ragged %s M=%d" % (shape, M))
+
+
+@pytest.mark.parametrize("name", ["qkv", "gate_up", "down"])
+@pytest.mark.parametrize("M", [1, 2, 4, 8, 16, 32])
+def test_workloads_sampled(oracle, name, M):
+    case = inputs.CASES[name]
+    P = prepared(name)
+    x = case.activations(M)
+    _check(oracle, P, x, _sample_rows(P.N, seed=M), "%s M=%d" % (name, M))
+
+
+@pytest.mark.parametrize("M", [1, 5, 8, 16, 32])
+def test_bf16_output_is_rounded_fp32(M):
+    P = prepared("tiny")
+    xd = to_dev(inputs.TINY.activations(M))
+    for fn, w in ((w12.w12_gemm, P.wt), (w12.bf16_gemm, P.w_bf16)):
+        yf = fn(xd, w, torch.float32)
+        yb = fn(xd, w, torch.bfloat16)
+        torch.cuda.synchronize()
+        expect = yf.cpu().to(torch.bfloat16).view(torch.int16)
+        assert torch.equal(yb.cpu().view(torch.int16), expect)
+
+
+@pytest.mark.parametrize("M", [1, 8, 16, 32])
+def test_strided_x_and_y(oracle, M):
+    P = prepared((1000, 640))
+    x_full = inputs.gaussian_bf16((M, 640 + 64), 1.0, 5 + M)
+    xd = to_dev(x_full)[:, :640]
+    y_full = torch.full((M, 1000 + 24), -7.0, dtype=torch.float32, device="cuda")
+    y = y_full[:, :1000]
+    w12.w12_gemm(xd, P.wt, y=y)
+    torch.cuda.synchronize()
+    x = np.ascontiguousarray(x_full[:, :640])
+    w_ref = P.ref_rows(oracle, np.arange(1000))
+    assert_gemm_close(y.cpu().numpy(), oracle.gemm_bf16_f64(x, w_ref),
+                      oracle.tolerance(x, w_ref), "strided M=%d" % M)
+    assert torch.all(y_full[:, 1000:] == -7.0)
+
+
+@pytest.mark.parametrize("M", [1, 4, 8, 16, 32])
+def test_one_hot_rows_rebuild_weights_exactly(oracle, M):
+    """x rows = unit vectors: y[m, :] is column k_m of W, bit for bit, i.e.
+    the in-register reassembly reproduces the BF16 weights exactly."""
+    P = prepared("qkv")
+    K = P.K
+    ks = np.random.default_rng(M).choice(K, size=M, replace=False)
+    x = np.zeros((M, K), np.uint16)
+    x[np.arange(M), ks] = 0x3F80
+    y12, y16 = _run_both(x, P)
+    rows = np.arange(P.N)
+    w_ref = P.ref_rows(oracle, rows)
+    expect = oracle.bf16_bits_to_f64(w_ref[:, ks].T).astype(np.float32)
+    assert np.array_equal(y12.cpu().numpy().view(np.uint32) & 0x7FFFFFFF,
+                          expect.view(np.uint32) & 0x7FFFFFFF)
+    assert np.array_equal(y12.cpu().numpy(), expect)
+
+
+def test_ieee_specials(oracle):
+    require_gpu()
+    K = 256
+    w = np.zeros((6, K), np.uint16)
+    w[0, 5] = 0x7F80            # +Inf
+    w[1, 6] = 0x7FC0            # NaN
+    w[2, :] = 0x3F80
+    w[3, 7] = 0xFF80            # -Inf
+    P = Prepared(w)
+    x = np.zeros((2, K), np.uint16)
+    x[0, 5] = 0xBF80
+    x[0, 6] = 0x3F80
+    x[0, 7] = 0x3F80
+    for out in (torch.float32, torch.bfloat16):
+        y12, y16 = _run_both(x, P, out)
+        yh = y12.float().cpu().numpy().astype(np.float64)
+        ref = oracle.gemm_bf16_f64(x, w)
+        assert np.array_equal(np.isnan(yh), np.isnan(ref))
+        fin = ~np.isnan(ref)
+        assert np.array_equal(yh[fin], ref[fin])
