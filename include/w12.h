@@ -16,9 +16,17 @@
  *   stored   = exponents {0, 1} and [2*beta+2, 2*beta+15] (4096 values);
  *   nibbles  = P0 = v[3:0], P1 = v[7:4], P2 = sign<<3 | h with h = 0 for
  *              E <= 1, else h = (E >> 1) - beta (1..7);
- *   layout   = plane p is u8[N][K/2]; element k of row n is in byte
- *              n*K/2 + 4*(k/8) + (k%8)%4, low nibble if k%8 < 4, else high;
- *   meta     = u8[N][K/128]: beta | 0x80 if the group is unencodable.
+ *   layout   = rows are padded to Np = N rounded up to 16 (W12_TILE_ROWS);
+ *              each plane is Np*K/2 bytes of 1 KB blocks, one per (16-row
+ *              tile T = n/16, group g = k/128), ordered by (T, g); in a
+ *              block, the 16-byte piece L = 16*q + c (q = 0..3, c = n%16)
+ *              holds row n and, in its dword b (0..3), the 8 weights
+ *              k = 128*g + 32*b + 8*q + e (e = 0..7): byte e%4 of the dword,
+ *              low nibble for e < 4, high nibble for e >= 4;
+ *   meta     = Np*K/128 bytes, 16 per (T, g), byte c = beta | 0x80 if the
+ *              group of row 16*T + c is unencodable.
+ * This order makes every load of a GEMM wave read 1 KB of contiguous memory
+ * (one block of one plane), for both the GEMV and the MFMA kernels.
  *
  * A group holding an exponent in [2, 2*beta+1] cannot be stored exactly: the
  * packer flags it (meta bit 7), counts it, and stores that element as the
@@ -49,6 +57,7 @@ extern "C" {
 
 #define W12_ABI_VERSION 1
 #define W12_GROUP 128
+#define W12_TILE_ROWS 16
 #define W12_MAX_M 32
 
 typedef enum {
@@ -72,17 +81,25 @@ int w12_abi_version(void);
 /* Static, never-NULL description of a status code. */
 const char *w12_status_string(int status);
 
-/* Bytes of ONE nibble plane for an [N, K] weight: N*K/2 (0 on bad shape). */
+/* Rows of the container: N rounded up to a multiple of 16 (0 if N < 1). */
+int64_t w12_padded_rows(int64_t N);
+
+/* Bytes of ONE nibble plane for an [N, K] weight: Np*K/2, i.e. exactly 0.75x
+ * the BF16 bytes / 3 when N % 16 == 0 (0 on bad shape). */
 size_t w12_plane_bytes(int64_t N, int64_t K);
 
-/* Bytes of the metadata array: N*K/128 (0 on bad shape). */
+/* Bytes of the metadata array: Np*K/128 (0 on bad shape). */
 size_t w12_meta_bytes(int64_t N, int64_t K);
+
+/* Bytes of a BF16 weight in the control layout: Np*K*2 (0 on bad shape). */
+size_t w12_bf16_tiled_bytes(int64_t N, int64_t K);
 
 /*
  * w12_pack -- BF16 [N, K] (row-major, contiguous) -> three planes + meta.
  * The format's encoder (a1): one 128-weight group at a time, integer only.
  *   w          : device, N*K BF16 words, 16-byte aligned.
- *   p0, p1, p2 : device outputs, w12_plane_bytes(N, K) bytes each, 16-byte aligned.
+ *   p0, p1, p2 : device outputs, w12_plane_bytes(N, K) bytes each, 16-byte
+ *                aligned; padding rows are written as zeros.
  *   meta       : device output, w12_meta_bytes(N, K) bytes.
  *   bad_groups : device uint32 counter or NULL; the number of unencodable
  *                groups is ADDED to it (the caller zeroes it beforehand).
@@ -112,8 +129,9 @@ int w12_unpack(const void *p0, const void *p1, const void *p2,
  *   p0..meta: the container of an [N, K] weight as written by w12_pack.
  *   y      : device output [M, N], row stride ldy elements (ldy >= N),
  *            BF16 bits (2-byte aligned) or fp32 (4-byte aligned) per y_type.
- * M <= 8 runs a wavefront-reduction GEMV; 9 <= M <= 32 runs bf16 MFMA with
- * x padded to 16 or 32 rows.
+ * By default M <= 4 runs a wavefront-reduction GEMV (v_dot2c_f32_bf16) and
+ * 5 <= M <= 32 runs bf16 MFMA with x padded to 16 or 32 rows (measured
+ * crossover); w12_gemm_ex selects either explicitly (GEMV up to M = 8).
  * Errors: W12_ERR_NULL, W12_ERR_SHAPE, W12_ERR_ALIGN, W12_ERR_DTYPE,
  *         W12_ERR_UNSUPPORTED (M > 32), W12_ERR_HIP.
  */
@@ -123,15 +141,65 @@ int w12_gemm(const uint16_t *x, int64_t M, int64_t ldx,
              void *y, int64_t ldy, int y_type, void *stream);
 
 /*
- * bf16_gemm -- the control: the same kernels, tiling and summation order as
- * w12_gemm, with W read as plain BF16 (a8).  For W = unpack(pack(W)) the two
- * calls return bitwise identical y.
- *   w : device BF16 [N, K], row-major contiguous, 16-byte aligned.
+ * w12_bf16_tile -- row-major BF16 [N, K] -> the layout of the BF16 control
+ * (a8): the same (tile, group) blocks and lane order as the W12 planes,
+ * with whole BF16 words: block (T, g) of 2048 words, 1 KB sub-block b, lane
+ * L's 8 words k = 128*g + 32*b + 8*q + e in natural order; padding rows zero.
+ *   w       : device, N*K words, 16-byte aligned.
+ *   w_tiled : device output, w12_bf16_tiled_bytes(N, K) bytes, 16-byte aligned.
+ * Errors: W12_ERR_NULL, W12_ERR_SHAPE, W12_ERR_ALIGN, W12_ERR_HIP.
+ */
+int w12_bf16_tile(const uint16_t *w, int64_t N, int64_t K, uint16_t *w_tiled,
+                  void *stream);
+
+/*
+ * bf16_gemm -- the control: the same kernels, tiling, memory access order and
+ * summation order as w12_gemm, with W read as plain BF16 words (a8).  For
+ * w_tiled = w12_bf16_tile(unpack(pack(W))) the two calls return bitwise
+ * identical y.
+ *   w_tiled : device, the [N, K] weight in the control layout (see
+ *             w12_bf16_tile), 16-byte aligned.
  *   other arguments and errors as w12_gemm.
  */
 int bf16_gemm(const uint16_t *x, int64_t M, int64_t ldx,
-              const uint16_t *w, int64_t N, int64_t K,
+              const uint16_t *w_tiled, int64_t N, int64_t K,
               void *y, int64_t ldy, int y_type, void *stream);
+
+/*
+ * Explicit tiling, for callers that tune the kernels on their own shapes.
+ *   kind  : 0 = wavefront-reduction GEMV (M <= 8), 1 = bf16 MFMA (M <= 32).
+ *   r     : 16-row weight tiles per wave (1, 2).
+ *   kw    : waves of a 256-thread workgroup that split K (1, 2, 4).
+ *   depth : 128-weight groups each wave keeps in flight
+ *           (r = 1: 2, 4 or 8; r = 2: 2 or 4).
+ * When x does not fit LDS at once it is streamed in chunks; some kw x depth
+ * combinations then need more than 64 KB of LDS and are rejected.
+ * The summation order depends on the tiling; w12 and bf16 kernels with the
+ * same tiling sum in the same order.
+ */
+typedef struct {
+    int32_t kind;
+    int32_t r;
+    int32_t kw;
+    int32_t depth;
+} w12_tiling_t;
+
+/* The tiling w12_gemm / bf16_gemm use for this shape.  Returns W12_OK, or
+ * W12_ERR_NULL / W12_ERR_SHAPE / W12_ERR_UNSUPPORTED. */
+int w12_default_tiling(int64_t M, int64_t N, int64_t K, w12_tiling_t *out);
+
+/* w12_gemm / bf16_gemm with an explicit tiling (NULL = the default).
+ * Additional error: W12_ERR_UNSUPPORTED for a tiling that is not built or
+ * does not fit M (GEMV needs M <= 8). */
+int w12_gemm_ex(const uint16_t *x, int64_t M, int64_t ldx,
+                const void *p0, const void *p1, const void *p2,
+                const uint8_t *meta, int64_t N, int64_t K,
+                void *y, int64_t ldy, int y_type, const w12_tiling_t *tiling,
+                void *stream);
+int bf16_gemm_ex(const uint16_t *x, int64_t M, int64_t ldx,
+                 const uint16_t *w_tiled, int64_t N, int64_t K,
+                 void *y, int64_t ldy, int y_type, const w12_tiling_t *tiling,
+                 void *stream);
 
 /*
  * Name of the kernel variant w12_gemm / bf16_gemm launch for this shape

@@ -18,7 +18,12 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libw12.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
-SOURCES = ["w12_api.hip", "w12_pack.hip", "w12_gemm.hip"]
+# (source, object name, extra defines): the kernel instantiation unit is
+# compiled once per x height so the build runs in parallel.
+SOURCES = [("w12_api.hip", "w12_api", []), ("w12_pack.hip", "w12_pack", []),
+           ("w12_gemm.hip", "w12_gemm", [])]
+SOURCES += [("w12_gemm_inst.hip", "w12_gemv_m%d" % m, ["-DW12_INST_M=%d" % m]) for m in range(1, 9)]
+SOURCES += [("w12_gemm_inst.hip", "w12_mfma", ["-DW12_INST_MFMA"])]
 ARCH = os.environ.get("W12_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -29,9 +34,10 @@ FLAGS = [
 ]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(item) -> str:
+    src, name, defines = item
+    obj = os.path.join(BUILD_DIR, name + ".o")
+    cmd = [HIPCC, *FLAGS, *defines, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     # the host pass does not know the device-only feature flag: drop that note
     err = "\n".join(l for l in r.stderr.splitlines()
@@ -45,7 +51,8 @@ def _compile(src: str) -> str:
 
 def build() -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+    workers = max(1, min(len(SOURCES), os.cpu_count() or 1))
+    with ThreadPoolExecutor(max_workers=workers) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = OUT + ".tmp%d" % os.getpid()
     subprocess.check_call([HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", *objs, "-o", tmp])

@@ -16,7 +16,7 @@ constexpr int64_t kMaxElems = (int64_t)1 << 40;
 
 int check_weight_shape(int64_t N, int64_t K) {
     if (N < 1 || K < W12_GROUP || K % W12_GROUP != 0) return W12_ERR_SHAPE;
-    if (N > kMaxElems / K) return W12_ERR_SHAPE;
+    if (N + W12_TILE_ROWS > kMaxElems / K) return W12_ERR_SHAPE;
     return W12_OK;
 }
 
@@ -63,20 +63,34 @@ const char* w12_status_string(int status) {
         case W12_ERR_SHAPE: return "bad shape (need N >= 1, K a positive multiple of 128, M >= 1, ldx >= K, ldy >= N)";
         case W12_ERR_ALIGN: return "misaligned pointer or leading dimension (16-byte tensors, ldx % 8 == 0)";
         case W12_ERR_DTYPE: return "unknown output type";
-        case W12_ERR_UNSUPPORTED: return "unsupported size (M > 32)";
+        case W12_ERR_UNSUPPORTED: return "unsupported size or tiling (M > 32, or a tiling that is not built for this shape)";
         case W12_ERR_HIP: return "HIP launch failed";
         default: return "unknown status";
     }
 }
 
+int64_t w12_padded_rows(int64_t N) { return N < 1 ? 0 : (N + W12_TILE_ROWS - 1) / W12_TILE_ROWS * W12_TILE_ROWS; }
+
 size_t w12_plane_bytes(int64_t N, int64_t K) {
     if (check_weight_shape(N, K) != W12_OK) return 0;
-    return (size_t)(N * K / 2);
+    return (size_t)(w12_padded_rows(N) * K / 2);
 }
 
 size_t w12_meta_bytes(int64_t N, int64_t K) {
     if (check_weight_shape(N, K) != W12_OK) return 0;
-    return (size_t)(N * (K / W12_GROUP));
+    return (size_t)(w12_padded_rows(N) * (K / W12_GROUP));
+}
+
+size_t w12_bf16_tiled_bytes(int64_t N, int64_t K) {
+    if (check_weight_shape(N, K) != W12_OK) return 0;
+    return (size_t)(w12_padded_rows(N) * K * 2);
+}
+
+int w12_bf16_tile(const uint16_t* w, int64_t N, int64_t K, uint16_t* w_tiled, void* stream) {
+    if (!w || !w_tiled) return W12_ERR_NULL;
+    if (int rc = check_weight_shape(N, K)) return rc;
+    if (!aligned16(w) || !aligned16(w_tiled)) return W12_ERR_ALIGN;
+    return status_of(w12::launch_bf16_tile(w, N, K, w_tiled, static_cast<hipStream_t>(stream)));
 }
 
 int w12_pack(const uint16_t* w, int64_t N, int64_t K, void* p0, void* p1, void* p2, uint8_t* meta,
@@ -98,30 +112,74 @@ int w12_unpack(const void* p0, const void* p1, const void* p2, const uint8_t* me
                                         static_cast<hipStream_t>(stream)));
 }
 
-int w12_gemm(const uint16_t* x, int64_t M, int64_t ldx, const void* p0, const void* p1,
-             const void* p2, const uint8_t* meta, int64_t N, int64_t K, void* y, int64_t ldy,
-             int y_type, void* stream) {
+static int resolve_tiling(const w12_tiling_t* tiling, int64_t M, int64_t N, int64_t K,
+                          w12::Tiling* out) {
+    if (tiling == nullptr) {
+        *out = w12::choose_tiling((int)M, N, K);
+        return W12_OK;
+    }
+    w12::Tiling t{};
+    t.mfma = tiling->kind != 0;
+    if (tiling->kind != 0 && tiling->kind != 1) return W12_ERR_UNSUPPORTED;
+    t.r = tiling->r;
+    t.kw = tiling->kw;
+    t.depth = tiling->depth;
+    if (!w12::complete_tiling(t, (int)M, K)) return W12_ERR_UNSUPPORTED;
+    *out = t;
+    return W12_OK;
+}
+
+int w12_gemm_ex(const uint16_t* x, int64_t M, int64_t ldx, const void* p0, const void* p1,
+                const void* p2, const uint8_t* meta, int64_t N, int64_t K, void* y, int64_t ldy,
+                int y_type, const w12_tiling_t* tiling, void* stream) {
     if (!p0 || !p1 || !p2 || !meta) return W12_ERR_NULL;
     if (int rc = check_gemm_common(x, M, ldx, N, K, y, ldy, y_type)) return rc;
     if (!aligned16(p0) || !aligned16(p1) || !aligned16(p2)) return W12_ERR_ALIGN;
+    w12::Tiling t;
+    if (int rc = resolve_tiling(tiling, M, N, K, &t)) return rc;
     w12::GemmArgs a = make_args(x, M, ldx, N, K, y, ldy, y_type);
     a.p0 = static_cast<const uint8_t*>(p0);
     a.p1 = static_cast<const uint8_t*>(p1);
     a.p2 = static_cast<const uint8_t*>(p2);
     a.meta = meta;
-    const w12::Tiling t = w12::choose_tiling((int)M, N, K);
     return status_of(w12::launch_gemm(a, t, true, static_cast<hipStream_t>(stream)));
+}
+
+int bf16_gemm_ex(const uint16_t* x, int64_t M, int64_t ldx, const uint16_t* w, int64_t N,
+                 int64_t K, void* y, int64_t ldy, int y_type, const w12_tiling_t* tiling,
+                 void* stream) {
+    if (!w) return W12_ERR_NULL;
+    if (int rc = check_gemm_common(x, M, ldx, N, K, y, ldy, y_type)) return rc;
+    if (!aligned16(w)) return W12_ERR_ALIGN;
+    w12::Tiling t;
+    if (int rc = resolve_tiling(tiling, M, N, K, &t)) return rc;
+    w12::GemmArgs a = make_args(x, M, ldx, N, K, y, ldy, y_type);
+    a.w = w;
+    return status_of(w12::launch_gemm(a, t, false, static_cast<hipStream_t>(stream)));
+}
+
+int w12_gemm(const uint16_t* x, int64_t M, int64_t ldx, const void* p0, const void* p1,
+             const void* p2, const uint8_t* meta, int64_t N, int64_t K, void* y, int64_t ldy,
+             int y_type, void* stream) {
+    return w12_gemm_ex(x, M, ldx, p0, p1, p2, meta, N, K, y, ldy, y_type, nullptr, stream);
 }
 
 int bf16_gemm(const uint16_t* x, int64_t M, int64_t ldx, const uint16_t* w, int64_t N, int64_t K,
               void* y, int64_t ldy, int y_type, void* stream) {
-    if (!w) return W12_ERR_NULL;
-    if (int rc = check_gemm_common(x, M, ldx, N, K, y, ldy, y_type)) return rc;
-    if (!aligned16(w)) return W12_ERR_ALIGN;
-    w12::GemmArgs a = make_args(x, M, ldx, N, K, y, ldy, y_type);
-    a.w = w;
+    return bf16_gemm_ex(x, M, ldx, w, N, K, y, ldy, y_type, nullptr, stream);
+}
+
+int w12_default_tiling(int64_t M, int64_t N, int64_t K, w12_tiling_t* out) {
+    if (out == nullptr) return W12_ERR_NULL;
+    if (int rc = check_weight_shape(N, K)) return rc;
+    if (M < 1) return W12_ERR_SHAPE;
+    if (M > W12_MAX_M) return W12_ERR_UNSUPPORTED;
     const w12::Tiling t = w12::choose_tiling((int)M, N, K);
-    return status_of(w12::launch_gemm(a, t, false, static_cast<hipStream_t>(stream)));
+    out->kind = t.mfma;
+    out->r = t.r;
+    out->kw = t.kw;
+    out->depth = t.depth;
+    return W12_OK;
 }
 
 const char* w12_gemm_variant(int64_t M, int64_t N, int64_t K, int is_w12) {

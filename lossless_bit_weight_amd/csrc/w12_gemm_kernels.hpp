@@ -1,0 +1,527 @@
+// w12_gemm_kernels.hpp -- kernel templates of the small-M decode GEMM
+// y = x . W^T for gfx950; W is fetched either from a W12 container (rebuilt
+// to BF16 in registers) or from the BF16 control layout.  Instantiated per x
+// height by w12_gemm_inst.hip and launched through w12_gemm.hip.
+//
+// The pages: in single-request decoding every step reads all target weights
+// while only a few tokens are accepted, and kernels are tuned against the
+// memory-bandwidth limit (AI Radar summary of SpecPilot, English edition,
+// opening paragraph); W12 is rebuilt bit-exactly inside the GEMM at batch
+// 1-32 (HotRepo digest of StargazerX0/SpecPilot, project introduction).  So
+// the kernel is a weight stream -- 1.5 B per weight for W12, 2 B for BF16 --
+// with x small enough to sit in LDS.
+//
+// Structure shared by both variants and both weight fetches:
+//   * both weight layouts are tiled: one (16-row tile, 128-weight group)
+//     block is 1 KB per plane (W12) or 4 x 1 KB (BF16), stored in lane
+//     order, so every load instruction of a wave reads 1 KB of contiguous
+//     memory.  Lane L = 16 q + col holds row col of the tile and the 32
+//     weights k = 128 g + 32 b + 8 q + e; its 8-weight block b is ready as
+//     4 dwords of BF16 pairs after decode;
+//   * a workgroup (4 waves) owns R tiles per row-wave over the whole K
+//     range; KW of its waves split the groups (group i goes to K-wave
+//     i % KW) and add their partial sums through LDS in a fixed order;
+//   * each lane keeps D groups in flight in a register ring unrolled at
+//     compile time; every ring load is issued unconditionally (indices are
+//     clamped to valid memory), so the compiler waits only for the oldest
+//     group instead of draining the ring;
+//   * x lives in LDS.  If it fits it is loaded once, before the ring is
+//     primed, so the prologue barrier waits for x only.  Otherwise it is
+//     double-buffered in chunks of KC columns loaded one chunk ahead, one
+//     barrier per chunk, between ring windows;
+// GEMV (M <= 8): v_dot2c_f32_bf16 into fp32, x[m] read from LDS as a
+// broadcast (all 16 lanes of a quarter read the same 16 bytes); the 4
+// quarter sums of a row are added with a fixed xor butterfly.
+// MFMA (M <= 32): v_mfma_f32_16x16x32_bf16; block b of lane (col, q) is the
+// B fragment of MFMA b, which therefore contracts the K set
+// {32 b + 8 q + e}; the A fragment (x row col) is read with the same
+// permutation, so the four MFMAs of a group cover its 128 K exactly once.
+// The W12 and BF16 fetches feed identical operands in identical order, so
+// for W = unpack(pack(W)) both return bitwise equal y.
+#pragma once
+
+#include "w12_decode.hpp"
+#include "w12_internal.hpp"
+
+namespace w12 {
+namespace kern {
+
+constexpr int kThreads = 256;
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float dot2(uint32_t w, uint32_t x, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w),
+                                           __builtin_bit_cast(bf16x2_t, x), acc, false);
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);  // quiet NaN
+    return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+__device__ __forceinline__ void store_y(const GemmArgs& g, int m, int64_t n, float v) {
+    if (g.y_f32)
+        reinterpret_cast<float*>(g.y)[(int64_t)m * g.ldy + n] = v;
+    else
+        reinterpret_cast<uint16_t*>(g.y)[(int64_t)m * g.ldy + n] = f32_to_bf16_rne(v);
+}
+
+// ---- weight fetch policies ------------------------------------------------
+// load(): the 32 weights lane `lane` owns in block `blk` (= tile * G + group)
+// into raw registers; block(): its 8-weight block b (0..3) as 4 dwords of
+// BF16 pairs in natural k order.
+
+struct FetchW12 {
+    struct Raw {
+        uint4 a, b, c;
+        uint32_t beta;
+    };
+    __device__ __forceinline__ static void load(const GemmArgs& g, int64_t blk, int lane, Raw& r) {
+        const int64_t off = blk * 1024 + 16 * lane;
+        r.a = *reinterpret_cast<const uint4*>(g.p0 + off);
+        r.b = *reinterpret_cast<const uint4*>(g.p1 + off);
+        r.c = *reinterpret_cast<const uint4*>(g.p2 + off);
+        r.beta = g.meta[blk * 16 + (lane & 15)];
+    }
+    __device__ __forceinline__ static void block(const Raw& r, int b, uint32_t out[4]) {
+        const Lut t = make_lut(r.beta & 0x7Fu);
+        const uint32_t pa = b == 0 ? r.a.x : b == 1 ? r.a.y : b == 2 ? r.a.z : r.a.w;
+        const uint32_t pb = b == 0 ? r.b.x : b == 1 ? r.b.y : b == 2 ? r.b.z : r.b.w;
+        const uint32_t pc = b == 0 ? r.c.x : b == 1 ? r.c.y : b == 2 ? r.c.z : r.c.w;
+        decode8(pa, pb, pc, t, out);
+    }
+};
+
+struct FetchBF16 {
+    struct Raw {
+        uint4 q[4];
+    };
+    __device__ __forceinline__ static void load(const GemmArgs& g, int64_t blk, int lane, Raw& r) {
+        const uint4* p = reinterpret_cast<const uint4*>(g.w) + blk * 256 + lane;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) r.q[b] = p[64 * b];
+    }
+    __device__ __forceinline__ static void block(const Raw& r, int b, uint32_t out[4]) {
+        out[0] = r.q[b].x;
+        out[1] = r.q[b].y;
+        out[2] = r.q[b].z;
+        out[3] = r.q[b].w;
+    }
+};
+
+// ---- x staging ----------------------------------------------------------------
+// x[0:MROWS][k0:k0+KC] -> LDS in 16-byte units (8 BF16); rows >= M and
+// columns >= K are zero.  Layout::phys(row, unit) is the LDS slot.
+
+template <int MROWS, int KC>
+struct XChunk {
+    static constexpr int kUnitsPerRow = KC / 8;
+    static constexpr int kUnits = MROWS * kUnitsPerRow;
+    static constexpr int kPerThread = (kUnits + kThreads - 1) / kThreads;
+    uint4 v[kPerThread];
+
+    // Every lane issues every load (addresses clamped into x), and values
+    // outside x are zeroed afterwards: unpredicated loads let the compiler
+    // count outstanding loads exactly instead of draining the weight ring.
+    __device__ __forceinline__ void load(const GemmArgs& g, int64_t k0) {
+#pragma unroll
+        for (int j = 0; j < kPerThread; ++j) {
+            const int id = threadIdx.x + kThreads * j;
+            const int m = id / kUnitsPerRow;
+            const int64_t k = k0 + 8 * (id % kUnitsPerRow);
+            const bool ok = id < kUnits && m < g.M && k < g.K;
+            const int mc = m < g.M ? m : g.M - 1;
+            const int64_t kc = k < g.K ? k : g.K - 8;
+            const uint4 v0 = *reinterpret_cast<const uint4*>(g.x + (int64_t)mc * g.ldx + kc);
+            v[j] = ok ? v0 : make_uint4(0, 0, 0, 0);
+        }
+    }
+    template <class Layout>
+    __device__ __forceinline__ void store(uint4* buf) const {
+#pragma unroll
+        for (int j = 0; j < kPerThread; ++j) {
+            const int id = threadIdx.x + kThreads * j;
+            if (id < kUnits) buf[Layout::phys(id / kUnitsPerRow, id % kUnitsPerRow)] = v[j];
+        }
+    }
+};
+
+// Whole-x staging when all of x fits (at most kSingleBytes): loaded into
+// registers before the weight ring is primed, stored to LDS after it, so
+// waiting for x never waits for weights.  The registers die after the store.
+constexpr int kSingleBytes = 40 * 1024;
+constexpr int kSingleUnits = kSingleBytes / 16 / kThreads;  // per thread
+
+struct XAll {
+    uint4 v[kSingleUnits];
+    int units, units_per_row;
+
+    __device__ __forceinline__ void load(const GemmArgs& g, int mrows) {
+        units_per_row = (int)(g.K / 8);
+        units = mrows * units_per_row;
+#pragma unroll
+        for (int j = 0; j < kSingleUnits; ++j) {
+            const int id = threadIdx.x + kThreads * j;
+            const int m = id / units_per_row;
+            const int64_t k = 8 * (int64_t)(id % units_per_row);
+            const bool ok = id < units && m < g.M;
+            const int mc = m < g.M ? m : g.M - 1;
+            const uint4 v0 = *reinterpret_cast<const uint4*>(g.x + (int64_t)mc * g.ldx + k);
+            v[j] = ok ? v0 : make_uint4(0, 0, 0, 0);
+        }
+    }
+    template <class Layout>
+    __device__ __forceinline__ void store(uint4* buf) const {
+#pragma unroll
+        for (int j = 0; j < kSingleUnits; ++j) {
+            const int id = threadIdx.x + kThreads * j;
+            if (id < units)
+                buf[Layout::phys(id / units_per_row, id % units_per_row, units_per_row)] = v[j];
+        }
+    }
+};
+
+// x layout in LDS: row m, 16-byte unit u at slot m * units_per_row +
+// (u ^ (m & 7)).  The MFMA reads one unit of rows m = 0..15 per instruction
+// and the xor spreads them over 8 different 16-byte bank slots; the GEMV
+// reads the same unit of a row from all lanes of a quarter (a broadcast).
+struct XLayout {
+    __device__ __forceinline__ static int phys(int m, int u, int units_per_row) {
+        return m * units_per_row + (u ^ (m & 7));
+    }
+};
+
+template <class L, int UPR>
+struct FixedLayout {
+    __device__ __forceinline__ static int phys(int m, int u) { return L::phys(m, u, UPR); }
+};
+
+// ---- compile-time chunk sizes ---------------------------------------------------
+// Chunked mode double-buffers KC columns of x.  KC is a multiple of one ring
+// window of the workgroup (D slices of each of the KW K-waves), so chunk
+// transitions fall between ring windows.
+
+__host__ __device__ constexpr int gemv_kc(int M, int KW, int D) {
+    const int base = M <= 1 ? 8192 : M <= 2 ? 4096 : M <= 4 ? 2048 : 1024;
+    const int window = 128 * KW * D;
+    return base < window ? window : base;
+}
+__host__ __device__ constexpr int mfma_kc(int MT, int KW, int D) {
+    const int base = MT == 16 ? 512 : 256;
+    const int window = 128 * KW * D;
+    return base < window ? window : base;
+}
+// A chunked variant is built only if its double buffer fits 64 KB of LDS
+// (x rows * KC <= 16384), which also caps the x registers at 8 x 16 bytes
+// per thread.
+__host__ __device__ constexpr bool chunk_ok(int rows, int kc) { return rows * kc <= 16384; }
+__host__ __device__ constexpr int kc_of(bool mfma, int rows, int KW, int D) {
+    return mfma ? mfma_kc(rows, KW, D) : gemv_kc(rows, KW, D);
+}
+
+// The main loop shared by both variants.  `fetch(j, ring[d])` loads wave
+// slice j (clamped to the wave's last slice, so it always issues the same
+// loads), `compute(ring[d], j)` consumes it, `xbuf` is the LDS chunk base.
+// Ring slot d always holds slice jb + d, so the compiler sees straight-line
+// loads and waits exactly for the oldest slice.
+#define W12_RING_LOOP(D, CHUNKED, J, L, nchunks, xr, store_next, fetch, compute)          \
+    {                                                                                     \
+        int jb = 0;                                                                       \
+        for (; jb + (D) <= (J); jb += (D)) {                                              \
+            if constexpr (CHUNKED) {                                                      \
+                if (jb == next_boundary) {                                                \
+                    store_next();                                                         \
+                    __syncthreads();                                                      \
+                    ++c;                                                                  \
+                    next_boundary += (L);                                                 \
+                    xr.load(g, (int64_t)(c + 1 < (nchunks) ? c + 1 : c) * KC);            \
+                }                                                                         \
+            }                                                                             \
+            _Pragma("unroll") for (int d = 0; d < (D); ++d) {                             \
+                compute(ring[d], jb + d);                                                 \
+                fetch(jb + d + (D), ring[d]);                                             \
+            }                                                                             \
+        }                                                                                 \
+        if constexpr (CHUNKED) {                                                          \
+            if (jb < (J) && jb == next_boundary) {                                        \
+                store_next();                                                             \
+                __syncthreads();                                                          \
+                ++c;                                                                      \
+                next_boundary += (L);                                                     \
+                xr.load(g, (int64_t)(c + 1 < (nchunks) ? c + 1 : c) * KC);                \
+            }                                                                             \
+        }                                                                                 \
+        _Pragma("unroll") for (int d = 0; d < (D); ++d) {                                 \
+            if (jb + d < (J)) compute(ring[d], jb + d);                                   \
+        }                                                                                 \
+        /* Every thread stages its share of every x chunk, so a wave that ran */         \
+        /* out of slices still performs the chunk transitions it did not reach. */        \
+        if constexpr (CHUNKED) {                                                          \
+            while (c + 1 < (nchunks)) {                                                   \
+                store_next();                                                             \
+                __syncthreads();                                                          \
+                ++c;                                                                      \
+                xr.load(g, (int64_t)(c + 1 < (nchunks) ? c + 1 : c) * KC);                \
+            }                                                                             \
+        }                                                                                 \
+    }
+
+// ---- the kernel ----------------------------------------------------------------------
+// MFMA = false: GEMV, MR = M (1..8).  MFMA = true: MR = 16 or 32 (x rows,
+// zero padded).
+
+template <class F, bool MFMA, int MR, int R, int KW, int D, bool CHUNKED>
+__global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
+    constexpr int KC = kc_of(MFMA, MR, KW, D);
+    constexpr int kRowWaves = 4 / KW;
+    constexpr int kBuf = MR * KC / 8;                 // uint4 per x chunk buffer
+    constexpr int L = KC / (128 * KW);                // wave groups per chunk (multiple of D)
+    constexpr int kMT = MR / 16;                      // MFMA: 16-row tiles of x
+    using Raw = typename F::Raw;
+    extern __shared__ uint4 lds[];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int col = lane & 15;   // weight row in the tile; A row for the MFMA
+    const int q = lane >> 4;     // quarter: weights 8q..8q+7 of each 32
+    const int kw = wave % KW;
+    const int nw = wave / KW;
+    const int64_t G = g.K / 128;
+    const int64_t ntiles = (g.N + 15) / 16;
+    const int64_t tile0 = ((int64_t)blockIdx.x * kRowWaves + nw) * R;  // tile r: tile0 + r
+
+    int64_t tload[R];  // tiles past the end are clamped for loading
+#pragma unroll
+    for (int r = 0; r < R; ++r) tload[r] = tile0 + r < ntiles ? tile0 + r : ntiles - 1;
+
+    const int J = G > kw ? (int)((G - kw + KW - 1) / KW) : 0;  // this wave's groups
+    const int Jlast = J > 0 ? J - 1 : 0;
+    const int units_per_row = CHUNKED ? KC / 8 : (int)(g.K / 8);
+    const int64_t nchunks = CHUNKED ? (g.K + KC - 1) / KC : 1;
+    int c = 0;
+    int next_boundary = CHUNKED && nchunks > 1 ? L : 1 << 30;
+
+    Raw ring[D][R];
+    auto fetch = [&](int j, Raw (&dst)[R]) {
+        j = j < Jlast ? j : Jlast;
+        int64_t grp = kw + (int64_t)j * KW;
+        grp = grp < G ? grp : G - 1;   // only when this wave has no group at all
+#pragma unroll
+        for (int r = 0; r < R; ++r) F::load(g, tload[r] * G + grp, lane, dst[r]);
+    };
+
+    float gacc[MFMA ? 1 : R][MFMA ? 1 : MR];
+    f32x4_t macc[MFMA ? R : 1][MFMA ? kMT : 1];
+    if constexpr (MFMA) {
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int i = 0; i < kMT; ++i) macc[r][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    } else {
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int m = 0; m < MR; ++m) gacc[r][m] = 0.f;
+    }
+
+    auto compute = [&](const Raw (&rr)[R], int j) {
+        const uint4* xb = lds + (CHUNKED ? (c & 1) * kBuf : 0);
+        const int64_t grp = kw + (int64_t)j * KW;
+        // unit of (block b) = (128 grp + 32 b + 8 q) / 8, chunk relative
+        const int u0 = (int)(16 * grp - (int64_t)c * (KC / 8)) + q;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            if constexpr (MFMA) {
+                bf16x8_t a[kMT];
+#pragma unroll
+                for (int mt = 0; mt < kMT; ++mt)
+                    a[mt] = __builtin_bit_cast(bf16x8_t,
+                                               xb[XLayout::phys(16 * mt + col, u0 + 4 * b, units_per_row)]);
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    uint32_t wv[4];
+                    F::block(rr[r], b, wv);
+                    const bf16x8_t bw = __builtin_bit_cast(bf16x8_t, make_uint4(wv[0], wv[1], wv[2], wv[3]));
+#pragma unroll
+                    for (int mt = 0; mt < kMT; ++mt)
+                        macc[r][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mt], bw, macc[r][mt], 0, 0, 0);
+                }
+            } else {
+                uint4 xv[MR];
+#pragma unroll
+                for (int m = 0; m < MR; ++m) xv[m] = xb[XLayout::phys(m, u0 + 4 * b, units_per_row)];
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    uint32_t wv[4];
+                    F::block(rr[r], b, wv);
+#pragma unroll
+                    for (int m = 0; m < MR; ++m) {
+                        float a = gacc[r][m];
+                        a = dot2(wv[0], xv[m].x, a);
+                        a = dot2(wv[1], xv[m].y, a);
+                        a = dot2(wv[2], xv[m].z, a);
+                        a = dot2(wv[3], xv[m].w, a);
+                        gacc[r][m] = a;
+                    }
+                }
+            }
+        }
+    };
+
+    // Prologue: x first, then the ring, so the barrier waits for x only.
+    XChunk<MR, KC> xr;
+    XAll xa;
+    if constexpr (CHUNKED)
+        xr.load(g, 0);
+    else
+        xa.load(g, MR);
+#pragma unroll
+    for (int d = 0; d < D; ++d) fetch(d, ring[d]);
+    if constexpr (CHUNKED)
+        xr.template store<FixedLayout<XLayout, KC / 8>>(lds);
+    else
+        xa.template store<XLayout>(lds);
+    __syncthreads();
+    if constexpr (CHUNKED) xr.load(g, (int64_t)(nchunks > 1 ? 1 : 0) * KC);
+
+    auto store_next = [&]() {
+        xr.template store<FixedLayout<XLayout, KC / 8>>(lds + ((c + 1) & 1) * kBuf);
+    };
+    W12_RING_LOOP(D, CHUNKED, J, L, nchunks, xr, store_next, fetch, compute)
+
+    if constexpr (MFMA) {
+        if constexpr (KW > 1) {
+            __syncthreads();  // every wave is done reading x
+            f32x4_t* red = reinterpret_cast<f32x4_t*>(lds);
+            constexpr int kPer = R * kMT;
+            if (kw > 0) {
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+#pragma unroll
+                    for (int mt = 0; mt < kMT; ++mt)
+                        red[(((kw - 1) * kRowWaves + nw) * 64 + lane) * kPer + r * kMT + mt] = macc[r][mt];
+            }
+            __syncthreads();
+            if (kw != 0) return;
+            for (int p = 1; p < KW; ++p)
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+#pragma unroll
+                    for (int mt = 0; mt < kMT; ++mt)
+                        macc[r][mt] += red[(((p - 1) * kRowWaves + nw) * 64 + lane) * kPer + r * kMT + mt];
+        }
+        // D layout of the 16x16 MFMA: lane (col, q) holds rows 4q..4q+3 of
+        // column col, i.e. y[m = 16 mt + 4q + e][n = 16 tile + col].
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int64_t n = (tile0 + r) * 16 + col;
+            if (n >= g.N) continue;
+#pragma unroll
+            for (int mt = 0; mt < kMT; ++mt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int m = 16 * mt + 4 * q + e;
+                    if (m < g.M) store_y(g, m, n, macc[r][mt][e]);
+                }
+        }
+    } else {
+        // Add the 4 quarter sums of each row (fixed butterfly order).
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int m = 0; m < MR; ++m) {
+                float v = gacc[r][m];
+                v += __shfl_xor(v, 16);
+                v += __shfl_xor(v, 32);
+                gacc[r][m] = v;
+            }
+        if constexpr (KW > 1) {
+            __syncthreads();  // every wave is done reading x
+            float* red = reinterpret_cast<float*>(lds);
+            if (kw > 0 && q == 0) {
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+#pragma unroll
+                    for (int m = 0; m < MR; ++m)
+                        red[(((kw - 1) * kRowWaves + nw) * 16 + col) * (R * MR) + r * MR + m] = gacc[r][m];
+            }
+            __syncthreads();
+            if (kw != 0) return;
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+                for (int m = 0; m < MR; ++m) {
+                    float v = gacc[r][m];
+                    for (int p = 1; p < KW; ++p)
+                        v += red[(((p - 1) * kRowWaves + nw) * 16 + col) * (R * MR) + r * MR + m];
+                    gacc[r][m] = v;
+                }
+        }
+        // Lane (col, q) stores the outputs m with m % 4 == q.
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int64_t n = (tile0 + r) * 16 + col;
+#pragma unroll
+            for (int m = 0; m < MR; ++m)
+                if ((m & 3) == q && n < g.N && m < g.M) store_y(g, m, n, gacc[r][m]);
+        }
+    }
+}
+
+// ---- launch helpers ----------------------------------------------------------------------
+
+// Bytes of LDS a launch needs (x buffers; the reductions reuse them).
+template <bool MFMA, int MR, int R, int KW, int D, bool CHUNKED>
+size_t lds_bytes(int64_t K) {
+    const size_t x = CHUNKED ? 2 * (size_t)MR * kc_of(MFMA, MR, KW, D) * 2 : (size_t)MR * (K / 8) * 16;
+    const size_t red = KW == 1 ? 0
+                       : MFMA ? (size_t)(KW - 1) * (4 / KW) * 64 * R * (MR / 16) * 16
+                              : (size_t)(KW - 1) * (4 / KW) * 16 * R * MR * 4;
+    return x > red ? x : red;
+}
+
+template <class F, bool MFMA, int MR, int R, int KW, int D, bool CHUNKED>
+hipError_t launch_one(const GemmArgs& a, hipStream_t s) {
+    constexpr int kTilesPerWG = (4 / KW) * R;
+    const int64_t ntiles = (a.N + 15) / 16;
+    const dim3 grid((unsigned)((ntiles + kTilesPerWG - 1) / kTilesPerWG));
+    const size_t lds = lds_bytes<MFMA, MR, R, KW, D, CHUNKED>(a.K);
+    hipLaunchKernelGGL((gemm_kernel<F, MFMA, MR, R, KW, D, CHUNKED>), grid, dim3(kThreads), lds, s, a);
+    return hipGetLastError();
+}
+
+template <class F, bool MFMA, int MR, int R, int KW, int D>
+hipError_t launch_ch(const GemmArgs& a, bool chunked, hipStream_t s) {
+    if (!chunked) return launch_one<F, MFMA, MR, R, KW, D, false>(a, s);
+    if constexpr (chunk_ok(MR, kc_of(MFMA, MR, KW, D))) return launch_one<F, MFMA, MR, R, KW, D, true>(a, s);
+    return hipErrorInvalidValue;
+}
+
+template <class F, bool MFMA, int MR, int R, int D>
+hipError_t launch_kw(const GemmArgs& a, const Tiling& t, hipStream_t s) {
+    const bool ch = t.chunked != 0;
+    switch (t.kw) {
+        case 1: return launch_ch<F, MFMA, MR, R, 1, D>(a, ch, s);
+        case 2: return launch_ch<F, MFMA, MR, R, 2, D>(a, ch, s);
+        case 4: return launch_ch<F, MFMA, MR, R, 4, D>(a, ch, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+// (r, depth) pairs that are instantiated: see gemm_pair_built().
+template <class F, bool MFMA, int MR>
+hipError_t dispatch(const GemmArgs& a, const Tiling& t, hipStream_t s) {
+    if (t.r == 1 && t.depth == 2) return launch_kw<F, MFMA, MR, 1, 2>(a, t, s);
+    if (t.r == 1 && t.depth == 4) return launch_kw<F, MFMA, MR, 1, 4>(a, t, s);
+    if (t.r == 1 && t.depth == 8) return launch_kw<F, MFMA, MR, 1, 8>(a, t, s);
+    if (t.r == 2 && t.depth == 2) return launch_kw<F, MFMA, MR, 2, 2>(a, t, s);
+    if (t.r == 2 && t.depth == 4) return launch_kw<F, MFMA, MR, 2, 4>(a, t, s);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace kern
+}  // namespace w12

@@ -25,26 +25,38 @@ struct GemmArgs {
 };
 
 // Tiling of one GEMM launch.
-//   mfma = 0: GEMV; every 16 lanes own a row, R rows per lane group.
-//   mfma = 1: MFMA 16x16x32 bf16; a wave owns R tiles of 16 rows.
-//   kw   = waves of a workgroup that split K between them (1, 2 or 4).
+//   mfma    = 0: GEMV (v_dot2c_f32_bf16); 1: MFMA 16x16x32 bf16.
+//   r       = 16-row weight tiles per wave (1 or 2).
+//   mt      = GEMV: M (1..8); MFMA: x rows padded to 16 or 32.
+//   kw      = waves of a workgroup that split K between them (1, 2 or 4).
+//   depth   = 32-weight slices each lane keeps in flight (2, 4 or 8).
+//   chunked = 0 if all of x is staged in LDS at once, 1 if it is streamed
+//             through LDS in double-buffered chunks (set from the shape).
 struct Tiling {
     int mfma;
-    int mt;   // GEMV: M; MFMA: padded M (16 or 32)
+    int mt;
     int r;
     int kw;
+    int depth;
+    int chunked;
 };
 
 // Pick the tiling used by w12_gemm / bf16_gemm for this shape.
 Tiling choose_tiling(int M, int64_t N, int64_t K);
-bool tiling_valid(const Tiling& t, int M);
+// Complete a caller-given tiling (mt, chunked) for this shape; false if the
+// combination is not built.
+bool complete_tiling(Tiling& t, int M, int64_t K);
 const char* tiling_name(const Tiling& t, bool is_w12);
 
 hipError_t launch_gemm(const GemmArgs& a, const Tiling& t, bool is_w12, hipStream_t s);
+// Per-M (GEMV) and per-MT (MFMA) launchers, one object file each.
+hipError_t launch_gemv_m(int M, const GemmArgs& a, const Tiling& t, bool is_w12, hipStream_t s);
+hipError_t launch_mfma_mt(int MT, const GemmArgs& a, const Tiling& t, bool is_w12, hipStream_t s);
 hipError_t launch_pack(const uint16_t* w, int64_t N, int64_t K, void* p0, void* p1,
                        void* p2, uint8_t* meta, uint32_t* bad, hipStream_t s);
 hipError_t launch_unpack(const void* p0, const void* p1, const void* p2,
                          const uint8_t* meta, int64_t N, int64_t K, uint16_t* w,
                          hipStream_t s);
+hipError_t launch_bf16_tile(const uint16_t* w, int64_t N, int64_t K, uint16_t* out, hipStream_t s);
 
 }  // namespace w12

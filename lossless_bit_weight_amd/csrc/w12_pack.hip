@@ -1,16 +1,18 @@
-// w12_pack.hip -- W12-v1 encoder (pack) and streaming decoder (unpack).
+// w12_pack.hip -- W12-v1 encoder (pack), streaming decoder (unpack) and the
+// BF16 control layout (bf16_tile).
 //
 // Format: see w12.h.  The pages say only that BF16 is split into three 4-bit
 // planes and that the format is lossless (AI Radar summary of SpecPilot,
-// English edition, "Reasons"); the group/base rule and the layout are this
-// library's W12-v1.
+// English edition, "Reasons"); the group/base rule and the tiled layout are
+// this library's W12-v1.
 //
-// Work split: one thread owns 32 consecutive weights of the row-major
-// tensor, i.e. one 16-byte slice of each plane and a quarter of a 128-weight
-// group; 4 neighbouring lanes of a wave form one group.  Because K % 128 == 0
-// a group never straddles rows, so the flat index is all a thread needs.
-// Both kernels are single streaming passes: 64 B read + 48 B written per
-// thread (pack), 48 B + 1 B read and 64 B written (unpack).
+// Work split: one wave per (16-row tile T, 128-weight group g).  Lane
+// L = 16 q + c owns row n = 16 T + c and the 32 weights
+// k = 128 g + 32 b + 8 q + e (b, e = 0..3, 0..7) -- exactly the 16-byte
+// piece L of the block in each plane, so every plane store of a wave is one
+// contiguous 1 KB.  The four lanes of a row (q = 0..3) form the group and
+// agree on its base through two xor shuffles.  Rows >= N (padding of the
+// last tile) are encoded as zeros.
 #include "w12_decode.hpp"
 #include "w12_internal.hpp"
 
@@ -21,40 +23,43 @@ constexpr int kThreads = 256;
 
 __device__ __forceinline__ uint32_t max_u32(uint32_t a, uint32_t b) { return a > b ? a : b; }
 
-__global__ __launch_bounds__(kThreads) void pack_kernel(const uint4* __restrict__ w,
-                                                        int64_t slices,
+__global__ __launch_bounds__(kThreads) void pack_kernel(const uint16_t* __restrict__ w, int64_t N,
+                                                        int64_t K, int64_t nblocks,
                                                         uint4* __restrict__ p0,
                                                         uint4* __restrict__ p1,
                                                         uint4* __restrict__ p2,
                                                         uint8_t* __restrict__ meta,
                                                         uint32_t* __restrict__ bad_count) {
-    const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-    const bool active = i < slices;
+    const int64_t blk = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+    if (blk >= nblocks) return;  // whole waves only
+    const int lane = threadIdx.x & 63;
+    const int c = lane & 15;
+    const int q = lane >> 4;
+    const int64_t G = K / 128;
+    const int64_t n = (blk / G) * 16 + c;
+    const int64_t g = blk % G;
+    const bool valid = n < N;
 
-    uint32_t v[16];  // 32 BF16 words, two per dword, natural order
-    if (active) {
+    uint32_t v[16];  // block b: v[4b .. 4b+3] = 8 BF16 words, natural order
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const uint4 d = w[4 * i + q];
-            v[4 * q + 0] = d.x;
-            v[4 * q + 1] = d.y;
-            v[4 * q + 2] = d.z;
-            v[4 * q + 3] = d.w;
-        }
-    } else {
-#pragma unroll
-        for (int q = 0; q < 16; ++q) v[q] = 0;
+    for (int b = 0; b < 4; ++b) {
+        uint4 d = make_uint4(0, 0, 0, 0);
+        if (valid) d = *reinterpret_cast<const uint4*>(w + n * K + 128 * g + 32 * b + 8 * q);
+        v[4 * b + 0] = d.x;
+        v[4 * b + 1] = d.y;
+        v[4 * b + 2] = d.z;
+        v[4 * b + 3] = d.w;
     }
 
-    // Largest biased exponent over the group (4 lanes x 32 weights).
+    // Largest biased exponent of the group (its 4 lanes).
     uint32_t emax = 0;
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-        emax = max_u32(emax, (v[q] >> 7) & 0xFFu);
-        emax = max_u32(emax, (v[q] >> 23) & 0xFFu);
+    for (int i = 0; i < 16; ++i) {
+        emax = max_u32(emax, (v[i] >> 7) & 0xFFu);
+        emax = max_u32(emax, (v[i] >> 23) & 0xFFu);
     }
-    emax = max_u32(emax, (uint32_t)__shfl_xor((int)emax, 1));
-    emax = max_u32(emax, (uint32_t)__shfl_xor((int)emax, 2));
+    emax = max_u32(emax, (uint32_t)__shfl_xor((int)emax, 16));
+    emax = max_u32(emax, (uint32_t)__shfl_xor((int)emax, 32));
     const uint32_t beta = emax <= 15u ? 0u : (emax - 14u) >> 1;
     const uint32_t floor_e = 2u * beta + 2u;
 
@@ -62,8 +67,8 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(const uint4* __restrict_
     uint32_t lo[32], code[32];
     uint32_t bad = 0;
 #pragma unroll
-    for (int e = 0; e < 32; ++e) {
-        const uint32_t word = (v[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+    for (int i = 0; i < 32; ++i) {
+        const uint32_t word = (v[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
         const uint32_t ex = (word >> 7) & 0xFFu;
         const uint32_t s = word >> 15;
         uint32_t l = word & 0xFFu;
@@ -77,12 +82,12 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(const uint4* __restrict_
             l = 0u;
             bad = 1u;
         }
-        lo[e] = l;
-        code[e] = (s << 3) | h;
+        lo[i] = l;
+        code[i] = (s << 3) | h;
     }
 
-    // Split-nibble order: dword b of a plane holds weights 8b..8b+7; byte j
-    // carries weight 8b+j (low nibble) and 8b+j+4 (high nibble).
+    // Split-nibble order: dword b holds weights 8b..8b+7 of the lane; byte j
+    // carries weight j (low nibble) and j+4 (high nibble).
     uint32_t o0[4], o1[4], o2[4];
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
@@ -98,52 +103,78 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(const uint4* __restrict_
         o1[b] = a1;
         o2[b] = a2;
     }
+    bad |= (uint32_t)__shfl_xor((int)bad, 16);
+    bad |= (uint32_t)__shfl_xor((int)bad, 32);
 
-    bad |= (uint32_t)__shfl_xor((int)bad, 1);
-    bad |= (uint32_t)__shfl_xor((int)bad, 2);
+    p0[blk * 64 + lane] = make_uint4(o0[0], o0[1], o0[2], o0[3]);
+    p1[blk * 64 + lane] = make_uint4(o1[0], o1[1], o1[2], o1[3]);
+    p2[blk * 64 + lane] = make_uint4(o2[0], o2[1], o2[2], o2[3]);
+    if (q == 0) meta[blk * 16 + c] = (uint8_t)(beta | (bad << 7));
 
-    if (active) {
-        p0[i] = make_uint4(o0[0], o0[1], o0[2], o0[3]);
-        p1[i] = make_uint4(o1[0], o1[1], o1[2], o1[3]);
-        p2[i] = make_uint4(o2[0], o2[1], o2[2], o2[3]);
-        if ((i & 3) == 0) meta[i >> 2] = (uint8_t)(beta | (bad << 7));
-    }
-
-    // One atomic per wave: the number of flagged groups led by this wave.
-    const uint64_t leaders = __ballot(active && (i & 3) == 0 && bad);
-    if (bad_count != nullptr && (threadIdx.x & 63) == 0 && leaders != 0)
-        atomicAdd(bad_count, (uint32_t)__popcll(leaders));
+    // One atomic per wave: the flagged groups of this block.
+    const uint64_t flagged = __ballot(q == 0 && valid && bad);
+    if (bad_count != nullptr && lane == 0 && flagged != 0)
+        atomicAdd(bad_count, (uint32_t)__popcll(flagged));
 }
 
 __global__ __launch_bounds__(kThreads) void unpack_kernel(const uint4* __restrict__ p0,
                                                           const uint4* __restrict__ p1,
                                                           const uint4* __restrict__ p2,
                                                           const uint8_t* __restrict__ meta,
-                                                          int64_t slices,
-                                                          uint4* __restrict__ w) {
-    const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-    if (i >= slices) return;
-    const uint4 a = p0[i], b = p1[i], c = p2[i];
-    const Lut t = make_lut(meta[i >> 2] & 0x7Fu);
+                                                          int64_t N, int64_t K, int64_t nblocks,
+                                                          uint16_t* __restrict__ w) {
+    const int64_t blk = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+    if (blk >= nblocks) return;
+    const int lane = threadIdx.x & 63;
+    const int c = lane & 15;
+    const int q = lane >> 4;
+    const int64_t G = K / 128;
+    const int64_t n = (blk / G) * 16 + c;
+    const int64_t g = blk % G;
+    const uint4 a = p0[blk * 64 + lane], b4 = p1[blk * 64 + lane], c4 = p2[blk * 64 + lane];
+    const Lut t = make_lut(meta[blk * 16 + c] & 0x7Fu);
+    if (n >= N) return;
     const uint32_t pa[4] = {a.x, a.y, a.z, a.w};
-    const uint32_t pb[4] = {b.x, b.y, b.z, b.w};
-    const uint32_t pc[4] = {c.x, c.y, c.z, c.w};
+    const uint32_t pb[4] = {b4.x, b4.y, b4.z, b4.w};
+    const uint32_t pc[4] = {c4.x, c4.y, c4.z, c4.w};
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int b = 0; b < 4; ++b) {
         uint32_t o[4];
-        decode8(pa[q], pb[q], pc[q], t, o);
-        w[4 * i + q] = make_uint4(o[0], o[1], o[2], o[3]);
+        decode8(pa[b], pb[b], pc[b], t, o);
+        *reinterpret_cast<uint4*>(w + n * K + 128 * g + 32 * b + 8 * q) = make_uint4(o[0], o[1], o[2], o[3]);
     }
 }
+
+// Row-major BF16 [N, K] -> control layout: block (T, g) of 2048 words, 1 KB
+// sub-block b, lane L's 8 words k = 128 g + 32 b + 8 q + e.
+__global__ __launch_bounds__(kThreads) void bf16_tile_kernel(const uint16_t* __restrict__ w,
+                                                             int64_t N, int64_t K, int64_t nblocks,
+                                                             uint4* __restrict__ out) {
+    const int64_t blk = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+    if (blk >= nblocks) return;
+    const int lane = threadIdx.x & 63;
+    const int c = lane & 15;
+    const int q = lane >> 4;
+    const int64_t G = K / 128;
+    const int64_t n = (blk / G) * 16 + c;
+    const int64_t g = blk % G;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        uint4 d = make_uint4(0, 0, 0, 0);
+        if (n < N) d = *reinterpret_cast<const uint4*>(w + n * K + 128 * g + 32 * b + 8 * q);
+        out[(blk * 4 + b) * 64 + lane] = d;
+    }
+}
+
+int64_t blocks_of(int64_t N, int64_t K) { return (N + 15) / 16 * (K / 128); }
 
 }  // namespace
 
 hipError_t launch_pack(const uint16_t* w, int64_t N, int64_t K, void* p0, void* p1, void* p2,
                        uint8_t* meta, uint32_t* bad, hipStream_t s) {
-    const int64_t slices = N * K / 32;
-    const int64_t blocks = (slices + kThreads - 1) / kThreads;
-    hipLaunchKernelGGL(pack_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, s,
-                       reinterpret_cast<const uint4*>(w), slices,
+    const int64_t nb = blocks_of(N, K);
+    const int64_t grid = (nb + 3) / 4;
+    hipLaunchKernelGGL(pack_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, w, N, K, nb,
                        reinterpret_cast<uint4*>(p0), reinterpret_cast<uint4*>(p1),
                        reinterpret_cast<uint4*>(p2), meta, bad);
     return hipGetLastError();
@@ -151,12 +182,19 @@ hipError_t launch_pack(const uint16_t* w, int64_t N, int64_t K, void* p0, void* 
 
 hipError_t launch_unpack(const void* p0, const void* p1, const void* p2, const uint8_t* meta,
                          int64_t N, int64_t K, uint16_t* w, hipStream_t s) {
-    const int64_t slices = N * K / 32;
-    const int64_t blocks = (slices + kThreads - 1) / kThreads;
-    hipLaunchKernelGGL(unpack_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, s,
+    const int64_t nb = blocks_of(N, K);
+    const int64_t grid = (nb + 3) / 4;
+    hipLaunchKernelGGL(unpack_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s,
                        reinterpret_cast<const uint4*>(p0), reinterpret_cast<const uint4*>(p1),
-                       reinterpret_cast<const uint4*>(p2), meta, slices,
-                       reinterpret_cast<uint4*>(w));
+                       reinterpret_cast<const uint4*>(p2), meta, N, K, nb, w);
+    return hipGetLastError();
+}
+
+hipError_t launch_bf16_tile(const uint16_t* w, int64_t N, int64_t K, uint16_t* out, hipStream_t s) {
+    const int64_t nb = blocks_of(N, K);
+    const int64_t grid = (nb + 3) / 4;
+    hipLaunchKernelGGL(bf16_tile_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, w, N, K, nb,
+                       reinterpret_cast<uint4*>(out));
     return hipGetLastError();
 }
 

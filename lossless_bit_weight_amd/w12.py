@@ -43,6 +43,32 @@ class W12UnencodableError(ValueError):
     """Raised by pack(..., strict=True) when some group cannot round-trip."""
 
 
+class Tiling(ctypes.Structure):
+    """w12_tiling_t: kind (0 GEMV, 1 MFMA), r, kw, depth."""
+    _fields_ = [("kind", ctypes.c_int32), ("r", ctypes.c_int32), ("kw", ctypes.c_int32),
+                ("depth", ctypes.c_int32)]
+
+    def astuple(self):
+        return (self.kind, self.r, self.kw, self.depth)
+
+    def __repr__(self):
+        return "Tiling(kind=%d, r=%d, kw=%d, depth=%d)" % self.astuple()
+
+
+# Every tiling the library instantiates: (kind, r, kw, depth).
+_PAIRS = ((1, 2), (1, 4), (1, 8), (2, 2), (2, 4))
+GEMV_TILINGS = [(0, r, kw, d) for (r, d) in _PAIRS for kw in (1, 2, 4)]
+MFMA_TILINGS = [(1, r, kw, d) for (r, d) in _PAIRS for kw in (1, 2, 4)]
+
+
+def _tiling_arg(tiling):
+    if tiling is None:
+        return None
+    if not isinstance(tiling, Tiling):
+        tiling = Tiling(*tiling)
+    return ctypes.byref(tiling)
+
+
 _lib = None
 
 
@@ -60,6 +86,12 @@ def lib() -> ctypes.CDLL:
     L.w12_abi_version.restype = i32
     L.w12_status_string.argtypes = [i32]
     L.w12_status_string.restype = ctypes.c_char_p
+    L.w12_padded_rows.argtypes = [i64]
+    L.w12_padded_rows.restype = i64
+    L.w12_bf16_tiled_bytes.argtypes = [i64, i64]
+    L.w12_bf16_tiled_bytes.restype = ctypes.c_size_t
+    L.w12_bf16_tile.argtypes = [p, i64, i64, p, p]
+    L.w12_bf16_tile.restype = i32
     L.w12_plane_bytes.argtypes = [i64, i64]
     L.w12_plane_bytes.restype = ctypes.c_size_t
     L.w12_meta_bytes.argtypes = [i64, i64]
@@ -72,6 +104,12 @@ def lib() -> ctypes.CDLL:
     L.w12_gemm.restype = i32
     L.bf16_gemm.argtypes = [p, i64, i64, p, i64, i64, p, i64, i32, p]
     L.bf16_gemm.restype = i32
+    L.w12_gemm_ex.argtypes = [p, i64, i64, p, p, p, p, i64, i64, p, i64, i32, p, p]
+    L.w12_gemm_ex.restype = i32
+    L.bf16_gemm_ex.argtypes = [p, i64, i64, p, i64, i64, p, i64, i32, p, p]
+    L.bf16_gemm_ex.restype = i32
+    L.w12_default_tiling.argtypes = [i64, i64, i64, ctypes.POINTER(Tiling)]
+    L.w12_default_tiling.restype = i32
     L.w12_gemm_variant.argtypes = [i64, i64, i64, i32]
     L.w12_gemm_variant.restype = ctypes.c_char_p
     _lib = L
@@ -124,12 +162,26 @@ def w12_status_string(status: int) -> str:
     return lib().w12_status_string(int(status)).decode()
 
 
+def w12_padded_rows(N: int) -> int:
+    return int(lib().w12_padded_rows(int(N)))
+
+
+def w12_bf16_tiled_bytes(N: int, K: int) -> int:
+    return int(lib().w12_bf16_tiled_bytes(int(N), int(K)))
+
+
 def w12_plane_bytes(N: int, K: int) -> int:
     return int(lib().w12_plane_bytes(int(N), int(K)))
 
 
 def w12_meta_bytes(N: int, K: int) -> int:
     return int(lib().w12_meta_bytes(int(N), int(K)))
+
+
+def w12_default_tiling(M: int, N: int, K: int) -> Tiling:
+    t = Tiling()
+    _check(lib().w12_default_tiling(int(M), int(N), int(K), ctypes.byref(t)), "w12_default_tiling")
+    return t
 
 
 def w12_gemm_variant(M: int, N: int, K: int, is_w12: bool = True) -> str | None:
@@ -139,7 +191,8 @@ def w12_gemm_variant(M: int, N: int, K: int, is_w12: bool = True) -> str | None:
 
 @dataclass
 class W12Weight:
-    """A packed [N, K] weight: three uint8 planes [N, K/2] and meta [N, K/128]."""
+    """A packed [N, K] weight: three flat uint8 planes of w12_plane_bytes(N, K)
+    and a flat uint8 meta array of w12_meta_bytes(N, K) (tiled layout)."""
     p0: torch.Tensor
     p1: torch.Tensor
     p2: torch.Tensor
@@ -152,13 +205,39 @@ class W12Weight:
         return 3 * self.p0.numel() + self.meta.numel()
 
 
+@dataclass
+class BF16Tiled:
+    """An [N, K] BF16 weight in the control layout (flat, padded rows)."""
+    w: torch.Tensor
+    N: int
+    K: int
+
+    @property
+    def nbytes(self) -> int:
+        return 2 * self.w.numel()
+
+
 def empty_weight(N: int, K: int, device="cuda") -> W12Weight:
     pb, mb = w12_plane_bytes(N, K), w12_meta_bytes(N, K)
     if pb == 0:
         raise W12Error(-2, "empty_weight(%d, %d)" % (N, K))
-    mk = lambda: torch.empty((N, K // 2), dtype=torch.uint8, device=device)
-    return W12Weight(mk(), mk(), mk(), torch.empty((N, K // GROUP), dtype=torch.uint8,
-                                                   device=device), N, K)
+    mk = lambda: torch.empty(pb, dtype=torch.uint8, device=device)
+    return W12Weight(mk(), mk(), mk(), torch.empty(mb, dtype=torch.uint8, device=device), N, K)
+
+
+def w12_bf16_tile(w: torch.Tensor) -> BF16Tiled:
+    """Arrange a row-major BF16 [N, K] weight in the control layout."""
+    w = _bf16_2d(w, "w")
+    if not w.is_contiguous():
+        raise ValueError("w must be contiguous")
+    N, K = w.shape
+    nb = w12_bf16_tiled_bytes(N, K)
+    if nb == 0:
+        raise W12Error(-2, "w12_bf16_tile(%d, %d)" % (N, K))
+    out = torch.empty(nb // 2, dtype=torch.bfloat16, device=w.device)
+    _check(lib().w12_bf16_tile(_dev_ptr(w, "w"), N, K, _dev_ptr(out, "w_tiled"), _stream()),
+           "w12_bf16_tile")
+    return BF16Tiled(out, N, K)
 
 
 def w12_pack(w: torch.Tensor, out: W12Weight | None = None,
@@ -232,29 +311,36 @@ def _x_args(x: torch.Tensor) -> tuple[int, int]:
 
 
 def w12_gemm(x: torch.Tensor, wt: W12Weight, out_dtype: torch.dtype = torch.float32,
-             y: torch.Tensor | None = None) -> torch.Tensor:
-    """y[m, n] = sum_k x[m, k] W[n, k] with W rebuilt from the container."""
+             y: torch.Tensor | None = None, tiling=None) -> torch.Tensor:
+    """y[m, n] = sum_k x[m, k] W[n, k] with W rebuilt from the container.
+    `tiling` (a Tiling or a (kind, r, kw, depth) tuple) selects w12_gemm_ex."""
     M, ldx = _x_args(x)
     if y is None:
         y, _ = _out_tensor(M, wt.N, out_dtype, x.device)
     ldy, yt = _y_args(y)
-    _check(lib().w12_gemm(_dev_ptr(x, "x"), M, ldx, _dev_ptr(wt.p0, "p0"), _dev_ptr(wt.p1, "p1"),
-                          _dev_ptr(wt.p2, "p2"), _dev_ptr(wt.meta, "meta"), wt.N, wt.K,
-                          _dev_ptr(y, "y"), ldy, yt, _stream()), "w12_gemm")
+    args = (_dev_ptr(x, "x"), M, ldx, _dev_ptr(wt.p0, "p0"), _dev_ptr(wt.p1, "p1"),
+            _dev_ptr(wt.p2, "p2"), _dev_ptr(wt.meta, "meta"), wt.N, wt.K, _dev_ptr(y, "y"),
+            ldy, yt)
+    if tiling is None:
+        _check(lib().w12_gemm(*args, _stream()), "w12_gemm")
+    else:
+        _check(lib().w12_gemm_ex(*args, _tiling_arg(tiling), _stream()), "w12_gemm_ex")
     return y
 
 
-def bf16_gemm(x: torch.Tensor, w: torch.Tensor, out_dtype: torch.dtype = torch.float32,
-              y: torch.Tensor | None = None) -> torch.Tensor:
-    """The same-tiling control: y = x . W^T with W read as plain BF16 [N, K]."""
+def bf16_gemm(x: torch.Tensor, wt: BF16Tiled, out_dtype: torch.dtype = torch.float32,
+              y: torch.Tensor | None = None, tiling=None) -> torch.Tensor:
+    """The same-tiling control: y = x . W^T with W read as BF16 words from the
+    control layout (see w12_bf16_tile)."""
     M, ldx = _x_args(x)
-    w = _bf16_2d(w, "w")
-    if not w.is_contiguous():
-        raise ValueError("w must be contiguous")
-    N, K = w.shape
+    if not isinstance(wt, BF16Tiled):
+        raise TypeError("bf16_gemm takes a BF16Tiled weight (w12_bf16_tile)")
     if y is None:
-        y, _ = _out_tensor(M, N, out_dtype, x.device)
+        y, _ = _out_tensor(M, wt.N, out_dtype, x.device)
     ldy, yt = _y_args(y)
-    _check(lib().bf16_gemm(_dev_ptr(x, "x"), M, ldx, _dev_ptr(w, "w"), N, K, _dev_ptr(y, "y"),
-                           ldy, yt, _stream()), "bf16_gemm")
+    args = (_dev_ptr(x, "x"), M, ldx, _dev_ptr(wt.w, "w_tiled"), wt.N, wt.K, _dev_ptr(y, "y"), ldy, yt)
+    if tiling is None:
+        _check(lib().bf16_gemm(*args, _stream()), "bf16_gemm")
+    else:
+        _check(lib().bf16_gemm_ex(*args, _tiling_arg(tiling), _stream()), "bf16_gemm_ex")
     return y

@@ -67,6 +67,8 @@ def _load():
     lib.w12o_pack.restype = i64
     lib.w12o_unpack.argtypes = [p, p, p, p, i64, i64, p]
     lib.w12o_unpack.restype = i32
+    lib.w12o_bf16_tile.argtypes = [p, i64, i64, p]
+    lib.w12o_bf16_tile.restype = i32
     lib.w12o_gemm_bf16_f64.argtypes = [p, i64, i64, p, i64, p]
     lib.w12o_gemm_bf16_f64.restype = i32
     lib.w12o_gemm_w12_f64.argtypes = [p, i64, i64, p, p, p, p, i64, p, i32]
@@ -124,26 +126,40 @@ def decode_many(code: np.ndarray, beta: int) -> np.ndarray:
 
 # ---- tensor level ----------------------------------------------------------
 
+def padded_rows(N: int) -> int:
+    """Rows of the container: N rounded up to a multiple of 16 (tile height)."""
+    return (N + 15) // 16 * 16
+
+
 def plane_bytes(N: int, K: int) -> int:
-    return N * K // 2
+    return padded_rows(N) * K // 2
 
 
 def meta_bytes(N: int, K: int) -> int:
-    return N * (K // GROUP)
+    return padded_rows(N) * (K // GROUP)
+
+
+def meta_of(meta: np.ndarray, N: int, K: int) -> np.ndarray:
+    """View a flat meta array as [N, K/128] (row n, group g), undoing the
+    16-row tiling: byte ((n // 16) * (K/128) + g) * 16 + n % 16."""
+    G = K // GROUP
+    m = np.asarray(meta, dtype=np.uint8).reshape(-1, G, 16)      # [tile, g, row]
+    return m.transpose(0, 2, 1).reshape(-1, G)[:N]
 
 
 def pack(w: np.ndarray):
     """BF16 bits [N, K] -> (p0, p1, p2, meta, bad_groups).
 
-    p0/p1/p2 are uint8 [N, K/2]; meta is uint8 [N, K/128]."""
+    p0/p1/p2 are flat uint8 arrays of plane_bytes(N, K); meta is a flat uint8
+    array of meta_bytes(N, K) (tiled layout, see w12_oracle.c)."""
     w = _u16(w)
     N, K = w.shape
     if K % GROUP:
         raise ValueError("K must be a multiple of 128")
-    p0 = np.zeros((N, K // 2), np.uint8)
-    p1 = np.zeros((N, K // 2), np.uint8)
-    p2 = np.zeros((N, K // 2), np.uint8)
-    meta = np.zeros((N, K // GROUP), np.uint8)
+    p0 = np.zeros(plane_bytes(N, K), np.uint8)
+    p1 = np.zeros(plane_bytes(N, K), np.uint8)
+    p2 = np.zeros(plane_bytes(N, K), np.uint8)
+    meta = np.zeros(meta_bytes(N, K), np.uint8)
     bad = _load().w12o_pack(_ptr(w), N, K, _ptr(p0), _ptr(p1), _ptr(p2), _ptr(meta))
     if bad < 0:
         raise ValueError("oracle pack rejected shape %r" % ((N, K),))
@@ -151,14 +167,24 @@ def pack(w: np.ndarray):
 
 
 def unpack(p0, p1, p2, meta, N: int, K: int) -> np.ndarray:
-    arrs = [np.ascontiguousarray(a, dtype=np.uint8) for a in (p0, p1, p2, meta)]
-    for a, n in zip(arrs, (N * K // 2,) * 3 + (N * (K // GROUP),)):
+    arrs = [np.ascontiguousarray(a, dtype=np.uint8).reshape(-1) for a in (p0, p1, p2, meta)]
+    for a, n in zip(arrs, (plane_bytes(N, K),) * 3 + (meta_bytes(N, K),)):
         if a.size != n:
             raise ValueError("container size mismatch")
     w = np.empty((N, K), np.uint16)
     if _load().w12o_unpack(*(_ptr(a) for a in arrs), N, K, _ptr(w)) != 0:
         raise ValueError("oracle unpack rejected shape %r" % ((N, K),))
     return w
+
+
+def bf16_tile(w: np.ndarray) -> np.ndarray:
+    """Row-major BF16 [N, K] -> the control layout (flat, padded_rows(N)*K words)."""
+    w = _u16(w)
+    N, K = w.shape
+    out = np.empty(padded_rows(N) * K, np.uint16)
+    if _load().w12o_bf16_tile(_ptr(w), N, K, _ptr(out)) != 0:
+        raise ValueError("oracle bf16_tile rejected shape %r" % ((N, K),))
+    return out
 
 
 def gemm_bf16_f64(x: np.ndarray, w: np.ndarray) -> np.ndarray:
@@ -177,7 +203,10 @@ def gemm_w12_f64(x: np.ndarray, p0, p1, p2, meta, N: int, nthreads: int = 1) -> 
     """Decode the container row by row and form y = x . W^T in fp64."""
     x = _u16(x)
     M, K = x.shape
-    arrs = [np.ascontiguousarray(a, dtype=np.uint8) for a in (p0, p1, p2, meta)]
+    arrs = [np.ascontiguousarray(a, dtype=np.uint8).reshape(-1) for a in (p0, p1, p2, meta)]
+    for a, n in zip(arrs, (plane_bytes(N, K),) * 3 + (meta_bytes(N, K),)):
+        if a.size != n:
+            raise ValueError("container size mismatch")
     y = np.empty((M, N), np.float64)
     rc = _load().w12o_gemm_w12_f64(_ptr(x), M, K, *(_ptr(a) for a in arrs), N,
                                    _ptr(y), int(nthreads))

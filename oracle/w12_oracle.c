@@ -29,10 +29,19 @@
  *   group is flagged (bit 7 of its metadata byte) and the offending element
  *   is written as the window floor +-2^(2*beta+2-127) (sign kept).
  *
- * Layout (per row n, K % 128 == 0):
- *   plane p is u8[N][K/2]; element k lives in byte n*K/2 + 4*(k/8) + (k%8)%4,
- *   low nibble when k%8 < 4, high nibble otherwise ("split-nibble" order);
- *   meta is u8[N][K/128] = beta | (bad ? 0x80 : 0).
+ * Layout (K % 128 == 0; rows padded to Np = N rounded up to a multiple of 16,
+ * padding rows hold zero nibbles and a zero meta byte):
+ *   each plane is Np*K/2 bytes made of 1024-byte blocks, one per (16-row
+ *   tile T = n/16, 128-weight group g = k/128), blocks ordered by (T, g);
+ *   inside a block, 64 pieces of 16 bytes; piece L = 16*q + c (q = 0..3,
+ *   c = n%16) holds row n and, in its dword b (b = 0..3), the 8 weights
+ *   k = 128*g + 32*b + 8*q + e (e = 0..7) in "split-nibble" order: byte e%4
+ *   of the dword, low nibble for e < 4, high nibble for e >= 4;
+ *   meta is Np*K/128 bytes: 16 bytes per (T, g), one per row c, each
+ *   beta | (bad ? 0x80 : 0).
+ * The same order with whole BF16 words is the layout of the BF16 control
+ * (w12o_bf16_tile): block (T, g) of 2048 words, sub-block b of 512 words,
+ * 8 words per piece L, words k = 128*g + 32*b + 8*q + e in natural order.
  *
  * Build: gcc -O2 -std=c11 -shared -fPIC w12_oracle.c -o libw12_oracle.so -lpthread
  * (no -ffast-math: the GEMM must keep IEEE semantics).
@@ -138,16 +147,30 @@ void w12o_decode_many(const uint16_t *code, int64_t n, int beta, uint16_t *v)
         v[i] = w12o_decode(code[i], beta);
 }
 
-/* ---- plane addressing (split-nibble order) ----------------------------- */
+/* ---- plane addressing (16 x 128 tiles, split-nibble order) ------------- */
+
+int64_t w12o_padded_rows(int64_t N)
+{
+    return (N + 15) / 16 * 16;
+}
 
 static int64_t nibble_byte(int64_t n, int64_t K, int64_t k)
 {
-    return n * (K / 2) + 4 * (k / 8) + (k % 8) % 4;
+    int64_t tile = n / 16, c = n % 16;
+    int64_t group = k / W12O_GROUP, r = k % W12O_GROUP;
+    int64_t b = r / 32, q = (r % 32) / 8, e = r % 8;
+    int64_t block = tile * (K / W12O_GROUP) + group;
+    return block * 1024 + (16 * q + c) * 16 + 4 * b + e % 4;
 }
 
 static int nibble_shift(int64_t k)
 {
     return (k % 8) < 4 ? 0 : 4;
+}
+
+static int64_t meta_byte(int64_t n, int64_t K, int64_t k)
+{
+    return ((n / 16) * (K / W12O_GROUP) + k / W12O_GROUP) * 16 + n % 16;
 }
 
 static void put_nibble(uint8_t *plane, int64_t n, int64_t K, int64_t k, int nib)
@@ -165,6 +188,8 @@ static int get_nibble(const uint8_t *plane, int64_t n, int64_t K, int64_t k)
 /* ---- pack / unpack ------------------------------------------------------- */
 
 /* Returns the number of unencodable (flagged) groups, or -1 on bad shape. */
+/* The planes and meta must hold w12o_padded_rows(N) rows; padding rows are
+ * written as zeros. */
 int64_t w12o_pack(const uint16_t *w, int64_t N, int64_t K,
                   uint8_t *p0, uint8_t *p1, uint8_t *p2, uint8_t *meta)
 {
@@ -172,6 +197,11 @@ int64_t w12o_pack(const uint16_t *w, int64_t N, int64_t K,
         return -1;
     int64_t groups = K / W12O_GROUP;
     int64_t bad_groups = 0;
+    int64_t Np = w12o_padded_rows(N);
+    memset(p0, 0, (size_t)(Np * K / 2));
+    memset(p1, 0, (size_t)(Np * K / 2));
+    memset(p2, 0, (size_t)(Np * K / 2));
+    memset(meta, 0, (size_t)(Np * groups));
     for (int64_t n = 0; n < N; n++) {
         for (int64_t g = 0; g < groups; g++) {
             int emax = 0;
@@ -192,7 +222,7 @@ int64_t w12o_pack(const uint16_t *w, int64_t N, int64_t K,
                 put_nibble(p1, n, K, k, (code >> 4) & 0xF);
                 put_nibble(p2, n, K, k, (code >> 8) & 0xF);
             }
-            meta[n * groups + g] = (uint8_t)(beta | (bad ? 0x80 : 0));
+            meta[meta_byte(n, K, g * W12O_GROUP)] = (uint8_t)(beta | (bad ? 0x80 : 0));
             bad_groups += bad;
         }
     }
@@ -206,14 +236,34 @@ int w12o_unpack(const uint8_t *p0, const uint8_t *p1, const uint8_t *p2,
 {
     if (N < 0 || K < 0 || K % W12O_GROUP != 0)
         return -1;
-    int64_t groups = K / W12O_GROUP;
     for (int64_t n = 0; n < N; n++) {
         for (int64_t k = 0; k < K; k++) {
-            int beta = meta[n * groups + k / W12O_GROUP] & 0x7F;
+            int beta = meta[meta_byte(n, K, k)] & 0x7F;
             uint16_t code = (uint16_t)((get_nibble(p2, n, K, k) << 8) |
                                        (get_nibble(p1, n, K, k) << 4) |
                                        get_nibble(p0, n, K, k));
             w[n * K + k] = w12o_decode(code, beta);
+        }
+    }
+    return 0;
+}
+
+/* ---- BF16 control layout ----------------------------------------------------
+ * Row-major BF16 [N, K] -> the tiled word order of the control GEMM
+ * (w12o_padded_rows(N) * K words; padding rows are zero). */
+int w12o_bf16_tile(const uint16_t *w, int64_t N, int64_t K, uint16_t *out)
+{
+    if (N < 0 || K < 0 || K % W12O_GROUP != 0)
+        return -1;
+    int64_t Np = w12o_padded_rows(N);
+    memset(out, 0, (size_t)(Np * K) * sizeof(uint16_t));
+    for (int64_t n = 0; n < N; n++) {
+        for (int64_t k = 0; k < K; k++) {
+            int64_t tile = n / 16, c = n % 16;
+            int64_t group = k / W12O_GROUP, r = k % W12O_GROUP;
+            int64_t b = r / 32, q = (r % 32) / 8, e = r % 8;
+            int64_t block = tile * (K / W12O_GROUP) + group;
+            out[block * 2048 + b * 512 + (16 * q + c) * 8 + e] = w[n * K + k];
         }
     }
     return 0;
@@ -253,12 +303,11 @@ struct gemm_w12_job {
 static void *gemm_w12_rows(void *arg)
 {
     struct gemm_w12_job *j = (struct gemm_w12_job *)arg;
-    int64_t groups = j->K / W12O_GROUP;
     for (int64_t n = j->n_begin; n < j->n_end; n++) {
         for (int64_t m = 0; m < j->M; m++) {
             double acc = 0.0;
             for (int64_t k = 0; k < j->K; k++) {
-                int beta = j->meta[n * groups + k / W12O_GROUP] & 0x7F;
+                int beta = j->meta[meta_byte(n, j->K, k)] & 0x7F;
                 uint16_t code = (uint16_t)((get_nibble(j->p2, n, j->K, k) << 8) |
                                            (get_nibble(j->p1, n, j->K, k) << 4) |
                                            get_nibble(j->p0, n, j->K, k));

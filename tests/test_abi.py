@@ -14,7 +14,7 @@ MIS = P(4098)       # every call below fails validation before any launch)
 def test_loads_and_exports_every_declared_symbol():
     L = w12.lib()
     names = w12.header_functions()
-    assert set(names) >= {"w12_pack", "w12_unpack", "w12_gemm", "bf16_gemm",
+    assert set(names) >= {"w12_pack", "w12_unpack", "w12_gemm", "bf16_gemm", "w12_bf16_tile",
                           "w12_plane_bytes", "w12_meta_bytes", "w12_status_string",
                           "w12_abi_version", "w12_gemm_variant"}
     for n in names:
@@ -25,6 +25,10 @@ def test_loads_and_exports_every_declared_symbol():
 def test_sizes():
     assert w12.w12_plane_bytes(7168, 5120) == 7168 * 5120 // 2
     assert w12.w12_meta_bytes(7168, 5120) == 7168 * 40
+    assert w12.w12_padded_rows(1) == 16 and w12.w12_padded_rows(32) == 32
+    assert w12.w12_plane_bytes(3, 128) == 16 * 64
+    assert w12.w12_meta_bytes(17, 256) == 32 * 2
+    assert w12.w12_bf16_tiled_bytes(17, 256) == 32 * 256 * 2
     assert w12.w12_plane_bytes(3, 100) == 0
     assert w12.w12_meta_bytes(0, 128) == 0
 
@@ -64,6 +68,9 @@ def test_bf16_gemm_rejects():
 
 def test_pack_unpack_reject():
     L = w12.lib()
+    assert L.w12_bf16_tile(None, 4, 128, A16, None) == -1
+    assert L.w12_bf16_tile(A16, 4, 100, A16, None) == -2
+    assert L.w12_bf16_tile(A16, 4, 128, MIS, None) == -3
     assert L.w12_pack(None, 4, 128, A16, A16, A16, A16, None, None) == -1
     assert L.w12_pack(A16, 4, 130, A16, A16, A16, A16, None, None) == -2
     assert L.w12_pack(MIS, 4, 128, A16, A16, A16, A16, None, None) == -3
@@ -75,9 +82,33 @@ def test_pack_unpack_reject():
 
 def test_variant_selection():
     assert w12.w12_gemm_variant(1, 7168, 5120).startswith("w12_gemv_m1_")
-    assert w12.w12_gemm_variant(8, 7168, 5120, False).startswith("bf16_gemv_m8_")
+    assert w12.w12_gemm_variant(4, 7168, 5120, False).startswith("bf16_gemv_m4_")
+    assert w12.w12_gemm_variant(8, 7168, 5120).startswith("w12_mfma_mt16_")
     assert w12.w12_gemm_variant(9, 7168, 5120).startswith("w12_mfma_mt16_")
     assert w12.w12_gemm_variant(16, 34816, 5120).startswith("w12_mfma_mt16_")
     assert w12.w12_gemm_variant(17, 5120, 17408).startswith("w12_mfma_mt32_")
     assert w12.w12_gemm_variant(33, 5120, 17408) is None
     assert w12.w12_gemm_variant(1, 5120, 100) is None
+
+
+def test_explicit_tiling_rejects():
+    L = w12.lib()
+    args = (A16, 9, 512, A16, A16, A16, A16, 64, 512, A16, 64, 0)
+    bad = [w12.Tiling(0, 1, 1, 4),      # GEMV needs M <= 8
+           w12.Tiling(2, 1, 1, 4),      # unknown kind
+           w12.Tiling(1, 3, 1, 2),      # r not built
+           w12.Tiling(1, 1, 3, 2),      # kw not built
+           w12.Tiling(1, 2, 1, 8)]      # (r, depth) pair not built
+    for t in bad:
+        assert L.w12_gemm_ex(*args, w12._tiling_arg(t), None) == -6, t
+    assert L.bf16_gemm_ex(A16, 9, 512, A16, 64, 512, A16, 64, 0,
+                          w12._tiling_arg(w12.Tiling(0, 1, 1, 2)), None) == -6
+
+
+def test_default_tiling():
+    t = w12.w12_default_tiling(1, 7168, 5120)
+    assert t.kind == 0 and t.astuple() in w12.GEMV_TILINGS
+    t = w12.w12_default_tiling(16, 34816, 5120)
+    assert t.kind == 1 and t.astuple() in w12.MFMA_TILINGS
+    with pytest.raises(w12.W12Error):
+        w12.w12_default_tiling(40, 64, 512)

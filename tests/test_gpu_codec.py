@@ -59,7 +59,8 @@ def test_every_code_of_every_base(oracle):
     wt, back, bad = _check_pack(oracle, bits, "all codes")
     assert bad == 0
     assert np.array_equal(back, bits)
-    assert np.array_equal(to_host_u8(wt.meta)[:, 0], np.arange(121, dtype=np.uint8))
+    assert np.array_equal(oracle.meta_of(to_host_u8(wt.meta), 121, 4096)[:, 0],
+                          np.arange(121, dtype=np.uint8))
 
 
 @pytest.mark.parametrize("name", ["tiny", "qkv", "gate_up", "down"])
@@ -111,3 +112,14 @@ def test_strict_pack_raises():
     raw = inputs.TINY.weights_raw()
     with pytest.raises(w12.W12UnencodableError):
         w12.pack(to_dev(raw), strict=True)
+
+
+@pytest.mark.parametrize("N,K", [(1, 128), (37, 384), (1000, 640), (7168, 5120)])
+def test_bf16_control_layout(oracle, N, K):
+    """w12_bf16_tile is the oracle's control-layout permutation, word for word."""
+    require_gpu()
+    rng = np.random.default_rng(N + K)
+    bits = rng.integers(0, 65536, size=(N, K), dtype=np.uint32).astype(np.uint16)
+    t = w12.w12_bf16_tile(to_dev(bits))
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host_u16(t.w), oracle.bf16_tile(bits))

@@ -31,6 +31,7 @@ class Prepared:
         self.N, self.K = raw.shape
         self.wt = w12.w12_pack(to_dev(raw))
         self.w_bf16 = w12.w12_unpack(self.wt)
+        self.w_tiled = w12.w12_bf16_tile(self.w_bf16)
         torch.cuda.synchronize()
 
     def ref_rows(self, oracle, rows):
@@ -64,7 +65,7 @@ def _sample_rows(N, n=384, seed=0):
 def _run_both(x_bits, P: Prepared, out=torch.float32):
     xd = to_dev(x_bits)
     y12 = w12.w12_gemm(xd, P.wt, out)
-    y16 = w12.bf16_gemm(xd, P.w_bf16, out)
+    y16 = w12.bf16_gemm(xd, P.w_tiled, out)
     torch.cuda.synchronize()
     return y12, y16
 
@@ -110,7 +111,7 @@ def test_workloads_sampled(oracle, name, M):
 def test_bf16_output_is_rounded_fp32(M):
     P = prepared("tiny")
     xd = to_dev(inputs.TINY.activations(M))
-    for fn, w in ((w12.w12_gemm, P.wt), (w12.bf16_gemm, P.w_bf16)):
+    for fn, w in ((w12.w12_gemm, P.wt), (w12.bf16_gemm, P.w_tiled)):
         yf = fn(xd, w, torch.float32)
         yb = fn(xd, w, torch.bfloat16)
         torch.cuda.synchronize()
@@ -172,3 +173,32 @@ def test_ieee_specials(oracle):
         assert np.array_equal(np.isnan(yh), np.isnan(ref))
         fin = ~np.isnan(ref)
         assert np.array_equal(yh[fin], ref[fin])
+
+
+@pytest.mark.parametrize("tiling", w12.GEMV_TILINGS + w12.MFMA_TILINGS,
+                         ids=lambda t: "k%d_r%d_kw%d_d%d" % t)
+def test_every_tiling(oracle, tiling):
+    """Every instantiated variant, single-chunk and chunked x, ragged rows and
+    a K tail, against the oracle; W12 and BF16 bitwise equal per tiling."""
+    Ms = [1, 3, 8] if tiling[0] == 0 else [9, 16, 17, 32]
+    for shape in ((301, 640), (33, 2688), (45, 5120), (77, 17408)):
+        P = prepared(shape)
+        rows = np.arange(P.N)
+        w_ref = P.ref_rows(oracle, rows)
+        for M in Ms:
+            what = "tiling %s %s M=%d" % (tiling, shape, M)
+            print(what, flush=True)
+            x = inputs.gaussian_bf16((M, shape[1]), 1.0, 3 * M + shape[1])
+            xd = to_dev(x)
+            try:
+                y12 = w12.w12_gemm(xd, P.wt, tiling=tiling)
+            except w12.W12Error as e:
+                # a chunked x buffer for this tiling would not fit LDS
+                rows = M if tiling[0] == 0 else (16 if M <= 16 else 32)
+                assert e.status == -6 and rows * shape[1] * 2 > 40 * 1024, what
+                continue
+            y16 = w12.bf16_gemm(xd, P.w_tiled, tiling=tiling)
+            torch.cuda.synchronize()
+            y12h, y16h = y12.cpu().numpy(), y16.cpu().numpy()
+            assert np.array_equal(y12h.view(np.uint32), y16h.view(np.uint32)), what
+            assert_gemm_close(y12h, oracle.gemm_bf16_f64(x, w_ref), oracle.tolerance(x, w_ref), what)

@@ -103,26 +103,52 @@ def test_layout_worked_example(oracle, variant, k7):
     w[0, :8] = [0x3F80, 0xBF00, 0x3C01, 0x8000, 0x3A5B, 0x0001, 0xB9C7, k7]
     p0, p1, p2, meta, bad = oracle.pack(w)
     for name, plane in (("p0", p0), ("p1", p1), ("p2", p2)):
-        assert plane.shape == (1, 64)
-        assert list(plane[0, :4]) == g[variant + "." + name]
-        assert not plane[0, 4:].any()
-    assert list(meta[0]) == g[variant + ".meta"]
+        assert plane.shape == (1024,)           # one 16-row tile x one group
+        assert list(plane[:4]) == g[variant + "." + name]
+        assert not plane[4:].any()
+    assert meta.shape == (16,)
+    assert list(meta[:1]) == g[variant + ".meta"]
+    assert not meta[1:].any()                   # padding rows
     assert bad == g[variant + ".bad"][0]
     out = oracle.unpack(p0, p1, p2, meta, 1, 128)
     assert list(out[0, :8]) == g[variant + ".unpacked"]
     assert not out[0, 8:].any()
 
 
-def test_container_bytes_are_three_quarters(oracle):
-    """Packed planes are exactly 0.75x the BF16 bytes (12 of 16 bits), plus
-    one metadata byte per 128-weight group."""
-    for N, K in ((1, 128), (3, 256), (1024, 512), (7, 17408)):
+def test_tile_addressing(oracle):
+    """Where each weight lands in the tiled layout: a single marked weight at
+    (n, k) shows up as one nibble at the byte the layout rule gives, and the
+    meta byte of its (row, group) is the only non-zero meta byte."""
+    N, K = 37, 384
+    for (n, k) in [(0, 0), (0, 4), (0, 9), (5, 31), (15, 32), (3, 45), (16, 0), (17, 130),
+                   (36, 383), (20, 200)]:
         w = np.zeros((N, K), np.uint16)
+        w[n, k] = 0x3F8F                      # 1.0 with mantissa low nibble 0xF
         p0, p1, p2, meta, _ = oracle.pack(w)
-        assert p0.nbytes + p1.nbytes + p2.nbytes == 0.75 * (2 * N * K)
-        assert meta.nbytes == N * K // 128
-        assert oracle.plane_bytes(N, K) * 3 == 3 * N * K // 2
-        assert oracle.meta_bytes(N, K) == meta.nbytes
+        G = K // 128
+        r = k % 128
+        b, q, e = r // 32, (r % 32) // 8, r % 8
+        byte = ((n // 16) * G + k // 128) * 1024 + (16 * q + n % 16) * 16 + 4 * b + e % 4
+        shift = 0 if e < 4 else 4
+        nz = np.flatnonzero(p0)
+        assert list(nz) == [byte] and p0[byte] == 0xF << shift, (n, k)
+        mz = np.flatnonzero(meta)
+        assert list(mz) == [((n // 16) * G + k // 128) * 16 + n % 16], (n, k)
+        assert oracle.meta_of(meta, N, K)[n, k // 128] == meta[mz[0]]
+
+
+def test_container_bytes_are_three_quarters(oracle):
+    """Packed planes are exactly 0.75x the BF16 bytes (12 of 16 bits) when N
+    is a multiple of the 16-row tile (else 0.75x the padded rows), plus one
+    metadata byte per 128-weight group."""
+    for N, K in ((16, 128), (48, 256), (1024, 512), (16, 17408), (7168, 5120)):
+        assert 3 * oracle.plane_bytes(N, K) == 0.75 * (2 * N * K)
+        assert oracle.meta_bytes(N, K) == N * K // 128
+    for N, K in ((1, 128), (3, 256), (7, 17408)):
+        p0, p1, p2, meta, _ = oracle.pack(np.zeros((N, K), np.uint16))
+        Np = (N + 15) // 16 * 16
+        assert p0.nbytes + p1.nbytes + p2.nbytes == 0.75 * (2 * Np * K)
+        assert meta.nbytes == Np * K // 128
 
 
 def _groups_random(rng, rows, gap_rows):
@@ -144,7 +170,7 @@ def test_flag_iff_not_lossless(oracle):
     p0, p1, p2, meta, bad = oracle.pack(b)
     back = oracle.unpack(p0, p1, p2, meta, 400, 128)
     changed = np.any(back != b, axis=1)
-    flagged = (meta[:, 0] & 0x80) != 0
+    flagged = (oracle.meta_of(meta, 400, 128)[:, 0] & 0x80) != 0
     assert np.array_equal(changed, flagged)
     assert bad == int(flagged.sum())
     assert flagged[::7].all()
@@ -178,4 +204,26 @@ def test_special_values_round_trip(oracle):
     p0, p1, p2, meta, bad = oracle.pack(w)
     assert bad == 0
     assert np.array_equal(oracle.unpack(p0, p1, p2, meta, 3, 128), w)
-    assert list(meta[:, 0]) == [0, 120, 120]
+    assert list(oracle.meta_of(meta, 3, 128)[:, 0]) == [0, 120, 120]
+
+
+def test_bf16_control_layout_is_the_same_permutation(oracle):
+    """The BF16 control order places word (n, k) where the W12 planes place
+    its nibbles: word index = 2 * (plane byte) + (nibble is high), read per
+    1 KB sub-block -- checked by packing single marked weights."""
+    N, K = 21, 256
+    rng = np.random.default_rng(4)
+    w = rng.integers(0, 65536, size=(N, K), dtype=np.uint32).astype(np.uint16)
+    t = oracle.bf16_tile(w)
+    assert t.shape == (oracle.padded_rows(N) * K,)
+    assert sorted(t[t != 0].tolist()) == sorted(w[w != 0].tolist())
+    for (n, k) in [(0, 0), (0, 7), (0, 8), (0, 32), (1, 0), (15, 127), (16, 128), (20, 255)]:
+        marked = np.zeros((N, K), np.uint16)
+        marked[n, k] = 0x3F81
+        p0, _, _, _, _ = oracle.pack(marked)
+        byte = int(np.flatnonzero(p0)[0])
+        block, inblock = divmod(byte, 1024)
+        lane, within = divmod(inblock, 16)
+        b, j = divmod(within, 4)
+        e = j + (4 if p0[byte] >= 16 else 0)
+        assert t[block * 2048 + b * 512 + lane * 8 + e] == w[n, k], (n, k)
