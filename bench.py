@@ -40,6 +40,7 @@ if HERE not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0           # MI355X HBM3E, published
 ROTATE_BYTES = 1 << 30           # >= 1 GiB of distinct weights per rotation
+CALIB_BYTES = 256 << 20          # size of the counter-calibration copy
 METRIC = "w12_gemm effective weight GB/s & % HBM peak; speedup vs BF16 GEMM, M=1–32"
 
 
@@ -53,6 +54,14 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU-oracle work to time")
     ap.add_argument("--sweep-ms", type=str, default="1,2,4,8,16,32")
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("KERNEL_STATS_CSV", "VARIANT"),
+                    help="print a markdown summary of a rocprofv3 --stats kernel table")
+    ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "VARIANT"),
+                    help="print a markdown summary of FETCH_SIZE / WRITE_SIZE counter runs")
+    ap.add_argument("--command", default="", help="command line recorded in a summary")
+    ap.add_argument("--pmc-calibration", action="store_true",
+                    help="also run a plain 256 MiB device-to-device copy 4 times (the "
+                         "known-size reference for HBM byte counters)")
     return ap.parse_args()
 
 
@@ -156,20 +165,104 @@ def measure(torch, w12, wl: Workload, M, steps, warmup, out_dtype):
     }
 
 
+def template_of(variant: str) -> str:
+    """rocprofv3's demangled name of the kernel a variant name refers to, e.g.
+    w12_gemv_m1_r1_kw4_d2_single -> gemm_kernel<w12::kern::FetchW12, false, 1, 1, 4, 2, false>."""
+    f, kind, mr, r, kw, d, mode = variant.split("_")
+    mr = mr.replace("mt", "").replace("m", "")
+    return "gemm_kernel<w12::kern::%s, %s, %s, %s, %s, %s, %s>" % (
+        "FetchW12" if f == "w12" else "FetchBF16", "true" if kind == "mfma" else "false",
+        mr, r[1:], kw[2:], d[1:], "true" if mode == "chunked" else "false")
+
+
+TRAFFIC_TAG = "traffic_record: "
+
+
 def stored_traffic(kernel: str):
-    """HBM bytes per launch from committed rocprofv3 counter readings, if
-    they were taken on the current kernel sources; else None."""
-    path = os.path.join(HERE, "profiles", "traffic.json")
-    if not os.path.exists(path):
+    """HBM bytes per launch from a committed counter summary under profiles/,
+    if it was taken on the current kernel sources; else None."""
+    pdir = os.path.join(HERE, "profiles")
+    if not os.path.isdir(pdir):
         return None
+    for fn in sorted(os.listdir(pdir)):
+        if not fn.endswith(".md"):
+            continue
+        with open(os.path.join(pdir, fn)) as f:
+            for line in f:
+                if line.startswith(TRAFFIC_TAG):
+                    rec = json.loads(line[len(TRAFFIC_TAG):])
+                    if rec.get("kernel") == kernel and rec.get("source_sha") == source_sha():
+                        return rec.get("hbm_bytes_per_launch")
+    return None
+
+
+def _read_csv(path):
+    import csv
     with open(path) as f:
-        rec = json.load(f)
-    if rec.get("source_sha") != source_sha():
-        return None
-    k = rec.get("kernels", {}).get(kernel)
-    if not k:
-        return None
-    return k.get("hbm_bytes_per_launch")
+        return list(csv.DictReader(f))
+
+
+def summarize_trace(path, variant, command):
+    rows = _read_csv(path)
+    lines = ["# rocprofv3 kernel trace: %s" % variant, "",
+             "Command (run from the repository root on the GPU box):", "",
+             "    " + command, "",
+             "Kernel-source hash: `%s`" % source_sha(), "",
+             "| kernel | calls | average ns | min ns | max ns |", "|---|---|---|---|---|"]
+    for r in rows:
+        lines.append("| `%s` | %s | %.0f | %s | %s |" % (r["Name"][:110], r["Calls"],
+                                                        float(r["AverageNs"]), r["MinNs"], r["MaxNs"]))
+    want = template_of(variant)
+    hit = [r for r in rows if want in r["Name"]]
+    if hit:
+        lines += ["", "Average duration of `%s` (%s): %.3f us over %s calls (graph-replayed "
+                  "launches plus warm-up launches)." % (variant, want, float(hit[0]["AverageNs"]) / 1e3,
+                                                        hit[0]["Calls"])]
+    print("\n".join(lines))
+
+
+def summarize_pmc(fetch_path, write_path, variant, command):
+    import statistics
+    want = template_of(variant)
+    def per_kernel(path):
+        out = {}
+        for r in _read_csv(path):
+            out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return out
+    fetch, write = per_kernel(fetch_path), per_kernel(write_path)
+    calib_kib = CALIB_BYTES / 1024
+    # The calibration copies are the only device copies that large; the fill
+    # of the copy source writes the same 256 MiB.
+    f_cal = max(v for k, vs in fetch.items() if "copyBuffer" in k for v in vs)
+    w_cal = max(v for vs in write.values() for v in vs)
+    f_scale, w_scale = calib_kib / f_cal, calib_kib / w_cal
+    fk = [k for k in fetch if want in k]
+    wk = [k for k in write if want in k]
+    f_med = statistics.median(fetch[fk[0]])
+    w_med = statistics.median(write[wk[0]])
+    hbm = f_med * 1024 * f_scale + w_med * 1024 * w_scale
+    lines = ["# HBM bytes of %s (rocprofv3 FETCH_SIZE / WRITE_SIZE)" % variant, "",
+             "Commands (run from the repository root on the GPU box, one counter per run):", "",
+             "    " + command.replace("{CTR}", "FETCH_SIZE"),
+             "    " + command.replace("{CTR}", "WRITE_SIZE"), "",
+             "Kernel-source hash: `%s`" % source_sha(), "",
+             "Calibration: a plain %d MiB device-to-device copy (bench.py --pmc-calibration) "
+             "reads FETCH_SIZE = %.1f KiB and its source fill writes WRITE_SIZE = %.1f KiB, "
+             "so the counters are scaled by %.4f (fetch) and %.4f (write)."
+             % (CALIB_BYTES >> 20, f_cal, w_cal, f_scale, w_scale), "",
+             "| kernel | dispatches | FETCH_SIZE KiB (median) | WRITE_SIZE KiB (median) |",
+             "|---|---|---|---|"]
+    for k in sorted(fetch):
+        if k in write:
+            lines.append("| `%s` | %d | %.1f | %.1f |" % (k[:110], len(fetch[k]), statistics.median(fetch[k]),
+                                                          statistics.median(write[k])))
+    lines += ["", "HBM bytes per launch of `%s`: %.0f (fetch %.0f + write %.0f)."
+              % (variant, hbm, f_med * 1024 * f_scale, w_med * 1024 * w_scale), "",
+              TRAFFIC_TAG + json.dumps({"kernel": variant, "source_sha": source_sha(),
+                                        "hbm_bytes_per_launch": round(hbm),
+                                        "fetch_kib": f_med, "write_kib": w_med,
+                                        "fetch_scale": f_scale, "write_scale": w_scale})]
+    print("\n".join(lines))
 
 
 def cpu_baseline(case, M, seconds):
@@ -202,6 +295,12 @@ def cpu_baseline(case, M, seconds):
 
 def main():
     args = parse()
+    if args.summarize_trace:
+        summarize_trace(*args.summarize_trace, args.command)
+        return
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc, args.command)
+        return
     if args.gpus != 1:
         print("bench.py runs on one GPU only: the W12 decode GEMM of one weight on "
               "one MI355X; --gpus %d is not supported" % args.gpus, file=sys.stderr)
@@ -222,6 +321,14 @@ def main():
           file=sys.stderr, flush=True)
     head = measure(torch, w12, wl, 1, args.steps, args.warmup, torch.float32)
     print("headline: %s" % json.dumps(head), file=sys.stderr, flush=True)
+
+    if args.pmc_calibration:
+        src = torch.empty(CALIB_BYTES // 4, dtype=torch.int32, device="cuda").fill_(7)
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     sweep = []
     if not args.no_sweep:

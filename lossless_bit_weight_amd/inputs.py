@@ -27,11 +27,12 @@ import numpy as np
 def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
     """Round fp32 to the nearest BF16 (ties to even); NaN stays a quiet NaN."""
     a = np.ascontiguousarray(a, dtype=np.float32)
-    u = a.view(np.uint32).astype(np.uint64)
-    rounded = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+    u = a.view(np.uint32)
+    # no uint32 overflow: the largest non-NaN pattern 0xFF800000 + 0x8000 fits
+    rounded = ((u + np.uint32(0x7FFF) + ((u >> 16) & np.uint32(1))) >> 16).astype(np.uint16)
     nan = np.isnan(a)
     if nan.any():
-        rounded[nan] = ((u[nan] >> 16).astype(np.uint16) | 0x0040)
+        rounded[nan] = ((u[nan] >> 16).astype(np.uint16) | np.uint16(0x0040))
     return rounded
 
 

@@ -32,8 +32,9 @@ def test_deterministic_and_seeded():
 
 
 def test_value_structure():
-    w = inputs.QKV.weights_raw()
-    assert w.shape == (7168, 5120) and w.dtype == np.uint16
+    case = inputs.GemmCase("qkv rows", 1024, 5120, 1, 0.02, 1.0, 201, 202, 203)
+    w = case.weights_raw()
+    assert w.shape == (1024, 5120) and w.dtype == np.uint16
     zeros = (w & 0x7FFF) == 0
     frac = zeros.mean()
     assert 0.0008 < frac < 0.0012
