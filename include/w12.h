@@ -172,6 +172,9 @@ int bf16_gemm(const uint16_t *x, int64_t M, int64_t ldx,
  *   kw    : waves of a 256-thread workgroup that split K (1, 2, 4).
  *   depth : 128-weight groups each wave keeps in flight
  *           (r = 1: 2, 4 or 8; r = 2: 2 or 4).
+ *   x_direct : GEMV with M <= 4 only: 1 = each lane loads the x values of a
+ *           group together with its weights (no LDS staging, no barrier);
+ *           0 = x is staged in LDS.
  * When x does not fit LDS at once it is streamed in chunks; some kw x depth
  * combinations then need more than 64 KB of LDS and are rejected.
  * The summation order depends on the tiling; w12 and bf16 kernels with the
@@ -182,6 +185,7 @@ typedef struct {
     int32_t r;
     int32_t kw;
     int32_t depth;
+    int32_t x_direct;
 } w12_tiling_t;
 
 /* The tiling w12_gemm / bf16_gemm use for this shape.  Returns W12_OK, or

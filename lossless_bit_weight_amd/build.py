@@ -9,6 +9,7 @@ selection is disabled for device code.
 from __future__ import annotations
 
 import os
+import re
 import subprocess
 import sys
 from concurrent.futures import ThreadPoolExecutor
@@ -29,9 +30,27 @@ ARCH = os.environ.get("W12_OFFLOAD_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
+    "-Rpass-analysis=kernel-resource-usage",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function", "-I" + os.path.join(ROOT, "include"),
 ]
+
+
+def _check_resources(src: str, remarks: list[str]) -> None:
+    """Fail the build if any kernel spills registers or uses scratch memory:
+    a spilling variant is never worth shipping."""
+    kernel = None
+    bad = []
+    for line in remarks:
+        m = re.search(r"remark: Function Name: (\S+)", line)
+        if m:
+            kernel = m.group(1)
+            continue
+        m = re.search(r"remark: +(VGPRs Spill|SGPRs Spill|ScratchSize \[bytes/lane\]): (\d+)", line)
+        if m and int(m.group(2)) > 0:
+            bad.append("%s: %s = %s" % (kernel, m.group(1), m.group(2)))
+    if bad:
+        raise RuntimeError("kernels in %s spill or use scratch:\n  %s" % (src, "\n  ".join(bad)))
 
 
 def _compile(item) -> str:
@@ -39,13 +58,15 @@ def _compile(item) -> str:
     obj = os.path.join(BUILD_DIR, name + ".o")
     cmd = [HIPCC, *FLAGS, *defines, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
+    lines = r.stderr.splitlines()
+    remarks = [l for l in lines if "remark:" in l]
     # the host pass does not know the device-only feature flag: drop that note
-    err = "\n".join(l for l in r.stderr.splitlines()
-                    if "packed-fp32-ops" not in l and l.strip())
+    err = "\n".join(l for l in lines
+                    if "packed-fp32-ops" not in l and "remark:" not in l and l.strip()
+                    and not l.lstrip().startswith(("|", "^")) and not re.match(r"^\s*\d+ \|", l))
     if r.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s" % (src, err))
-    if err:
-        print(err, file=sys.stderr)
+    _check_resources(name, remarks)
     return obj
 
 

@@ -124,6 +124,8 @@ static int resolve_tiling(const w12_tiling_t* tiling, int64_t M, int64_t N, int6
     t.r = tiling->r;
     t.kw = tiling->kw;
     t.depth = tiling->depth;
+    if (tiling->x_direct != 0 && tiling->x_direct != 1) return W12_ERR_UNSUPPORTED;
+    t.xdirect = tiling->x_direct;
     if (!w12::complete_tiling(t, (int)M, K)) return W12_ERR_UNSUPPORTED;
     *out = t;
     return W12_OK;
@@ -179,6 +181,7 @@ int w12_default_tiling(int64_t M, int64_t N, int64_t K, w12_tiling_t* out) {
     out->r = t.r;
     out->kw = t.kw;
     out->depth = t.depth;
+    out->x_direct = t.xdirect;
     return W12_OK;
 }
 

@@ -55,10 +55,16 @@ bool complete_tiling(Tiling& t, int M, int64_t K) {
         if (!pair_built(t.r, t.depth)) return false;
         t.chunked = (int64_t)t.mt * K * 2 > kern::kSingleBytes;
         if (t.chunked && !kern::chunk_ok(t.mt, kern::mfma_kc(t.mt, t.kw, t.depth))) return false;
+        if (t.xdirect) return false;
     } else {
         if (M < 1 || M > 8) return false;
         t.mt = M;
         if (!pair_built(t.r, t.depth)) return false;
+        if (t.xdirect) {
+            if (!kern::xd_ok(false, M, t.r, t.depth)) return false;
+            t.chunked = 0;
+            return true;
+        }
         t.chunked = (int64_t)M * K * 2 > kern::kSingleBytes;
         if (t.chunked && !kern::chunk_ok(M, kern::gemv_kc(M, t.kw, t.depth))) return false;
     }
@@ -103,15 +109,15 @@ Tiling choose_tiling(int M, int64_t N, int64_t K) {
 const char* tiling_name(const Tiling& t, bool is_w12) {
     static std::mutex mu;
     static std::unordered_map<int, std::string> names;
-    const int key = (is_w12 << 24) | (t.mfma << 23) | (t.chunked << 22) | (t.mt << 12) |
-                    (t.r << 8) | (t.kw << 4) | t.depth;
+    const int key = (is_w12 << 25) | (t.xdirect << 24) | (t.mfma << 23) | (t.chunked << 22) |
+                    (t.mt << 12) | (t.r << 8) | (t.kw << 4) | t.depth;
     std::lock_guard<std::mutex> lock(mu);
     auto it = names.find(key);
     if (it != names.end()) return it->second.c_str();
     std::string n = is_w12 ? "w12_" : "bf16_";
     n += t.mfma ? "mfma_mt" : "gemv_m";
     n += std::to_string(t.mt) + "_r" + std::to_string(t.r) + "_kw" + std::to_string(t.kw) + "_d" +
-         std::to_string(t.depth) + (t.chunked ? "_chunked" : "_single");
+         std::to_string(t.depth) + (t.xdirect ? "_xdirect" : t.chunked ? "_chunked" : "_single");
     return names.emplace(key, std::move(n)).first->second.c_str();
 }
 

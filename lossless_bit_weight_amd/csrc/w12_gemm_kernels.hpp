@@ -80,12 +80,21 @@ struct FetchW12 {
         uint4 a, b, c;
         uint32_t beta;
     };
-    __device__ __forceinline__ static void load(const GemmArgs& g, int64_t blk, int lane, Raw& r) {
-        const int64_t off = blk * 1024 + 16 * lane;
-        r.a = *reinterpret_cast<const uint4*>(g.p0 + off);
-        r.b = *reinterpret_cast<const uint4*>(g.p1 + off);
-        r.c = *reinterpret_cast<const uint4*>(g.p2 + off);
-        r.beta = g.meta[blk * 16 + (lane & 15)];
+    // Wave-uniform part of the addresses of tile `tile` (all groups); the
+    // lane part is added per load.
+    struct Base {
+        const uint8_t *p0, *p1, *p2, *meta;
+    };
+    __device__ __forceinline__ static Base base(const GemmArgs& g, int64_t tile) {
+        const int64_t blk0 = tile * (g.K / 128);
+        return Base{g.p0 + blk0 * 1024, g.p1 + blk0 * 1024, g.p2 + blk0 * 1024, g.meta + blk0 * 16};
+    }
+    __device__ __forceinline__ static void load(const Base& b, int grp, int lane, Raw& r) {
+        const uint32_t off = (uint32_t)grp * 1024u + 16u * (uint32_t)lane;
+        r.a = *reinterpret_cast<const uint4*>(b.p0 + off);
+        r.b = *reinterpret_cast<const uint4*>(b.p1 + off);
+        r.c = *reinterpret_cast<const uint4*>(b.p2 + off);
+        r.beta = b.meta[(uint32_t)grp * 16u + (uint32_t)(lane & 15)];
     }
     __device__ __forceinline__ static void block(const Raw& r, int b, uint32_t out[4]) {
         const Lut t = make_lut(r.beta & 0x7Fu);
@@ -100,10 +109,16 @@ struct FetchBF16 {
     struct Raw {
         uint4 q[4];
     };
-    __device__ __forceinline__ static void load(const GemmArgs& g, int64_t blk, int lane, Raw& r) {
-        const uint4* p = reinterpret_cast<const uint4*>(g.w) + blk * 256 + lane;
+    struct Base {
+        const uint8_t* w;
+    };
+    __device__ __forceinline__ static Base base(const GemmArgs& g, int64_t tile) {
+        return Base{reinterpret_cast<const uint8_t*>(g.w) + tile * (g.K / 128) * 4096};
+    }
+    __device__ __forceinline__ static void load(const Base& b, int grp, int lane, Raw& r) {
+        const uint32_t off = (uint32_t)grp * 4096u + 16u * (uint32_t)lane;
 #pragma unroll
-        for (int b = 0; b < 4; ++b) r.q[b] = p[64 * b];
+        for (int i = 0; i < 4; ++i) r.q[i] = *reinterpret_cast<const uint4*>(b.w + off + 1024u * i);
     }
     __device__ __forceinline__ static void block(const Raw& r, int b, uint32_t out[4]) {
         out[0] = r.q[b].x;
@@ -165,13 +180,18 @@ struct XAll {
         units = mrows * units_per_row;
 #pragma unroll
         for (int j = 0; j < kSingleUnits; ++j) {
-            const int id = threadIdx.x + kThreads * j;
-            const int m = id / units_per_row;
-            const int64_t k = 8 * (int64_t)(id % units_per_row);
-            const bool ok = id < units && m < g.M;
-            const int mc = m < g.M ? m : g.M - 1;
-            const uint4 v0 = *reinterpret_cast<const uint4*>(g.x + (int64_t)mc * g.ldx + k);
-            v[j] = ok ? v0 : make_uint4(0, 0, 0, 0);
+            // The guard is uniform over the workgroup (it depends on j and
+            // the shape only), so the loads of a round are all issued or all
+            // skipped and the count of later loads stays known.
+            if (kThreads * j < units) {
+                const int id = threadIdx.x + kThreads * j;
+                const int m = id / units_per_row;
+                const int64_t k = 8 * (int64_t)(id % units_per_row);
+                const bool ok = id < units && m < g.M;
+                const int mc = m < g.M ? m : g.M - 1;
+                const uint4 v0 = *reinterpret_cast<const uint4*>(g.x + (int64_t)mc * g.ldx + k);
+                v[j] = ok ? v0 : make_uint4(0, 0, 0, 0);
+            }
         }
     }
     template <class Layout>
@@ -244,6 +264,8 @@ __host__ __device__ constexpr int kc_of(bool mfma, int rows, int KW, int D) {
             _Pragma("unroll") for (int d = 0; d < (D); ++d) {                             \
                 compute(ring[d], jb + d);                                                 \
                 fetch(jb + d + (D), ring[d]);                                             \
+                /* keep the next slot's arithmetic below this slot's loads */             \
+                __builtin_amdgcn_sched_barrier(0);                                        \
             }                                                                             \
         }                                                                                 \
         if constexpr (CHUNKED) {                                                          \
@@ -274,8 +296,13 @@ __host__ __device__ constexpr int kc_of(bool mfma, int rows, int KW, int D) {
 // MFMA = false: GEMV, MR = M (1..8).  MFMA = true: MR = 16 or 32 (x rows,
 // zero padded).
 
-template <class F, bool MFMA, int MR, int R, int KW, int D, bool CHUNKED>
+// XD (GEMV only): x is not staged in LDS; each ring slot also carries the
+// x values of its group, loaded straight from memory (they are the same for
+// the 16 lanes of a quarter and stay in L1/L2), so there is no prologue
+// barrier at all.
+template <class F, bool MFMA, int MR, int R, int KW, int D, bool CHUNKED, bool XD>
 __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
+    static_assert(!(XD && (MFMA || CHUNKED)), "direct x is a single-pass GEMV mode");
     constexpr int KC = kc_of(MFMA, MR, KW, D);
     constexpr int kRowWaves = 4 / KW;
     constexpr int kBuf = MR * KC / 8;                 // uint4 per x chunk buffer
@@ -305,13 +332,32 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
     int c = 0;
     int next_boundary = CHUNKED && nchunks > 1 ? L : 1 << 30;
 
-    Raw ring[D][R];
-    auto fetch = [&](int j, Raw (&dst)[R]) {
-        j = j < Jlast ? j : Jlast;
-        int64_t grp = kw + (int64_t)j * KW;
-        grp = grp < G ? grp : G - 1;   // only when this wave has no group at all
+    typename F::Base wbase[R];
 #pragma unroll
-        for (int r = 0; r < R; ++r) F::load(g, tload[r] * G + grp, lane, dst[r]);
+    for (int r = 0; r < R; ++r) wbase[r] = F::base(g, tload[r]);
+    const int glast = (int)G - 1;
+
+    struct Slot {
+        Raw w[R];
+        uint4 x[XD ? MR : 1][4];
+    };
+    Slot ring[D];
+    auto fetch = [&](int j, Slot& dst) {
+        j = j < Jlast ? j : Jlast;
+        int grp = kw + j * KW;
+        grp = grp < glast ? grp : glast;   // only when this wave has no group at all
+#pragma unroll
+        for (int r = 0; r < R; ++r) F::load(wbase[r], grp, lane, dst.w[r]);
+        if constexpr (XD) {
+#pragma unroll
+            for (int m = 0; m < MR; ++m) {
+                const int mc = m < g.M ? m : g.M - 1;   // rows past M: valid address, unused
+#pragma unroll
+                for (int b = 0; b < 4; ++b)
+                    dst.x[m][b] = *reinterpret_cast<const uint4*>(
+                        g.x + (int64_t)mc * g.ldx + 128 * grp + 32 * b + 8 * q);
+            }
+        }
     };
 
     float gacc[MFMA ? 1 : R][MFMA ? 1 : MR];
@@ -328,7 +374,8 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
             for (int m = 0; m < MR; ++m) gacc[r][m] = 0.f;
     }
 
-    auto compute = [&](const Raw (&rr)[R], int j) {
+    auto compute = [&](const Slot& slot, int j) {
+        const Raw(&rr)[R] = slot.w;
         const uint4* xb = lds + (CHUNKED ? (c & 1) * kBuf : 0);
         const int64_t grp = kw + (int64_t)j * KW;
         // unit of (block b) = (128 grp + 32 b + 8 q) / 8, chunk relative
@@ -353,7 +400,12 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
             } else {
                 uint4 xv[MR];
 #pragma unroll
-                for (int m = 0; m < MR; ++m) xv[m] = xb[XLayout::phys(m, u0 + 4 * b, units_per_row)];
+                for (int m = 0; m < MR; ++m) {
+                    if constexpr (XD)
+                        xv[m] = m < g.M ? slot.x[m][b] : make_uint4(0, 0, 0, 0);
+                    else
+                        xv[m] = xb[XLayout::phys(m, u0 + 4 * b, units_per_row)];
+                }
 #pragma unroll
                 for (int r = 0; r < R; ++r) {
                     uint32_t wv[4];
@@ -377,15 +429,15 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
     XAll xa;
     if constexpr (CHUNKED)
         xr.load(g, 0);
-    else
+    else if constexpr (!XD)
         xa.load(g, MR);
 #pragma unroll
     for (int d = 0; d < D; ++d) fetch(d, ring[d]);
     if constexpr (CHUNKED)
         xr.template store<FixedLayout<XLayout, KC / 8>>(lds);
-    else
+    else if constexpr (!XD)
         xa.template store<XLayout>(lds);
-    __syncthreads();
+    if constexpr (!XD) __syncthreads();
     if constexpr (CHUNKED) xr.load(g, (int64_t)(nchunks > 1 ? 1 : 0) * KC);
 
     auto store_next = [&]() {
@@ -440,7 +492,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
                 gacc[r][m] = v;
             }
         if constexpr (KW > 1) {
-            __syncthreads();  // every wave is done reading x
+            if constexpr (!XD) __syncthreads();  // every wave is done reading x
             float* red = reinterpret_cast<float*>(lds);
             if (kw > 0 && q == 0) {
 #pragma unroll
@@ -475,44 +527,57 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
 // ---- launch helpers ----------------------------------------------------------------------
 
 // Bytes of LDS a launch needs (x buffers; the reductions reuse them).
-template <bool MFMA, int MR, int R, int KW, int D, bool CHUNKED>
+template <bool MFMA, int MR, int R, int KW, int D, bool CHUNKED, bool XD>
 size_t lds_bytes(int64_t K) {
-    const size_t x = CHUNKED ? 2 * (size_t)MR * kc_of(MFMA, MR, KW, D) * 2 : (size_t)MR * (K / 8) * 16;
+    const size_t x = XD ? 0
+                     : CHUNKED ? 2 * (size_t)MR * kc_of(MFMA, MR, KW, D) * 2
+                               : (size_t)MR * (K / 8) * 16;
     const size_t red = KW == 1 ? 0
                        : MFMA ? (size_t)(KW - 1) * (4 / KW) * 64 * R * (MR / 16) * 16
                               : (size_t)(KW - 1) * (4 / KW) * 16 * R * MR * 4;
     return x > red ? x : red;
 }
 
-template <class F, bool MFMA, int MR, int R, int KW, int D, bool CHUNKED>
+template <class F, bool MFMA, int MR, int R, int KW, int D, bool CHUNKED, bool XD>
 hipError_t launch_one(const GemmArgs& a, hipStream_t s) {
     constexpr int kTilesPerWG = (4 / KW) * R;
     const int64_t ntiles = (a.N + 15) / 16;
     const dim3 grid((unsigned)((ntiles + kTilesPerWG - 1) / kTilesPerWG));
-    const size_t lds = lds_bytes<MFMA, MR, R, KW, D, CHUNKED>(a.K);
-    hipLaunchKernelGGL((gemm_kernel<F, MFMA, MR, R, KW, D, CHUNKED>), grid, dim3(kThreads), lds, s, a);
+    const size_t lds = lds_bytes<MFMA, MR, R, KW, D, CHUNKED, XD>(a.K);
+    hipLaunchKernelGGL((gemm_kernel<F, MFMA, MR, R, KW, D, CHUNKED, XD>), grid, dim3(kThreads), lds, s, a);
     return hipGetLastError();
 }
 
+// Direct x is built for the GEMV up to M = 4, when the ring (weights plus
+// 16 x-registers per x row, per slot) fits about 192 VGPRs; larger rings
+// spill.
+__host__ __device__ constexpr bool xd_ok(bool mfma, int mr, int r, int d) {
+    return !mfma && mr <= 4 && d * 16 * (r + mr) <= 192;
+}
+
 template <class F, bool MFMA, int MR, int R, int KW, int D>
-hipError_t launch_ch(const GemmArgs& a, bool chunked, hipStream_t s) {
-    if (!chunked) return launch_one<F, MFMA, MR, R, KW, D, false>(a, s);
-    if constexpr (chunk_ok(MR, kc_of(MFMA, MR, KW, D))) return launch_one<F, MFMA, MR, R, KW, D, true>(a, s);
+hipError_t launch_ch(const GemmArgs& a, const Tiling& t, hipStream_t s) {
+    if (t.xdirect) {
+        if constexpr (xd_ok(MFMA, MR, R, D)) return launch_one<F, MFMA, MR, R, KW, D, false, true>(a, s);
+        return hipErrorInvalidValue;
+    }
+    if (!t.chunked) return launch_one<F, MFMA, MR, R, KW, D, false, false>(a, s);
+    if constexpr (chunk_ok(MR, kc_of(MFMA, MR, KW, D)))
+        return launch_one<F, MFMA, MR, R, KW, D, true, false>(a, s);
     return hipErrorInvalidValue;
 }
 
 template <class F, bool MFMA, int MR, int R, int D>
 hipError_t launch_kw(const GemmArgs& a, const Tiling& t, hipStream_t s) {
-    const bool ch = t.chunked != 0;
     switch (t.kw) {
-        case 1: return launch_ch<F, MFMA, MR, R, 1, D>(a, ch, s);
-        case 2: return launch_ch<F, MFMA, MR, R, 2, D>(a, ch, s);
-        case 4: return launch_ch<F, MFMA, MR, R, 4, D>(a, ch, s);
+        case 1: return launch_ch<F, MFMA, MR, R, 1, D>(a, t, s);
+        case 2: return launch_ch<F, MFMA, MR, R, 2, D>(a, t, s);
+        case 4: return launch_ch<F, MFMA, MR, R, 4, D>(a, t, s);
         default: return hipErrorInvalidValue;
     }
 }
 
-// (r, depth) pairs that are instantiated: see gemm_pair_built().
+// (r, depth) pairs that are instantiated: see pair_built() in w12_gemm.hip.
 template <class F, bool MFMA, int MR>
 hipError_t dispatch(const GemmArgs& a, const Tiling& t, hipStream_t s) {
     if (t.r == 1 && t.depth == 2) return launch_kw<F, MFMA, MR, 1, 2>(a, t, s);

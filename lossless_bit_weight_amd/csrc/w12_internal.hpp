@@ -30,6 +30,8 @@ struct GemmArgs {
 //   mt      = GEMV: M (1..8); MFMA: x rows padded to 16 or 32.
 //   kw      = waves of a workgroup that split K between them (1, 2 or 4).
 //   depth   = 32-weight slices each lane keeps in flight (2, 4 or 8).
+//   xdirect = 1: GEMV only, M <= 4: x is read by each lane with its weights
+//             instead of being staged in LDS.
 //   chunked = 0 if all of x is staged in LDS at once, 1 if it is streamed
 //             through LDS in double-buffered chunks (set from the shape).
 struct Tiling {
@@ -38,6 +40,7 @@ struct Tiling {
     int r;
     int kw;
     int depth;
+    int xdirect;
     int chunked;
 };
 

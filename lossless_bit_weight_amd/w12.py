@@ -44,21 +44,27 @@ class W12UnencodableError(ValueError):
 
 
 class Tiling(ctypes.Structure):
-    """w12_tiling_t: kind (0 GEMV, 1 MFMA), r, kw, depth."""
+    """w12_tiling_t: kind (0 GEMV, 1 MFMA), r, kw, depth, x_direct."""
     _fields_ = [("kind", ctypes.c_int32), ("r", ctypes.c_int32), ("kw", ctypes.c_int32),
-                ("depth", ctypes.c_int32)]
+                ("depth", ctypes.c_int32), ("x_direct", ctypes.c_int32)]
 
     def astuple(self):
-        return (self.kind, self.r, self.kw, self.depth)
+        return (self.kind, self.r, self.kw, self.depth, self.x_direct)
 
     def __repr__(self):
-        return "Tiling(kind=%d, r=%d, kw=%d, depth=%d)" % self.astuple()
+        return "Tiling(kind=%d, r=%d, kw=%d, depth=%d, x_direct=%d)" % self.astuple()
 
 
-# Every tiling the library instantiates: (kind, r, kw, depth).
+# Every tiling the library instantiates: (kind, r, kw, depth, x_direct).
+# x_direct needs the GEMV, M <= 4 and a ring of at most 192 registers:
+# depth * 16 * (r + M) <= 192 (x_direct_fits).
 _PAIRS = ((1, 2), (1, 4), (1, 8), (2, 2), (2, 4))
-GEMV_TILINGS = [(0, r, kw, d) for (r, d) in _PAIRS for kw in (1, 2, 4)]
-MFMA_TILINGS = [(1, r, kw, d) for (r, d) in _PAIRS for kw in (1, 2, 4)]
+GEMV_TILINGS = [(0, r, kw, d, xd) for (r, d) in _PAIRS for kw in (1, 2, 4) for xd in (0, 1)]
+MFMA_TILINGS = [(1, r, kw, d, 0) for (r, d) in _PAIRS for kw in (1, 2, 4)]
+
+
+def x_direct_fits(M: int, r: int, depth: int) -> bool:
+    return M <= 4 and depth * 16 * (r + M) <= 192
 
 
 def _tiling_arg(tiling):

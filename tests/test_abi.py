@@ -94,11 +94,15 @@ def test_variant_selection():
 def test_explicit_tiling_rejects():
     L = w12.lib()
     args = (A16, 9, 512, A16, A16, A16, A16, 64, 512, A16, 64, 0)
+    assert L.w12_gemm_ex(A16, 5, 512, A16, A16, A16, A16, 64, 512, A16, 64, 0,
+                         w12._tiling_arg(w12.Tiling(0, 1, 1, 2, 1)), None) == -6  # x_direct: M <= 4
     bad = [w12.Tiling(0, 1, 1, 4),      # GEMV needs M <= 8
            w12.Tiling(2, 1, 1, 4),      # unknown kind
            w12.Tiling(1, 3, 1, 2),      # r not built
            w12.Tiling(1, 1, 3, 2),      # kw not built
-           w12.Tiling(1, 2, 1, 8)]      # (r, depth) pair not built
+           w12.Tiling(1, 2, 1, 8),      # (r, depth) pair not built
+           w12.Tiling(1, 1, 1, 2, 1),   # direct x is a GEMV mode
+           w12.Tiling(0, 1, 1, 2, 2)]   # x_direct is 0 or 1
     for t in bad:
         assert L.w12_gemm_ex(*args, w12._tiling_arg(t), None) == -6, t
     assert L.bf16_gemm_ex(A16, 9, 512, A16, 64, 512, A16, 64, 0,

@@ -176,11 +176,11 @@ def test_ieee_specials(oracle):
 
 
 @pytest.mark.parametrize("tiling", w12.GEMV_TILINGS + w12.MFMA_TILINGS,
-                         ids=lambda t: "k%d_r%d_kw%d_d%d" % t)
+                         ids=lambda t: "k%d_r%d_kw%d_d%d_x%d" % t)
 def test_every_tiling(oracle, tiling):
     """Every instantiated variant, single-chunk and chunked x, ragged rows and
     a K tail, against the oracle; W12 and BF16 bitwise equal per tiling."""
-    Ms = [1, 3, 8] if tiling[0] == 0 else [9, 16, 17, 32]
+    Ms = ([1, 2, 4] if tiling[4] else [1, 3, 8]) if tiling[0] == 0 else [9, 16, 17, 32]
     for shape in ((301, 640), (33, 2688), (45, 5120), (77, 17408)):
         P = prepared(shape)
         rows = np.arange(P.N)
@@ -193,9 +193,12 @@ def test_every_tiling(oracle, tiling):
             try:
                 y12 = w12.w12_gemm(xd, P.wt, tiling=tiling)
             except w12.W12Error as e:
-                # a chunked x buffer for this tiling would not fit LDS
+                # only a chunked x buffer that would not fit LDS is rejected
                 rows = M if tiling[0] == 0 else (16 if M <= 16 else 32)
-                assert e.status == -6 and rows * shape[1] * 2 > 40 * 1024, what
+                if tiling[4]:
+                    assert e.status == -6 and not w12.x_direct_fits(M, tiling[1], tiling[3]), what
+                else:
+                    assert e.status == -6 and rows * shape[1] * 2 > 40 * 1024, what
                 continue
             y16 = w12.bf16_gemm(xd, P.w_tiled, tiling=tiling)
             torch.cuda.synchronize()
