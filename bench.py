@@ -1,6 +1,7 @@
 """Benchmark of the W12 decode GEMM on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-sweep] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-sweep] [--no-stack]
+                    [--no-cpu-baseline]
 
 Prints ONE JSON line.  The headline workload is the attention QKV projection
 of a ~27B dense decoder at single-request decode: W [7168, 5120] packed to
@@ -21,6 +22,11 @@ start; AI Radar summary of SpecPilot, English edition, opening paragraph):
 The same protocol times the same-tiling BF16 control; `speedup_vs_bf16` is
 the ratio of the two.  `cpu_baseline` times the CPU oracle (decode + fp64
 GEMM, all host threads) on the same workload.
+
+Beside the headline: the M sweep over the QKV, gate+up and down weights;
+pack / unpack throughput on the QKV weight; and one decode step over the
+64-layer linear stack (256 GEMMs, 31.9 GB of W12 weights, captured as one
+graph) at M in {1, 4, 8, 16, 32}.
 """
 from __future__ import annotations
 
@@ -51,6 +57,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--no-sweep", action="store_true", help="headline workload only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-stack", action="store_true",
+                    help="skip the 64-layer linear-stack decode step")
+    ap.add_argument("--stack-ms", type=str, default="1,4,8,16,32")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU-oracle work to time")
     ap.add_argument("--sweep-ms", type=str, default="1,2,4,8,16,32")
@@ -167,12 +176,14 @@ def measure(torch, w12, wl: Workload, M, steps, warmup, out_dtype):
 
 def template_of(variant: str) -> str:
     """rocprofv3's demangled name of the kernel a variant name refers to, e.g.
-    w12_gemv_m1_r1_kw4_d2_single -> gemm_kernel<w12::kern::FetchW12, false, 1, 1, 4, 2, false>."""
+    w12_gemv_m1_r1_kw4_d2_single ->
+    gemm_kernel<w12::kern::FetchW12, false, 1, 1, 4, 2, false, false>."""
     f, kind, mr, r, kw, d, mode = variant.split("_")
     mr = mr.replace("mt", "").replace("m", "")
-    return "gemm_kernel<w12::kern::%s, %s, %s, %s, %s, %s, %s>" % (
-        "FetchW12" if f == "w12" else "FetchBF16", "true" if kind == "mfma" else "false",
-        mr, r[1:], kw[2:], d[1:], "true" if mode == "chunked" else "false")
+    tf = lambda b: "true" if b else "false"
+    return "gemm_kernel<w12::kern::%s, %s, %s, %s, %s, %s, %s, %s>" % (
+        "FetchW12" if f == "w12" else "FetchBF16", tf(kind == "mfma"),
+        mr, r[1:], kw[2:], d[1:], tf(mode == "chunked"), tf(mode == "xdirect"))
 
 
 TRAFFIC_TAG = "traffic_record: "
@@ -265,6 +276,84 @@ def summarize_pmc(fetch_path, write_path, variant, command):
     print("\n".join(lines))
 
 
+def time_codec(torch, w12, wl: Workload, steps):
+    """Pack, unpack and control-layout throughput on the workload's weight
+    (events around back-to-back launches; inputs resident in HBM)."""
+    w = w12.w12_unpack(wl.w12_copies[0])
+    out = w12.empty_weight(wl.N, wl.K)
+    wb = torch.empty_like(w)
+    res = {}
+    for name, fn, nbytes in (
+            ("pack", lambda: w12.w12_pack(w, out=out), 2 * wl.N * wl.K + wl.w12_bytes),
+            ("unpack", lambda: w12.w12_unpack(wl.w12_copies[0], out=wb), 2 * wl.N * wl.K + wl.w12_bytes)):
+        for _ in range(5):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        n = max(10, steps // 10)
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / n
+        res[name] = {"us": round(ms * 1e3, 2), "gbps": round(nbytes / ms / 1e6, 1), "bytes": nbytes}
+    return res
+
+
+def stack_step(torch, w12, inputs, ms, steps, warmup):
+    """One decode step over the 64-layer linear stack (QKV, O, gate+up, down
+    per layer): 256 GEMMs back to back, W12 and the BF16 control."""
+    layers = []
+    raw_bad = 0
+    w12_bytes = bf16_bytes = 0
+    for layer in range(inputs.STACK_LAYERS):
+        row = []
+        for j, (N, K) in enumerate(inputs.STACK_SHAPES):
+            w = inputs.device_weights(torch, N, K, 10000 + 10 * layer + j)
+            first, bad = w12.pack(w)
+            raw_bad += bad
+            wc = w12.w12_unpack(first)
+            del first
+            wt, bad = w12.pack(wc)
+            if bad:
+                raise RuntimeError("projected stack weight still has unencodable groups")
+            bt = w12.w12_bf16_tile(wc)
+            del w, wc
+            row.append((wt, bt))
+            w12_bytes += wt.nbytes
+            bf16_bytes += bt.nbytes
+        layers.append(row)
+    torch.cuda.synchronize()
+    print("stack ready: %.2f GB W12, %.2f GB BF16 (raw unencodable groups %d)"
+          % (w12_bytes / 1e9, bf16_bytes / 1e9, raw_bad), file=sys.stderr, flush=True)
+    out = {"layers": inputs.STACK_LAYERS, "w12_gb": round(w12_bytes / 1e9, 3),
+           "bf16_gb": round(bf16_bytes / 1e9, 3), "raw_unencodable_groups": raw_bad, "by_m": []}
+    for M in ms:
+        xs = {K: torch.from_numpy(inputs.gaussian_bf16((M, K), 1.0, 20000 + M).view(np.int16)).cuda()
+              for K in {k for _, k in inputs.STACK_SHAPES}}
+        ys = {N: torch.empty((M, N), dtype=torch.float32, device="cuda")
+              for N in {n for n, _ in inputs.STACK_SHAPES}}
+        def step(fn, idx):
+            def run():
+                for row in layers:
+                    for (wt, bt), (N, K) in zip(row, inputs.STACK_SHAPES):
+                        fn(xs[K], (wt, bt)[idx], y=ys[N])
+            return run
+        ms12, _ = time_graph(torch, [step(w12.w12_gemm, 0)], max(3, steps // 100), max(1, warmup // 20))
+        ms16, _ = time_graph(torch, [step(w12.bf16_gemm, 1)], max(3, steps // 100), max(1, warmup // 20))
+        r = {"M": M, "w12_ms": round(ms12, 4), "bf16_ms": round(ms16, 4),
+             "w12_weight_gbps": round(w12_bytes / ms12 / 1e6, 1),
+             "bf16_weight_gbps": round(bf16_bytes / ms16 / 1e6, 1),
+             "speedup_vs_bf16": round(ms16 / ms12, 4)}
+        out["by_m"].append(r)
+        print("stack M=%d: w12 %.3f ms (%.0f GB/s) bf16 %.3f ms speedup %.3f"
+              % (M, ms12, r["w12_weight_gbps"], ms16, r["speedup_vs_bf16"]), file=sys.stderr, flush=True)
+    del layers
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(case, M, seconds):
     """The CPU oracle as it stands: container decode + fp64 GEMM over the whole
     headline weight on all host threads, repeated until ~`seconds` passed."""
@@ -320,6 +409,7 @@ def main():
     print("headline workload ready (%s, raw unencodable groups %d)" % (head_case.name, wl.raw_bad),
           file=sys.stderr, flush=True)
     head = measure(torch, w12, wl, 1, args.steps, args.warmup, torch.float32)
+    rotation = len(wl.w12_copies)
     print("headline: %s" % json.dumps(head), file=sys.stderr, flush=True)
 
     if args.pmc_calibration:
@@ -346,6 +436,16 @@ def main():
                 del wlc
                 torch.cuda.empty_cache()
 
+    codec = time_codec(torch, w12, wl, args.steps)
+    print("codec: %s" % json.dumps(codec), file=sys.stderr, flush=True)
+
+    stack = None
+    if not args.no_stack:
+        del wl
+        torch.cuda.empty_cache()
+        stack = stack_step(torch, w12, inputs, [int(m) for m in args.stack_ms.split(",") if m],
+                           args.steps, args.warmup)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(head_case, 1, args.cpu_seconds)
@@ -370,7 +470,7 @@ def main():
         "config": {"workload": "QKV projection W[7168,5120] as W12 (group 128), x[1,5120] "
                                "BF16, y fp32; single-request decode GEMV",
                    "N": head_case.N, "K": head_case.K, "M": 1, "group": 128,
-                   "rotation_copies": len(wl.w12_copies)},
+                   "rotation_copies": rotation},
         "pct_hbm_peak": round(100.0 * head["w12_weight_gbps"] / HBM_PEAK_GBPS, 2),
         "w12_us": round(head["w12_us"], 3),
         "bf16_us": round(head["bf16_us"], 3),
@@ -382,6 +482,8 @@ def main():
         "cpu_baseline": cpu,
         "sweep": [{k: (round(v, 3) if isinstance(v, float) else v) for k, v in r.items()}
                   for r in sweep],
+        "codec": codec,
+        "stack": stack,
         "source_sha": source_sha(),
     }
     print(json.dumps(out), flush=True)

@@ -16,6 +16,10 @@ Recipe (numpy PCG64 via ``default_rng``):
     even), then a Bernoulli(p_zero) mask drawn from its own seed replaces an
     element by a zero that keeps the drawn sign (so +0 and -0 both occur);
   * activations: fp32 standard normal * sigma_x, rounded to BF16.
+
+The 64-layer stack (21.1 billion weights) is drawn by the same recipe on the
+device instead (``device_weights``: torch's seeded Philox generator), since
+drawing it on the host takes minutes; it only feeds throughput figures.
 """
 from __future__ import annotations
 
@@ -96,6 +100,22 @@ CASES = {c.name.split()[0]: c for c in (TINY, QKV, GATE_UP, DOWN)}
 # 64-layer stack: per layer QKV, O, gate+up, down (N, K).
 STACK_LAYERS = 64
 STACK_SHAPES = ((7168, 5120), (5120, 5120), (34816, 5120), (5120, 17408))
+
+
+def device_weights(torch, N: int, K: int, seed: int, sigma: float = 0.02,
+                   p_zero: float = 0.001):
+    """The weight recipe drawn on the current GPU with a seeded torch
+    generator: fp32 N(0, sigma) -> BF16 (torch rounds to nearest even), then a
+    Bernoulli(p_zero) subset set to zero with the drawn sign."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    w = torch.randn((N, K), generator=g, device="cuda", dtype=torch.float32)
+    w.mul_(sigma)
+    zero = torch.rand((N, K), generator=g, device="cuda") < p_zero
+    w = w.to(torch.bfloat16)
+    bits = w.view(torch.int16)
+    bits[zero] &= -0x8000                # keep only the sign bit
+    return w
 
 
 def stack_case(layer: int, j: int) -> GemmCase:
