@@ -1,7 +1,7 @@
 """Benchmark of the W12 decode GEMM on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-sweep] [--no-stack]
-                    [--no-cpu-baseline]
+                    [--no-cpu-baseline] [--workload qkv|gate_up|down] [--m M]
 
 Prints ONE JSON line.  The headline workload is the attention QKV projection
 of a ~27B dense decoder at single-request decode: W [7168, 5120] packed to
@@ -48,6 +48,8 @@ HBM_PEAK_GBPS = 8000.0           # MI355X HBM3E, published
 ROTATE_BYTES = 1 << 30           # >= 1 GiB of distinct weights per rotation
 CALIB_BYTES = 256 << 20          # size of the counter-calibration copy
 METRIC = "w12_gemm effective weight GB/s & % HBM peak; speedup vs BF16 GEMM, M=1–32"
+WORKLOAD_NAMES = {"qkv": "QKV projection", "gate_up": "MLP fused gate+up projection",
+                  "down": "MLP down projection"}
 
 
 def parse():
@@ -63,6 +65,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU-oracle work to time")
     ap.add_argument("--sweep-ms", type=str, default="1,2,4,8,16,32")
+    ap.add_argument("--workload", default="qkv", choices=["qkv", "gate_up", "down"],
+                    help="headline weight (default: the QKV projection)")
+    ap.add_argument("--m", type=int, default=1, help="headline x rows (default 1)")
     ap.add_argument("--summarize-trace", nargs=2, metavar=("KERNEL_STATS_CSV", "VARIANT"),
                     help="print a markdown summary of a rocprofv3 --stats kernel table")
     ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "VARIANT"),
@@ -152,8 +157,12 @@ def measure(torch, w12, wl: Workload, M, steps, warmup, out_dtype):
     x = torch.from_numpy(wl.case.activations(M).view(np.int16)).cuda()
     y = torch.empty((M, wl.N), dtype=out_dtype, device="cuda")
     out_b = 4 if out_dtype == torch.float32 else 2
-    l12 = [(lambda c=c: w12.w12_gemm(x, c, y=y)) for c in wl.w12_copies]
-    l16 = [(lambda c=c: w12.bf16_gemm(x, c, y=y)) for c in wl.bf16_copies]
+    # one zero-filled split-K workspace for every launch (allocated outside
+    # the graph; each launch leaves its counters at zero)
+    ws = torch.zeros(max(256, w12.w12_gemm_workspace_bytes(M, wl.N, wl.K)), dtype=torch.uint8,
+                     device="cuda")
+    l12 = [(lambda c=c: w12.w12_gemm(x, c, y=y, workspace=ws)) for c in wl.w12_copies]
+    l16 = [(lambda c=c: w12.bf16_gemm(x, c, y=y, workspace=ws)) for c in wl.bf16_copies]
     ms12, n12 = time_graph(torch, l12, steps, warmup)
     ms16, n16 = time_graph(torch, l16, steps, warmup)
     b12 = gemm_bytes(wl.N, wl.K, M, out_b, wl.w12_bytes)
@@ -177,8 +186,9 @@ def measure(torch, w12, wl: Workload, M, steps, warmup, out_dtype):
 def template_of(variant: str) -> str:
     """rocprofv3's demangled name of the kernel a variant name refers to, e.g.
     w12_gemv_m1_r1_kw4_d2_single ->
-    gemm_kernel<w12::kern::FetchW12, false, 1, 1, 4, 2, false, false>."""
-    f, kind, mr, r, kw, d, mode = variant.split("_")
+    gemm_kernel<w12::kern::FetchW12, false, 1, 1, 4, 2, false, false>
+    (a split-K suffix _sN does not change the kernel)."""
+    f, kind, mr, r, kw, d, mode = variant.split("_")[:7]
     mr = mr.replace("mt", "").replace("m", "")
     tf = lambda b: "true" if b else "false"
     return "gemm_kernel<w12::kern::%s, %s, %s, %s, %s, %s, %s, %s>" % (
@@ -334,11 +344,14 @@ def stack_step(torch, w12, inputs, ms, steps, warmup):
               for K in {k for _, k in inputs.STACK_SHAPES}}
         ys = {N: torch.empty((M, N), dtype=torch.float32, device="cuda")
               for N in {n for n, _ in inputs.STACK_SHAPES}}
+        ws = torch.zeros(max([256] + [w12.w12_gemm_workspace_bytes(M, N, K)
+                                      for N, K in inputs.STACK_SHAPES]),
+                         dtype=torch.uint8, device="cuda")
         def step(fn, idx):
             def run():
                 for row in layers:
                     for (wt, bt), (N, K) in zip(row, inputs.STACK_SHAPES):
-                        fn(xs[K], (wt, bt)[idx], y=ys[N])
+                        fn(xs[K], (wt, bt)[idx], y=ys[N], workspace=ws)
             return run
         ms12, _ = time_graph(torch, [step(w12.w12_gemm, 0)], max(3, steps // 100), max(1, warmup // 20))
         ms16, _ = time_graph(torch, [step(w12.bf16_gemm, 1)], max(3, steps // 100), max(1, warmup // 20))
@@ -404,11 +417,12 @@ def main():
     print("device: %s, %d CUs" % (props.name, props.multi_processor_count), file=sys.stderr,
           flush=True)
 
-    head_case = inputs.QKV
+    head_case = inputs.CASES[args.workload]
+    head_m = args.m
     wl = Workload(head_case, torch, w12)
     print("headline workload ready (%s, raw unencodable groups %d)" % (head_case.name, wl.raw_bad),
           file=sys.stderr, flush=True)
-    head = measure(torch, w12, wl, 1, args.steps, args.warmup, torch.float32)
+    head = measure(torch, w12, wl, head_m, args.steps, args.warmup, torch.float32)
     rotation = len(wl.w12_copies)
     print("headline: %s" % json.dumps(head), file=sys.stderr, flush=True)
 
@@ -448,7 +462,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(head_case, 1, args.cpu_seconds)
+        cpu = cpu_baseline(head_case, head_m, args.cpu_seconds)
         print("cpu baseline: %s" % json.dumps(cpu), file=sys.stderr, flush=True)
 
     kernel = head["w12_kernel"]
@@ -467,9 +481,10 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "QKV projection W[7168,5120] as W12 (group 128), x[1,5120] "
-                               "BF16, y fp32; single-request decode GEMV",
-                   "N": head_case.N, "K": head_case.K, "M": 1, "group": 128,
+        "config": {"workload": "%s: W[%d,%d] as W12 (group 128), x[%d,%d] BF16, y fp32%s"
+                               % (WORKLOAD_NAMES[args.workload], head_case.N, head_case.K, head_m,
+                                  head_case.K, "; single-request decode GEMV" if head_m == 1 else ""),
+                   "N": head_case.N, "K": head_case.K, "M": head_m, "group": 128,
                    "rotation_copies": rotation},
         "pct_hbm_peak": round(100.0 * head["w12_weight_gbps"] / HBM_PEAK_GBPS, 2),
         "w12_us": round(head["w12_us"], 3),

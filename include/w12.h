@@ -43,7 +43,11 @@
  *     is enqueued and a negative w12_status_t is returned;
  *   - launch failures return W12_ERR_HIP;
  *   - calls on different streams are independent (the library is stateless
- *     and thread-safe); outputs must not alias inputs.
+ *     and thread-safe); outputs must not alias inputs;
+ *   - the *_ws / *_ex GEMM calls may split K over workgroups; they then use a
+ *     caller-owned device workspace (w12_gemm_workspace_bytes) that must be
+ *     zero-filled before its first use and is left in that state by every
+ *     call.  Calls that may run at the same time need separate workspaces.
  */
 #ifndef W12_H
 #define W12_H
@@ -55,7 +59,7 @@
 extern "C" {
 #endif
 
-#define W12_ABI_VERSION 1
+#define W12_ABI_VERSION 2
 #define W12_GROUP 128
 #define W12_TILE_ROWS 16
 #define W12_MAX_M 32
@@ -67,7 +71,8 @@ typedef enum {
     W12_ERR_ALIGN = -3,       /* pointer or leading dimension misaligned     */
     W12_ERR_DTYPE = -4,       /* unknown output type                         */
     W12_ERR_UNSUPPORTED = -6, /* M > 32                                      */
-    W12_ERR_HIP = -7          /* the HIP launch reported an error            */
+    W12_ERR_HIP = -7,         /* the HIP launch reported an error            */
+    W12_ERR_WORKSPACE = -8    /* split-K workspace NULL, short or misaligned */
 } w12_status_t;
 
 typedef enum {
@@ -132,6 +137,8 @@ int w12_unpack(const void *p0, const void *p1, const void *p2,
  * By default M <= 4 runs a wavefront-reduction GEMV (v_dot2c_f32_bf16) and
  * 5 <= M <= 32 runs bf16 MFMA with x padded to 16 or 32 rows (measured
  * crossover); w12_gemm_ex selects either explicitly (GEMV up to M = 8).
+ * Each workgroup covers all of K for its rows, so no workspace is needed;
+ * w12_gemm_ws adds the split-K tilings.
  * Errors: W12_ERR_NULL, W12_ERR_SHAPE, W12_ERR_ALIGN, W12_ERR_DTYPE,
  *         W12_ERR_UNSUPPORTED (M > 32), W12_ERR_HIP.
  */
@@ -175,10 +182,17 @@ int bf16_gemm(const uint16_t *x, int64_t M, int64_t ldx,
  *   x_direct : GEMV with M <= 4 only: 1 = each lane loads the x values of a
  *           group together with its weights (no LDS staging, no barrier);
  *           0 = x is staged in LDS.
- * When x does not fit LDS at once it is streamed in chunks; some kw x depth
- * combinations then need more than 64 KB of LDS and are rejected.
- * The summation order depends on the tiling; w12 and bf16 kernels with the
- * same tiling sum in the same order.
+ *   splitk : workgroups that split K between them (0 or 1 = none, up to
+ *           64); the groups are dealt out in contiguous slices of
+ *           ceil(G / splitk) groups (G = K / 128), so the launch uses
+ *           ceil(G / that) slices.  Each slice's fp32 partial sums go to the
+ *           workspace; the last workgroup of a row block to finish adds them
+ *           in slice order and writes y.
+ * When the x columns of a slice do not fit LDS at once they are streamed in
+ * chunks; some kw x depth combinations then need more than 64 KB of LDS and
+ * are rejected.  The summation order depends on the tiling and never on
+ * scheduling; w12 and bf16 kernels with the same tiling sum in the same
+ * order.
  */
 typedef struct {
     int32_t kind;
@@ -186,31 +200,69 @@ typedef struct {
     int32_t kw;
     int32_t depth;
     int32_t x_direct;
+    int32_t splitk;
 } w12_tiling_t;
 
-/* The tiling w12_gemm / bf16_gemm use for this shape.  Returns W12_OK, or
- * W12_ERR_NULL / W12_ERR_SHAPE / W12_ERR_UNSUPPORTED. */
-int w12_default_tiling(int64_t M, int64_t N, int64_t K, w12_tiling_t *out);
+/* The tiling the GEMMs use for this shape: that of w12_gemm / bf16_gemm
+ * (allow_splitk = 0) or of w12_gemm_ws / bf16_gemm_ws (allow_splitk = 1).
+ * Returns W12_OK, or W12_ERR_NULL / W12_ERR_SHAPE / W12_ERR_UNSUPPORTED. */
+int w12_default_tiling(int64_t M, int64_t N, int64_t K, int allow_splitk,
+                       w12_tiling_t *out);
 
-/* w12_gemm / bf16_gemm with an explicit tiling (NULL = the default).
- * Additional error: W12_ERR_UNSUPPORTED for a tiling that is not built or
- * does not fit M (GEMV needs M <= 8). */
+/*
+ * Workspace bytes a GEMM of this shape needs with `tiling` (NULL = the
+ * w12_gemm_ws default); 0 when the tiling does not split K.  The workspace
+ * holds a 64 KB counter area (one 32-bit counter per row block, at most
+ * 16384 row blocks, so a split-K tiling with more is W12_ERR_UNSUPPORTED)
+ * and then splitk * M * Np fp32 partial sums (Np = N rounded up to 16).
+ * The counter area sits at the start for every shape, so one workspace can
+ * serve GEMMs of different shapes in turn.
+ * Returns W12_OK, or W12_ERR_NULL / W12_ERR_SHAPE / W12_ERR_UNSUPPORTED.
+ */
+int w12_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K,
+                             const w12_tiling_t *tiling, size_t *bytes);
+
+/*
+ * w12_gemm / bf16_gemm with the default tiling including split K, which
+ * fills the GPU on shapes with few row blocks (small N, long K).
+ *   workspace       : device, at least w12_gemm_workspace_bytes(M, N, K,
+ *                     NULL) bytes, 256-byte aligned, zero-filled before its
+ *                     first use (every call leaves its counters at zero);
+ *                     may be NULL when that size is 0.
+ * Additional error: W12_ERR_WORKSPACE.
+ */
+int w12_gemm_ws(const uint16_t *x, int64_t M, int64_t ldx,
+                const void *p0, const void *p1, const void *p2,
+                const uint8_t *meta, int64_t N, int64_t K,
+                void *y, int64_t ldy, int y_type,
+                void *workspace, size_t workspace_bytes, void *stream);
+int bf16_gemm_ws(const uint16_t *x, int64_t M, int64_t ldx,
+                 const uint16_t *w_tiled, int64_t N, int64_t K,
+                 void *y, int64_t ldy, int y_type,
+                 void *workspace, size_t workspace_bytes, void *stream);
+
+/* The GEMMs with an explicit tiling.  tiling = NULL selects the default of
+ * w12_gemm_ws if a workspace is given, else that of w12_gemm.  A tiling with
+ * splitk > 1 needs the workspace w12_gemm_workspace_bytes reports for it.
+ * Additional errors: W12_ERR_UNSUPPORTED for a tiling that is not built or
+ * does not fit M (GEMV needs M <= 8); W12_ERR_WORKSPACE. */
 int w12_gemm_ex(const uint16_t *x, int64_t M, int64_t ldx,
                 const void *p0, const void *p1, const void *p2,
                 const uint8_t *meta, int64_t N, int64_t K,
                 void *y, int64_t ldy, int y_type, const w12_tiling_t *tiling,
-                void *stream);
+                void *workspace, size_t workspace_bytes, void *stream);
 int bf16_gemm_ex(const uint16_t *x, int64_t M, int64_t ldx,
                  const uint16_t *w_tiled, int64_t N, int64_t K,
                  void *y, int64_t ldy, int y_type, const w12_tiling_t *tiling,
-                 void *stream);
+                 void *workspace, size_t workspace_bytes, void *stream);
 
 /*
- * Name of the kernel variant w12_gemm / bf16_gemm launch for this shape
- * (static string, for reports and profiles), or NULL if the shape is
- * rejected.  `is_w12` selects the weight fetch.
+ * Name of the kernel variant the GEMMs launch for this shape (static string,
+ * for reports and profiles), or NULL if the shape is rejected.  `is_w12`
+ * selects the weight fetch, `allow_splitk` the w12_gemm_ws default.
  */
-const char *w12_gemm_variant(int64_t M, int64_t N, int64_t K, int is_w12);
+const char *w12_gemm_variant(int64_t M, int64_t N, int64_t K, int is_w12,
+                             int allow_splitk);
 
 #ifdef __cplusplus
 }

@@ -1,6 +1,7 @@
 // w12_api.hip -- the C ABI declared in include/w12.h: host-side argument
 // checks, tiling choice, and launches on the caller's stream.  Nothing here
-// allocates, synchronises or keeps state.
+// allocates, synchronises or keeps state (split-K launches keep their
+// counters in the caller's workspace).
 #include <stdint.h>
 
 #include "../../include/w12.h"
@@ -65,6 +66,7 @@ const char* w12_status_string(int status) {
         case W12_ERR_DTYPE: return "unknown output type";
         case W12_ERR_UNSUPPORTED: return "unsupported size or tiling (M > 32, or a tiling that is not built for this shape)";
         case W12_ERR_HIP: return "HIP launch failed";
+        case W12_ERR_WORKSPACE: return "workspace missing, too small or not 256-byte aligned for this split-K tiling";
         default: return "unknown status";
     }
 }
@@ -112,10 +114,10 @@ int w12_unpack(const void* p0, const void* p1, const void* p2, const uint8_t* me
                                         static_cast<hipStream_t>(stream)));
 }
 
-static int resolve_tiling(const w12_tiling_t* tiling, int64_t M, int64_t N, int64_t K,
-                          w12::Tiling* out) {
+static int resolve_tiling(const w12_tiling_t* tiling, bool allow_splitk, int64_t M, int64_t N,
+                          int64_t K, w12::Tiling* out) {
     if (tiling == nullptr) {
-        *out = w12::choose_tiling((int)M, N, K);
+        *out = w12::choose_tiling((int)M, N, K, allow_splitk);
         return W12_OK;
     }
     w12::Tiling t{};
@@ -126,68 +128,125 @@ static int resolve_tiling(const w12_tiling_t* tiling, int64_t M, int64_t N, int6
     t.depth = tiling->depth;
     if (tiling->x_direct != 0 && tiling->x_direct != 1) return W12_ERR_UNSUPPORTED;
     t.xdirect = tiling->x_direct;
-    if (!w12::complete_tiling(t, (int)M, K)) return W12_ERR_UNSUPPORTED;
+    t.splitk = tiling->splitk == 0 ? 1 : tiling->splitk;
+    if (!w12::complete_tiling(t, (int)M, N, K)) return W12_ERR_UNSUPPORTED;
     *out = t;
     return W12_OK;
 }
 
-int w12_gemm_ex(const uint16_t* x, int64_t M, int64_t ldx, const void* p0, const void* p1,
-                const void* p2, const uint8_t* meta, int64_t N, int64_t K, void* y, int64_t ldy,
-                int y_type, const w12_tiling_t* tiling, void* stream) {
+static int check_workspace(const w12::Tiling& t, int64_t M, int64_t N, void* ws, size_t bytes) {
+    const size_t need = w12::workspace_bytes(t, (int)M, N);
+    if (need == 0) return W12_OK;
+    if (ws == nullptr || bytes < need || (reinterpret_cast<uintptr_t>(ws) & 255u)) return W12_ERR_WORKSPACE;
+    return W12_OK;
+}
+
+static int gemm_w12(const uint16_t* x, int64_t M, int64_t ldx, const void* p0, const void* p1,
+                    const void* p2, const uint8_t* meta, int64_t N, int64_t K, void* y,
+                    int64_t ldy, int y_type, const w12_tiling_t* tiling, bool allow_splitk,
+                    void* ws, size_t ws_bytes, void* stream) {
     if (!p0 || !p1 || !p2 || !meta) return W12_ERR_NULL;
     if (int rc = check_gemm_common(x, M, ldx, N, K, y, ldy, y_type)) return rc;
     if (!aligned16(p0) || !aligned16(p1) || !aligned16(p2)) return W12_ERR_ALIGN;
     w12::Tiling t;
-    if (int rc = resolve_tiling(tiling, M, N, K, &t)) return rc;
+    if (int rc = resolve_tiling(tiling, allow_splitk, M, N, K, &t)) return rc;
+    if (int rc = check_workspace(t, M, N, ws, ws_bytes)) return rc;
     w12::GemmArgs a = make_args(x, M, ldx, N, K, y, ldy, y_type);
     a.p0 = static_cast<const uint8_t*>(p0);
     a.p1 = static_cast<const uint8_t*>(p1);
     a.p2 = static_cast<const uint8_t*>(p2);
     a.meta = meta;
+    w12::bind_split(a, t, ws);
     return status_of(w12::launch_gemm(a, t, true, static_cast<hipStream_t>(stream)));
 }
 
-int bf16_gemm_ex(const uint16_t* x, int64_t M, int64_t ldx, const uint16_t* w, int64_t N,
-                 int64_t K, void* y, int64_t ldy, int y_type, const w12_tiling_t* tiling,
-                 void* stream) {
+static int gemm_bf16(const uint16_t* x, int64_t M, int64_t ldx, const uint16_t* w, int64_t N,
+                     int64_t K, void* y, int64_t ldy, int y_type, const w12_tiling_t* tiling,
+                     bool allow_splitk, void* ws, size_t ws_bytes, void* stream) {
     if (!w) return W12_ERR_NULL;
     if (int rc = check_gemm_common(x, M, ldx, N, K, y, ldy, y_type)) return rc;
     if (!aligned16(w)) return W12_ERR_ALIGN;
     w12::Tiling t;
-    if (int rc = resolve_tiling(tiling, M, N, K, &t)) return rc;
+    if (int rc = resolve_tiling(tiling, allow_splitk, M, N, K, &t)) return rc;
+    if (int rc = check_workspace(t, M, N, ws, ws_bytes)) return rc;
     w12::GemmArgs a = make_args(x, M, ldx, N, K, y, ldy, y_type);
     a.w = w;
+    w12::bind_split(a, t, ws);
     return status_of(w12::launch_gemm(a, t, false, static_cast<hipStream_t>(stream)));
+}
+
+int w12_gemm_ex(const uint16_t* x, int64_t M, int64_t ldx, const void* p0, const void* p1,
+                const void* p2, const uint8_t* meta, int64_t N, int64_t K, void* y, int64_t ldy,
+                int y_type, const w12_tiling_t* tiling, void* workspace, size_t workspace_bytes,
+                void* stream) {
+    return gemm_w12(x, M, ldx, p0, p1, p2, meta, N, K, y, ldy, y_type, tiling, workspace != nullptr,
+                    workspace, workspace_bytes, stream);
+}
+
+int bf16_gemm_ex(const uint16_t* x, int64_t M, int64_t ldx, const uint16_t* w, int64_t N,
+                 int64_t K, void* y, int64_t ldy, int y_type, const w12_tiling_t* tiling,
+                 void* workspace, size_t workspace_bytes, void* stream) {
+    return gemm_bf16(x, M, ldx, w, N, K, y, ldy, y_type, tiling, workspace != nullptr, workspace,
+                     workspace_bytes, stream);
 }
 
 int w12_gemm(const uint16_t* x, int64_t M, int64_t ldx, const void* p0, const void* p1,
              const void* p2, const uint8_t* meta, int64_t N, int64_t K, void* y, int64_t ldy,
              int y_type, void* stream) {
-    return w12_gemm_ex(x, M, ldx, p0, p1, p2, meta, N, K, y, ldy, y_type, nullptr, stream);
+    return gemm_w12(x, M, ldx, p0, p1, p2, meta, N, K, y, ldy, y_type, nullptr, false, nullptr, 0,
+                    stream);
 }
 
 int bf16_gemm(const uint16_t* x, int64_t M, int64_t ldx, const uint16_t* w, int64_t N, int64_t K,
               void* y, int64_t ldy, int y_type, void* stream) {
-    return bf16_gemm_ex(x, M, ldx, w, N, K, y, ldy, y_type, nullptr, stream);
+    return gemm_bf16(x, M, ldx, w, N, K, y, ldy, y_type, nullptr, false, nullptr, 0, stream);
 }
 
-int w12_default_tiling(int64_t M, int64_t N, int64_t K, w12_tiling_t* out) {
+int w12_gemm_ws(const uint16_t* x, int64_t M, int64_t ldx, const void* p0, const void* p1,
+                const void* p2, const uint8_t* meta, int64_t N, int64_t K, void* y, int64_t ldy,
+                int y_type, void* workspace, size_t workspace_bytes, void* stream) {
+    return gemm_w12(x, M, ldx, p0, p1, p2, meta, N, K, y, ldy, y_type, nullptr, true, workspace,
+                    workspace_bytes, stream);
+}
+
+int bf16_gemm_ws(const uint16_t* x, int64_t M, int64_t ldx, const uint16_t* w, int64_t N,
+                 int64_t K, void* y, int64_t ldy, int y_type, void* workspace,
+                 size_t workspace_bytes, void* stream) {
+    return gemm_bf16(x, M, ldx, w, N, K, y, ldy, y_type, nullptr, true, workspace, workspace_bytes,
+                     stream);
+}
+
+int w12_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, const w12_tiling_t* tiling,
+                             size_t* bytes) {
+    if (bytes == nullptr) return W12_ERR_NULL;
+    *bytes = 0;
+    if (int rc = check_weight_shape(N, K)) return rc;
+    if (M < 1) return W12_ERR_SHAPE;
+    if (M > W12_MAX_M) return W12_ERR_UNSUPPORTED;
+    w12::Tiling t;
+    if (int rc = resolve_tiling(tiling, true, M, N, K, &t)) return rc;
+    *bytes = w12::workspace_bytes(t, (int)M, N);
+    return W12_OK;
+}
+
+int w12_default_tiling(int64_t M, int64_t N, int64_t K, int allow_splitk, w12_tiling_t* out) {
     if (out == nullptr) return W12_ERR_NULL;
     if (int rc = check_weight_shape(N, K)) return rc;
     if (M < 1) return W12_ERR_SHAPE;
     if (M > W12_MAX_M) return W12_ERR_UNSUPPORTED;
-    const w12::Tiling t = w12::choose_tiling((int)M, N, K);
+    const w12::Tiling t = w12::choose_tiling((int)M, N, K, allow_splitk != 0);
     out->kind = t.mfma;
     out->r = t.r;
     out->kw = t.kw;
     out->depth = t.depth;
     out->x_direct = t.xdirect;
+    out->splitk = t.splitk;
     return W12_OK;
 }
 
-const char* w12_gemm_variant(int64_t M, int64_t N, int64_t K, int is_w12) {
+const char* w12_gemm_variant(int64_t M, int64_t N, int64_t K, int is_w12, int allow_splitk) {
     if (check_weight_shape(N, K) != W12_OK || M < 1 || M > W12_MAX_M) return nullptr;
-    return w12::tiling_name(w12::choose_tiling((int)M, N, K), is_w12 != 0);
+    return w12::tiling_name(w12::choose_tiling((int)M, N, K, allow_splitk != 0), is_w12 != 0);
 }
 
 }  // extern "C"

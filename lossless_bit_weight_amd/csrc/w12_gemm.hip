@@ -3,7 +3,7 @@
 // x height by w12_gemm_inst.hip).
 #include <mutex>
 #include <string>
-#include <unordered_map>
+#include <unordered_set>
 
 #include "w12_gemm_kernels.hpp"
 #include "w12_internal.hpp"
@@ -40,20 +40,31 @@ bool pair_built(int r, int d) {
     return (r == 1 && (d == 2 || d == 4 || d == 8)) || (r == 2 && (d == 2 || d == 4));
 }
 
-int64_t waves_of(const Tiling& t, int64_t N) {
-    const int64_t tiles_per_wg = (int64_t)(4 / t.kw) * t.r;
-    return ((N + 15) / 16 + tiles_per_wg - 1) / tiles_per_wg * 4;
-}
+int64_t waves_of(const Tiling& t, int64_t N) { return row_blocks(t, N) * 4; }
 
 }  // namespace
 
-bool complete_tiling(Tiling& t, int M, int64_t K) {
+int64_t row_blocks(const Tiling& t, int64_t N) {
+    const int64_t tiles_per_wg = (int64_t)(4 / t.kw) * t.r;
+    return ((N + 15) / 16 + tiles_per_wg - 1) / tiles_per_wg;
+}
+
+bool complete_tiling(Tiling& t, int M, int64_t N, int64_t K) {
     if (t.kw != 1 && t.kw != 2 && t.kw != 4) return false;
+    if (t.splitk < 1 || t.splitk > kMaxSplitK) return false;
+    // Slices of gs groups; a request above the group count gives one group
+    // per slice.
+    const int64_t G = K / 128;
+    const int64_t gs = (G + t.splitk - 1) / t.splitk;
+    t.gs = (int)gs;
+    t.splitk = (int)((G + gs - 1) / gs);
+    if (t.splitk > 1 && row_blocks(t, N) > kMaxSplitRowBlocks) return false;
+    const int64_t width = gs * 128;  // x columns one workgroup reads
     if (t.mfma) {
         if (M > 32) return false;
         t.mt = M <= 16 ? 16 : 32;
         if (!pair_built(t.r, t.depth)) return false;
-        t.chunked = (int64_t)t.mt * K * 2 > kern::kSingleBytes;
+        t.chunked = (int64_t)t.mt * width * 2 > kern::kSingleBytes;
         if (t.chunked && !kern::chunk_ok(t.mt, kern::mfma_kc(t.mt, t.kw, t.depth))) return false;
         if (t.xdirect) return false;
     } else {
@@ -65,37 +76,64 @@ bool complete_tiling(Tiling& t, int M, int64_t K) {
             t.chunked = 0;
             return true;
         }
-        t.chunked = (int64_t)M * K * 2 > kern::kSingleBytes;
+        t.chunked = (int64_t)M * width * 2 > kern::kSingleBytes;
         if (t.chunked && !kern::chunk_ok(M, kern::gemv_kc(M, t.kw, t.depth))) return false;
     }
     return true;
 }
 
+size_t workspace_bytes(const Tiling& t, int M, int64_t N) {
+    if (t.splitk <= 1) return 0;
+    const int64_t np = (N + 15) / 16 * 16;
+    return (size_t)(kCounterBytes + (int64_t)t.splitk * M * np * 4);
+}
+
+void bind_split(GemmArgs& a, const Tiling& t, void* ws) {
+    a.S = t.splitk;
+    a.gs = t.gs;
+    a.cnt = nullptr;
+    a.ws = nullptr;
+    if (t.splitk > 1) {
+        a.cnt = static_cast<uint32_t*>(ws);
+        a.ws = reinterpret_cast<float*>(static_cast<char*>(ws) + kCounterBytes);
+    }
+}
+
 // Defaults measured on MI355X over the QKV (7168x5120), gate+up (34816x5120)
-// and down (5120x17408) shapes: the GEMV wins up to M = 4 with all four
-// waves of a workgroup splitting K; from M = 5 on the MFMA wins (the VALU
-// work of eight dot2 rows outweighs the padded MFMA tile).  Splitting K
-// helps until there are ~4000 waves; a chunked 32-row x limits KW through
-// the LDS budget.
-Tiling choose_tiling(int M, int64_t N, int64_t K) {
+// and down (5120x17408) shapes, M in {1, 4, 8, 16, 32}: the GEMV wins up to
+// M = 4 with all four waves of a workgroup splitting K (ring depth 4 at
+// M <= 2, 2 above); from M = 5 on the MFMA wins (the VALU work of eight dot2
+// rows outweighs the padded MFMA tile): 4 K-waves up to M = 8, 2 above.
+// Splitting K across workgroups pays only on long K: slices of at least 40
+// groups (5120 weights) keep each workgroup's prologue and epilogue small
+// against its stream, and there is no point once the grid has ~2048
+// workgroups.  On the down shape (136 groups, 320 tiles) three slices cut
+// M = 16-32 from 40-51 us to 31-38 us; on the 40-group shapes any split was
+// slower.
+Tiling choose_tiling(int M, int64_t N, int64_t K, bool allow_splitk) {
     Tiling t{};
     t.r = 1;
-    t.depth = 2;
+    t.splitk = 1;
     if (M <= 4) {
         t.mfma = 0;
         t.kw = 4;
+        t.depth = M <= 2 ? 4 : 2;
     } else {
         t.mfma = 1;
-        t.kw = 1;
-        const int64_t ntiles = (N + 15) / 16;
-        if (M <= 16) {
-            while (t.kw < 4 && waves_of(t, N) < 4000) t.kw *= 2;
-        } else {
-            t.kw = ntiles >= 2048 ? 1 : 2;
-        }
+        t.kw = M <= 8 ? 4 : 2;
+        t.depth = 2;
+    }
+    if (allow_splitk) {
+        const int64_t G = K / 128;
+        const int64_t nb = row_blocks(t, N);
+        int64_t s = G / 40;
+        const int64_t fill = (2048 + nb - 1) / nb;
+        s = s < fill ? s : fill;
+        s = s < kMaxSplitK ? s : kMaxSplitK;
+        t.splitk = s > 1 ? (int)s : 1;
     }
     // Step down to a built combination (a chunked x buffer must fit LDS).
-    while (!complete_tiling(t, M, K)) {
+    while (!complete_tiling(t, M, N, K)) {
         if (t.depth > 2)
             t.depth /= 2;
         else if (t.kw > 1)
@@ -108,17 +146,14 @@ Tiling choose_tiling(int M, int64_t N, int64_t K) {
 
 const char* tiling_name(const Tiling& t, bool is_w12) {
     static std::mutex mu;
-    static std::unordered_map<int, std::string> names;
-    const int key = (is_w12 << 25) | (t.xdirect << 24) | (t.mfma << 23) | (t.chunked << 22) |
-                    (t.mt << 12) | (t.r << 8) | (t.kw << 4) | t.depth;
-    std::lock_guard<std::mutex> lock(mu);
-    auto it = names.find(key);
-    if (it != names.end()) return it->second.c_str();
+    static std::unordered_set<std::string> names;  // node-based: c_str() stays valid
     std::string n = is_w12 ? "w12_" : "bf16_";
     n += t.mfma ? "mfma_mt" : "gemv_m";
     n += std::to_string(t.mt) + "_r" + std::to_string(t.r) + "_kw" + std::to_string(t.kw) + "_d" +
          std::to_string(t.depth) + (t.xdirect ? "_xdirect" : t.chunked ? "_chunked" : "_single");
-    return names.emplace(key, std::move(n)).first->second.c_str();
+    if (t.splitk > 1) n += "_s" + std::to_string(t.splitk);
+    std::lock_guard<std::mutex> lock(mu);
+    return names.insert(std::move(n)).first->c_str();
 }
 
 hipError_t launch_gemm(const GemmArgs& a, const Tiling& t, bool is_w12, hipStream_t s) {

@@ -18,17 +18,23 @@
 //     memory.  Lane L = 16 q + col holds row col of the tile and the 32
 //     weights k = 128 g + 32 b + 8 q + e; its 8-weight block b is ready as
 //     4 dwords of BF16 pairs after decode;
-//   * a workgroup (4 waves) owns R tiles per row-wave over the whole K
-//     range; KW of its waves split the groups (group i goes to K-wave
-//     i % KW) and add their partial sums through LDS in a fixed order;
+//   * a workgroup (4 waves) owns R tiles per row-wave over one K slice
+//     (grid y; the whole K unless K is split across workgroups); KW of its
+//     waves split the slice's groups (group g0 + i goes to K-wave i % KW)
+//     and add their partial sums through LDS in a fixed order;
+//   * with K split over S workgroups, each writes its slice's fp32 sums to a
+//     workspace and the last of a row block to finish (an atomic counter)
+//     adds the S slices in slice order and writes y -- so the result never
+//     depends on which workgroup finishes last, and no workgroup waits;
 //   * each lane keeps D groups in flight in a register ring unrolled at
 //     compile time; every ring load is issued unconditionally (indices are
 //     clamped to valid memory), so the compiler waits only for the oldest
 //     group instead of draining the ring;
-//   * x lives in LDS.  If it fits it is loaded once, before the ring is
-//     primed, so the prologue barrier waits for x only.  Otherwise it is
-//     double-buffered in chunks of KC columns loaded one chunk ahead, one
-//     barrier per chunk, between ring windows;
+//   * x lives in LDS (the columns of the workgroup's K slice).  If they fit
+//     they are loaded once, before the ring is primed, so the prologue
+//     barrier waits for x only.  Otherwise they are double-buffered in
+//     chunks of KC columns loaded one chunk ahead, one barrier per chunk,
+//     between ring windows;
 // GEMV (M <= 8): v_dot2c_f32_bf16 into fp32, x[m] read from LDS as a
 // broadcast (all 16 lanes of a quarter read the same 16 bytes); the 4
 // quarter sums of a row are added with a fixed xor butterfly.
@@ -68,6 +74,61 @@ __device__ __forceinline__ void store_y(const GemmArgs& g, int m, int64_t n, flo
         reinterpret_cast<float*>(g.y)[(int64_t)m * g.ldy + n] = v;
     else
         reinterpret_cast<uint16_t*>(g.y)[(int64_t)m * g.ldy + n] = f32_to_bf16_rne(v);
+}
+
+// A finished sum of one K slice: y itself when K is not split, else the
+// slice's partial sum ws[s][m][n] (Np = N rounded up to 16 columns), stored
+// with device scope (written through to the device coherence point, so no
+// cache maintenance is needed to publish it).
+__device__ __forceinline__ void out_value(const GemmArgs& g, int m, int64_t n, float v) {
+    if (gridDim.y == 1) {
+        store_y(g, m, n, v);
+    } else {
+        const int64_t np = (g.N + 15) / 16 * 16;
+        __hip_atomic_store(g.ws + ((int64_t)blockIdx.y * g.M + m) * np + n, v, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+// Split-K epilogue, run by every thread of a workgroup after its partial
+// sums are stored.  The workgroups of one row block count themselves in
+// cnt[block]; the last one to arrive adds the S partial sums of the block in
+// slice order 0, 1, ..., S-1 (the same order whichever workgroup is last, so
+// y is deterministic) and resets the counter to zero for the next launch.
+// No workgroup waits for another.
+//
+// Publication without whole-cache maintenance: partial sums are written and
+// read with device-scope accesses (they bypass the per-XCD caches), each
+// wave waits until its own stores have completed before the workgroup
+// barrier, and only then does one thread bump the device-scope counter.  A
+// workgroup that sees the count reach S - 1 therefore reads complete sums.
+// (A release/acquire fence here would write back and invalidate the whole
+// L2 of the XCD once per workgroup, which serialised the launch.)
+template <int kTilesPerWG>
+__device__ __forceinline__ void split_finish(const GemmArgs& g) {
+    __shared__ int last;
+    __builtin_amdgcn_s_waitcnt(0);   // this wave's partial-sum stores are complete
+    __syncthreads();
+    if (threadIdx.x == 0)
+        last = __hip_atomic_fetch_add(g.cnt + blockIdx.x, 1u, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT) == gridDim.y - 1;
+    __syncthreads();
+    if (!last) return;
+    constexpr int kRows = kTilesPerWG * 16;
+    const int64_t np = (g.N + 15) / 16 * 16;
+    const int64_t n0 = (int64_t)blockIdx.x * kRows;
+    const int64_t slice = (int64_t)g.M * np;
+    for (int i = threadIdx.x; i < kRows * g.M; i += kThreads) {
+        const int m = i / kRows;
+        const int64_t n = n0 + i % kRows;
+        if (n >= g.N) continue;
+        const float* p = g.ws + (int64_t)m * np + n;
+        float v = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int s = 1; s < (int)gridDim.y; ++s)
+            v += __hip_atomic_load(p + s * slice, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        store_y(g, m, n, v);
+    }
+    if (threadIdx.x == 0) __hip_atomic_store(g.cnt + blockIdx.x, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---- weight fetch policies ------------------------------------------------
@@ -175,8 +236,10 @@ struct XAll {
     uint4 v[kSingleUnits];
     int units, units_per_row;
 
-    __device__ __forceinline__ void load(const GemmArgs& g, int mrows) {
-        units_per_row = (int)(g.K / 8);
+    // Columns [k0, k0 + 8 * upr) of rows 0..mrows-1 (mrows * upr <=
+    // kSingleUnits * kThreads, checked on the host).
+    __device__ __forceinline__ void load(const GemmArgs& g, int mrows, int64_t k0, int upr) {
+        units_per_row = upr;
         units = mrows * units_per_row;
 #pragma unroll
         for (int j = 0; j < kSingleUnits; ++j) {
@@ -186,7 +249,7 @@ struct XAll {
             if (kThreads * j < units) {
                 const int id = threadIdx.x + kThreads * j;
                 const int m = id / units_per_row;
-                const int64_t k = 8 * (int64_t)(id % units_per_row);
+                const int64_t k = k0 + 8 * (int64_t)(id % units_per_row);
                 const bool ok = id < units && m < g.M;
                 const int mc = m < g.M ? m : g.M - 1;
                 const uint4 v0 = *reinterpret_cast<const uint4*>(g.x + (int64_t)mc * g.ldx + k);
@@ -258,7 +321,7 @@ __host__ __device__ constexpr int kc_of(bool mfma, int rows, int KW, int D) {
                     __syncthreads();                                                      \
                     ++c;                                                                  \
                     next_boundary += (L);                                                 \
-                    xr.load(g, (int64_t)(c + 1 < (nchunks) ? c + 1 : c) * KC);            \
+                    xr.load(g, kbase + (int64_t)(c + 1 < (nchunks) ? c + 1 : c) * KC);    \
                 }                                                                         \
             }                                                                             \
             _Pragma("unroll") for (int d = 0; d < (D); ++d) {                             \
@@ -274,7 +337,7 @@ __host__ __device__ constexpr int kc_of(bool mfma, int rows, int KW, int D) {
                 __syncthreads();                                                          \
                 ++c;                                                                      \
                 next_boundary += (L);                                                     \
-                xr.load(g, (int64_t)(c + 1 < (nchunks) ? c + 1 : c) * KC);                \
+                xr.load(g, kbase + (int64_t)(c + 1 < (nchunks) ? c + 1 : c) * KC);        \
             }                                                                             \
         }                                                                                 \
         _Pragma("unroll") for (int d = 0; d < (D); ++d) {                                 \
@@ -287,7 +350,7 @@ __host__ __device__ constexpr int kc_of(bool mfma, int rows, int KW, int D) {
                 store_next();                                                             \
                 __syncthreads();                                                          \
                 ++c;                                                                      \
-                xr.load(g, (int64_t)(c + 1 < (nchunks) ? c + 1 : c) * KC);                \
+                xr.load(g, kbase + (int64_t)(c + 1 < (nchunks) ? c + 1 : c) * KC);        \
             }                                                                             \
         }                                                                                 \
     }
@@ -325,17 +388,21 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
 #pragma unroll
     for (int r = 0; r < R; ++r) tload[r] = tile0 + r < ntiles ? tile0 + r : ntiles - 1;
 
-    const int J = G > kw ? (int)((G - kw + KW - 1) / KW) : 0;  // this wave's groups
+    // K slice of this workgroup: groups g0 .. g0 + gn - 1 (gn >= 1).
+    const int g0 = (int)blockIdx.y * g.gs;
+    const int gn = G - g0 < g.gs ? (int)(G - g0) : g.gs;
+    const int64_t kbase = (int64_t)g0 * 128;
+    const int J = gn > kw ? (gn - kw + KW - 1) / KW : 0;  // this wave's groups
     const int Jlast = J > 0 ? J - 1 : 0;
-    const int units_per_row = CHUNKED ? KC / 8 : (int)(g.K / 8);
-    const int64_t nchunks = CHUNKED ? (g.K + KC - 1) / KC : 1;
+    const int units_per_row = CHUNKED ? KC / 8 : gn * 16;
+    const int64_t nchunks = CHUNKED ? ((int64_t)gn * 128 + KC - 1) / KC : 1;
     int c = 0;
     int next_boundary = CHUNKED && nchunks > 1 ? L : 1 << 30;
 
     typename F::Base wbase[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) wbase[r] = F::base(g, tload[r]);
-    const int glast = (int)G - 1;
+    const int glast = g0 + gn - 1;
 
     struct Slot {
         Raw w[R];
@@ -344,7 +411,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
     Slot ring[D];
     auto fetch = [&](int j, Slot& dst) {
         j = j < Jlast ? j : Jlast;
-        int grp = kw + j * KW;
+        int grp = g0 + kw + j * KW;
         grp = grp < glast ? grp : glast;   // only when this wave has no group at all
 #pragma unroll
         for (int r = 0; r < R; ++r) F::load(wbase[r], grp, lane, dst.w[r]);
@@ -377,9 +444,10 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
     auto compute = [&](const Slot& slot, int j) {
         const Raw(&rr)[R] = slot.w;
         const uint4* xb = lds + (CHUNKED ? (c & 1) * kBuf : 0);
-        const int64_t grp = kw + (int64_t)j * KW;
-        // unit of (block b) = (128 grp + 32 b + 8 q) / 8, chunk relative
-        const int u0 = (int)(16 * grp - (int64_t)c * (KC / 8)) + q;
+        const int grp = g0 + kw + j * KW;
+        // unit of (block b) = (128 grp + 32 b + 8 q) / 8, relative to the
+        // slice and the chunk
+        const int u0 = 16 * (grp - g0) - c * (KC / 8) + q;
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
             if constexpr (MFMA) {
@@ -428,9 +496,9 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
     XChunk<MR, KC> xr;
     XAll xa;
     if constexpr (CHUNKED)
-        xr.load(g, 0);
+        xr.load(g, kbase);
     else if constexpr (!XD)
-        xa.load(g, MR);
+        xa.load(g, MR, kbase, units_per_row);
 #pragma unroll
     for (int d = 0; d < D; ++d) fetch(d, ring[d]);
     if constexpr (CHUNKED)
@@ -438,7 +506,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
     else if constexpr (!XD)
         xa.template store<XLayout>(lds);
     if constexpr (!XD) __syncthreads();
-    if constexpr (CHUNKED) xr.load(g, (int64_t)(nchunks > 1 ? 1 : 0) * KC);
+    if constexpr (CHUNKED) xr.load(g, kbase + (int64_t)(nchunks > 1 ? 1 : 0) * KC);
 
     auto store_next = [&]() {
         xr.template store<FixedLayout<XLayout, KC / 8>>(lds + ((c + 1) & 1) * kBuf);
@@ -458,27 +526,31 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
                         red[(((kw - 1) * kRowWaves + nw) * 64 + lane) * kPer + r * kMT + mt] = macc[r][mt];
             }
             __syncthreads();
-            if (kw != 0) return;
-            for (int p = 1; p < KW; ++p)
+            if (kw == 0) {
+                for (int p = 1; p < KW; ++p)
 #pragma unroll
-                for (int r = 0; r < R; ++r)
+                    for (int r = 0; r < R; ++r)
 #pragma unroll
-                    for (int mt = 0; mt < kMT; ++mt)
-                        macc[r][mt] += red[(((p - 1) * kRowWaves + nw) * 64 + lane) * kPer + r * kMT + mt];
+                        for (int mt = 0; mt < kMT; ++mt)
+                            macc[r][mt] += red[(((p - 1) * kRowWaves + nw) * 64 + lane) * kPer + r * kMT + mt];
+            }
         }
         // D layout of the 16x16 MFMA: lane (col, q) holds rows 4q..4q+3 of
-        // column col, i.e. y[m = 16 mt + 4q + e][n = 16 tile + col].
+        // column col, i.e. y[m = 16 mt + 4q + e][n = 16 tile + col].  With a
+        // split K the values go to this slice's partial sums instead.
+        if (kw == 0) {
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const int64_t n = (tile0 + r) * 16 + col;
-            if (n >= g.N) continue;
+            for (int r = 0; r < R; ++r) {
+                const int64_t n = (tile0 + r) * 16 + col;
+                if (n >= g.N) continue;
 #pragma unroll
-            for (int mt = 0; mt < kMT; ++mt)
+                for (int mt = 0; mt < kMT; ++mt)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int m = 16 * mt + 4 * q + e;
-                    if (m < g.M) store_y(g, m, n, macc[r][mt][e]);
-                }
+                    for (int e = 0; e < 4; ++e) {
+                        const int m = 16 * mt + 4 * q + e;
+                        if (m < g.M) out_value(g, m, n, macc[r][mt][e]);
+                    }
+            }
         }
     } else {
         // Add the 4 quarter sums of each row (fixed butterfly order).
@@ -502,36 +574,41 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
                         red[(((kw - 1) * kRowWaves + nw) * 16 + col) * (R * MR) + r * MR + m] = gacc[r][m];
             }
             __syncthreads();
-            if (kw != 0) return;
+            if (kw == 0) {
 #pragma unroll
-            for (int r = 0; r < R; ++r)
+                for (int r = 0; r < R; ++r)
 #pragma unroll
-                for (int m = 0; m < MR; ++m) {
-                    float v = gacc[r][m];
-                    for (int p = 1; p < KW; ++p)
-                        v += red[(((p - 1) * kRowWaves + nw) * 16 + col) * (R * MR) + r * MR + m];
-                    gacc[r][m] = v;
-                }
+                    for (int m = 0; m < MR; ++m) {
+                        float v = gacc[r][m];
+                        for (int p = 1; p < KW; ++p)
+                            v += red[(((p - 1) * kRowWaves + nw) * 16 + col) * (R * MR) + r * MR + m];
+                        gacc[r][m] = v;
+                    }
+            }
         }
         // Lane (col, q) stores the outputs m with m % 4 == q.
+        if (kw == 0) {
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const int64_t n = (tile0 + r) * 16 + col;
+            for (int r = 0; r < R; ++r) {
+                const int64_t n = (tile0 + r) * 16 + col;
 #pragma unroll
-            for (int m = 0; m < MR; ++m)
-                if ((m & 3) == q && n < g.N && m < g.M) store_y(g, m, n, gacc[r][m]);
+                for (int m = 0; m < MR; ++m)
+                    if ((m & 3) == q && n < g.N && m < g.M) out_value(g, m, n, gacc[r][m]);
+            }
         }
     }
+    if (gridDim.y > 1) split_finish<kRowWaves * R>(g);
 }
 
 // ---- launch helpers ----------------------------------------------------------------------
 
-// Bytes of LDS a launch needs (x buffers; the reductions reuse them).
+// Bytes of LDS a launch needs (x buffers of one K slice of gs groups; the
+// reductions reuse them).
 template <bool MFMA, int MR, int R, int KW, int D, bool CHUNKED, bool XD>
-size_t lds_bytes(int64_t K) {
+size_t lds_bytes(int gs) {
     const size_t x = XD ? 0
                      : CHUNKED ? 2 * (size_t)MR * kc_of(MFMA, MR, KW, D) * 2
-                               : (size_t)MR * (K / 8) * 16;
+                               : (size_t)MR * gs * 128 * 2;
     const size_t red = KW == 1 ? 0
                        : MFMA ? (size_t)(KW - 1) * (4 / KW) * 64 * R * (MR / 16) * 16
                               : (size_t)(KW - 1) * (4 / KW) * 16 * R * MR * 4;
@@ -542,8 +619,8 @@ template <class F, bool MFMA, int MR, int R, int KW, int D, bool CHUNKED, bool X
 hipError_t launch_one(const GemmArgs& a, hipStream_t s) {
     constexpr int kTilesPerWG = (4 / KW) * R;
     const int64_t ntiles = (a.N + 15) / 16;
-    const dim3 grid((unsigned)((ntiles + kTilesPerWG - 1) / kTilesPerWG));
-    const size_t lds = lds_bytes<MFMA, MR, R, KW, D, CHUNKED, XD>(a.K);
+    const dim3 grid((unsigned)((ntiles + kTilesPerWG - 1) / kTilesPerWG), (unsigned)a.S);
+    const size_t lds = lds_bytes<MFMA, MR, R, KW, D, CHUNKED, XD>(a.gs);
     hipLaunchKernelGGL((gemm_kernel<F, MFMA, MR, R, KW, D, CHUNKED, XD>), grid, dim3(kThreads), lds, s, a);
     return hipGetLastError();
 }

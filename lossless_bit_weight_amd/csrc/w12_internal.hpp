@@ -22,6 +22,14 @@ struct GemmArgs {
     void* y;
     int64_t ldy;
     int y_f32;
+    // K split across workgroups (grid y): slice s holds groups
+    // [s * gs, min(G, (s + 1) * gs)); with S > 1 every workgroup writes its
+    // fp32 partial sums to ws[s][m][Np] and the last of the S workgroups of a
+    // row block (counted in cnt[block]) adds them in slice order and writes y.
+    int S;
+    int gs;
+    float* ws;
+    uint32_t* cnt;
 };
 
 // Tiling of one GEMM launch.
@@ -32,8 +40,11 @@ struct GemmArgs {
 //   depth   = 32-weight slices each lane keeps in flight (2, 4 or 8).
 //   xdirect = 1: GEMV only, M <= 4: x is read by each lane with its weights
 //             instead of being staged in LDS.
-//   chunked = 0 if all of x is staged in LDS at once, 1 if it is streamed
-//             through LDS in double-buffered chunks (set from the shape).
+//   splitk  = workgroups that split K between them (1 = none); completed to
+//             the number of non-empty slices of gs groups each.
+//   chunked = 0 if the x columns of a K slice are staged in LDS at once, 1 if
+//             they are streamed through LDS in double-buffered chunks (set
+//             from the shape).
 struct Tiling {
     int mfma;
     int mt;
@@ -41,15 +52,34 @@ struct Tiling {
     int kw;
     int depth;
     int xdirect;
+    int splitk;
+    int gs;
     int chunked;
 };
 
-// Pick the tiling used by w12_gemm / bf16_gemm for this shape.
-Tiling choose_tiling(int M, int64_t N, int64_t K);
-// Complete a caller-given tiling (mt, chunked) for this shape; false if the
-// combination is not built.
-bool complete_tiling(Tiling& t, int M, int64_t K);
+constexpr int kMaxSplitK = 64;
+// A split-K workspace starts with a fixed counter area, so that the counters
+// of any launch lie outside the partial sums of any other launch and stay
+// zero between launches of different shapes; split K therefore needs at most
+// kMaxSplitRowBlocks workgroups along N.
+constexpr int64_t kCounterBytes = 65536;
+constexpr int64_t kMaxSplitRowBlocks = kCounterBytes / 4;
+
+// Pick the tiling used by w12_gemm / bf16_gemm for this shape; split-K
+// tilings (which need a workspace) only if allow_splitk.
+Tiling choose_tiling(int M, int64_t N, int64_t K, bool allow_splitk);
+// Complete a caller-given tiling (mt, splitk, gs, chunked) for this shape;
+// false if the combination is not built (or splits K over more than
+// kMaxSplitRowBlocks row blocks).
+bool complete_tiling(Tiling& t, int M, int64_t N, int64_t K);
 const char* tiling_name(const Tiling& t, bool is_w12);
+// Workgroups along N (grid x) of a launch with this tiling.
+int64_t row_blocks(const Tiling& t, int64_t N);
+// Workspace a completed tiling needs: 0 without split-K, else the counter
+// area (kCounterBytes) followed by S * M * Np fp32 partials.
+size_t workspace_bytes(const Tiling& t, int M, int64_t N);
+// Point the split-K fields of `a` at `ws` (which holds workspace_bytes).
+void bind_split(GemmArgs& a, const Tiling& t, void* ws);
 
 hipError_t launch_gemm(const GemmArgs& a, const Tiling& t, bool is_w12, hipStream_t s);
 // Per-M (GEMV) and per-MT (MFMA) launchers, one object file each.

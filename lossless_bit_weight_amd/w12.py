@@ -29,6 +29,7 @@ OUT_F32 = 1
 STATUS = {
     0: "W12_OK", -1: "W12_ERR_NULL", -2: "W12_ERR_SHAPE", -3: "W12_ERR_ALIGN",
     -4: "W12_ERR_DTYPE", -6: "W12_ERR_UNSUPPORTED", -7: "W12_ERR_HIP",
+    -8: "W12_ERR_WORKSPACE",
 }
 
 
@@ -44,18 +45,21 @@ class W12UnencodableError(ValueError):
 
 
 class Tiling(ctypes.Structure):
-    """w12_tiling_t: kind (0 GEMV, 1 MFMA), r, kw, depth, x_direct."""
+    """w12_tiling_t: kind (0 GEMV, 1 MFMA), r, kw, depth, x_direct, splitk
+    (0 or 1 = K not split across workgroups)."""
     _fields_ = [("kind", ctypes.c_int32), ("r", ctypes.c_int32), ("kw", ctypes.c_int32),
-                ("depth", ctypes.c_int32), ("x_direct", ctypes.c_int32)]
+                ("depth", ctypes.c_int32), ("x_direct", ctypes.c_int32),
+                ("splitk", ctypes.c_int32)]
 
     def astuple(self):
-        return (self.kind, self.r, self.kw, self.depth, self.x_direct)
+        return (self.kind, self.r, self.kw, self.depth, self.x_direct, self.splitk)
 
     def __repr__(self):
-        return "Tiling(kind=%d, r=%d, kw=%d, depth=%d, x_direct=%d)" % self.astuple()
+        return "Tiling(kind=%d, r=%d, kw=%d, depth=%d, x_direct=%d, splitk=%d)" % self.astuple()
 
 
-# Every tiling the library instantiates: (kind, r, kw, depth, x_direct).
+# Every tiling the library instantiates: (kind, r, kw, depth, x_direct); any
+# of them may add a sixth entry, the split-K factor (1..64).
 # x_direct needs the GEMV, M <= 4 and a ring of at most 192 registers:
 # depth * 16 * (r + M) <= 192 (x_direct_fits).
 _PAIRS = ((1, 2), (1, 4), (1, 8), (2, 2), (2, 4))
@@ -110,13 +114,20 @@ def lib() -> ctypes.CDLL:
     L.w12_gemm.restype = i32
     L.bf16_gemm.argtypes = [p, i64, i64, p, i64, i64, p, i64, i32, p]
     L.bf16_gemm.restype = i32
-    L.w12_gemm_ex.argtypes = [p, i64, i64, p, p, p, p, i64, i64, p, i64, i32, p, p]
+    sz = ctypes.c_size_t
+    L.w12_gemm_ex.argtypes = [p, i64, i64, p, p, p, p, i64, i64, p, i64, i32, p, p, sz, p]
     L.w12_gemm_ex.restype = i32
-    L.bf16_gemm_ex.argtypes = [p, i64, i64, p, i64, i64, p, i64, i32, p, p]
+    L.bf16_gemm_ex.argtypes = [p, i64, i64, p, i64, i64, p, i64, i32, p, p, sz, p]
     L.bf16_gemm_ex.restype = i32
-    L.w12_default_tiling.argtypes = [i64, i64, i64, ctypes.POINTER(Tiling)]
+    L.w12_gemm_ws.argtypes = [p, i64, i64, p, p, p, p, i64, i64, p, i64, i32, p, sz, p]
+    L.w12_gemm_ws.restype = i32
+    L.bf16_gemm_ws.argtypes = [p, i64, i64, p, i64, i64, p, i64, i32, p, sz, p]
+    L.bf16_gemm_ws.restype = i32
+    L.w12_gemm_workspace_bytes.argtypes = [i64, i64, i64, p, ctypes.POINTER(sz)]
+    L.w12_gemm_workspace_bytes.restype = i32
+    L.w12_default_tiling.argtypes = [i64, i64, i64, i32, ctypes.POINTER(Tiling)]
     L.w12_default_tiling.restype = i32
-    L.w12_gemm_variant.argtypes = [i64, i64, i64, i32]
+    L.w12_gemm_variant.argtypes = [i64, i64, i64, i32, i32]
     L.w12_gemm_variant.restype = ctypes.c_char_p
     _lib = L
     return L
@@ -184,15 +195,44 @@ def w12_meta_bytes(N: int, K: int) -> int:
     return int(lib().w12_meta_bytes(int(N), int(K)))
 
 
-def w12_default_tiling(M: int, N: int, K: int) -> Tiling:
+def w12_default_tiling(M: int, N: int, K: int, allow_splitk: bool = True) -> Tiling:
     t = Tiling()
-    _check(lib().w12_default_tiling(int(M), int(N), int(K), ctypes.byref(t)), "w12_default_tiling")
+    _check(lib().w12_default_tiling(int(M), int(N), int(K), int(bool(allow_splitk)), ctypes.byref(t)),
+           "w12_default_tiling")
     return t
 
 
-def w12_gemm_variant(M: int, N: int, K: int, is_w12: bool = True) -> str | None:
-    r = lib().w12_gemm_variant(int(M), int(N), int(K), int(bool(is_w12)))
+def w12_gemm_variant(M: int, N: int, K: int, is_w12: bool = True,
+                     allow_splitk: bool = True) -> str | None:
+    r = lib().w12_gemm_variant(int(M), int(N), int(K), int(bool(is_w12)), int(bool(allow_splitk)))
     return None if r is None else r.decode()
+
+
+def w12_gemm_workspace_bytes(M: int, N: int, K: int, tiling=None) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().w12_gemm_workspace_bytes(int(M), int(N), int(K), _tiling_arg(tiling),
+                                          ctypes.byref(n)), "w12_gemm_workspace_bytes")
+    return int(n.value)
+
+
+# One zero-filled split-K workspace per (device, stream): launches on one
+# stream run in order, so they can share it (each leaves its counters at
+# zero); launches on another stream get their own.  The first split-K call on
+# a stream allocates it, so make that call before capturing the stream in a
+# graph.
+_workspaces: dict = {}
+
+
+def workspace(nbytes: int) -> torch.Tensor:
+    """The binding's split-K workspace for the current device and stream,
+    grown (and zero-filled anew) to at least `nbytes`."""
+    dev = torch.cuda.current_device()
+    key = (dev, torch.cuda.current_stream().cuda_stream)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(int(nbytes), 1 << 20), dtype=torch.uint8, device="cuda:%d" % dev)
+        _workspaces[key] = ws
+    return ws
 
 
 @dataclass
@@ -316,10 +356,28 @@ def _x_args(x: torch.Tensor) -> tuple[int, int]:
     return x.shape[0], x.stride(0)
 
 
+def _ws_args(M: int, N: int, K: int, tiling, split_k: bool, ws: torch.Tensor | None):
+    """(pointer, bytes) of the workspace a call needs, or (None, 0)."""
+    if tiling is None and not split_k:
+        return None, 0
+    need = w12_gemm_workspace_bytes(M, N, K, tiling)
+    if need == 0:
+        return None, 0
+    if ws is None:
+        ws = workspace(need)
+    elif ws.numel() * ws.element_size() < need:
+        raise ValueError("workspace holds %d bytes, this call needs %d"
+                         % (ws.numel() * ws.element_size(), need))
+    return _dev_ptr(ws, "workspace"), ws.numel() * ws.element_size()
+
+
 def w12_gemm(x: torch.Tensor, wt: W12Weight, out_dtype: torch.dtype = torch.float32,
-             y: torch.Tensor | None = None, tiling=None) -> torch.Tensor:
+             y: torch.Tensor | None = None, tiling=None, split_k: bool = True,
+             workspace: torch.Tensor | None = None) -> torch.Tensor:
     """y[m, n] = sum_k x[m, k] W[n, k] with W rebuilt from the container.
-    `tiling` (a Tiling or a (kind, r, kw, depth) tuple) selects w12_gemm_ex."""
+    Default: w12_gemm_ws (K may be split over workgroups, using `workspace`
+    or the binding's own); split_k=False: w12_gemm.  `tiling` (a Tiling or a
+    (kind, r, kw, depth, x_direct[, splitk]) tuple) selects w12_gemm_ex."""
     M, ldx = _x_args(x)
     if y is None:
         y, _ = _out_tensor(M, wt.N, out_dtype, x.device)
@@ -327,17 +385,21 @@ def w12_gemm(x: torch.Tensor, wt: W12Weight, out_dtype: torch.dtype = torch.floa
     args = (_dev_ptr(x, "x"), M, ldx, _dev_ptr(wt.p0, "p0"), _dev_ptr(wt.p1, "p1"),
             _dev_ptr(wt.p2, "p2"), _dev_ptr(wt.meta, "meta"), wt.N, wt.K, _dev_ptr(y, "y"),
             ldy, yt)
-    if tiling is None:
-        _check(lib().w12_gemm(*args, _stream()), "w12_gemm")
+    wsp, wsb = _ws_args(M, wt.N, wt.K, tiling, split_k, workspace)
+    if tiling is not None:
+        _check(lib().w12_gemm_ex(*args, _tiling_arg(tiling), wsp, wsb, _stream()), "w12_gemm_ex")
+    elif split_k:
+        _check(lib().w12_gemm_ws(*args, wsp, wsb, _stream()), "w12_gemm_ws")
     else:
-        _check(lib().w12_gemm_ex(*args, _tiling_arg(tiling), _stream()), "w12_gemm_ex")
+        _check(lib().w12_gemm(*args, _stream()), "w12_gemm")
     return y
 
 
 def bf16_gemm(x: torch.Tensor, wt: BF16Tiled, out_dtype: torch.dtype = torch.float32,
-              y: torch.Tensor | None = None, tiling=None) -> torch.Tensor:
+              y: torch.Tensor | None = None, tiling=None, split_k: bool = True,
+              workspace: torch.Tensor | None = None) -> torch.Tensor:
     """The same-tiling control: y = x . W^T with W read as BF16 words from the
-    control layout (see w12_bf16_tile)."""
+    control layout (see w12_bf16_tile).  Arguments as w12_gemm."""
     M, ldx = _x_args(x)
     if not isinstance(wt, BF16Tiled):
         raise TypeError("bf16_gemm takes a BF16Tiled weight (w12_bf16_tile)")
@@ -345,8 +407,11 @@ def bf16_gemm(x: torch.Tensor, wt: BF16Tiled, out_dtype: torch.dtype = torch.flo
         y, _ = _out_tensor(M, wt.N, out_dtype, x.device)
     ldy, yt = _y_args(y)
     args = (_dev_ptr(x, "x"), M, ldx, _dev_ptr(wt.w, "w_tiled"), wt.N, wt.K, _dev_ptr(y, "y"), ldy, yt)
-    if tiling is None:
-        _check(lib().bf16_gemm(*args, _stream()), "bf16_gemm")
+    wsp, wsb = _ws_args(M, wt.N, wt.K, tiling, split_k, workspace)
+    if tiling is not None:
+        _check(lib().bf16_gemm_ex(*args, _tiling_arg(tiling), wsp, wsb, _stream()), "bf16_gemm_ex")
+    elif split_k:
+        _check(lib().bf16_gemm_ws(*args, wsp, wsb, _stream()), "bf16_gemm_ws")
     else:
-        _check(lib().bf16_gemm_ex(*args, _tiling_arg(tiling), _stream()), "bf16_gemm_ex")
+        _check(lib().bf16_gemm(*args, _stream()), "bf16_gemm")
     return y

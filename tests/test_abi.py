@@ -16,10 +16,11 @@ def test_loads_and_exports_every_declared_symbol():
     names = w12.header_functions()
     assert set(names) >= {"w12_pack", "w12_unpack", "w12_gemm", "bf16_gemm", "w12_bf16_tile",
                           "w12_plane_bytes", "w12_meta_bytes", "w12_status_string",
-                          "w12_abi_version", "w12_gemm_variant"}
+                          "w12_abi_version", "w12_gemm_variant", "w12_gemm_ws", "bf16_gemm_ws",
+                          "w12_gemm_workspace_bytes", "w12_gemm_ex", "bf16_gemm_ex"}
     for n in names:
         assert hasattr(L, n), n
-    assert w12.w12_abi_version() == 1
+    assert w12.w12_abi_version() == 2
 
 
 def test_sizes():
@@ -34,7 +35,7 @@ def test_sizes():
 
 
 def test_status_strings():
-    for s in (0, -1, -2, -3, -4, -6, -7, 99):
+    for s in (0, -1, -2, -3, -4, -6, -7, -8, 99):
         assert isinstance(w12.w12_status_string(s), str) and w12.w12_status_string(s)
 
 
@@ -95,7 +96,7 @@ def test_explicit_tiling_rejects():
     L = w12.lib()
     args = (A16, 9, 512, A16, A16, A16, A16, 64, 512, A16, 64, 0)
     assert L.w12_gemm_ex(A16, 5, 512, A16, A16, A16, A16, 64, 512, A16, 64, 0,
-                         w12._tiling_arg(w12.Tiling(0, 1, 1, 2, 1)), None) == -6  # x_direct: M <= 4
+                         w12._tiling_arg(w12.Tiling(0, 1, 1, 2, 1)), None, 0, None) == -6  # x_direct: M <= 4
     bad = [w12.Tiling(0, 1, 1, 4),      # GEMV needs M <= 8
            w12.Tiling(2, 1, 1, 4),      # unknown kind
            w12.Tiling(1, 3, 1, 2),      # r not built
@@ -103,16 +104,77 @@ def test_explicit_tiling_rejects():
            w12.Tiling(1, 2, 1, 8),      # (r, depth) pair not built
            w12.Tiling(1, 1, 1, 2, 1),   # direct x is a GEMV mode
            w12.Tiling(0, 1, 1, 2, 2)]   # x_direct is 0 or 1
+    bad += [w12.Tiling(1, 1, 1, 2, 0, 65),   # split-K factor above 64
+            w12.Tiling(1, 1, 1, 2, 0, -1)]
     for t in bad:
-        assert L.w12_gemm_ex(*args, w12._tiling_arg(t), None) == -6, t
+        assert L.w12_gemm_ex(*args, w12._tiling_arg(t), None, 0, None) == -6, t
     assert L.bf16_gemm_ex(A16, 9, 512, A16, 64, 512, A16, 64, 0,
-                          w12._tiling_arg(w12.Tiling(0, 1, 1, 2)), None) == -6
+                          w12._tiling_arg(w12.Tiling(0, 1, 1, 2)), None, 0, None) == -6
+
+
+def test_workspace_bytes():
+    # M=4, N=100 (Np=112, 7 tiles), K=1024 (G=8): a 64 KB counter area, then
+    # the partial sums of every slice.
+    C = 65536
+    t = lambda s: (0, 1, 4, 2, 0, s)
+    assert w12.w12_gemm_workspace_bytes(4, 100, 1024, t(1)) == 0
+    assert w12.w12_gemm_workspace_bytes(4, 100, 1024, t(0)) == 0
+    assert w12.w12_gemm_workspace_bytes(4, 100, 1024, t(4)) == C + 4 * 4 * 112 * 4
+    assert w12.w12_gemm_workspace_bytes(4, 100, 1024, t(3)) == C + 3 * 4 * 112 * 4  # 3+3+2
+    assert w12.w12_gemm_workspace_bytes(4, 100, 1024, t(5)) == C + 4 * 4 * 112 * 4  # 2 each
+    assert w12.w12_gemm_workspace_bytes(4, 100, 1024, t(64)) == C + 8 * 4 * 112 * 4
+    assert w12.w12_gemm_workspace_bytes(4, 100, 1024, (1, 1, 1, 2, 0, 2)) == C + 2 * 4 * 112 * 4
+    with pytest.raises(w12.W12Error):
+        w12.w12_gemm_workspace_bytes(4, 100, 1000)
+    with pytest.raises(w12.W12Error):
+        w12.w12_gemm_workspace_bytes(4, 100, 1024, (0, 1, 4, 2, 0, 65))
+    # at most 16384 row blocks may split K (one tile per workgroup with kw=4)
+    assert w12.w12_gemm_workspace_bytes(1, 16384 * 16, 256, t(2)) == C + 2 * 16384 * 16 * 4
+    with pytest.raises(w12.W12Error):
+        w12.w12_gemm_workspace_bytes(1, 16384 * 16 + 1, 256, t(2))
+    assert w12.w12_gemm_workspace_bytes(1, 16384 * 16 + 1, 256, t(1)) == 0
+    assert w12.w12_default_tiling(1, 16384 * 16 + 1, 256).splitk == 1
+
+
+def test_workspace_rejects():
+    L = w12.lib()
+    args = (A16, 4, 1024, A16, A16, A16, A16, 100, 1024, A16, 100, 0)
+    t = w12._tiling_arg(w12.Tiling(0, 1, 4, 2, 0, 4))
+    need = 65536 + 4 * 4 * 112 * 4
+    assert L.w12_gemm_ex(*args, t, None, 0, None) == -8
+    assert L.w12_gemm_ex(*args, t, A16, need - 1, None) == -8
+    assert L.w12_gemm_ex(*args, t, P(4096 + 16), need, None) == -8   # not 256-byte aligned
+    assert L.bf16_gemm_ex(A16, 4, 1024, A16, 100, 1024, A16, 100, 0, t, None, 0, None) == -8
+    # a shape whose default splits K: 4 row blocks, 136 groups
+    K = 17408
+    assert w12.w12_default_tiling(1, 64, K).splitk == 3
+    assert w12.w12_default_tiling(1, 64, K, allow_splitk=False).splitk == 1
+    assert w12.w12_gemm_variant(1, 64, K).endswith("_s3")
+    assert L.w12_gemm_ws(A16, 1, K, A16, A16, A16, A16, 64, K, A16, 64, 0, None, 0, None) == -8
+    assert L.bf16_gemm_ws(A16, 1, K, A16, 64, K, A16, 64, 0, None, 0, None) == -8
+    # argument errors still come first
+    assert L.w12_gemm_ws(None, 1, K, A16, A16, A16, A16, 64, K, A16, 64, 0, None, 0, None) == -1
+    assert L.w12_gemm_ws(A16, 33, K, A16, A16, A16, A16, 64, K, A16, 64, 0, None, 0, None) == -6
+
+
+def test_default_split_rule():
+    """Slices of at least 40 groups, and none once ~2048 workgroups fill the
+    grid: the 40-group shapes never split, the 136-group down shape splits
+    in three, a very tall long-K weight does not."""
+    assert w12.w12_default_tiling(1, 7168, 5120).splitk == 1
+    assert w12.w12_default_tiling(32, 34816, 5120).splitk == 1
+    for M in (1, 4, 8, 16, 32):
+        assert w12.w12_default_tiling(M, 5120, 17408).splitk == 3
+    assert w12.w12_default_tiling(32, 5120 * 64, 17408).splitk == 1
 
 
 def test_default_tiling():
-    t = w12.w12_default_tiling(1, 7168, 5120)
-    assert t.kind == 0 and t.astuple() in w12.GEMV_TILINGS
-    t = w12.w12_default_tiling(16, 34816, 5120)
-    assert t.kind == 1 and t.astuple() in w12.MFMA_TILINGS
+    for split in (False, True):
+        t = w12.w12_default_tiling(1, 7168, 5120, split)
+        assert t.kind == 0 and t.astuple()[:5] in w12.GEMV_TILINGS and t.splitk >= 1
+        t = w12.w12_default_tiling(16, 34816, 5120, split)
+        assert t.kind == 1 and t.astuple()[:5] in w12.MFMA_TILINGS and t.splitk >= 1
+        if not split:
+            assert t.splitk == 1
     with pytest.raises(w12.W12Error):
         w12.w12_default_tiling(40, 64, 512)

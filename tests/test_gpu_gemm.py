@@ -8,6 +8,9 @@ introduction, batch 1-32).  Pass rule for fp32 outputs, per element:
 the round-to-nearest-even of the same kernel's fp32 output bit for bit, and
 w12_gemm must equal bf16_gemm on the unpacked weights bit for bit (same
 kernels, same summation order; only the weight fetch differs).
+
+The binding's default GEMM is the split-K capable w12_gemm_ws; the checks
+below also run the plain w12_gemm (split_k=False) on every case.
 """
 import numpy as np
 import pytest
@@ -73,13 +76,17 @@ def _run_both(x_bits, P: Prepared, out=torch.float32):
 def _check(oracle, P: Prepared, x_bits, rows, what):
     print("gemm parity:", what, flush=True)
     y12, y16 = _run_both(x_bits, P)
-    y12h = y12.cpu().numpy()
-    y16h = y16.cpu().numpy()
-    assert np.array_equal(y12h.view(np.uint32), y16h.view(np.uint32)), what + ": w12 != bf16 bitwise"
+    xd = to_dev(x_bits)
+    n12 = w12.w12_gemm(xd, P.wt, split_k=False)
+    n16 = w12.bf16_gemm(xd, P.w_tiled, split_k=False)
+    torch.cuda.synchronize()
     w_ref = P.ref_rows(oracle, rows)
     y_ref = oracle.gemm_bf16_f64(x_bits, w_ref)
     tol = oracle.tolerance(x_bits, w_ref)
-    assert_gemm_close(y12h[:, rows], y_ref, tol, what)
+    for a, b, kind in ((y12, y16, "w12_gemm_ws"), (n12, n16, "w12_gemm")):
+        ah, bh = a.cpu().numpy(), b.cpu().numpy()
+        assert np.array_equal(ah.view(np.uint32), bh.view(np.uint32)), what + ": w12 != bf16 bitwise"
+        assert_gemm_close(ah[:, rows], y_ref, tol, "%s %s" % (what, kind))
     return y12
 
 
@@ -205,3 +212,73 @@ def test_every_tiling(oracle, tiling):
             y12h, y16h = y12.cpu().numpy(), y16.cpu().numpy()
             assert np.array_equal(y12h.view(np.uint32), y16h.view(np.uint32)), what
             assert_gemm_close(y12h, oracle.gemm_bf16_f64(x, w_ref), oracle.tolerance(x, w_ref), what)
+
+
+SPLIT_BASES = [(0, 1, 4, 2, 0), (0, 2, 1, 2, 0), (0, 1, 2, 4, 1),
+               (1, 1, 1, 2, 0), (1, 2, 4, 2, 0), (1, 1, 2, 4, 0)]
+
+
+@pytest.mark.parametrize("base", SPLIT_BASES, ids=lambda t: "k%d_r%d_kw%d_d%d_x%d" % t)
+@pytest.mark.parametrize("splitk", [2, 3, 7, 64])
+def test_split_k(oracle, base, splitk):
+    """K split over workgroups: ragged slices (G not a multiple of the
+    factor), one group per slice (64 > G), chunked x inside a slice (K =
+    17408 at 32 rows); W12 and BF16 bitwise equal, oracle tolerance."""
+    tiling = base + (splitk,)
+    Ms = ([1, 2, 4] if base[4] else [1, 3, 8]) if base[0] == 0 else [9, 16, 17, 32]
+    for shape in ((301, 640), (33, 2688), (45, 5120), (77, 17408)):
+        P = prepared(shape)
+        rows = np.arange(P.N)
+        w_ref = P.ref_rows(oracle, rows)
+        for M in Ms:
+            what = "split tiling %s %s M=%d" % (tiling, shape, M)
+            print(what, flush=True)
+            if base[4] and not w12.x_direct_fits(M, base[1], base[3]):
+                continue
+            x = inputs.gaussian_bf16((M, shape[1]), 1.0, 5 * M + shape[1])
+            xd = to_dev(x)
+            try:
+                y12 = w12.w12_gemm(xd, P.wt, tiling=tiling)
+            except w12.W12Error as e:
+                assert e.status == -6, what   # a chunked x buffer too large for LDS
+                continue
+            y16 = w12.bf16_gemm(xd, P.w_tiled, tiling=tiling)
+            torch.cuda.synchronize()
+            y12h, y16h = y12.cpu().numpy(), y16.cpu().numpy()
+            assert np.array_equal(y12h.view(np.uint32), y16h.view(np.uint32)), what
+            assert_gemm_close(y12h, oracle.gemm_bf16_f64(x, w_ref), oracle.tolerance(x, w_ref), what)
+
+
+def test_split_k_counters_reset(oracle):
+    """Every split-K launch leaves its row-block counters at zero, so the next
+    launch on the same workspace writes all of y again (y is prefilled with
+    NaN) and is correct -- also when a launch with many row blocks follows one
+    with few row blocks and large partial sums."""
+    ws = torch.zeros(1 << 22, dtype=torch.uint8, device="cuda")
+    seq = [((130, 1152), 16, (1, 1, 1, 2, 0, 8)),   # 3 row blocks, 5 slices
+           ((4099, 384), 1, (0, 1, 4, 2, 0, 3)),    # 257 row blocks
+           ((1000, 640), 16, (1, 1, 1, 2, 0, 8)),
+           ((1000, 640), 16, (1, 1, 1, 2, 0, 8)),
+           ((4099, 384), 3, (0, 1, 4, 2, 0, 2))]
+    for i, (shape, M, tiling) in enumerate(seq):
+        P = prepared(shape)
+        x = inputs.gaussian_bf16((M, shape[1]), 1.0, 100 + i)
+        y = torch.full((M, shape[0]), float("nan"), dtype=torch.float32, device="cuda")
+        w12.w12_gemm(to_dev(x), P.wt, y=y, tiling=tiling, workspace=ws)
+        torch.cuda.synchronize()
+        assert w12.w12_gemm_workspace_bytes(M, shape[0], shape[1], tiling) > 65536
+        assert int(ws[:65536].count_nonzero()) == 0, "counters not reset"
+        w_ref = P.ref_rows(oracle, np.arange(P.N))
+        assert_gemm_close(y.cpu().numpy(), oracle.gemm_bf16_f64(x, w_ref),
+                          oracle.tolerance(x, w_ref), "counters %s %s" % (tiling, shape))
+
+
+def test_split_k_bf16_output():
+    P = prepared((1000, 640))
+    xd = to_dev(inputs.gaussian_bf16((16, 640), 1.0, 9))
+    for tiling in ((0, 1, 4, 2, 0, 3), (1, 1, 2, 2, 0, 5)):
+        M = 4 if tiling[0] == 0 else 16
+        yf = w12.w12_gemm(xd[:M], P.wt, torch.float32, tiling=tiling)
+        yb = w12.w12_gemm(xd[:M], P.wt, torch.bfloat16, tiling=tiling)
+        torch.cuda.synchronize()
+        assert torch.equal(yb.cpu().view(torch.int16), yf.cpu().to(torch.bfloat16).view(torch.int16))
