@@ -72,10 +72,13 @@ def parse():
                     help="print a markdown summary of a rocprofv3 --stats kernel table")
     ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "VARIANT"),
                     help="print a markdown summary of FETCH_SIZE / WRITE_SIZE counter runs")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("COUNTER_CSV", "VARIANT"),
+                    help="print a markdown summary of any rocprofv3 --pmc run")
     ap.add_argument("--command", default="", help="command line recorded in a summary")
     ap.add_argument("--pmc-calibration", action="store_true",
-                    help="also run a plain 256 MiB device-to-device copy 4 times (the "
-                         "known-size reference for HBM byte counters)")
+                    help="also run a plain elementwise kernel over 256 MiB (bitwise not: "
+                         "reads and writes 256 MiB) 4 times, the known-size reference for "
+                         "HBM byte counters")
     return ap.parse_args()
 
 
@@ -252,10 +255,10 @@ def summarize_pmc(fetch_path, write_path, variant, command):
         return out
     fetch, write = per_kernel(fetch_path), per_kernel(write_path)
     calib_kib = CALIB_BYTES / 1024
-    # The calibration copies are the only device copies that large; the fill
-    # of the copy source writes the same 256 MiB.
-    f_cal = max(v for k, vs in fetch.items() if "copyBuffer" in k for v in vs)
-    w_cal = max(v for vs in write.values() for v in vs)
+    # The calibration kernel (bench.py --pmc-calibration) is the only bitwise
+    # not; it reads and writes CALIB_BYTES.
+    f_cal = statistics.median(v for k, vs in fetch.items() if "bitwise_not" in k for v in vs)
+    w_cal = statistics.median(v for k, vs in write.items() if "bitwise_not" in k for v in vs)
     f_scale, w_scale = calib_kib / f_cal, calib_kib / w_cal
     fk = [k for k in fetch if want in k]
     wk = [k for k in write if want in k]
@@ -267,8 +270,8 @@ def summarize_pmc(fetch_path, write_path, variant, command):
              "    " + command.replace("{CTR}", "FETCH_SIZE"),
              "    " + command.replace("{CTR}", "WRITE_SIZE"), "",
              "Kernel-source hash: `%s`" % source_sha(), "",
-             "Calibration: a plain %d MiB device-to-device copy (bench.py --pmc-calibration) "
-             "reads FETCH_SIZE = %.1f KiB and its source fill writes WRITE_SIZE = %.1f KiB, "
+             "Calibration: a plain elementwise kernel over %d MiB (bitwise not, bench.py "
+             "--pmc-calibration) reads FETCH_SIZE = %.1f KiB and writes WRITE_SIZE = %.1f KiB, "
              "so the counters are scaled by %.4f (fetch) and %.4f (write)."
              % (CALIB_BYTES >> 20, f_cal, w_cal, f_scale, w_scale), "",
              "| kernel | dispatches | FETCH_SIZE KiB (median) | WRITE_SIZE KiB (median) |",
@@ -283,6 +286,38 @@ def summarize_pmc(fetch_path, write_path, variant, command):
                                         "hbm_bytes_per_launch": round(hbm),
                                         "fetch_kib": f_med, "write_kib": w_med,
                                         "fetch_scale": f_scale, "write_scale": w_scale})]
+    print("\n".join(lines))
+
+
+def summarize_counters(path, variant, command):
+    """Per-kernel medians of the counters of one `rocprofv3 --pmc` run; with
+    SQ_VALU_MFMA_BUSY_CYCLES and GRBM_GUI_ACTIVE, also the MFMA busy share
+    (busy cycles summed over the SIMDs / (active cycles x SIMDs))."""
+    import statistics
+    rows = _read_csv(path)
+    want = template_of(variant)
+    vals = {}
+    for r in rows:
+        vals.setdefault((r["Kernel_Name"], r["Counter_Name"]), []).append(float(r["Counter_Value"]))
+    kernels = sorted({k for k, _ in vals})
+    ctrs = sorted({c for _, c in vals})
+    lines = ["# rocprofv3 counters of %s" % variant, "",
+             "Command (run from the repository root on the GPU box):", "",
+             "    " + command, "",
+             "Kernel-source hash: `%s`" % source_sha(), "",
+             "| kernel | dispatches | " + " | ".join("%s (median)" % c for c in ctrs) + " |",
+             "|---|---|" + "---|" * len(ctrs)]
+    for k in kernels:
+        n = max(len(vals.get((k, c), [])) for c in ctrs)
+        cells = ["%.4g" % statistics.median(vals[(k, c)]) if (k, c) in vals else "" for c in ctrs]
+        lines.append("| `%s` | %d | %s |" % (k[:110], n, " | ".join(cells)))
+    hit = [k for k in kernels if want in k]
+    if hit and (hit[0], "SQ_VALU_MFMA_BUSY_CYCLES") in vals and (hit[0], "GRBM_GUI_ACTIVE") in vals:
+        busy = statistics.median(vals[(hit[0], "SQ_VALU_MFMA_BUSY_CYCLES")])
+        active = statistics.median(vals[(hit[0], "GRBM_GUI_ACTIVE")])
+        simds = 4 * 256
+        lines += ["", "MFMA busy share of `%s`: %.2f%% (SQ_VALU_MFMA_BUSY_CYCLES / "
+                  "(GRBM_GUI_ACTIVE x %d SIMDs))." % (variant, 100.0 * busy / (active * simds), simds)]
     print("\n".join(lines))
 
 
@@ -403,6 +438,9 @@ def main():
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc, args.command)
         return
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters, args.command)
+        return
     if args.gpus != 1:
         print("bench.py runs on one GPU only: the W12 decode GEMM of one weight on "
               "one MI355X; --gpus %d is not supported" % args.gpus, file=sys.stderr)
@@ -427,10 +465,12 @@ def main():
     print("headline: %s" % json.dumps(head), file=sys.stderr, flush=True)
 
     if args.pmc_calibration:
+        # a kernel of its own (bitwise not) that reads and writes exactly
+        # CALIB_BYTES, so the summary finds it among the other launches
         src = torch.empty(CALIB_BYTES // 4, dtype=torch.int32, device="cuda").fill_(7)
         dst = torch.empty_like(src)
         for _ in range(4):
-            dst.copy_(src)
+            torch.bitwise_not(src, out=dst)
         torch.cuda.synchronize()
         del src, dst
 
