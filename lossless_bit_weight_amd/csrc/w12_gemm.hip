@@ -64,9 +64,13 @@ bool complete_tiling(Tiling& t, int M, int64_t N, int64_t K) {
         if (M > 32) return false;
         t.mt = M <= 16 ? 16 : 32;
         if (!pair_built(t.r, t.depth)) return false;
+        if (t.xdirect) {
+            if (!kern::xd_ok(true, t.mt, t.r, t.depth)) return false;
+            t.chunked = 0;
+            return true;
+        }
         t.chunked = (int64_t)t.mt * width * 2 > kern::kSingleBytes;
         if (t.chunked && !kern::chunk_ok(t.mt, kern::mfma_kc(t.mt, t.kw, t.depth))) return false;
-        if (t.xdirect) return false;
     } else {
         if (M < 1 || M > 8) return false;
         t.mt = M;
@@ -103,7 +107,10 @@ void bind_split(GemmArgs& a, const Tiling& t, void* ws) {
 // and down (5120x17408) shapes, M in {1, 4, 8, 16, 32}: the GEMV wins up to
 // M = 4 with all four waves of a workgroup splitting K (ring depth 4 at
 // M <= 2, 2 above); from M = 5 on the MFMA wins (the VALU work of eight dot2
-// rows outweighs the padded MFMA tile): 4 K-waves up to M = 8, 2 above.
+// rows outweighs the padded MFMA tile).  Up to M = 8 the MFMA reads its A
+// fragments straight from memory, two tiles per wave, four K-waves (no x
+// barrier: QKV M = 8 13.4 us against 14.7 us through LDS); above, x goes
+// through LDS with two K-waves.
 // Splitting K across workgroups pays only on long K: slices of at least 40
 // groups (5120 weights) keep each workgroup's prologue and epilogue small
 // against its stream, and there is no point once the grid has ~2048
@@ -118,9 +125,15 @@ Tiling choose_tiling(int M, int64_t N, int64_t K, bool allow_splitk) {
         t.mfma = 0;
         t.kw = 4;
         t.depth = M <= 2 ? 4 : 2;
+    } else if (M <= 8) {
+        t.mfma = 1;
+        t.r = 2;
+        t.kw = 4;
+        t.depth = 2;
+        t.xdirect = 1;
     } else {
         t.mfma = 1;
-        t.kw = M <= 8 ? 4 : 2;
+        t.kw = 2;
         t.depth = 2;
     }
     if (allow_splitk) {

@@ -359,13 +359,15 @@ __host__ __device__ constexpr int kc_of(bool mfma, int rows, int KW, int D) {
 // MFMA = false: GEMV, MR = M (1..8).  MFMA = true: MR = 16 or 32 (x rows,
 // zero padded).
 
-// XD (GEMV only): x is not staged in LDS; each ring slot also carries the
-// x values of its group, loaded straight from memory (they are the same for
-// the 16 lanes of a quarter and stay in L1/L2), so there is no prologue
-// barrier at all.
+// XD: x is not staged in LDS; each ring slot also carries the x values of
+// its group, loaded straight from memory (x is small and stays in L1/L2), so
+// there is no x barrier at all.  GEMV: the 16 lanes of a quarter load the
+// same 16 bytes of each x row.  MFMA: each lane loads its own A fragments
+// (row 16 mt + col); rows past M repeat row M - 1 instead of being zero --
+// they only feed output rows that are never stored.
 template <class F, bool MFMA, int MR, int R, int KW, int D, bool CHUNKED, bool XD>
 __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
-    static_assert(!(XD && (MFMA || CHUNKED)), "direct x is a single-pass GEMV mode");
+    static_assert(!(XD && CHUNKED), "direct x is never chunked");
     constexpr int KC = kc_of(MFMA, MR, KW, D);
     constexpr int kRowWaves = 4 / KW;
     constexpr int kBuf = MR * KC / 8;                 // uint4 per x chunk buffer
@@ -404,9 +406,10 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
     for (int r = 0; r < R; ++r) wbase[r] = F::base(g, tload[r]);
     const int glast = g0 + gn - 1;
 
+    constexpr int kXRows = XD ? (MFMA ? kMT : MR) : 1;  // x registers per slot, per block
     struct Slot {
         Raw w[R];
-        uint4 x[XD ? MR : 1][4];
+        uint4 x[kXRows][4];
     };
     Slot ring[D];
     auto fetch = [&](int j, Slot& dst) {
@@ -417,11 +420,12 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
         for (int r = 0; r < R; ++r) F::load(wbase[r], grp, lane, dst.w[r]);
         if constexpr (XD) {
 #pragma unroll
-            for (int m = 0; m < MR; ++m) {
+            for (int i = 0; i < kXRows; ++i) {
+                const int m = MFMA ? 16 * i + col : i;
                 const int mc = m < g.M ? m : g.M - 1;   // rows past M: valid address, unused
 #pragma unroll
                 for (int b = 0; b < 4; ++b)
-                    dst.x[m][b] = *reinterpret_cast<const uint4*>(
+                    dst.x[i][b] = *reinterpret_cast<const uint4*>(
                         g.x + (int64_t)mc * g.ldx + 128 * grp + 32 * b + 8 * q);
             }
         }
@@ -453,9 +457,13 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
             if constexpr (MFMA) {
                 bf16x8_t a[kMT];
 #pragma unroll
-                for (int mt = 0; mt < kMT; ++mt)
-                    a[mt] = __builtin_bit_cast(bf16x8_t,
-                                               xb[XLayout::phys(16 * mt + col, u0 + 4 * b, units_per_row)]);
+                for (int mt = 0; mt < kMT; ++mt) {
+                    if constexpr (XD)
+                        a[mt] = __builtin_bit_cast(bf16x8_t, slot.x[mt][b]);
+                    else
+                        a[mt] = __builtin_bit_cast(bf16x8_t,
+                                                   xb[XLayout::phys(16 * mt + col, u0 + 4 * b, units_per_row)]);
+                }
 #pragma unroll
                 for (int r = 0; r < R; ++r) {
                     uint32_t wv[4];
@@ -515,7 +523,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
 
     if constexpr (MFMA) {
         if constexpr (KW > 1) {
-            __syncthreads();  // every wave is done reading x
+            if constexpr (!XD) __syncthreads();  // every wave is done reading x
             f32x4_t* red = reinterpret_cast<f32x4_t*>(lds);
             constexpr int kPer = R * kMT;
             if (kw > 0) {
@@ -625,11 +633,11 @@ hipError_t launch_one(const GemmArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
-// Direct x is built for the GEMV up to M = 4, when the ring (weights plus
-// 16 x-registers per x row, per slot) fits about 192 VGPRs; larger rings
-// spill.
+// Direct x is built when the ring (weights plus 16 x-registers per x row
+// (GEMV, up to M = 4) or per 16-row A tile (MFMA), per slot) fits about 192
+// VGPRs; larger rings spill.
 __host__ __device__ constexpr bool xd_ok(bool mfma, int mr, int r, int d) {
-    return !mfma && mr <= 4 && d * 16 * (r + mr) <= 192;
+    return mfma ? d * 16 * (r + mr / 16) <= 192 : (mr <= 4 && d * 16 * (r + mr) <= 192);
 }
 
 template <class F, bool MFMA, int MR, int R, int KW, int D>

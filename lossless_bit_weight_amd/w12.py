@@ -59,15 +59,18 @@ class Tiling(ctypes.Structure):
 
 
 # Every tiling the library instantiates: (kind, r, kw, depth, x_direct); any
-# of them may add a sixth entry, the split-K factor (1..64).
-# x_direct needs the GEMV, M <= 4 and a ring of at most 192 registers:
-# depth * 16 * (r + M) <= 192 (x_direct_fits).
+# of them may add a sixth entry, the split-K factor (1..64).  x_direct needs a
+# ring of at most 192 registers: depth * 16 * (r + M) for the GEMV (M <= 4),
+# depth * 16 * (r + A tiles) for the MFMA (1 tile up to M = 16, 2 above); see
+# x_direct_fits.
 _PAIRS = ((1, 2), (1, 4), (1, 8), (2, 2), (2, 4))
 GEMV_TILINGS = [(0, r, kw, d, xd) for (r, d) in _PAIRS for kw in (1, 2, 4) for xd in (0, 1)]
-MFMA_TILINGS = [(1, r, kw, d, 0) for (r, d) in _PAIRS for kw in (1, 2, 4)]
+MFMA_TILINGS = [(1, r, kw, d, xd) for (r, d) in _PAIRS for kw in (1, 2, 4) for xd in (0, 1)]
 
 
-def x_direct_fits(M: int, r: int, depth: int) -> bool:
+def x_direct_fits(M: int, r: int, depth: int, kind: int = 0) -> bool:
+    if kind == 1:
+        return depth * 16 * (r + (1 if M <= 16 else 2)) <= 192
     return M <= 4 and depth * 16 * (r + M) <= 192
 
 

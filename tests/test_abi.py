@@ -94,7 +94,7 @@ def test_variant_selection():
 
 def test_explicit_tiling_rejects():
     L = w12.lib()
-    args = (A16, 9, 512, A16, A16, A16, A16, 64, 512, A16, 64, 0)
+    args = (A16, 17, 512, A16, A16, A16, A16, 64, 512, A16, 64, 0)
     assert L.w12_gemm_ex(A16, 5, 512, A16, A16, A16, A16, 64, 512, A16, 64, 0,
                          w12._tiling_arg(w12.Tiling(0, 1, 1, 2, 1)), None, 0, None) == -6  # x_direct: M <= 4
     bad = [w12.Tiling(0, 1, 1, 4),      # GEMV needs M <= 8
@@ -102,7 +102,8 @@ def test_explicit_tiling_rejects():
            w12.Tiling(1, 3, 1, 2),      # r not built
            w12.Tiling(1, 1, 3, 2),      # kw not built
            w12.Tiling(1, 2, 1, 8),      # (r, depth) pair not built
-           w12.Tiling(1, 1, 1, 2, 1),   # direct x is a GEMV mode
+           w12.Tiling(1, 1, 1, 8, 1),   # MFMA direct x: ring too large
+           w12.Tiling(1, 2, 1, 4, 1),   # (32-row A: 2 tiles -> 4 * 16 * 4 > 192)
            w12.Tiling(0, 1, 1, 2, 2)]   # x_direct is 0 or 1
     bad += [w12.Tiling(1, 1, 1, 2, 0, 65),   # split-K factor above 64
             w12.Tiling(1, 1, 1, 2, 0, -1)]

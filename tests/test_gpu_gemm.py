@@ -203,7 +203,8 @@ def test_every_tiling(oracle, tiling):
                 # only a chunked x buffer that would not fit LDS is rejected
                 rows = M if tiling[0] == 0 else (16 if M <= 16 else 32)
                 if tiling[4]:
-                    assert e.status == -6 and not w12.x_direct_fits(M, tiling[1], tiling[3]), what
+                    assert e.status == -6 and not w12.x_direct_fits(M, tiling[1], tiling[3],
+                                                                     tiling[0]), what
                 else:
                     assert e.status == -6 and rows * shape[1] * 2 > 40 * 1024, what
                 continue
@@ -215,7 +216,7 @@ def test_every_tiling(oracle, tiling):
 
 
 SPLIT_BASES = [(0, 1, 4, 2, 0), (0, 2, 1, 2, 0), (0, 1, 2, 4, 1),
-               (1, 1, 1, 2, 0), (1, 2, 4, 2, 0), (1, 1, 2, 4, 0)]
+               (1, 1, 1, 2, 0), (1, 2, 4, 2, 0), (1, 1, 2, 4, 0), (1, 1, 2, 2, 1), (1, 2, 1, 2, 1)]
 
 
 @pytest.mark.parametrize("base", SPLIT_BASES, ids=lambda t: "k%d_r%d_kw%d_d%d_x%d" % t)
@@ -233,7 +234,7 @@ def test_split_k(oracle, base, splitk):
         for M in Ms:
             what = "split tiling %s %s M=%d" % (tiling, shape, M)
             print(what, flush=True)
-            if base[4] and not w12.x_direct_fits(M, base[1], base[3]):
+            if base[4] and not w12.x_direct_fits(M, base[1], base[3], base[0]):
                 continue
             x = inputs.gaussian_bf16((M, shape[1]), 1.0, 5 * M + shape[1])
             xd = to_dev(x)
