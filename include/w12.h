@@ -134,8 +134,8 @@ int w12_unpack(const void *p0, const void *p1, const void *p2,
  *   p0..meta: the container of an [N, K] weight as written by w12_pack.
  *   y      : device output [M, N], row stride ldy elements (ldy >= N),
  *            BF16 bits (2-byte aligned) or fp32 (4-byte aligned) per y_type.
- * By default M <= 4 runs a wavefront-reduction GEMV (v_dot2c_f32_bf16) and
- * 5 <= M <= 32 runs bf16 MFMA with x padded to 16 or 32 rows (measured
+ * By default M = 1 runs a wavefront-reduction GEMV (v_dot2c_f32_bf16) and
+ * 2 <= M <= 32 runs bf16 MFMA with x padded to 16 or 32 rows (measured
  * crossover); w12_gemm_ex selects either explicitly (GEMV up to M = 8).
  * Each workgroup covers all of K for its rows, so no workspace is needed;
  * w12_gemm_ws adds the split-K tilings.

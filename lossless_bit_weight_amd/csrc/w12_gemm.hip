@@ -104,27 +104,21 @@ void bind_split(GemmArgs& a, const Tiling& t, void* ws) {
 }
 
 // Defaults measured on MI355X over the QKV (7168x5120), gate+up (34816x5120)
-// and down (5120x17408) shapes, M in {1, 4, 8, 16, 32}: the GEMV wins up to
-// M = 4 with all four waves of a workgroup splitting K (ring depth 4 at
-// M <= 2, 2 above); from M = 5 on the MFMA wins (the VALU work of eight dot2
-// rows outweighs the padded MFMA tile).  Up to M = 8 the MFMA reads its A
-// fragments straight from memory, two tiles per wave, four K-waves (no x
-// barrier: QKV M = 8 13.4 us against 14.7 us through LDS); above, x goes
-// through LDS with two K-waves.
-// Splitting K across workgroups pays only on long K: slices of at least 40
-// groups (5120 weights) keep each workgroup's prologue and epilogue small
-// against its stream, and there is no point once the grid has ~2048
-// workgroups.  On the down shape (136 groups, 320 tiles) three slices cut
-// M = 16-32 from 40-51 us to 31-38 us; on the 40-group shapes any split was
-// slower.
+// and down (5120x17408) shapes at M = 1-32.  M = 1 runs the wavefront-
+// reduction GEMV with all four waves of a workgroup splitting K.  From M = 2
+// each extra x row costs the GEMV four more dot2 per 8 weights, and the
+// MFMA, whose cost does not grow until 16 rows, measured faster on all
+// three shapes (QKV M = 4: 12.9 us against 14.6 us): up to M = 8 it reads its
+// A fragments straight from memory with two tiles per wave and four K-waves
+// (no x barrier); from M = 9 x goes through LDS with two K-waves.
 Tiling choose_tiling(int M, int64_t N, int64_t K, bool allow_splitk) {
     Tiling t{};
     t.r = 1;
     t.splitk = 1;
-    if (M <= 4) {
+    if (M == 1) {
         t.mfma = 0;
         t.kw = 4;
-        t.depth = M <= 2 ? 4 : 2;
+        t.depth = 4;
     } else if (M <= 8) {
         t.mfma = 1;
         t.r = 2;

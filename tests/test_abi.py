@@ -83,7 +83,8 @@ def test_pack_unpack_reject():
 
 def test_variant_selection():
     assert w12.w12_gemm_variant(1, 7168, 5120).startswith("w12_gemv_m1_")
-    assert w12.w12_gemm_variant(4, 7168, 5120, False).startswith("bf16_gemv_m4_")
+    assert w12.w12_gemm_variant(4, 7168, 5120, False).startswith("bf16_mfma_mt16_")
+    assert w12.w12_gemm_variant(2, 7168, 5120).startswith("w12_mfma_mt16_r2_kw4_d2_xdirect")
     assert w12.w12_gemm_variant(8, 7168, 5120).startswith("w12_mfma_mt16_")
     assert w12.w12_gemm_variant(9, 7168, 5120).startswith("w12_mfma_mt16_")
     assert w12.w12_gemm_variant(16, 34816, 5120).startswith("w12_mfma_mt16_")
