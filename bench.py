@@ -48,8 +48,8 @@ HBM_PEAK_GBPS = 8000.0           # MI355X HBM3E, published
 ROTATE_BYTES = 1 << 30           # >= 1 GiB of distinct weights per rotation
 CALIB_BYTES = 256 << 20          # size of the counter-calibration copy
 METRIC = "w12_gemm effective weight GB/s & % HBM peak; speedup vs BF16 GEMM, M=1–32"
-WORKLOAD_NAMES = {"qkv": "QKV projection", "gate_up": "MLP fused gate+up projection",
-                  "down": "MLP down projection"}
+WORKLOAD_NAMES = {"qkv": "QKV projection", "o": "attention output projection",
+                  "gate_up": "MLP fused gate+up projection", "down": "MLP down projection"}
 
 
 def parse():
@@ -65,7 +65,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU-oracle work to time")
     ap.add_argument("--sweep-ms", type=str, default="1,2,4,8,16,32")
-    ap.add_argument("--workload", default="qkv", choices=["qkv", "gate_up", "down"],
+    ap.add_argument("--workload", default="qkv", choices=["qkv", "o", "gate_up", "down"],
                     help="headline weight (default: the QKV projection)")
     ap.add_argument("--m", type=int, default=1, help="headline x rows (default 1)")
     ap.add_argument("--summarize-trace", nargs=2, metavar=("KERNEL_STATS_CSV", "VARIANT"),
@@ -477,7 +477,7 @@ def main():
     sweep = []
     if not args.no_sweep:
         ms = [int(m) for m in args.sweep_ms.split(",") if m]
-        for name in ("qkv", "gate_up", "down"):
+        for name in ("qkv", "o", "gate_up", "down"):
             case = inputs.CASES[name]
             wlc = wl if name == "qkv" else Workload(case, torch, w12)
             for M in ms:

@@ -94,8 +94,10 @@ TINY = GemmCase("tiny 1024x512", 1024, 512, 1, 0.02, 1.0, 101, 102, 103)
 QKV = GemmCase("qkv 7168x5120", 7168, 5120, 1, 0.02, 1.0, 201, 202, 203)
 GATE_UP = GemmCase("gate_up 34816x5120", 34816, 5120, 16, 0.02, 1.0, 301, 302, 303)
 DOWN = GemmCase("down 5120x17408", 5120, 17408, 32, 0.015, 0.5, 401, 402, 403)
+# the attention output projection of the same decoder (part of the stack)
+O_PROJ = GemmCase("o 5120x5120", 5120, 5120, 1, 0.02, 1.0, 501, 502, 503)
 
-CASES = {c.name.split()[0]: c for c in (TINY, QKV, GATE_UP, DOWN)}
+CASES = {c.name.split()[0]: c for c in (TINY, QKV, GATE_UP, DOWN, O_PROJ)}
 
 # 64-layer stack: per layer QKV, O, gate+up, down (N, K).
 STACK_LAYERS = 64
@@ -116,10 +118,3 @@ def device_weights(torch, N: int, K: int, seed: int, sigma: float = 0.02,
     bits = w.view(torch.int16)
     bits[zero] &= -0x8000                # keep only the sign bit
     return w
-
-
-def stack_case(layer: int, j: int) -> GemmCase:
-    N, K = STACK_SHAPES[j]
-    s = 10000 + 10 * layer + j
-    return GemmCase("stack L%d.%d %dx%d" % (layer, j, N, K), N, K, 1, 0.02, 1.0,
-                    s, 20000, s + 500000)

@@ -105,7 +105,7 @@ def test_ragged_shapes(oracle, shape, M):
     _check(oracle, P, x, np.arange(P.N), "ragged %s M=%d" % (shape, M))
 
 
-@pytest.mark.parametrize("name", ["qkv", "gate_up", "down"])
+@pytest.mark.parametrize("name", ["qkv", "gate_up", "down", "o"])
 @pytest.mark.parametrize("M", [1, 2, 4, 8, 16, 32])
 def test_workloads_sampled(oracle, name, M):
     case = inputs.CASES[name]
