@@ -72,6 +72,10 @@ def _load():
     lib.w12o_gemm_bf16_f64.argtypes = [p, i64, i64, p, i64, p]
     lib.w12o_gemm_bf16_f64.restype = i32
     lib.w12o_gemm_w12_f64.argtypes = [p, i64, i64, p, p, p, p, i64, p, i32]
+    lib.w12o_exceptions.argtypes = [p, i64, i64, p, p]
+    lib.w12o_exceptions.restype = i64
+    lib.w12o_apply_exceptions.argtypes = [p, i64, i64, p, p]
+    lib.w12o_apply_exceptions.restype = i32
     lib.w12o_gemm_w12_f64.restype = i32
     _lib = lib
     return lib
@@ -175,6 +179,37 @@ def unpack(p0, p1, p2, meta, N: int, K: int) -> np.ndarray:
     if _load().w12o_unpack(*(_ptr(a) for a in arrs), N, K, _ptr(w)) != 0:
         raise ValueError("oracle unpack rejected shape %r" % ((N, K),))
     return w
+
+
+def exceptions(w: np.ndarray):
+    """BF16 bits [N, K] -> (offsets, entries): the exception list of the
+    elements that fall below their group's window (see w12_oracle.c).
+    offsets: uint32[padded_rows(N)/16 + 1]; entries: uint32[count, 2] with
+    word 0 = (row in tile) << 24 | k and word 1 = the original BF16 word."""
+    w = _u16(w)
+    N, K = w.shape
+    lib = _load()
+    count = lib.w12o_exceptions(_ptr(w), N, K, None, None)
+    if count < 0:
+        raise ValueError("oracle exceptions rejected shape %r" % ((N, K),))
+    offsets = np.zeros(padded_rows(N) // 16 + 1, np.uint32)
+    entries = np.zeros((count, 2), np.uint32)
+    lib.w12o_exceptions(_ptr(w), N, K, _ptr(offsets), _ptr(entries) if count else None)
+    return offsets, entries
+
+
+def apply_exceptions(w: np.ndarray, offsets: np.ndarray, entries: np.ndarray) -> np.ndarray:
+    """A copy of the unpacked BF16 weight [N, K] with the exceptions written in."""
+    out = np.array(_u16(w), copy=True)
+    N, K = out.shape
+    offsets = np.ascontiguousarray(offsets, dtype=np.uint32)
+    entries = np.ascontiguousarray(entries, dtype=np.uint32).reshape(-1, 2)
+    if offsets.size != padded_rows(N) // 16 + 1 or entries.shape[0] < int(offsets[-1]):
+        raise ValueError("exception list size mismatch")
+    if _load().w12o_apply_exceptions(_ptr(out), N, K, _ptr(offsets),
+                                     _ptr(entries) if entries.size else None) != 0:
+        raise ValueError("exception entry outside the weight")
+    return out
 
 
 def bf16_tile(w: np.ndarray) -> np.ndarray:

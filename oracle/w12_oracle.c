@@ -248,6 +248,90 @@ int w12o_unpack(const uint8_t *p0, const uint8_t *p1, const uint8_t *p2,
     return 0;
 }
 
+/* ---- exception list: the escape path for unencodable groups --------------
+ * An element whose exponent falls below its group's window is stored in the
+ * planes as the clamp (above) and, in addition, as one exception entry of two
+ * 32-bit words:
+ *   word 0 = (c << 24) | k   c = n % 16 (row inside its 16-row tile), k < 2^24
+ *   word 1 = the element's original BF16 word
+ * Entries are grouped by tile T = n / 16: tile T owns entries
+ * offsets[T] .. offsets[T+1]-1 (offsets has Np/16 + 1 words, offsets[0] = 0).
+ * Inside a tile they follow the order in which the tiled layout stores the
+ * weights: group g, then piece L = 16*q + c, then dword b, then element e
+ * (k = 128*g + 32*b + 8*q + e).  With the list, unpack reproduces every
+ * element exactly, whatever the input.
+ *
+ * w12o_exceptions recomputes each group's base from the weights (it does not
+ * read a container).  offsets and entries may be NULL (then only the count is
+ * returned).  Returns the number of entries, or -1 on bad shape (K must be a
+ * multiple of 128 and below 2^24). */
+int64_t w12o_exceptions(const uint16_t *w, int64_t N, int64_t K,
+                        uint32_t *offsets, uint32_t *entries)
+{
+    if (N < 0 || K < 0 || K % W12O_GROUP != 0 || K >= ((int64_t)1 << 24))
+        return -1;
+    int64_t groups = K / W12O_GROUP;
+    int64_t ntiles = w12o_padded_rows(N) / 16;
+    int64_t count = 0;
+    for (int64_t T = 0; T < ntiles; T++) {
+        if (offsets)
+            offsets[T] = (uint32_t)count;
+        for (int64_t g = 0; g < groups; g++) {
+            int beta[16];
+            for (int c = 0; c < 16; c++) {
+                int64_t n = 16 * T + c;
+                int emax = 0;
+                for (int i = 0; n < N && i < W12O_GROUP; i++) {
+                    int e = bf16_exponent(w[n * K + g * W12O_GROUP + i]);
+                    if (e > emax)
+                        emax = e;
+                }
+                beta[c] = w12o_beta_for_emax(emax);
+            }
+            for (int L = 0; L < 64; L++) {
+                int q = L / 16, c = L % 16;
+                int64_t n = 16 * T + c;
+                if (n >= N)
+                    continue;
+                for (int bb = 0; bb < 4; bb++)
+                    for (int e = 0; e < 8; e++) {
+                        int64_t k = g * W12O_GROUP + 32 * bb + 8 * q + e;
+                        uint16_t v = w[n * K + k];
+                        if (w12o_encodable(v, beta[c]))
+                            continue;
+                        if (entries) {
+                            entries[2 * count] = ((uint32_t)c << 24) | (uint32_t)k;
+                            entries[2 * count + 1] = v;
+                        }
+                        count++;
+                    }
+            }
+        }
+    }
+    if (offsets)
+        offsets[ntiles] = (uint32_t)count;
+    return count;
+}
+
+/* Write the exceptions' original words over an unpacked [N, K] weight. */
+int w12o_apply_exceptions(uint16_t *w, int64_t N, int64_t K,
+                          const uint32_t *offsets, const uint32_t *entries)
+{
+    if (N < 0 || K < 0 || K % W12O_GROUP != 0)
+        return -1;
+    int64_t ntiles = w12o_padded_rows(N) / 16;
+    for (int64_t T = 0; T < ntiles; T++)
+        for (uint32_t i = offsets[T]; i < offsets[T + 1]; i++) {
+            int64_t c = entries[2 * i] >> 24;
+            int64_t k = entries[2 * i] & 0xFFFFFF;
+            int64_t n = 16 * T + c;
+            if (n >= N || k >= K)
+                return -1;
+            w[n * K + k] = (uint16_t)entries[2 * i + 1];
+        }
+    return 0;
+}
+
 /* ---- BF16 control layout ----------------------------------------------------
  * Row-major BF16 [N, K] -> the tiled word order of the control GEMM
  * (w12o_padded_rows(N) * K words; padding rows are zero). */
