@@ -31,7 +31,19 @@
  * A group holding an exponent in [2, 2*beta+1] cannot be stored exactly: the
  * packer flags it (meta bit 7), counts it, and stores that element as the
  * window floor +-2^(2*beta+2-127).  Unpack and GEMM ignore the flag and use
- * the stored (clamped) value.
+ * the stored (clamped) value -- unless the container carries an exception
+ * list (w12_exceptions), which keeps it lossless for every input:
+ *   exc_offsets = Np/16 + 1 uint32 words; tile T = n/16 owns entries
+ *                 exc_offsets[T] .. exc_offsets[T+1]-1 (exc_offsets[0] = 0);
+ *   exc_entries = two uint32 words per element below its window:
+ *                 (c << 24 | k) with c = n % 16, and the original BF16 word;
+ *                 inside a tile in storage order (group g, piece L, dword b,
+ *                 element e).
+ * Unpack writes the original words back; the GEMMs add x[m][k] * (original -
+ * clamp) for each entry after their main loop.  Every call that takes a
+ * container accepts exc_offsets = exc_entries = NULL for "no list"; a list
+ * must come from w12_exceptions for the same weight (it is not validated on
+ * the device), and needs K < 2^24.
  *
  * Conventions for every call below:
  *   - all tensor pointers are DEVICE memory owned by the caller; the library
@@ -59,7 +71,7 @@
 extern "C" {
 #endif
 
-#define W12_ABI_VERSION 2
+#define W12_ABI_VERSION 3
 #define W12_GROUP 128
 #define W12_TILE_ROWS 16
 #define W12_MAX_M 32
@@ -115,15 +127,42 @@ int w12_pack(const uint16_t *w, int64_t N, int64_t K,
              uint32_t *bad_groups, void *stream);
 
 /*
- * w12_unpack -- planes + meta -> BF16 [N, K] (a7, the inverse of w12_pack on
- * every unflagged group; same in-register decode as the GEMMs).
+ * w12_exceptions -- the exception list of a BF16 [N, K] weight (the escape
+ * path that makes the container lossless; format above).  Three launches:
+ * per-block counts into `workspace`, one scan, and the entries.
+ *   w           : device, the same N*K BF16 words given to w12_pack, 16-byte
+ *                 aligned.
+ *   workspace   : device, w12_exceptions_workspace_bytes(N, K) bytes, 4-byte
+ *                 aligned (no initial contents needed).
+ *   exc_offsets : device output, Np/16 + 1 uint32 words.
+ *   exc_entries : device output with room for `capacity` entries (2 words
+ *                 each), or NULL with capacity 0 to count only.
+ *   total       : device uint32 output: the number of entries.  Entries past
+ *                 `capacity` are not written; a caller that finds
+ *                 total > capacity calls again with more room.
+ * Needs K < 2^24 and N*K < 2^32.
+ * Errors: W12_ERR_NULL, W12_ERR_SHAPE, W12_ERR_ALIGN, W12_ERR_WORKSPACE,
+ *         W12_ERR_HIP.
+ */
+size_t w12_exceptions_workspace_bytes(int64_t N, int64_t K);
+int w12_exceptions(const uint16_t *w, int64_t N, int64_t K,
+                   void *workspace, size_t workspace_bytes,
+                   uint32_t *exc_offsets, uint32_t *exc_entries, int64_t capacity,
+                   uint32_t *total, void *stream);
+
+/*
+ * w12_unpack -- planes + meta (+ exception list) -> BF16 [N, K] (a7, the
+ * inverse of w12_pack on every unflagged group, and on every group when the
+ * exception list is given; same in-register decode as the GEMMs).
  *   p0, p1, p2 : device, w12_plane_bytes(N, K) bytes each, 16-byte aligned.
  *   meta       : device, w12_meta_bytes(N, K) bytes.
+ *   exc_offsets, exc_entries : the container's exception list, or both NULL.
  *   w_out      : device output, N*K BF16 words, 16-byte aligned.
  * Errors: W12_ERR_NULL, W12_ERR_SHAPE, W12_ERR_ALIGN, W12_ERR_HIP.
  */
 int w12_unpack(const void *p0, const void *p1, const void *p2,
-               const uint8_t *meta, int64_t N, int64_t K,
+               const uint8_t *meta, const uint32_t *exc_offsets,
+               const uint32_t *exc_entries, int64_t N, int64_t K,
                uint16_t *w_out, void *stream);
 
 /*
@@ -132,6 +171,10 @@ int w12_unpack(const void *p0, const void *p1, const void *p2,
  *   x      : device BF16 [M, K], row stride ldx elements (ldx >= K,
  *            ldx % 8 == 0), 16-byte aligned.  1 <= M <= 32.
  *   p0..meta: the container of an [N, K] weight as written by w12_pack.
+ *   exc_offsets, exc_entries: its exception list (w12_exceptions) or both
+ *            NULL; with a list the result is the GEMM of the original
+ *            weights (within the fp32 tolerance; the corrections are added
+ *            after the main loop).
  *   y      : device output [M, N], row stride ldy elements (ldy >= N),
  *            BF16 bits (2-byte aligned) or fp32 (4-byte aligned) per y_type.
  * By default M = 1 runs a wavefront-reduction GEMV (v_dot2c_f32_bf16) and
@@ -144,7 +187,8 @@ int w12_unpack(const void *p0, const void *p1, const void *p2,
  */
 int w12_gemm(const uint16_t *x, int64_t M, int64_t ldx,
              const void *p0, const void *p1, const void *p2,
-             const uint8_t *meta, int64_t N, int64_t K,
+             const uint8_t *meta, const uint32_t *exc_offsets,
+             const uint32_t *exc_entries, int64_t N, int64_t K,
              void *y, int64_t ldy, int y_type, void *stream);
 
 /*
@@ -233,7 +277,8 @@ int w12_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K,
  */
 int w12_gemm_ws(const uint16_t *x, int64_t M, int64_t ldx,
                 const void *p0, const void *p1, const void *p2,
-                const uint8_t *meta, int64_t N, int64_t K,
+                const uint8_t *meta, const uint32_t *exc_offsets,
+                const uint32_t *exc_entries, int64_t N, int64_t K,
                 void *y, int64_t ldy, int y_type,
                 void *workspace, size_t workspace_bytes, void *stream);
 int bf16_gemm_ws(const uint16_t *x, int64_t M, int64_t ldx,
@@ -248,7 +293,8 @@ int bf16_gemm_ws(const uint16_t *x, int64_t M, int64_t ldx,
  * does not fit M (GEMV needs M <= 8); W12_ERR_WORKSPACE. */
 int w12_gemm_ex(const uint16_t *x, int64_t M, int64_t ldx,
                 const void *p0, const void *p1, const void *p2,
-                const uint8_t *meta, int64_t N, int64_t K,
+                const uint8_t *meta, const uint32_t *exc_offsets,
+                const uint32_t *exc_entries, int64_t N, int64_t K,
                 void *y, int64_t ldy, int y_type, const w12_tiling_t *tiling,
                 void *workspace, size_t workspace_bytes, void *stream);
 int bf16_gemm_ex(const uint16_t *x, int64_t M, int64_t ldx,

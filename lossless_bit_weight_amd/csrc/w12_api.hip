@@ -37,6 +37,21 @@ int check_gemm_common(const uint16_t* x, int64_t M, int64_t ldx, int64_t N, int6
 
 int status_of(hipError_t e) { return e == hipSuccess ? W12_OK : W12_ERR_HIP; }
 
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+// Exception lists index k in 24 bits and elements in 32 bits.
+constexpr int64_t kExcMaxK = (int64_t)1 << 24;
+constexpr int64_t kExcMaxElems = (int64_t)1 << 32;
+
+// Both list pointers or neither; 4-byte aligned; a shape the list can index.
+int check_exceptions(const uint32_t* off, const uint32_t* ent, int64_t N, int64_t K) {
+    if ((off == nullptr) != (ent == nullptr)) return W12_ERR_NULL;
+    if (off == nullptr) return W12_OK;
+    if (!aligned4(off) || !aligned4(ent)) return W12_ERR_ALIGN;
+    if (K >= kExcMaxK || (N + W12_TILE_ROWS) * K >= kExcMaxElems) return W12_ERR_SHAPE;
+    return W12_OK;
+}
+
 w12::GemmArgs make_args(const uint16_t* x, int64_t M, int64_t ldx, int64_t N, int64_t K, void* y,
                         int64_t ldy, int y_type) {
     w12::GemmArgs a{};
@@ -105,13 +120,40 @@ int w12_pack(const uint16_t* w, int64_t N, int64_t K, void* p0, void* p1, void* 
                                       static_cast<hipStream_t>(stream)));
 }
 
-int w12_unpack(const void* p0, const void* p1, const void* p2, const uint8_t* meta, int64_t N,
-               int64_t K, uint16_t* w_out, void* stream) {
+size_t w12_exceptions_workspace_bytes(int64_t N, int64_t K) {
+    if (check_weight_shape(N, K) != W12_OK) return 0;
+    return (size_t)((N + W12_TILE_ROWS - 1) / W12_TILE_ROWS * (K / W12_GROUP) * 4);
+}
+
+int w12_exceptions(const uint16_t* w, int64_t N, int64_t K, void* workspace, size_t workspace_bytes,
+                   uint32_t* exc_offsets, uint32_t* exc_entries, int64_t capacity, uint32_t* total,
+                   void* stream) {
+    if (!w || !exc_offsets || !total) return W12_ERR_NULL;
+    if (int rc = check_weight_shape(N, K)) return rc;
+    if (K >= kExcMaxK || (N + W12_TILE_ROWS) * K >= kExcMaxElems) return W12_ERR_SHAPE;
+    if (capacity < 0 || (capacity > 0 && exc_entries == nullptr)) return W12_ERR_NULL;
+    if (!aligned16(w) || !aligned4(exc_offsets) || !aligned4(total) ||
+        (exc_entries && !aligned4(exc_entries)))
+        return W12_ERR_ALIGN;
+    if (workspace == nullptr || workspace_bytes < w12_exceptions_workspace_bytes(N, K) ||
+        !aligned4(workspace))
+        return W12_ERR_WORKSPACE;
+    return status_of(w12::launch_exceptions(w, N, K, static_cast<uint32_t*>(workspace), exc_offsets,
+                                            exc_entries, capacity, total,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+int w12_unpack(const void* p0, const void* p1, const void* p2, const uint8_t* meta,
+               const uint32_t* exc_offsets, const uint32_t* exc_entries, int64_t N, int64_t K,
+               uint16_t* w_out, void* stream) {
     if (!p0 || !p1 || !p2 || !meta || !w_out) return W12_ERR_NULL;
     if (int rc = check_weight_shape(N, K)) return rc;
     if (!aligned16(p0) || !aligned16(p1) || !aligned16(p2) || !aligned16(w_out)) return W12_ERR_ALIGN;
-    return status_of(w12::launch_unpack(p0, p1, p2, meta, N, K, w_out,
-                                        static_cast<hipStream_t>(stream)));
+    if (int rc = check_exceptions(exc_offsets, exc_entries, N, K)) return rc;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    if (int rc = status_of(w12::launch_unpack(p0, p1, p2, meta, N, K, w_out, s))) return rc;
+    if (exc_offsets == nullptr) return W12_OK;
+    return status_of(w12::launch_apply_exceptions(exc_offsets, exc_entries, N, K, w_out, s));
 }
 
 static int resolve_tiling(const w12_tiling_t* tiling, bool allow_splitk, int64_t M, int64_t N,
@@ -142,12 +184,14 @@ static int check_workspace(const w12::Tiling& t, int64_t M, int64_t N, void* ws,
 }
 
 static int gemm_w12(const uint16_t* x, int64_t M, int64_t ldx, const void* p0, const void* p1,
-                    const void* p2, const uint8_t* meta, int64_t N, int64_t K, void* y,
+                    const void* p2, const uint8_t* meta, const uint32_t* exc_off,
+                    const uint32_t* exc_ent, int64_t N, int64_t K, void* y,
                     int64_t ldy, int y_type, const w12_tiling_t* tiling, bool allow_splitk,
                     void* ws, size_t ws_bytes, void* stream) {
     if (!p0 || !p1 || !p2 || !meta) return W12_ERR_NULL;
     if (int rc = check_gemm_common(x, M, ldx, N, K, y, ldy, y_type)) return rc;
     if (!aligned16(p0) || !aligned16(p1) || !aligned16(p2)) return W12_ERR_ALIGN;
+    if (int rc = check_exceptions(exc_off, exc_ent, N, K)) return rc;
     w12::Tiling t;
     if (int rc = resolve_tiling(tiling, allow_splitk, M, N, K, &t)) return rc;
     if (int rc = check_workspace(t, M, N, ws, ws_bytes)) return rc;
@@ -156,6 +200,8 @@ static int gemm_w12(const uint16_t* x, int64_t M, int64_t ldx, const void* p0, c
     a.p1 = static_cast<const uint8_t*>(p1);
     a.p2 = static_cast<const uint8_t*>(p2);
     a.meta = meta;
+    a.exc_off = exc_off;
+    a.exc_ent = exc_ent;
     w12::bind_split(a, t, ws);
     return status_of(w12::launch_gemm(a, t, true, static_cast<hipStream_t>(stream)));
 }
@@ -176,11 +222,12 @@ static int gemm_bf16(const uint16_t* x, int64_t M, int64_t ldx, const uint16_t* 
 }
 
 int w12_gemm_ex(const uint16_t* x, int64_t M, int64_t ldx, const void* p0, const void* p1,
-                const void* p2, const uint8_t* meta, int64_t N, int64_t K, void* y, int64_t ldy,
+                const void* p2, const uint8_t* meta, const uint32_t* exc_offsets,
+                const uint32_t* exc_entries, int64_t N, int64_t K, void* y, int64_t ldy,
                 int y_type, const w12_tiling_t* tiling, void* workspace, size_t workspace_bytes,
                 void* stream) {
-    return gemm_w12(x, M, ldx, p0, p1, p2, meta, N, K, y, ldy, y_type, tiling, workspace != nullptr,
-                    workspace, workspace_bytes, stream);
+    return gemm_w12(x, M, ldx, p0, p1, p2, meta, exc_offsets, exc_entries, N, K, y, ldy, y_type,
+                    tiling, workspace != nullptr, workspace, workspace_bytes, stream);
 }
 
 int bf16_gemm_ex(const uint16_t* x, int64_t M, int64_t ldx, const uint16_t* w, int64_t N,
@@ -191,10 +238,11 @@ int bf16_gemm_ex(const uint16_t* x, int64_t M, int64_t ldx, const uint16_t* w, i
 }
 
 int w12_gemm(const uint16_t* x, int64_t M, int64_t ldx, const void* p0, const void* p1,
-             const void* p2, const uint8_t* meta, int64_t N, int64_t K, void* y, int64_t ldy,
-             int y_type, void* stream) {
-    return gemm_w12(x, M, ldx, p0, p1, p2, meta, N, K, y, ldy, y_type, nullptr, false, nullptr, 0,
-                    stream);
+             const void* p2, const uint8_t* meta, const uint32_t* exc_offsets,
+             const uint32_t* exc_entries, int64_t N, int64_t K, void* y, int64_t ldy, int y_type,
+             void* stream) {
+    return gemm_w12(x, M, ldx, p0, p1, p2, meta, exc_offsets, exc_entries, N, K, y, ldy, y_type,
+                    nullptr, false, nullptr, 0, stream);
 }
 
 int bf16_gemm(const uint16_t* x, int64_t M, int64_t ldx, const uint16_t* w, int64_t N, int64_t K,
@@ -203,10 +251,11 @@ int bf16_gemm(const uint16_t* x, int64_t M, int64_t ldx, const uint16_t* w, int6
 }
 
 int w12_gemm_ws(const uint16_t* x, int64_t M, int64_t ldx, const void* p0, const void* p1,
-                const void* p2, const uint8_t* meta, int64_t N, int64_t K, void* y, int64_t ldy,
+                const void* p2, const uint8_t* meta, const uint32_t* exc_offsets,
+                const uint32_t* exc_entries, int64_t N, int64_t K, void* y, int64_t ldy,
                 int y_type, void* workspace, size_t workspace_bytes, void* stream) {
-    return gemm_w12(x, M, ldx, p0, p1, p2, meta, N, K, y, ldy, y_type, nullptr, true, workspace,
-                    workspace_bytes, stream);
+    return gemm_w12(x, M, ldx, p0, p1, p2, meta, exc_offsets, exc_entries, N, K, y, ldy, y_type,
+                    nullptr, true, workspace, workspace_bytes, stream);
 }
 
 int bf16_gemm_ws(const uint16_t* x, int64_t M, int64_t ldx, const uint16_t* w, int64_t N,

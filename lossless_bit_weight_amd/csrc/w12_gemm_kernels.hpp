@@ -131,12 +131,41 @@ __device__ __forceinline__ void split_finish(const GemmArgs& g) {
     if (threadIdx.x == 0) __hip_atomic_store(g.cnt + blockIdx.x, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Exception corrections (W12 containers with an exception list): the main
+// loop multiplied each exception element's stored clamp (sign | window floor
+// 2^(2 beta + 2 - 127)); for every entry of `tile` whose group lies in this
+// workgroup's K slice [g0, g0 + gn), the sum first takes back x[m][k] * clamp
+// and then adds x[m][k] * original (two fused multiply-adds; a precomputed
+// difference would round away originals far below the clamp).  Entries are
+// read in list order by all lanes (a uniform loop); `apply(k, original,
+// clamp)` runs only on the lanes of the entry's row (col == c).
+__device__ __forceinline__ float bf16_to_f32(uint32_t v) { return __builtin_bit_cast(float, v << 16); }
+
+template <class Apply>
+__device__ __forceinline__ void exc_corrections(const GemmArgs& g, int64_t tile, int g0, int gn,
+                                                int col, Apply apply) {
+    const int64_t G = g.K / 128;
+    const uint32_t beg = g.exc_off[tile], end = g.exc_off[tile + 1];
+    for (uint32_t i = beg; i < end; ++i) {
+        const uint32_t pos = g.exc_ent[2 * (int64_t)i];
+        const int grp = (int)((pos & 0xFFFFFFu) >> 7);
+        if (grp < g0 || grp >= g0 + gn) continue;
+        const int c = (int)(pos >> 24);
+        if (c != col) continue;
+        const uint32_t val = g.exc_ent[2 * (int64_t)i + 1];
+        const uint32_t beta = g.meta[(tile * G + grp) * 16 + c] & 0x7Fu;
+        const uint32_t clamp = (val & 0x8000u) | ((2u * beta + 2u) << 7);
+        apply((int64_t)(pos & 0xFFFFFFu), bf16_to_f32(val), bf16_to_f32(clamp));
+    }
+}
+
 // ---- weight fetch policies ------------------------------------------------
 // load(): the 32 weights lane `lane` owns in block `blk` (= tile * G + group)
 // into raw registers; block(): its 8-weight block b (0..3) as 4 dwords of
 // BF16 pairs in natural k order.
 
 struct FetchW12 {
+    static constexpr bool kHasExceptions = true;
     struct Raw {
         uint4 a, b, c;
         uint32_t beta;
@@ -167,6 +196,7 @@ struct FetchW12 {
 };
 
 struct FetchBF16 {
+    static constexpr bool kHasExceptions = false;
     struct Raw {
         uint4 q[4];
     };
@@ -546,6 +576,26 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
         // D layout of the 16x16 MFMA: lane (col, q) holds rows 4q..4q+3 of
         // column col, i.e. y[m = 16 mt + 4q + e][n = 16 tile + col].  With a
         // split K the values go to this slice's partial sums instead.
+        if constexpr (F::kHasExceptions) {
+            if (kw == 0 && g.exc_off != nullptr) {
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    if (tile0 + r >= ntiles) continue;
+                    exc_corrections(g, tile0 + r, g0, gn, col, [&](int64_t k, float orig, float clamp) {
+#pragma unroll
+                        for (int mt = 0; mt < kMT; ++mt)
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                const int m = 16 * mt + 4 * q + e;
+                                if (m < g.M) {
+                                    const float xv = bf16_to_f32(g.x[(int64_t)m * g.ldx + k]);
+                                    macc[r][mt][e] = fmaf(xv, orig, fmaf(-xv, clamp, macc[r][mt][e]));
+                                }
+                            }
+                    });
+                }
+            }
+        }
         if (kw == 0) {
 #pragma unroll
             for (int r = 0; r < R; ++r) {
@@ -592,6 +642,22 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
                             v += red[(((p - 1) * kRowWaves + nw) * 16 + col) * (R * MR) + r * MR + m];
                         gacc[r][m] = v;
                     }
+            }
+        }
+        if constexpr (F::kHasExceptions) {
+            if (kw == 0 && g.exc_off != nullptr) {
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    if (tile0 + r >= ntiles) continue;
+                    exc_corrections(g, tile0 + r, g0, gn, col, [&](int64_t k, float orig, float clamp) {
+#pragma unroll
+                        for (int m = 0; m < MR; ++m)
+                            if (m < g.M) {
+                                const float xv = bf16_to_f32(g.x[(int64_t)m * g.ldx + k]);
+                                gacc[r][m] = fmaf(xv, orig, fmaf(-xv, clamp, gacc[r][m]));
+                            }
+                    });
+                }
             }
         }
         // Lane (col, q) stores the outputs m with m % 4 == q.

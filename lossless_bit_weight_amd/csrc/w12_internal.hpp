@@ -16,6 +16,10 @@ struct GemmArgs {
     const uint8_t* p1;
     const uint8_t* p2;
     const uint8_t* meta;
+    // Optional exception list of the container (both NULL when it has none):
+    // tile T owns entries exc_off[T] .. exc_off[T+1]-1, two words each.
+    const uint32_t* exc_off;
+    const uint32_t* exc_ent;
     const uint16_t* w;
     int64_t N;
     int64_t K;
@@ -90,6 +94,14 @@ hipError_t launch_pack(const uint16_t* w, int64_t N, int64_t K, void* p0, void* 
 hipError_t launch_unpack(const void* p0, const void* p1, const void* p2,
                          const uint8_t* meta, int64_t N, int64_t K, uint16_t* w,
                          hipStream_t s);
+// Exception list: count per block into ws (nblocks words), scan, write the
+// tile offsets, the total and at most `capacity` entries.
+hipError_t launch_exceptions(const uint16_t* w, int64_t N, int64_t K, uint32_t* ws,
+                             uint32_t* offsets, uint32_t* entries, int64_t capacity,
+                             uint32_t* total, hipStream_t s);
+// Write the exceptions' original words over an unpacked [N, K] weight.
+hipError_t launch_apply_exceptions(const uint32_t* offsets, const uint32_t* entries, int64_t N,
+                                   int64_t K, uint16_t* w, hipStream_t s);
 hipError_t launch_bf16_tile(const uint16_t* w, int64_t N, int64_t K, uint16_t* out, hipStream_t s);
 
 }  // namespace w12

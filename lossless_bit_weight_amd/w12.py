@@ -111,18 +111,22 @@ def lib() -> ctypes.CDLL:
     L.w12_meta_bytes.restype = ctypes.c_size_t
     L.w12_pack.argtypes = [p, i64, i64, p, p, p, p, p, p]
     L.w12_pack.restype = i32
-    L.w12_unpack.argtypes = [p, p, p, p, i64, i64, p, p]
+    L.w12_unpack.argtypes = [p, p, p, p, p, p, i64, i64, p, p]
     L.w12_unpack.restype = i32
-    L.w12_gemm.argtypes = [p, i64, i64, p, p, p, p, i64, i64, p, i64, i32, p]
+    L.w12_exceptions_workspace_bytes.argtypes = [i64, i64]
+    L.w12_exceptions_workspace_bytes.restype = ctypes.c_size_t
+    L.w12_exceptions.argtypes = [p, i64, i64, p, ctypes.c_size_t, p, p, i64, p, p]
+    L.w12_exceptions.restype = i32
+    L.w12_gemm.argtypes = [p, i64, i64, p, p, p, p, p, p, i64, i64, p, i64, i32, p]
     L.w12_gemm.restype = i32
     L.bf16_gemm.argtypes = [p, i64, i64, p, i64, i64, p, i64, i32, p]
     L.bf16_gemm.restype = i32
     sz = ctypes.c_size_t
-    L.w12_gemm_ex.argtypes = [p, i64, i64, p, p, p, p, i64, i64, p, i64, i32, p, p, sz, p]
+    L.w12_gemm_ex.argtypes = [p, i64, i64, p, p, p, p, p, p, i64, i64, p, i64, i32, p, p, sz, p]
     L.w12_gemm_ex.restype = i32
     L.bf16_gemm_ex.argtypes = [p, i64, i64, p, i64, i64, p, i64, i32, p, p, sz, p]
     L.bf16_gemm_ex.restype = i32
-    L.w12_gemm_ws.argtypes = [p, i64, i64, p, p, p, p, i64, i64, p, i64, i32, p, sz, p]
+    L.w12_gemm_ws.argtypes = [p, i64, i64, p, p, p, p, p, p, i64, i64, p, i64, i32, p, sz, p]
     L.w12_gemm_ws.restype = i32
     L.bf16_gemm_ws.argtypes = [p, i64, i64, p, i64, i64, p, i64, i32, p, sz, p]
     L.bf16_gemm_ws.restype = i32
@@ -241,17 +245,29 @@ def workspace(nbytes: int) -> torch.Tensor:
 @dataclass
 class W12Weight:
     """A packed [N, K] weight: three flat uint8 planes of w12_plane_bytes(N, K)
-    and a flat uint8 meta array of w12_meta_bytes(N, K) (tiled layout)."""
+    and a flat uint8 meta array of w12_meta_bytes(N, K) (tiled layout), plus
+    an optional exception list (int32 tensors: Np/16 + 1 tile offsets and
+    [count, 2] entries) that makes every group lossless."""
     p0: torch.Tensor
     p1: torch.Tensor
     p2: torch.Tensor
     meta: torch.Tensor
     N: int
     K: int
+    exc_offsets: torch.Tensor | None = None
+    exc_entries: torch.Tensor | None = None
 
     @property
     def nbytes(self) -> int:
-        return 3 * self.p0.numel() + self.meta.numel()
+        n = 3 * self.p0.numel() + self.meta.numel()
+        if self.exc_offsets is not None:
+            n += 4 * (self.exc_offsets.numel() + self.exc_entries.numel())
+        return n
+
+    def exc_ptrs(self) -> tuple:
+        if self.exc_offsets is None:
+            return None, None
+        return _dev_ptr(self.exc_offsets, "exc_offsets"), _dev_ptr(self.exc_entries, "exc_entries")
 
 
 @dataclass
@@ -311,15 +327,44 @@ def w12_pack(w: torch.Tensor, out: W12Weight | None = None,
     return out
 
 
-def pack(w: torch.Tensor, strict: bool = False) -> tuple[W12Weight, int]:
+def w12_exceptions(w: torch.Tensor) -> tuple[torch.Tensor, torch.Tensor]:
+    """The exception list of BF16 [N, K] (contiguous): (tile offsets,
+    entries [count, 2]) as int32 tensors.  Counts first, reads the count
+    (a stream synchronisation), then writes the entries."""
+    w = _bf16_2d(w, "w")
+    if not w.is_contiguous():
+        raise ValueError("w must be contiguous")
+    N, K = w.shape
+    wsb = int(lib().w12_exceptions_workspace_bytes(N, K))
+    if wsb == 0:
+        raise W12Error(-2, "w12_exceptions(%d, %d)" % (N, K))
+    ws = torch.empty(wsb // 4, dtype=torch.int32, device=w.device)
+    off = torch.empty(w12_padded_rows(N) // 16 + 1, dtype=torch.int32, device=w.device)
+    total = torch.zeros(1, dtype=torch.int32, device=w.device)
+    args = (_dev_ptr(w, "w"), N, K, _dev_ptr(ws, "workspace"), wsb, _dev_ptr(off, "exc_offsets"))
+    _check(lib().w12_exceptions(*args, None, 0, _dev_ptr(total, "total"), _stream()), "w12_exceptions")
+    count = int(total.item())
+    ent = torch.empty((max(count, 1), 2), dtype=torch.int32, device=w.device)
+    if count:
+        _check(lib().w12_exceptions(*args, _dev_ptr(ent, "exc_entries"), count,
+                                    _dev_ptr(total, "total"), _stream()), "w12_exceptions")
+    return off, ent
+
+
+def pack(w: torch.Tensor, strict: bool = False,
+         exceptions: bool = False) -> tuple[W12Weight, int]:
     """Pack and return (container, number of unencodable groups).  Reading the
-    count synchronises the stream; with strict=True a non-zero count raises."""
+    count synchronises the stream; with strict=True a non-zero count raises;
+    with exceptions=True a container with unencodable groups also gets its
+    exception list, which makes it lossless."""
     bad = torch.zeros(1, dtype=torch.int32, device=w.device)
     out = w12_pack(w, bad_groups=bad)
     n_bad = int(bad.item())
     if strict and n_bad:
         raise W12UnencodableError("%d of %d groups cannot be stored losslessly"
                                   % (n_bad, w.numel() // GROUP))
+    if exceptions and n_bad:
+        out.exc_offsets, out.exc_entries = w12_exceptions(w)
     return out, n_bad
 
 
@@ -329,7 +374,8 @@ def w12_unpack(wt: W12Weight, out: torch.Tensor | None = None) -> torch.Tensor:
         out = torch.empty((wt.N, wt.K), dtype=torch.bfloat16, device=wt.p0.device)
     _bf16_2d(out, "out")
     _check(lib().w12_unpack(_dev_ptr(wt.p0, "p0"), _dev_ptr(wt.p1, "p1"), _dev_ptr(wt.p2, "p2"),
-                            _dev_ptr(wt.meta, "meta"), wt.N, wt.K, _dev_ptr(out, "out"), _stream()),
+                            _dev_ptr(wt.meta, "meta"), *wt.exc_ptrs(), wt.N, wt.K,
+                            _dev_ptr(out, "out"), _stream()),
            "w12_unpack")
     return out
 
@@ -386,8 +432,8 @@ def w12_gemm(x: torch.Tensor, wt: W12Weight, out_dtype: torch.dtype = torch.floa
         y, _ = _out_tensor(M, wt.N, out_dtype, x.device)
     ldy, yt = _y_args(y)
     args = (_dev_ptr(x, "x"), M, ldx, _dev_ptr(wt.p0, "p0"), _dev_ptr(wt.p1, "p1"),
-            _dev_ptr(wt.p2, "p2"), _dev_ptr(wt.meta, "meta"), wt.N, wt.K, _dev_ptr(y, "y"),
-            ldy, yt)
+            _dev_ptr(wt.p2, "p2"), _dev_ptr(wt.meta, "meta"), *wt.exc_ptrs(), wt.N, wt.K,
+            _dev_ptr(y, "y"), ldy, yt)
     wsp, wsb = _ws_args(M, wt.N, wt.K, tiling, split_k, workspace)
     if tiling is not None:
         _check(lib().w12_gemm_ex(*args, _tiling_arg(tiling), wsp, wsb, _stream()), "w12_gemm_ex")

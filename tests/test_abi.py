@@ -17,10 +17,11 @@ def test_loads_and_exports_every_declared_symbol():
     assert set(names) >= {"w12_pack", "w12_unpack", "w12_gemm", "bf16_gemm", "w12_bf16_tile",
                           "w12_plane_bytes", "w12_meta_bytes", "w12_status_string",
                           "w12_abi_version", "w12_gemm_variant", "w12_gemm_ws", "bf16_gemm_ws",
-                          "w12_gemm_workspace_bytes", "w12_gemm_ex", "bf16_gemm_ex"}
+                          "w12_gemm_workspace_bytes", "w12_gemm_ex", "bf16_gemm_ex",
+                          "w12_exceptions", "w12_exceptions_workspace_bytes"}
     for n in names:
         assert hasattr(L, n), n
-    assert w12.w12_abi_version() == 2
+    assert w12.w12_abi_version() == 3
 
 
 def test_sizes():
@@ -44,7 +45,8 @@ def _gemm(**kw):
              ldy=64, yt=0)
     a.update(kw)
     return w12.lib().w12_gemm(a["x"], a["M"], a["ldx"], a["p0"], a["p1"], a["p2"], a["meta"],
-                              a["N"], a["K"], a["y"], a["ldy"], a["yt"], None)
+                              a.get("eo"), a.get("ee"), a["N"], a["K"], a["y"], a["ldy"], a["yt"],
+                              None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -54,6 +56,8 @@ def _gemm(**kw):
     (dict(M=33), -6), (dict(yt=2), -4),
     (dict(x=MIS), -3), (dict(ldx=516), -3), (dict(p2=MIS), -3),
     (dict(yt=1, y=P(4098)), -3),
+    (dict(eo=A16), -1), (dict(ee=A16), -1), (dict(eo=P(4098), ee=A16), -3),
+    (dict(eo=A16, ee=A16, K=1 << 24, ldx=1 << 24), -2),
 ])
 def test_gemm_rejects(kw, status):
     assert _gemm(**kw) == status
@@ -76,9 +80,34 @@ def test_pack_unpack_reject():
     assert L.w12_pack(A16, 4, 130, A16, A16, A16, A16, None, None) == -2
     assert L.w12_pack(MIS, 4, 128, A16, A16, A16, A16, None, None) == -3
     assert L.w12_pack(A16, 4, 128, A16, A16, A16, A16, P(4097), None) == -3
-    assert L.w12_unpack(A16, A16, A16, None, 4, 128, A16, None) == -1
-    assert L.w12_unpack(A16, A16, A16, A16, -1, 128, A16, None) == -2
-    assert L.w12_unpack(A16, A16, A16, A16, 4, 128, MIS, None) == -3
+    assert L.w12_unpack(A16, A16, A16, None, None, None, 4, 128, A16, None) == -1
+    assert L.w12_unpack(A16, A16, A16, A16, None, None, -1, 128, A16, None) == -2
+    assert L.w12_unpack(A16, A16, A16, A16, None, None, 4, 128, MIS, None) == -3
+    assert L.w12_unpack(A16, A16, A16, A16, A16, None, 4, 128, A16, None) == -1
+    assert L.w12_unpack(A16, A16, A16, A16, A16, P(4098), 4, 128, A16, None) == -3
+    assert L.w12_unpack(A16, A16, A16, A16, A16, A16, 4, 1 << 24, A16, None) == -2
+
+
+def test_exceptions_rejects():
+    L = w12.lib()
+    assert w12.lib().w12_exceptions_workspace_bytes(17, 256) == 2 * 2 * 4
+    assert w12.lib().w12_exceptions_workspace_bytes(17, 200) == 0
+    ws = 16
+    ok = (A16, 17, 256, A16, ws, A16, A16, 4, A16, None)
+    bad = [((None,) + ok[1:], -1),
+           (ok[:2] + (200,) + ok[3:], -2),
+           (ok[:2] + (1 << 24,) + ok[3:], -2),                 # k does not fit 24 bits
+           (ok[:1] + (1 << 20,) + (4096,) + ok[3:], -2),       # N*K not below 2^32
+           (ok[:5] + (None,) + ok[6:], -1),                     # offsets
+           (ok[:8] + (None,) + ok[9:], -1),                     # total
+           (ok[:6] + (None,) + ok[7:], -1),                     # capacity without room
+           (ok[:7] + (-1,) + ok[8:], -1),
+           ((MIS,) + ok[1:], -3),
+           (ok[:5] + (P(4098),) + ok[6:], -3),
+           (ok[:3] + (None,) + ok[4:], -8),                     # workspace
+           (ok[:4] + (15,) + ok[5:], -8)]
+    for args, status in bad:
+        assert L.w12_exceptions(*args) == status, args
 
 
 def test_variant_selection():
@@ -95,8 +124,8 @@ def test_variant_selection():
 
 def test_explicit_tiling_rejects():
     L = w12.lib()
-    args = (A16, 17, 512, A16, A16, A16, A16, 64, 512, A16, 64, 0)
-    assert L.w12_gemm_ex(A16, 5, 512, A16, A16, A16, A16, 64, 512, A16, 64, 0,
+    args = (A16, 17, 512, A16, A16, A16, A16, None, None, 64, 512, A16, 64, 0)
+    assert L.w12_gemm_ex(A16, 5, 512, A16, A16, A16, A16, None, None, 64, 512, A16, 64, 0,
                          w12._tiling_arg(w12.Tiling(0, 1, 1, 2, 1)), None, 0, None) == -6  # x_direct: M <= 4
     bad = [w12.Tiling(0, 1, 1, 4),      # GEMV needs M <= 8
            w12.Tiling(2, 1, 1, 4),      # unknown kind
@@ -140,7 +169,7 @@ def test_workspace_bytes():
 
 def test_workspace_rejects():
     L = w12.lib()
-    args = (A16, 4, 1024, A16, A16, A16, A16, 100, 1024, A16, 100, 0)
+    args = (A16, 4, 1024, A16, A16, A16, A16, None, None, 100, 1024, A16, 100, 0)
     t = w12._tiling_arg(w12.Tiling(0, 1, 4, 2, 0, 4))
     need = 65536 + 4 * 4 * 112 * 4
     assert L.w12_gemm_ex(*args, t, None, 0, None) == -8
@@ -152,11 +181,11 @@ def test_workspace_rejects():
     assert w12.w12_default_tiling(1, 64, K).splitk == 3
     assert w12.w12_default_tiling(1, 64, K, allow_splitk=False).splitk == 1
     assert w12.w12_gemm_variant(1, 64, K).endswith("_s3")
-    assert L.w12_gemm_ws(A16, 1, K, A16, A16, A16, A16, 64, K, A16, 64, 0, None, 0, None) == -8
+    assert L.w12_gemm_ws(A16, 1, K, A16, A16, A16, A16, None, None, 64, K, A16, 64, 0, None, 0, None) == -8
     assert L.bf16_gemm_ws(A16, 1, K, A16, 64, K, A16, 64, 0, None, 0, None) == -8
     # argument errors still come first
-    assert L.w12_gemm_ws(None, 1, K, A16, A16, A16, A16, 64, K, A16, 64, 0, None, 0, None) == -1
-    assert L.w12_gemm_ws(A16, 33, K, A16, A16, A16, A16, 64, K, A16, 64, 0, None, 0, None) == -6
+    assert L.w12_gemm_ws(None, 1, K, A16, A16, A16, A16, None, None, 64, K, A16, 64, 0, None, 0, None) == -1
+    assert L.w12_gemm_ws(A16, 33, K, A16, A16, A16, A16, None, None, 64, K, A16, 64, 0, None, 0, None) == -6
 
 
 def test_default_split_rule():
