@@ -23,10 +23,11 @@ The same protocol times the same-tiling BF16 control; `speedup_vs_bf16` is
 the ratio of the two.  `cpu_baseline` times the CPU oracle (decode + fp64
 GEMM, all host threads) on the same workload.
 
-Beside the headline: the M sweep over the QKV, gate+up and down weights;
-pack / unpack throughput on the QKV weight; and one decode step over the
-64-layer linear stack (256 GEMMs, 31.9 GB of W12 weights, captured as one
-graph) at M in {1, 4, 8, 16, 32}.
+Beside the headline: the M sweep over the QKV, O, gate+up and down weights;
+pack / unpack throughput on the QKV weight; the QKV GEMM on the raw
+(unprojected) weight made lossless by its exception list; and one decode
+step over the 64-layer linear stack (256 GEMMs, 31.9 GB of W12 weights,
+captured as one graph) at M in {1, 4, 8, 16, 32}.
 """
 from __future__ import annotations
 
@@ -402,6 +403,41 @@ def stack_step(torch, w12, inputs, ms, steps, warmup):
     return out
 
 
+def measure_exceptions(torch, w12, case, ms, steps, warmup):
+    """The raw (unprojected) weight packed with its exception list, so the
+    container is lossless: list size, and the W12 GEMM against the BF16
+    control on the same raw weight (same protocol as the headline)."""
+    raw = torch.from_numpy(case.weights_raw().view(np.int16)).cuda()
+    wt, bad = w12.pack(raw, exceptions=True)
+    w_tiled = w12.w12_bf16_tile(raw)
+    count = int(wt.exc_offsets[-1].item()) if wt.exc_offsets is not None else 0
+    r = max(2, math.ceil(ROTATE_BYTES / wt.nbytes))
+    clone = lambda t: None if t is None else t.clone()
+    copies = [wt] + [w12.W12Weight(wt.p0.clone(), wt.p1.clone(), wt.p2.clone(), wt.meta.clone(),
+                                   wt.N, wt.K, clone(wt.exc_offsets), clone(wt.exc_entries))
+                     for _ in range(r - 1)]
+    b16 = [w_tiled] + [w12.BF16Tiled(w_tiled.w.clone(), wt.N, wt.K)
+                       for _ in range(max(2, math.ceil(ROTATE_BYTES / w_tiled.nbytes)) - 1)]
+    out = {"workload": case.name + " raw (unprojected)", "flagged_groups": bad,
+           "exceptions": count, "list_bytes": wt.nbytes - 3 * wt.p0.numel() - wt.meta.numel(),
+           "by_m": []}
+    for M in ms:
+        x = torch.from_numpy(case.activations(M).view(np.int16)).cuda()
+        y = torch.empty((M, wt.N), dtype=torch.float32, device="cuda")
+        ws = torch.zeros(max(256, w12.w12_gemm_workspace_bytes(M, wt.N, wt.K)), dtype=torch.uint8,
+                         device="cuda")
+        ms12, _ = time_graph(torch, [(lambda c=c: w12.w12_gemm(x, c, y=y, workspace=ws)) for c in copies],
+                             steps, warmup)
+        ms16, _ = time_graph(torch, [(lambda c=c: w12.bf16_gemm(x, c, y=y, workspace=ws)) for c in b16],
+                             steps, warmup)
+        out["by_m"].append({"M": M, "w12_us": round(ms12 * 1e3, 3), "bf16_us": round(ms16 * 1e3, 3),
+                            "w12_weight_gbps": round(wt.nbytes / ms12 / 1e6, 1),
+                            "speedup_vs_bf16": round(ms16 / ms12, 4)})
+    del copies, b16
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(case, M, seconds):
     """The CPU oracle as it stands: container decode + fp64 GEMM over the whole
     headline weight on all host threads, repeated until ~`seconds` passed."""
@@ -493,6 +529,11 @@ def main():
     codec = time_codec(torch, w12, wl, args.steps)
     print("codec: %s" % json.dumps(codec), file=sys.stderr, flush=True)
 
+    exc = None
+    if not args.no_sweep:
+        exc = measure_exceptions(torch, w12, head_case, [1, 16], args.steps, args.warmup)
+        print("exceptions: %s" % json.dumps(exc), file=sys.stderr, flush=True)
+
     stack = None
     if not args.no_stack:
         del wl
@@ -538,6 +579,7 @@ def main():
         "sweep": [{k: (round(v, 3) if isinstance(v, float) else v) for k, v in r.items()}
                   for r in sweep],
         "codec": codec,
+        "exceptions": exc,
         "stack": stack,
         "source_sha": source_sha(),
     }

@@ -36,7 +36,8 @@
  *   exc_offsets = Np/16 + 1 uint32 words; tile T = n/16 owns entries
  *                 exc_offsets[T] .. exc_offsets[T+1]-1 (exc_offsets[0] = 0);
  *   exc_entries = two uint32 words per element below its window:
- *                 (c << 24 | k) with c = n % 16, and the original BF16 word;
+ *                 (c << 24 | k) with c = n % 16, and (beta << 16 | the
+ *                 original BF16 word) with beta the group's base;
  *                 inside a tile in storage order (group g, piece L, dword b,
  *                 element e).
  * Unpack writes the original words back; the GEMMs add x[m][k] * (original -

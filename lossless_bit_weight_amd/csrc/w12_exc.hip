@@ -29,6 +29,7 @@ __device__ __forceinline__ uint32_t max_u32(uint32_t a, uint32_t b) { return a >
 struct LaneWeights {
     uint32_t v[16];
     uint32_t mask;
+    uint32_t beta;
     int64_t n;
     int64_t kbase;  // k of bit 0: 128 g + 8 q
 };
@@ -62,6 +63,7 @@ __device__ __forceinline__ LaneWeights lane_weights(const uint16_t* __restrict__
     emax = max_u32(emax, (uint32_t)__shfl_xor((int)emax, 32));
     const uint32_t beta = emax <= 15u ? 0u : (emax - 14u) >> 1;
     const uint32_t floor_e = 2u * beta + 2u;
+    r.beta = beta;
     r.mask = 0;
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
@@ -156,7 +158,7 @@ __global__ __launch_bounds__(kThreads) void exc_write_kernel(const uint16_t* __r
             if (idx < capacity) {
                 const int64_t k = r.kbase + 32 * (i >> 3) + (i & 7);
                 entries[2 * idx] = (c << 24) | (uint32_t)k;
-                entries[2 * idx + 1] = word_of(r, i);
+                entries[2 * idx + 1] = (r.beta << 16) | word_of(r, i);
             }
             ++idx;
         }
@@ -173,7 +175,7 @@ __global__ __launch_bounds__(kThreads) void exc_apply_kernel(const uint32_t* __r
         const uint32_t pos = entries[2 * (int64_t)i];
         const int64_t n = 16 * t + (pos >> 24);
         const int64_t k = pos & 0xFFFFFFu;
-        if (n < N && k < K) w[n * K + k] = (uint16_t)entries[2 * (int64_t)i + 1];
+        if (n < N && k < K) w[n * K + k] = (uint16_t)(entries[2 * (int64_t)i + 1] & 0xFFFFu);
     }
 }
 

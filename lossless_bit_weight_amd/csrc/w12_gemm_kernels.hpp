@@ -136,26 +136,87 @@ __device__ __forceinline__ void split_finish(const GemmArgs& g) {
 // 2^(2 beta + 2 - 127)); for every entry of `tile` whose group lies in this
 // workgroup's K slice [g0, g0 + gn), the sum first takes back x[m][k] * clamp
 // and then adds x[m][k] * original (two fused multiply-adds; a precomputed
-// difference would round away originals far below the clamp).  Entries are
-// read in list order by all lanes (a uniform loop); `apply(k, original,
-// clamp)` runs only on the lanes of the entry's row (col == c).
+// difference would round away originals far below the clamp).
+//
+// Entries are handled 64 at a time by one wave: lane i loads entry i and the
+// x[m][k] it needs (all loads of a batch in flight together), stages them in
+// the wave's LDS area, and then every lane walks, in list order, only the
+// entries of its own row (col == c; found with one ballot per row).  The
+// per-wave area holds 64 x (original, clamp) words, a spare word, and
+// XR x 64 BF16 x values.
 __device__ __forceinline__ float bf16_to_f32(uint32_t v) { return __builtin_bit_cast(float, v << 16); }
 
-template <class Apply>
+template <int XR>
+struct ExcStage {
+    static constexpr int kBytes = 64 * 3 * 4 + XR * 64 * 2;
+};
+
+// apply(j, orig, clamp, xs) runs on the lanes of entry j's row; xs(m) reads
+// that entry's x[m][k] from LDS.
+template <int XR, class Apply>
 __device__ __forceinline__ void exc_corrections(const GemmArgs& g, int64_t tile, int g0, int gn,
-                                                int col, Apply apply) {
-    const int64_t G = g.K / 128;
+                                                int lane, int col, uint8_t* area, Apply apply) {
+    float* orig = reinterpret_cast<float*>(area + 256);
+    float* clamp = reinterpret_cast<float*>(area + 512);
+    uint16_t* xs = reinterpret_cast<uint16_t*>(area + 768);
     const uint32_t beg = g.exc_off[tile], end = g.exc_off[tile + 1];
-    for (uint32_t i = beg; i < end; ++i) {
-        const uint32_t pos = g.exc_ent[2 * (int64_t)i];
-        const int grp = (int)((pos & 0xFFFFFFu) >> 7);
-        if (grp < g0 || grp >= g0 + gn) continue;
-        const int c = (int)(pos >> 24);
-        if (c != col) continue;
-        const uint32_t val = g.exc_ent[2 * (int64_t)i + 1];
-        const uint32_t beta = g.meta[(tile * G + grp) * 16 + c] & 0x7Fu;
-        const uint32_t clamp = (val & 0x8000u) | ((2u * beta + 2u) << 7);
-        apply((int64_t)(pos & 0xFFFFFFu), bf16_to_f32(val), bf16_to_f32(clamp));
+    for (uint32_t base = beg; base < end; base += 64) {
+        const uint32_t i = base + (uint32_t)lane;
+        int c = -1;
+        float o = 0.f, cl = 0.f;
+        int64_t k = 0;
+        if (i < end) {
+            const uint32_t pos = g.exc_ent[2 * (int64_t)i];
+            const uint32_t val = g.exc_ent[2 * (int64_t)i + 1];
+            k = pos & 0xFFFFFFu;
+            const int grp = (int)(k >> 7);
+            if (grp >= g0 && grp < g0 + gn) {
+                c = (int)(pos >> 24);
+                o = bf16_to_f32(val & 0xFFFFu);
+                cl = bf16_to_f32((val & 0x8000u) | ((2u * ((val >> 16) & 0x7Fu) + 2u) << 7));
+            }
+        }
+        orig[lane] = o;
+        clamp[lane] = cl;
+        // x[m][k] for the batch, eight rows of loads in flight at a time;
+        // rows past M and lanes without an entry store zero (a zero x adds
+        // nothing, so the consumers need no row test)
+        const uint16_t* px = g.x + (c >= 0 ? k : 0);   // a per-lane running row pointer
+        const uint32_t keep = c >= 0 ? 0xFFFFu : 0u;
+#pragma unroll 1
+        for (int m0 = 0; m0 < XR; m0 += 8) {
+            uint16_t xv[8];
+#pragma unroll
+            for (int d = 0; d < 8; ++d) {
+                xv[d] = *px;
+                px += m0 + d + 1 < g.M ? g.ldx : 0;   // stays on the last row of x
+            }
+            const int valid = g.M - m0;
+#pragma unroll
+            for (int d = 0; d < 8; ++d)
+                if (m0 + d < XR) xs[(m0 + d) * 64 + lane] = (uint16_t)(d < valid ? xv[d] & keep : 0u);
+        }
+        // LDS accesses of one wave complete in order; keep the compiler from
+        // moving the reads below above the writes.
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // The batch entries of this lane's row, as a lane mask (list order =
+        // ascending bit); each lane then walks only its own entries.
+        uint64_t mine = 0;
+#pragma unroll 1
+        for (int cc = 0; cc < 16; ++cc) {
+            const uint64_t b = __ballot(c == cc);
+            if (col == cc) mine = b;
+        }
+        while (mine != 0) {
+            const int j = __ffsll((unsigned long long)mine) - 1;
+            mine &= mine - 1;
+            apply(orig[j], clamp[j], [&](int m) { return bf16_to_f32(xs[m * 64 + j]); });
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
 }
 
@@ -385,6 +446,26 @@ __host__ __device__ constexpr int kc_of(bool mfma, int rows, int KW, int D) {
         }                                                                                 \
     }
 
+// Bytes of LDS a launch needs (x buffers of one K slice of gs groups; the
+// reductions reuse them).
+template <bool MFMA, int MR, int R, int KW, int D, bool CHUNKED, bool XD>
+__host__ __device__ size_t lds_bytes(int gs) {
+    const size_t x = XD ? 0
+                     : CHUNKED ? 2 * (size_t)MR * kc_of(MFMA, MR, KW, D) * 2
+                               : (size_t)MR * gs * 128 * 2;
+    const size_t red = KW == 1 ? 0
+                       : MFMA ? (size_t)(KW - 1) * (4 / KW) * 64 * R * (MR / 16) * 16
+                              : (size_t)(KW - 1) * (4 / KW) * 16 * R * MR * 4;
+    const size_t m = x > red ? x : red;
+    return (m + 15) / 16 * 16;
+}
+// With an exception list the owner waves also stage correction batches, in
+// an area after everything else (so it never meets x or the reductions).
+template <bool MFMA, int MR, int KW>
+__host__ __device__ constexpr size_t exc_lds_bytes() {
+    return (size_t)(4 / KW) * ExcStage<MFMA ? 16 * (MR / 16) : MR>::kBytes;
+}
+
 // ---- the kernel ----------------------------------------------------------------------
 // MFMA = false: GEMV, MR = M (1..8).  MFMA = true: MR = 16 or 32 (x rows,
 // zero padded).
@@ -414,6 +495,8 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
     const int nw = wave / KW;
     const int64_t G = g.K / 128;
     const int64_t ntiles = (g.N + 15) / 16;
+    // start of the exception staging area (after the x buffers / reductions)
+    const size_t exc_base = lds_bytes<MFMA, MR, R, KW, D, CHUNKED, XD>(g.gs);
     const int64_t tile0 = ((int64_t)blockIdx.x * kRowWaves + nw) * R;  // tile r: tile0 + r
 
     int64_t tload[R];  // tiles past the end are clamped for loading
@@ -578,19 +661,18 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
         // split K the values go to this slice's partial sums instead.
         if constexpr (F::kHasExceptions) {
             if (kw == 0 && g.exc_off != nullptr) {
+                uint8_t* area = reinterpret_cast<uint8_t*>(lds) + exc_base + nw * ExcStage<16 * kMT>::kBytes;
 #pragma unroll
                 for (int r = 0; r < R; ++r) {
                     if (tile0 + r >= ntiles) continue;
-                    exc_corrections(g, tile0 + r, g0, gn, col, [&](int64_t k, float orig, float clamp) {
+                    exc_corrections<16 * kMT>(g, tile0 + r, g0, gn, lane, col, area,
+                                              [&](float orig, float clamp, auto xs) {
 #pragma unroll
                         for (int mt = 0; mt < kMT; ++mt)
 #pragma unroll
                             for (int e = 0; e < 4; ++e) {
-                                const int m = 16 * mt + 4 * q + e;
-                                if (m < g.M) {
-                                    const float xv = bf16_to_f32(g.x[(int64_t)m * g.ldx + k]);
-                                    macc[r][mt][e] = fmaf(xv, orig, fmaf(-xv, clamp, macc[r][mt][e]));
-                                }
+                                const float xv = xs(16 * mt + 4 * q + e);
+                                macc[r][mt][e] = fmaf(xv, orig, fmaf(-xv, clamp, macc[r][mt][e]));
                             }
                     });
                 }
@@ -646,16 +728,17 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
         }
         if constexpr (F::kHasExceptions) {
             if (kw == 0 && g.exc_off != nullptr) {
+                uint8_t* area = reinterpret_cast<uint8_t*>(lds) + exc_base + nw * ExcStage<MR>::kBytes;
 #pragma unroll
                 for (int r = 0; r < R; ++r) {
                     if (tile0 + r >= ntiles) continue;
-                    exc_corrections(g, tile0 + r, g0, gn, col, [&](int64_t k, float orig, float clamp) {
+                    exc_corrections<MR>(g, tile0 + r, g0, gn, lane, col, area,
+                                        [&](float orig, float clamp, auto xs) {
 #pragma unroll
-                        for (int m = 0; m < MR; ++m)
-                            if (m < g.M) {
-                                const float xv = bf16_to_f32(g.x[(int64_t)m * g.ldx + k]);
-                                gacc[r][m] = fmaf(xv, orig, fmaf(-xv, clamp, gacc[r][m]));
-                            }
+                        for (int m = 0; m < MR; ++m) {
+                            const float xv = xs(m);
+                            gacc[r][m] = fmaf(xv, orig, fmaf(-xv, clamp, gacc[r][m]));
+                        }
                     });
                 }
             }
@@ -676,25 +759,13 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
 
 // ---- launch helpers ----------------------------------------------------------------------
 
-// Bytes of LDS a launch needs (x buffers of one K slice of gs groups; the
-// reductions reuse them).
-template <bool MFMA, int MR, int R, int KW, int D, bool CHUNKED, bool XD>
-size_t lds_bytes(int gs) {
-    const size_t x = XD ? 0
-                     : CHUNKED ? 2 * (size_t)MR * kc_of(MFMA, MR, KW, D) * 2
-                               : (size_t)MR * gs * 128 * 2;
-    const size_t red = KW == 1 ? 0
-                       : MFMA ? (size_t)(KW - 1) * (4 / KW) * 64 * R * (MR / 16) * 16
-                              : (size_t)(KW - 1) * (4 / KW) * 16 * R * MR * 4;
-    return x > red ? x : red;
-}
-
 template <class F, bool MFMA, int MR, int R, int KW, int D, bool CHUNKED, bool XD>
 hipError_t launch_one(const GemmArgs& a, hipStream_t s) {
     constexpr int kTilesPerWG = (4 / KW) * R;
     const int64_t ntiles = (a.N + 15) / 16;
     const dim3 grid((unsigned)((ntiles + kTilesPerWG - 1) / kTilesPerWG), (unsigned)a.S);
-    const size_t lds = lds_bytes<MFMA, MR, R, KW, D, CHUNKED, XD>(a.gs);
+    size_t lds = lds_bytes<MFMA, MR, R, KW, D, CHUNKED, XD>(a.gs);
+    if (F::kHasExceptions && a.exc_off != nullptr) lds += exc_lds_bytes<MFMA, MR, KW>();
     hipLaunchKernelGGL((gemm_kernel<F, MFMA, MR, R, KW, D, CHUNKED, XD>), grid, dim3(kThreads), lds, s, a);
     return hipGetLastError();
 }

@@ -253,7 +253,9 @@ int w12o_unpack(const uint8_t *p0, const uint8_t *p1, const uint8_t *p2,
  * planes as the clamp (above) and, in addition, as one exception entry of two
  * 32-bit words:
  *   word 0 = (c << 24) | k   c = n % 16 (row inside its 16-row tile), k < 2^24
- *   word 1 = the element's original BF16 word
+ *   word 1 = (beta << 16) | the element's original BF16 word, beta being
+ *            the base of the element's group (so an entry alone gives both
+ *            the original and the clamp the planes hold)
  * Entries are grouped by tile T = n / 16: tile T owns entries
  * offsets[T] .. offsets[T+1]-1 (offsets has Np/16 + 1 words, offsets[0] = 0).
  * Inside a tile they follow the order in which the tiled layout stores the
@@ -301,7 +303,7 @@ int64_t w12o_exceptions(const uint16_t *w, int64_t N, int64_t K,
                             continue;
                         if (entries) {
                             entries[2 * count] = ((uint32_t)c << 24) | (uint32_t)k;
-                            entries[2 * count + 1] = v;
+                            entries[2 * count + 1] = ((uint32_t)beta[c] << 16) | v;
                         }
                         count++;
                     }
@@ -327,7 +329,7 @@ int w12o_apply_exceptions(uint16_t *w, int64_t N, int64_t K,
             int64_t n = 16 * T + c;
             if (n >= N || k >= K)
                 return -1;
-            w[n * K + k] = (uint16_t)entries[2 * i + 1];
+            w[n * K + k] = (uint16_t)(entries[2 * i + 1] & 0xFFFF);
         }
     return 0;
 }

@@ -51,6 +51,8 @@ def test_list_is_exactly_the_lossy_set(oracle, shape, sigma, seed):
     them back restores the weight bit for bit."""
     w = inputs.inject_zeros(inputs.gaussian_bf16(shape, sigma, seed), 0.01, seed + 1)
     back, lossy = _lossy_positions(oracle, w)
+    p0, p1, p2, meta, _ = oracle.pack(w)
+    betas = oracle.meta_of(meta, *shape) & 0x7F
     off, ent = oracle.exceptions(w)
     N, K = shape
     listed = {}
@@ -59,7 +61,9 @@ def test_list_is_exactly_the_lossy_set(oracle, shape, sigma, seed):
             c, k = int(ent[i, 0]) >> 24, int(ent[i, 0]) & 0xFFFFFF
             listed[(16 * T + c, k)] = int(ent[i, 1])
     assert set(listed) == lossy
-    assert all(w[n, k] == v for (n, k), v in listed.items())
+    assert all(w[n, k] == v & 0xFFFF for (n, k), v in listed.items())
+    # the base in each entry is the one the container holds for that group
+    assert all(v >> 16 == betas[n, k // 128] for (n, k), v in listed.items())
     assert np.array_equal(oracle.apply_exceptions(back, off, ent), w)
     assert off[-1] == len(ent) and np.all(np.diff(off.astype(np.int64)) >= 0)
 
