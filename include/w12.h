@@ -224,9 +224,11 @@ int bf16_gemm(const uint16_t *x, int64_t M, int64_t ldx,
  *   kw    : waves of a 256-thread workgroup that split K (1, 2, 4).
  *   depth : 128-weight groups each wave keeps in flight
  *           (r = 1: 2, 4 or 8; r = 2: 2 or 4).
- *   x_direct : GEMV with M <= 4 only: 1 = each lane loads the x values of a
- *           group together with its weights (no LDS staging, no barrier);
- *           0 = x is staged in LDS.
+ *   x_direct : 1 = each lane loads the x values of a group together with
+ *           its weights (no LDS staging, no x barrier); 0 = x is staged in
+ *           LDS.  Built when the register ring stays within ~192 VGPRs:
+ *           GEMV M <= 4 with depth * 16 * (r + M) <= 192; MFMA with
+ *           depth * 16 * (r + M/16 rounded up) <= 192.
  *   splitk : workgroups that split K between them (0 or 1 = none, up to
  *           64); the groups are dealt out in contiguous slices of
  *           ceil(G / splitk) groups (G = K / 128), so the launch uses

@@ -34,13 +34,14 @@
 //     they are loaded once, before the ring is primed, so the prologue
 //     barrier waits for x only.  Otherwise they are double-buffered in
 //     chunks of KC columns loaded one chunk ahead, one barrier per chunk,
-//     between ring windows;
-// GEMV (M <= 8): v_dot2c_f32_bf16 into fp32, x[m] read from LDS as a
-// broadcast (all 16 lanes of a quarter read the same 16 bytes); the 4
-// quarter sums of a row are added with a fixed xor butterfly.
-// MFMA (M <= 32): v_mfma_f32_16x16x32_bf16; block b of lane (col, q) is the
-// B fragment of MFMA b, which therefore contracts the K set
-// {32 b + 8 q + e}; the A fragment (x row col) is read with the same
+//     between ring windows.  In x-direct mode each ring slot carries its
+//     group's x values instead and there is no x barrier at all;
+// GEMV (M <= 8; the default at M = 1): v_dot2c_f32_bf16 into fp32, x[m]
+// read as a broadcast (all 16 lanes of a quarter read the same 16 bytes);
+// the 4 quarter sums of a row are added with a fixed xor butterfly.
+// MFMA (M <= 32; the default from M = 2): v_mfma_f32_16x16x32_bf16; block b
+// of lane (col, q) is the B fragment of MFMA b, which therefore contracts the
+// K set {32 b + 8 q + e}; the A fragment (x row col) is read with the same
 // permutation, so the four MFMAs of a group cover its 128 K exactly once.
 // The W12 and BF16 fetches feed identical operands in identical order, so
 // for W = unpack(pack(W)) both return bitwise equal y.

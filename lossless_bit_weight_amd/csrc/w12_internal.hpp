@@ -42,8 +42,9 @@ struct GemmArgs {
 //   mt      = GEMV: M (1..8); MFMA: x rows padded to 16 or 32.
 //   kw      = waves of a workgroup that split K between them (1, 2 or 4).
 //   depth   = 32-weight slices each lane keeps in flight (2, 4 or 8).
-//   xdirect = 1: GEMV only, M <= 4: x is read by each lane with its weights
-//             instead of being staged in LDS.
+//   xdirect = 1: x is read by each lane with its weights instead of being
+//             staged in LDS (GEMV up to M = 4, MFMA; within a register
+//             budget, see kern::xd_ok).
 //   splitk  = workgroups that split K between them (1 = none); completed to
 //             the number of non-empty slices of gs groups each.
 //   chunked = 0 if the x columns of a K slice are staged in LDS at once, 1 if
