@@ -164,3 +164,49 @@ def test_one_hot_rows_give_original_words(oracle, tiling):
         nz = expect != 0
         assert np.array_equal(yh[nz].view(np.uint32), expect[nz].view(np.uint32)), \
             "one-hot %s M=%d" % (tiling, M)
+
+
+@pytest.mark.parametrize("M", [1, 5, 16, 32])
+def test_bf16_output_and_strides_with_list(oracle, M):
+    """BF16 y equals the round-to-nearest-even of the same call's fp32 y, and
+    strided x / y views give the oracle's result, with corrections applied."""
+    K = 640
+    bits = _raw((300, K), 0.02, 41)
+    wt, _ = _pack_exc(bits)
+    x_full = inputs.gaussian_bf16((M, K + 64), 1.0, 43 + M)
+    xd = to_dev(x_full)[:, :K]
+    yf = w12.w12_gemm(xd, wt, torch.float32)
+    yb = w12.w12_gemm(xd, wt, torch.bfloat16)
+    y_full = torch.full((M, 300 + 20), -3.0, dtype=torch.float32, device="cuda")
+    w12.w12_gemm(xd, wt, y=y_full[:, :300])
+    torch.cuda.synchronize()
+    assert torch.equal(yb.cpu().view(torch.int16), yf.cpu().to(torch.bfloat16).view(torch.int16))
+    assert torch.equal(y_full[:, :300].cpu(), yf.cpu())
+    assert torch.all(y_full[:, 300:] == -3.0)
+    x = np.ascontiguousarray(x_full[:, :K])
+    assert_gemm_close(yf.cpu().numpy(), oracle.gemm_bf16_f64(x, bits), oracle.tolerance(x, bits),
+                      "strided with list M=%d" % M)
+
+
+def test_shared_workspace_mixed_containers(oracle):
+    """One split-K workspace serving, in turn, containers with and without an
+    exception list and of different shapes; each result matches the oracle."""
+    ws = torch.zeros(1 << 22, dtype=torch.uint8, device="cuda")
+    seq = [((77, 17408), True, 8), ((1000, 640), False, 1), ((77, 17408), False, 32),
+           ((130, 1152), True, 16), ((77, 17408), True, 1)]
+    for i, (shape, with_list, M) in enumerate(seq):
+        N, K = shape
+        bits = _raw(shape, 0.02, 60 + i)
+        if with_list:
+            wt, _ = _pack_exc(bits)
+            ref_w = bits
+        else:
+            wt = w12.w12_pack(to_dev(bits))
+            ref_w = to_host_u16(w12.w12_unpack(wt))
+        x = inputs.gaussian_bf16((M, K), 1.0, 70 + i)
+        y = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+        w12.w12_gemm(to_dev(x), wt, y=y, tiling=(1 if M > 1 else 0, 1, 2, 2, 0, 3), workspace=ws)
+        torch.cuda.synchronize()
+        assert int(ws[:65536].count_nonzero()) == 0
+        assert_gemm_close(y.cpu().numpy(), oracle.gemm_bf16_f64(x, ref_w),
+                          oracle.tolerance(x, ref_w), "mixed %d %s" % (i, shape))

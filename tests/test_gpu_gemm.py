@@ -283,3 +283,30 @@ def test_split_k_bf16_output():
         yb = w12.w12_gemm(xd[:M], P.wt, torch.bfloat16, tiling=tiling)
         torch.cuda.synchronize()
         assert torch.equal(yb.cpu().view(torch.int16), yf.cpu().to(torch.bfloat16).view(torch.int16))
+
+
+def test_ex_null_tiling_follows_workspace(oracle):
+    """w12_gemm_ex with no tiling takes the w12_gemm_ws default when given a
+    workspace and the w12_gemm default without one (bitwise the same calls)."""
+    import ctypes
+    P = prepared((77, 17408))
+    M = 16
+    x = inputs.gaussian_bf16((M, 17408), 1.0, 77)
+    xd = to_dev(x)
+    ref_ws = w12.w12_gemm(xd, P.wt)                    # w12_gemm_ws
+    ref_plain = w12.w12_gemm(xd, P.wt, split_k=False)  # w12_gemm
+    L = w12.lib()
+    need = w12.w12_gemm_workspace_bytes(M, P.N, P.K)
+    assert need > 0
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    outs = []
+    for wsp, wsb in ((ws.data_ptr(), need), (None, 0)):
+        y = torch.empty((M, P.N), dtype=torch.float32, device="cuda")
+        st = L.w12_gemm_ex(xd.data_ptr(), M, 17408, P.wt.p0.data_ptr(), P.wt.p1.data_ptr(),
+                           P.wt.p2.data_ptr(), P.wt.meta.data_ptr(), None, None, P.N, P.K,
+                           y.data_ptr(), P.N, 1, None, wsp, wsb, stream)
+        assert st == 0
+        outs.append(y)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], ref_ws) and torch.equal(outs[1], ref_plain)
