@@ -17,8 +17,9 @@ start; AI Radar summary of SpecPilot, English edition, opening paragraph):
   * R distinct copies of the weight (>= 1 GB in total, above the 256 MB
     last-level cache) are used in rotation, so every launch streams from HBM;
   * the R launches are captured once in a HIP graph; W warm-up launches run,
-    then the graph is replayed until K launches are done, bracketed by
-    synchronize + HIP events recorded on the launch stream.
+    the graph is replayed for a short settling time (0.5 s for the headline:
+    the clocks ramp up under load), then replayed until K launches are done,
+    bracketed by synchronize + HIP events recorded on the launch stream.
 The same protocol times the same-tiling BF16 control; `speedup_vs_bf16` is
 the ratio of the two.  `cpu_baseline` times the CPU oracle (decode + fp64
 GEMM, all host threads) on the same workload.
@@ -122,10 +123,12 @@ class Workload:
         torch.cuda.synchronize()
 
 
-def time_graph(torch, launches, steps, warmup):
+def time_graph(torch, launches, steps, warmup, settle_s=0.05):
     """Capture `launches` (callables, in rotation) into one graph, replay it
-    until `steps` launches ran; return average ms per launch measured with
-    events on the launch stream."""
+    for at least `settle_s` seconds (the GPU's clocks ramp up under load:
+    the first launches of a process ran a few percent slower), then replay
+    it until `steps` launches ran; return average ms per launch measured
+    with events on the launch stream."""
     R = len(launches)
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
@@ -141,6 +144,11 @@ def time_graph(torch, launches, steps, warmup):
     reps = max(1, math.ceil(steps / R))
     g.replay()
     torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < settle_s:
+        for _ in range(8):
+            g.replay()
+        torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
@@ -157,7 +165,7 @@ def gemm_bytes(N, K, M, out_bytes, w_bytes):
     return w_bytes + 2 * M * K + out_bytes * M * N
 
 
-def measure(torch, w12, wl: Workload, M, steps, warmup, out_dtype):
+def measure(torch, w12, wl: Workload, M, steps, warmup, out_dtype, settle_s=0.05):
     x = torch.from_numpy(wl.case.activations(M).view(np.int16)).cuda()
     y = torch.empty((M, wl.N), dtype=out_dtype, device="cuda")
     out_b = 4 if out_dtype == torch.float32 else 2
@@ -167,8 +175,8 @@ def measure(torch, w12, wl: Workload, M, steps, warmup, out_dtype):
                      device="cuda")
     l12 = [(lambda c=c: w12.w12_gemm(x, c, y=y, workspace=ws)) for c in wl.w12_copies]
     l16 = [(lambda c=c: w12.bf16_gemm(x, c, y=y, workspace=ws)) for c in wl.bf16_copies]
-    ms12, n12 = time_graph(torch, l12, steps, warmup)
-    ms16, n16 = time_graph(torch, l16, steps, warmup)
+    ms12, n12 = time_graph(torch, l12, steps, warmup, settle_s)
+    ms16, n16 = time_graph(torch, l16, steps, warmup, settle_s)
     b12 = gemm_bytes(wl.N, wl.K, M, out_b, wl.w12_bytes)
     b16 = gemm_bytes(wl.N, wl.K, M, out_b, wl.bf16_bytes)
     return {
@@ -496,7 +504,7 @@ def main():
     wl = Workload(head_case, torch, w12)
     print("headline workload ready (%s, raw unencodable groups %d)" % (head_case.name, wl.raw_bad),
           file=sys.stderr, flush=True)
-    head = measure(torch, w12, wl, head_m, args.steps, args.warmup, torch.float32)
+    head = measure(torch, w12, wl, head_m, args.steps, args.warmup, torch.float32, settle_s=0.5)
     rotation = len(wl.w12_copies)
     print("headline: %s" % json.dumps(head), file=sys.stderr, flush=True)
 

@@ -103,14 +103,25 @@ void bind_split(GemmArgs& a, const Tiling& t, void* ws) {
     }
 }
 
-// Defaults measured on MI355X over the QKV (7168x5120), gate+up (34816x5120)
-// and down (5120x17408) shapes at M = 1-32.  M = 1 runs the wavefront-
-// reduction GEMV with all four waves of a workgroup splitting K.  From M = 2
-// each extra x row costs the GEMV four more dot2 per 8 weights, and the
-// MFMA, whose cost does not grow until 16 rows, measured faster on all
-// three shapes (QKV M = 4: 12.9 us against 14.6 us): up to M = 8 it reads its
-// A fragments straight from memory with two tiles per wave and four K-waves
-// (no x barrier); from M = 9 x goes through LDS with two K-waves.
+// Defaults measured on MI355X over the QKV (7168x5120), O (5120x5120),
+// gate+up (34816x5120) and down (5120x17408) shapes at M = 1-32.  M = 1 runs
+// the wavefront-reduction GEMV with all four waves of a workgroup splitting
+// K.  From M = 2 each extra x row costs the GEMV four more dot2 per 8
+// weights, and the MFMA, whose cost does not grow until 16 rows, measured
+// faster on all shapes (QKV M = 4: 12.9 us against 14.6 us): up to M = 8 it
+// reads its A fragments straight from memory with two tiles per wave and
+// four K-waves (no x barrier); from M = 9 x goes through LDS with two
+// K-waves, or, above 16 rows, one when the grid has >= 1024 row blocks
+// anyway (gate+up M = 32: 64 us against 69.5 us).
+//
+// Splitting K across workgroups (the _ws entry points only): slices of at
+// least 40 groups (5120 weights) keep each workgroup's prologue and
+// epilogue small against its stream, up to ~2048 workgroups -- three
+// slices on the down shape (M = 16-32: 31-38 us instead of 40-51 us).  The
+// LDS path from M = 9 also splits until it has ~480 workgroups, with slices
+// of at least 13 groups: its x chunks make few large workgroups slow (O,
+// 160 row blocks, three slices: M = 12-24 5-7% faster; QKV, 224 row
+// blocks, two slices at M = 24-32; three were 30% slower).
 Tiling choose_tiling(int M, int64_t N, int64_t K, bool allow_splitk) {
     Tiling t{};
     t.r = 1;
@@ -129,6 +140,7 @@ Tiling choose_tiling(int M, int64_t N, int64_t K, bool allow_splitk) {
         t.mfma = 1;
         t.kw = 2;
         t.depth = 2;
+        if (M > 16 && row_blocks(t, N) >= 1024) t.kw = 1;
     }
     if (allow_splitk) {
         const int64_t G = K / 128;
@@ -136,6 +148,11 @@ Tiling choose_tiling(int M, int64_t N, int64_t K, bool allow_splitk) {
         int64_t s = G / 40;
         const int64_t fill = (2048 + nb - 1) / nb;
         s = s < fill ? s : fill;
+        if (t.mfma && !t.xdirect) {
+            int64_t s2 = 480 / nb;
+            s2 = s2 < G / 13 ? s2 : G / 13;
+            s = s > s2 ? s : s2;
+        }
         s = s < kMaxSplitK ? s : kMaxSplitK;
         t.splitk = s > 1 ? (int)s : 1;
     }
