@@ -80,7 +80,8 @@ extern "C" {
 typedef enum {
     W12_OK = 0,
     W12_ERR_NULL = -1,        /* a required pointer is NULL                  */
-    W12_ERR_SHAPE = -2,       /* N < 1, K < 128, K % 128 != 0, M < 1, ld < K/N */
+    W12_ERR_SHAPE = -2,       /* N < 1, K < 128, K % 128 != 0, K >= 2^24,
+                                 N*K >= 2^40, M < 1, ld < K/N               */
     W12_ERR_ALIGN = -3,       /* pointer or leading dimension misaligned     */
     W12_ERR_DTYPE = -4,       /* unknown output type                         */
     W12_ERR_UNSUPPORTED = -6, /* M > 32                                      */

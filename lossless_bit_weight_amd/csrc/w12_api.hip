@@ -12,11 +12,13 @@ namespace {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // Largest element count a launch accepts: keeps every grid below 2^31 blocks
-// and every byte offset far inside int64.
+// and every byte offset far inside int64.  K below 2^24 keeps the in-tile
+// offsets the kernels form in 32 bits (group * 1024 + lane * 16, 128 * group).
 constexpr int64_t kMaxElems = (int64_t)1 << 40;
+constexpr int64_t kMaxK = (int64_t)1 << 24;
 
 int check_weight_shape(int64_t N, int64_t K) {
-    if (N < 1 || K < W12_GROUP || K % W12_GROUP != 0) return W12_ERR_SHAPE;
+    if (N < 1 || K < W12_GROUP || K % W12_GROUP != 0 || K >= kMaxK) return W12_ERR_SHAPE;
     if (N + W12_TILE_ROWS > kMaxElems / K) return W12_ERR_SHAPE;
     return W12_OK;
 }

@@ -32,6 +32,8 @@ def test_sizes():
     assert w12.w12_meta_bytes(17, 256) == 32 * 2
     assert w12.w12_bf16_tiled_bytes(17, 256) == 32 * 256 * 2
     assert w12.w12_plane_bytes(3, 100) == 0
+    assert w12.w12_plane_bytes(1, (1 << 24) - 128) == 16 * ((1 << 24) - 128) // 2
+    assert w12.w12_plane_bytes(1, 1 << 24) == 0
     assert w12.w12_meta_bytes(0, 128) == 0
 
 
@@ -52,6 +54,7 @@ def _gemm(**kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(x=None), -1), (dict(p1=None), -1), (dict(meta=None), -1), (dict(y=None), -1),
     (dict(K=500), -2), (dict(K=0), -2), (dict(N=0), -2), (dict(M=0), -2),
+    (dict(K=1 << 24, ldx=1 << 24), -2), (dict(N=1 << 26, K=1 << 14, ldx=1 << 14, ldy=1 << 26), -2),
     (dict(ldx=256), -2), (dict(ldy=63), -2),
     (dict(M=33), -6), (dict(yt=2), -4),
     (dict(x=MIS), -3), (dict(ldx=516), -3), (dict(p2=MIS), -3),
