@@ -195,6 +195,28 @@ def measure(torch, w12, wl: Workload, M, steps, warmup, out_dtype, settle_s=0.05
     }
 
 
+def read_ceiling(torch, w12, nbytes, steps, warmup):
+    """The library's plain streaming-read kernel (w12_read_probe) over
+    buffers of `nbytes`, rotated like the weights (>= 1 GiB in total), timed
+    with the same graph protocol: the rate a kernel that reads each byte
+    once can reach at this size on this device."""
+    nbytes = (nbytes + 15) // 16 * 16
+    R = max(2, math.ceil(ROTATE_BYTES / nbytes))
+    bufs = [torch.full((nbytes,), i, dtype=torch.uint8, device="cuda") for i in range(R)]
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ms, n = time_graph(torch, [(lambda b=b: w12.w12_read_probe(b, sink)) for b in bufs], steps, warmup)
+    del bufs
+    torch.cuda.empty_cache()
+    return {"bytes": nbytes, "us": ms * 1e3, "gbps": nbytes / (ms * 1e-3) / 1e9, "launches": n}
+
+
+def attach_ceiling(r, c12, c16):
+    """Fractions of the measured read ceiling (same bytes, same protocol)."""
+    r["w12_frac_of_read_ceiling"] = r["w12_weight_gbps"] / c12["gbps"]
+    r["bf16_frac_of_read_ceiling"] = r["bf16_weight_gbps"] / c16["gbps"]
+    return r
+
+
 def template_of(variant: str) -> str:
     """rocprofv3's demangled name of the kernel a variant name refers to, e.g.
     w12_gemv_m1_r1_kw4_d2_single ->
@@ -506,6 +528,10 @@ def main():
           file=sys.stderr, flush=True)
     head = measure(torch, w12, wl, head_m, args.steps, args.warmup, torch.float32, settle_s=0.5)
     rotation = len(wl.w12_copies)
+    ceilings = {}
+    ceilings[args.workload] = (read_ceiling(torch, w12, wl.w12_bytes, args.steps, args.warmup),
+                               read_ceiling(torch, w12, wl.bf16_bytes, args.steps, args.warmup))
+    attach_ceiling(head, *ceilings[args.workload])
     print("headline: %s" % json.dumps(head), file=sys.stderr, flush=True)
 
     if args.pmc_calibration:
@@ -523,9 +549,13 @@ def main():
         ms = [int(m) for m in args.sweep_ms.split(",") if m]
         for name in ("qkv", "o", "gate_up", "down"):
             case = inputs.CASES[name]
-            wlc = wl if name == "qkv" else Workload(case, torch, w12)
+            wlc = wl if name == args.workload else Workload(case, torch, w12)
+            if name not in ceilings:
+                ceilings[name] = (read_ceiling(torch, w12, wlc.w12_bytes, args.steps, args.warmup),
+                                  read_ceiling(torch, w12, wlc.bf16_bytes, args.steps, args.warmup))
             for M in ms:
-                r = measure(torch, w12, wlc, M, args.steps, args.warmup, torch.float32)
+                r = attach_ceiling(measure(torch, w12, wlc, M, args.steps, args.warmup, torch.float32),
+                                   *ceilings[name])
                 sweep.append(r)
                 print("sweep: %s M=%d w12 %.2f us (%.0f GB/s) bf16 %.2f us speedup %.3f"
                       % (name, M, r["w12_us"], r["w12_weight_gbps"], r["bf16_us"],
@@ -576,6 +606,15 @@ def main():
                    "N": head_case.N, "K": head_case.K, "M": head_m, "group": 128,
                    "rotation_copies": rotation},
         "pct_hbm_peak": round(100.0 * head["w12_weight_gbps"] / HBM_PEAK_GBPS, 2),
+        "read_ceiling": {"w12_bytes": ceilings[args.workload][0]["bytes"],
+                         "w12_bytes_gbps": round(ceilings[args.workload][0]["gbps"], 1),
+                         "bf16_bytes": ceilings[args.workload][1]["bytes"],
+                         "bf16_bytes_gbps": round(ceilings[args.workload][1]["gbps"], 1),
+                         "w12_frac": round(head["w12_frac_of_read_ceiling"], 4),
+                         "bf16_frac": round(head["bf16_frac_of_read_ceiling"], 4),
+                         "by_workload": {k: {"w12_bytes_gbps": round(v[0]["gbps"], 1),
+                                             "bf16_bytes_gbps": round(v[1]["gbps"], 1)}
+                                         for k, v in ceilings.items()}},
         "w12_us": round(head["w12_us"], 3),
         "bf16_us": round(head["bf16_us"], 3),
         "speedup_vs_bf16": round(head["speedup_vs_bf16"], 4),

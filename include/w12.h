@@ -72,7 +72,7 @@
 extern "C" {
 #endif
 
-#define W12_ABI_VERSION 3
+#define W12_ABI_VERSION 4
 #define W12_GROUP 128
 #define W12_TILE_ROWS 16
 #define W12_MAX_M 32
@@ -228,7 +228,7 @@ int bf16_gemm(const uint16_t *x, int64_t M, int64_t ldx,
  *   x_direct : 1 = each lane loads the x values of a group together with
  *           its weights (no LDS staging, no x barrier); 0 = x is staged in
  *           LDS.  Built when the register ring stays within ~192 VGPRs:
- *           GEMV M <= 4 with depth * 16 * (r + M) <= 192; MFMA with
+ *           GEMV M <= 4 with depth * (16 * r + 4 * M) <= 192; MFMA with
  *           depth * 16 * (r + M/16 rounded up) <= 192.
  *   splitk : workgroups that split K between them (0 or 1 = none, up to
  *           64); the groups are dealt out in contiguous slices of
@@ -313,6 +313,21 @@ int bf16_gemm_ex(const uint16_t *x, int64_t M, int64_t ldx,
  */
 const char *w12_gemm_variant(int64_t M, int64_t N, int64_t K, int is_w12,
                              int allow_splitk);
+
+/*
+ * w12_read_probe -- measurement aid, not part of the W12 operation: reads
+ * `bytes` of device memory with 16-byte non-temporal loads (each wave a
+ * contiguous run, eight loads in flight per lane) and writes nothing but a
+ * word to sink[0] in the rare case that the xor of all words read equals
+ * 0x9E3779B9.  A GEMM that streams its weights once is bounded by this
+ * rate on a buffer of the same size; the benchmark reports both.  The pages
+ * tune kernels against the memory-bandwidth limit (AI Radar paper summary
+ * of SpecPilot, English edition, opening paragraph).
+ *   buf   : device, 16-byte aligned, bytes % 16 == 0, bytes > 0.
+ *   sink  : device, 4 bytes, 4-byte aligned.
+ * Errors: W12_ERR_NULL, W12_ERR_ALIGN, W12_ERR_SHAPE (bytes == 0), W12_ERR_HIP.
+ */
+int w12_read_probe(const void *buf, size_t bytes, uint32_t *sink, void *stream);
 
 #ifdef __cplusplus
 }

@@ -22,7 +22,8 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 # (source, object name, extra defines): the kernel instantiation unit is
 # compiled once per x height so the build runs in parallel.
 SOURCES = [("w12_api.hip", "w12_api", []), ("w12_pack.hip", "w12_pack", []),
-           ("w12_exc.hip", "w12_exc", []), ("w12_gemm.hip", "w12_gemm", [])]
+           ("w12_exc.hip", "w12_exc", []), ("w12_gemm.hip", "w12_gemm", []),
+           ("w12_probe.hip", "w12_probe", [])]
 SOURCES += [("w12_gemm_inst.hip", "w12_gemv_m%d" % m, ["-DW12_INST_M=%d" % m]) for m in range(1, 9)]
 SOURCES += [("w12_gemm_inst.hip", "w12_mfma", ["-DW12_INST_MFMA"])]
 ARCH = os.environ.get("W12_OFFLOAD_ARCH", "gfx950")

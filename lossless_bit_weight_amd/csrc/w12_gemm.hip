@@ -105,8 +105,11 @@ void bind_split(GemmArgs& a, const Tiling& t, void* ws) {
 
 // Defaults measured on MI355X over the QKV (7168x5120), O (5120x5120),
 // gate+up (34816x5120) and down (5120x17408) shapes at M = 1-32.  M = 1 runs
-// the wavefront-reduction GEMV with all four waves of a workgroup splitting
-// K.  From M = 2 each extra x row costs the GEMV four more dot2 per 8
+// the wavefront-reduction GEMV with x read directly (no x barrier), four
+// groups in flight per wave, and two K-waves per 16-row tile -- or four
+// when the weight has more than 1024 tiles (QKV 10.9 us against 11.3 us
+// with x staged in LDS, O 9.3 against 10.2; gate+up 43.0 us with four
+// K-waves against 46.3 with two).  From M = 2 each extra x row costs the GEMV four more dot2 per 8
 // weights, and the MFMA, whose cost does not grow until 16 rows, measured
 // faster on all shapes (QKV M = 4: 12.9 us against 14.6 us): up to M = 8 it
 // reads its A fragments straight from memory with two tiles per wave and
@@ -128,8 +131,9 @@ Tiling choose_tiling(int M, int64_t N, int64_t K, bool allow_splitk) {
     t.splitk = 1;
     if (M == 1) {
         t.mfma = 0;
-        t.kw = 4;
+        t.kw = (N + 15) / 16 <= 1024 ? 2 : 4;
         t.depth = 4;
+        t.xdirect = 1;
     } else if (M <= 8) {
         t.mfma = 1;
         t.r = 2;

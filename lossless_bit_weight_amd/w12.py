@@ -60,9 +60,9 @@ class Tiling(ctypes.Structure):
 
 # Every tiling the library instantiates: (kind, r, kw, depth, x_direct); any
 # of them may add a sixth entry, the split-K factor (1..64).  x_direct needs a
-# ring of at most 192 registers: depth * 16 * (r + M) for the GEMV (M <= 4),
-# depth * 16 * (r + A tiles) for the MFMA (1 tile up to M = 16, 2 above); see
-# x_direct_fits.
+# ring of at most 192 registers: depth * (16 * r + 4 * M) for the GEMV
+# (M <= 4), depth * 16 * (r + A tiles) for the MFMA (1 tile up to M = 16, 2
+# above); see x_direct_fits.
 _PAIRS = ((1, 2), (1, 4), (1, 8), (2, 2), (2, 4))
 GEMV_TILINGS = [(0, r, kw, d, xd) for (r, d) in _PAIRS for kw in (1, 2, 4) for xd in (0, 1)]
 MFMA_TILINGS = [(1, r, kw, d, xd) for (r, d) in _PAIRS for kw in (1, 2, 4) for xd in (0, 1)]
@@ -71,7 +71,7 @@ MFMA_TILINGS = [(1, r, kw, d, xd) for (r, d) in _PAIRS for kw in (1, 2, 4) for x
 def x_direct_fits(M: int, r: int, depth: int, kind: int = 0) -> bool:
     if kind == 1:
         return depth * 16 * (r + (1 if M <= 16 else 2)) <= 192
-    return M <= 4 and depth * 16 * (r + M) <= 192
+    return M <= 4 and depth * (16 * r + 4 * M) <= 192
 
 
 def _tiling_arg(tiling):
@@ -134,6 +134,8 @@ def lib() -> ctypes.CDLL:
     L.w12_gemm_workspace_bytes.restype = i32
     L.w12_default_tiling.argtypes = [i64, i64, i64, i32, ctypes.POINTER(Tiling)]
     L.w12_default_tiling.restype = i32
+    L.w12_read_probe.argtypes = [p, ctypes.c_size_t, p, p]
+    L.w12_read_probe.restype = i32
     L.w12_gemm_variant.argtypes = [i64, i64, i64, i32, i32]
     L.w12_gemm_variant.restype = ctypes.c_char_p
     _lib = L
@@ -464,3 +466,17 @@ def bf16_gemm(x: torch.Tensor, wt: BF16Tiled, out_dtype: torch.dtype = torch.flo
     else:
         _check(lib().bf16_gemm(*args, _stream()), "bf16_gemm")
     return y
+
+
+def w12_read_probe(buf: torch.Tensor, sink: torch.Tensor) -> None:
+    """Measurement aid: stream all bytes of `buf` (a contiguous GPU tensor,
+    16-byte aligned, size a multiple of 16) through the library's plain read
+    kernel; `sink` is a GPU tensor of at least 4 bytes that is written only
+    in the rare case described in include/w12.h."""
+    if not buf.is_contiguous():
+        raise ValueError("buf must be contiguous")
+    if sink.numel() * sink.element_size() < 4:
+        raise ValueError("sink must hold at least 4 bytes")
+    nbytes = buf.numel() * buf.element_size()
+    _check(lib().w12_read_probe(_dev_ptr(buf, "buf"), nbytes, _dev_ptr(sink, "sink"), _stream()),
+           "w12_read_probe")

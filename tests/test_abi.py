@@ -21,7 +21,7 @@ def test_loads_and_exports_every_declared_symbol():
                           "w12_exceptions", "w12_exceptions_workspace_bytes"}
     for n in names:
         assert hasattr(L, n), n
-    assert w12.w12_abi_version() == 3
+    assert w12.w12_abi_version() == 4
 
 
 def test_sizes():
@@ -212,3 +212,13 @@ def test_default_tiling():
             assert t.splitk == 1
     with pytest.raises(w12.W12Error):
         w12.w12_default_tiling(40, 64, 512)
+
+
+def test_read_probe_rejects():
+    L = w12.lib()
+    assert L.w12_read_probe(None, 16, A16, None) == -1
+    assert L.w12_read_probe(A16, 16, None, None) == -1
+    assert L.w12_read_probe(MIS, 16, A16, None) == -3
+    assert L.w12_read_probe(A16, 24, A16, None) == -3
+    assert L.w12_read_probe(A16, 16, P(4097), None) == -3
+    assert L.w12_read_probe(A16, 0, A16, None) == -2
