@@ -38,8 +38,10 @@ FLAGS = [
 
 
 def _check_resources(src: str, remarks: list[str]) -> None:
-    """Fail the build if any kernel spills registers or uses scratch memory:
-    a spilling variant is never worth shipping."""
+    """Fail the build if any kernel spills to scratch memory: a variant that
+    round-trips registers through memory is never worth shipping.  (A VGPR
+    spilled into an accumulation register, with no scratch, costs two moves
+    and is allowed.)"""
     kernel = None
     bad = []
     for line in remarks:
@@ -47,7 +49,7 @@ def _check_resources(src: str, remarks: list[str]) -> None:
         if m:
             kernel = m.group(1)
             continue
-        m = re.search(r"remark: +(VGPRs Spill|SGPRs Spill|ScratchSize \[bytes/lane\]): (\d+)", line)
+        m = re.search(r"remark: +(ScratchSize \[bytes/lane\]): (\d+)", line)
         if m and int(m.group(2)) > 0:
             bad.append("%s: %s = %s" % (kernel, m.group(1), m.group(2)))
     if bad:

@@ -113,9 +113,12 @@ void bind_split(GemmArgs& a, const Tiling& t, void* ws) {
 // weights, and the MFMA, whose cost does not grow until 16 rows, measured
 // faster on all shapes (QKV M = 4: 12.9 us against 14.6 us): up to M = 8 it
 // reads its A fragments straight from memory with two tiles per wave and
-// four K-waves (no x barrier); from M = 9 x goes through LDS with two
-// K-waves, or, above 16 rows, one when the grid has >= 1024 row blocks
-// anyway (gate+up M = 32: 64 us against 69.5 us).
+// four K-waves (no x barrier).  So does M = 9-32 on weights of at most 1024
+// tiles and 64 groups per row (QKV M = 16: 13.4 us against 15.4 us with x
+// in LDS; M = 32: 18.7 against 19.2; O M = 16: 12.7 against 13.7).  On
+// larger weights x goes through LDS from M = 9, shared by the waves of a
+// workgroup, with two K-waves or, above 16 rows, one when the grid has
+// >= 1024 row blocks anyway (gate+up M = 32: 64 us against 69.5 us).
 //
 // Splitting K across workgroups (the _ws entry points only): slices of at
 // least 40 groups (5120 weights) keep each workgroup's prologue and
@@ -134,7 +137,7 @@ Tiling choose_tiling(int M, int64_t N, int64_t K, bool allow_splitk) {
         t.kw = (N + 15) / 16 <= 1024 ? 2 : 4;
         t.depth = 4;
         t.xdirect = 1;
-    } else if (M <= 8) {
+    } else if (M <= 8 || ((N + 15) / 16 <= 1024 && K / 128 <= 64)) {
         t.mfma = 1;
         t.r = 2;
         t.kw = 4;
