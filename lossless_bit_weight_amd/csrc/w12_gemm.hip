@@ -106,10 +106,12 @@ void bind_split(GemmArgs& a, const Tiling& t, void* ws) {
 // Defaults measured on MI355X over the QKV (7168x5120), O (5120x5120),
 // gate+up (34816x5120) and down (5120x17408) shapes at M = 1-32.  M = 1 runs
 // the wavefront-reduction GEMV with x read directly (no x barrier), four
-// groups in flight per wave, and two K-waves per 16-row tile -- or four
-// when the weight has more than 1024 tiles (QKV 10.9 us against 11.3 us
-// with x staged in LDS, O 9.3 against 10.2; gate+up 43.0 us with four
-// K-waves against 46.3 with two).  From M = 2 each extra x row costs the GEMV four more dot2 per 8
+// groups in flight per wave, and two K-waves per 16-row tile on weights of
+// 256-1024 tiles, four otherwise (QKV 10.9 us against 11.3 us with x staged
+// in LDS, O 9.3 against 10.2; gate+up 43.0 us with four K-waves against 46.3
+// with two; N = 896: 5.8 us against 7.4), and K is never split across
+// workgroups: no split factor 2-16 was faster on any weight measured (N =
+// 640-34816, K = 2176-17408; down 24.4 us unsplit against 25.2 in three).  From M = 2 each extra x row costs the GEMV four more dot2 per 8
 // weights, and the MFMA, whose cost does not grow until 16 rows, measured
 // faster on all shapes (QKV M = 4: 12.9 us against 14.6 us): up to M = 8 it
 // reads its A fragments straight from memory with two tiles per wave and
@@ -120,7 +122,7 @@ void bind_split(GemmArgs& a, const Tiling& t, void* ws) {
 // workgroup, with two K-waves or, above 16 rows, one when the grid has
 // >= 1024 row blocks anyway (gate+up M = 32: 64 us against 69.5 us).
 //
-// Splitting K across workgroups (the _ws entry points only): slices of at
+// Splitting K across workgroups (the _ws entry points, MFMA only): slices of at
 // least 40 groups (5120 weights) keep each workgroup's prologue and
 // epilogue small against its stream, up to ~2048 workgroups -- three
 // slices on the down shape (M = 16-32: 31-38 us instead of 40-51 us).  The
@@ -132,12 +134,13 @@ Tiling choose_tiling(int M, int64_t N, int64_t K, bool allow_splitk) {
     Tiling t{};
     t.r = 1;
     t.splitk = 1;
+    const int64_t ntiles = (N + 15) / 16;
     if (M == 1) {
         t.mfma = 0;
-        t.kw = (N + 15) / 16 <= 1024 ? 2 : 4;
+        t.kw = ntiles >= 256 && ntiles <= 1024 ? 2 : 4;
         t.depth = 4;
         t.xdirect = 1;
-    } else if (M <= 8 || ((N + 15) / 16 <= 1024 && K / 128 <= 64)) {
+    } else if (M <= 8 || (ntiles <= 1024 && K / 128 <= 64)) {
         t.mfma = 1;
         t.r = 2;
         t.kw = 4;
@@ -149,7 +152,7 @@ Tiling choose_tiling(int M, int64_t N, int64_t K, bool allow_splitk) {
         t.depth = 2;
         if (M > 16 && row_blocks(t, N) >= 1024) t.kw = 1;
     }
-    if (allow_splitk) {
+    if (allow_splitk && t.mfma) {
         const int64_t G = K / 128;
         const int64_t nb = row_blocks(t, N);
         int64_t s = G / 40;

@@ -193,23 +193,24 @@ __device__ __forceinline__ void exc_corrections(const GemmArgs& g, int64_t tile,
         }
         orig[lane] = o;
         clamp[lane] = cl;
-        // x[m][k] for the batch, eight rows of loads in flight at a time;
+        // x[m][k] for the batch, sixteen rows of loads in flight at a time;
         // rows past M and lanes without an entry store zero (a zero x adds
         // nothing, so the consumers need no row test)
         const uint16_t* px = g.x + (c >= 0 ? k : 0);   // a per-lane running row pointer
         const uint32_t keep = c >= 0 ? 0xFFFFu : 0u;
+        constexpr int kRound = XR < 16 ? XR : 16;
 #pragma unroll 1
-        for (int m0 = 0; m0 < XR; m0 += 8) {
-            uint16_t xv[8];
+        for (int m0 = 0; m0 < XR; m0 += kRound) {
+            uint16_t xv[kRound];
 #pragma unroll
-            for (int d = 0; d < 8; ++d) {
+            for (int d = 0; d < kRound; ++d) {
                 xv[d] = *px;
                 px += m0 + d + 1 < g.M ? g.ldx : 0;   // stays on the last row of x
             }
             const int valid = g.M - m0;
 #pragma unroll
-            for (int d = 0; d < 8; ++d)
-                if (m0 + d < XR) xs[(m0 + d) * 64 + lane] = (uint16_t)(d < valid ? xv[d] & keep : 0u);
+            for (int d = 0; d < kRound; ++d)
+                xs[(m0 + d) * 64 + lane] = (uint16_t)(d < valid ? xv[d] & keep : 0u);
         }
         // LDS accesses of one wave complete in order; keep the compiler from
         // moving the reads below above the writes.

@@ -179,26 +179,30 @@ def test_workspace_rejects():
     assert L.w12_gemm_ex(*args, t, A16, need - 1, None) == -8
     assert L.w12_gemm_ex(*args, t, P(4096 + 16), need, None) == -8   # not 256-byte aligned
     assert L.bf16_gemm_ex(A16, 4, 1024, A16, 100, 1024, A16, 100, 0, t, None, 0, None) == -8
-    # a shape whose default splits K: 4 row blocks, 136 groups
+    # a shape whose default splits K (M = 4): 4 tiles, 136 groups
     K = 17408
-    assert w12.w12_default_tiling(1, 64, K).splitk == 3
-    assert w12.w12_default_tiling(1, 64, K, allow_splitk=False).splitk == 1
-    assert w12.w12_gemm_variant(1, 64, K).endswith("_s3")
-    assert L.w12_gemm_ws(A16, 1, K, A16, A16, A16, A16, None, None, 64, K, A16, 64, 0, None, 0, None) == -8
-    assert L.bf16_gemm_ws(A16, 1, K, A16, 64, K, A16, 64, 0, None, 0, None) == -8
+    assert w12.w12_default_tiling(4, 64, K).splitk == 3
+    assert w12.w12_default_tiling(4, 64, K, allow_splitk=False).splitk == 1
+    assert w12.w12_gemm_variant(4, 64, K).endswith("_s3")
+    assert L.w12_gemm_ws(A16, 4, K, A16, A16, A16, A16, None, None, 64, K, A16, 64, 0, None, 0, None) == -8
+    assert L.bf16_gemm_ws(A16, 4, K, A16, 64, K, A16, 64, 0, None, 0, None) == -8
     # argument errors still come first
-    assert L.w12_gemm_ws(None, 1, K, A16, A16, A16, A16, None, None, 64, K, A16, 64, 0, None, 0, None) == -1
+    assert L.w12_gemm_ws(None, 4, K, A16, A16, A16, A16, None, None, 64, K, A16, 64, 0, None, 0, None) == -1
     assert L.w12_gemm_ws(A16, 33, K, A16, A16, A16, A16, None, None, 64, K, A16, 64, 0, None, 0, None) == -6
 
 
 def test_default_split_rule():
-    """Slices of at least 40 groups, and none once ~2048 workgroups fill the
-    grid: the 40-group shapes never split, the 136-group down shape splits
-    in three, a very tall long-K weight does not."""
+    """MFMA: slices of at least 40 groups, and none once ~2048 workgroups
+    fill the grid: the 40-group shapes never split, the 136-group down shape
+    splits in three, a very tall long-K weight does not.  The GEMV (M = 1)
+    never splits."""
     assert w12.w12_default_tiling(1, 7168, 5120).splitk == 1
     assert w12.w12_default_tiling(32, 34816, 5120).splitk == 1
-    for M in (1, 4, 8, 16, 32):
+    for M in (4, 8, 16, 32):
         assert w12.w12_default_tiling(M, 5120, 17408).splitk == 3
+    # the M = 1 GEMV never splits K
+    for N, K in ((5120, 17408), (896, 5120), (640, 17408)):
+        assert w12.w12_default_tiling(1, N, K).splitk == 1
     assert w12.w12_default_tiling(32, 5120 * 64, 17408).splitk == 1
 
 
