@@ -220,14 +220,17 @@ def attach_ceiling(r, c12, c16):
 def template_of(variant: str) -> str:
     """rocprofv3's demangled name of the kernel a variant name refers to, e.g.
     w12_gemv_m1_r1_kw4_d2_single ->
-    gemm_kernel<w12::kern::FetchW12, false, 1, 1, 4, 2, false, false>
-    (a split-K suffix _sN does not change the kernel)."""
-    f, kind, mr, r, kw, d, mode = variant.split("_")[:7]
+    gemm_kernel<w12::kern::FetchW12, false, 1, 1, 4, 2, false, false, 4>
+    (the last argument is the wave count, 8 for a _w8 suffix; a split-K
+    suffix _sN does not change the kernel)."""
+    parts = variant.split("_")
+    f, kind, mr, r, kw, d, mode = parts[:7]
+    nw = 8 if "w8" in parts[7:] else 4
     mr = mr.replace("mt", "").replace("m", "")
     tf = lambda b: "true" if b else "false"
-    return "gemm_kernel<w12::kern::%s, %s, %s, %s, %s, %s, %s, %s>" % (
+    return "gemm_kernel<w12::kern::%s, %s, %s, %s, %s, %s, %s, %s, %d>" % (
         "FetchW12" if f == "w12" else "FetchBF16", tf(kind == "mfma"),
-        mr, r[1:], kw[2:], d[1:], tf(mode == "chunked"), tf(mode == "xdirect"))
+        mr, r[1:], kw[2:], d[1:], tf(mode == "chunked"), tf(mode == "xdirect"), nw)
 
 
 TRAFFIC_TAG = "traffic_record: "

@@ -72,7 +72,7 @@
 extern "C" {
 #endif
 
-#define W12_ABI_VERSION 4
+#define W12_ABI_VERSION 5
 #define W12_GROUP 128
 #define W12_TILE_ROWS 16
 #define W12_MAX_M 32
@@ -222,7 +222,8 @@ int bf16_gemm(const uint16_t *x, int64_t M, int64_t ldx,
  * Explicit tiling, for callers that tune the kernels on their own shapes.
  *   kind  : 0 = wavefront-reduction GEMV (M <= 8), 1 = bf16 MFMA (M <= 32).
  *   r     : 16-row weight tiles per wave (1, 2).
- *   kw    : waves of a 256-thread workgroup that split K (1, 2, 4).
+ *   kw    : waves of a workgroup that split K (1, 2, 4; 8 with waves = 8);
+ *           the workgroup's other waves take further weight tiles.
  *   depth : 128-weight groups each wave keeps in flight
  *           (r = 1: 2, 4 or 8; r = 2: 2 or 4).
  *   x_direct : 1 = each lane loads the x values of a group together with
@@ -236,11 +237,14 @@ int bf16_gemm(const uint16_t *x, int64_t M, int64_t ldx,
  *           ceil(G / that) slices.  Each slice's fp32 partial sums go to the
  *           workspace; the last workgroup of a row block to finish adds them
  *           in slice order and writes y.
+ *   waves : waves per workgroup: 0 or 4 = 256 threads; 8 = 512 threads,
+ *           built for kind 1 with x in LDS, r = 1 and depth = 2 (more waves
+ *           share each x tile staged in LDS).
  * When the x columns of a slice do not fit LDS at once they are streamed in
- * chunks; some kw x depth combinations then need more than 64 KB of LDS and
- * are rejected.  The summation order depends on the tiling and never on
- * scheduling; w12 and bf16 kernels with the same tiling sum in the same
- * order.
+ * chunks; some kw x depth combinations then need more than 64 KB of LDS
+ * (128 KB with waves = 8) and are rejected.  The summation order depends
+ * on the tiling and never on scheduling; w12 and bf16 kernels with the
+ * same tiling sum in the same order.
  */
 typedef struct {
     int32_t kind;
@@ -249,6 +253,7 @@ typedef struct {
     int32_t depth;
     int32_t x_direct;
     int32_t splitk;
+    int32_t waves;
 } w12_tiling_t;
 
 /* The tiling the GEMMs use for this shape: that of w12_gemm / bf16_gemm

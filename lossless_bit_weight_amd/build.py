@@ -25,7 +25,8 @@ SOURCES = [("w12_api.hip", "w12_api", []), ("w12_pack.hip", "w12_pack", []),
            ("w12_exc.hip", "w12_exc", []), ("w12_gemm.hip", "w12_gemm", []),
            ("w12_probe.hip", "w12_probe", [])]
 SOURCES += [("w12_gemm_inst.hip", "w12_gemv_m%d" % m, ["-DW12_INST_M=%d" % m]) for m in range(1, 9)]
-SOURCES += [("w12_gemm_inst.hip", "w12_mfma", ["-DW12_INST_MFMA"])]
+SOURCES += [("w12_gemm_inst.hip", "w12_mfma", ["-DW12_INST_MFMA"]),
+            ("w12_gemm_inst.hip", "w12_mfma8", ["-DW12_INST_MFMA8"])]
 ARCH = os.environ.get("W12_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

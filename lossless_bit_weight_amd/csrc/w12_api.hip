@@ -173,6 +173,7 @@ static int resolve_tiling(const w12_tiling_t* tiling, bool allow_splitk, int64_t
     if (tiling->x_direct != 0 && tiling->x_direct != 1) return W12_ERR_UNSUPPORTED;
     t.xdirect = tiling->x_direct;
     t.splitk = tiling->splitk == 0 ? 1 : tiling->splitk;
+    t.nw = tiling->waves == 0 ? 4 : tiling->waves;
     if (!w12::complete_tiling(t, (int)M, N, K)) return W12_ERR_UNSUPPORTED;
     *out = t;
     return W12_OK;
@@ -292,6 +293,7 @@ int w12_default_tiling(int64_t M, int64_t N, int64_t K, int allow_splitk, w12_ti
     out->depth = t.depth;
     out->x_direct = t.xdirect;
     out->splitk = t.splitk;
+    out->waves = t.nw;
     return W12_OK;
 }
 

@@ -40,17 +40,20 @@ bool pair_built(int r, int d) {
     return (r == 1 && (d == 2 || d == 4 || d == 8)) || (r == 2 && (d == 2 || d == 4));
 }
 
-int64_t waves_of(const Tiling& t, int64_t N) { return row_blocks(t, N) * 4; }
-
 }  // namespace
 
 int64_t row_blocks(const Tiling& t, int64_t N) {
-    const int64_t tiles_per_wg = (int64_t)(4 / t.kw) * t.r;
+    const int64_t tiles_per_wg = (int64_t)(t.nw / t.kw) * t.r;
     return ((N + 15) / 16 + tiles_per_wg - 1) / tiles_per_wg;
 }
 
 bool complete_tiling(Tiling& t, int M, int64_t N, int64_t K) {
-    if (t.kw != 1 && t.kw != 2 && t.kw != 4) return false;
+    if (t.nw == 0) t.nw = 4;
+    if (t.nw != 4 && t.nw != 8) return false;
+    if (t.kw != 1 && t.kw != 2 && t.kw != 4 && t.kw != 8) return false;
+    if (t.kw > t.nw) return false;
+    // eight-wave workgroups: MFMA with x in LDS, one tile per wave, depth 2
+    if (t.nw == 8 && (!t.mfma || t.xdirect || t.r != 1 || t.depth != 2)) return false;
     if (t.splitk < 1 || t.splitk > kMaxSplitK) return false;
     // Slices of gs groups; a request above the group count gives one group
     // per slice.
@@ -70,7 +73,7 @@ bool complete_tiling(Tiling& t, int M, int64_t N, int64_t K) {
             return true;
         }
         t.chunked = (int64_t)t.mt * width * 2 > kern::kSingleBytes;
-        if (t.chunked && !kern::chunk_ok(t.mt, kern::mfma_kc(t.mt, t.kw, t.depth))) return false;
+        if (t.chunked && !kern::chunk_ok(t.mt, kern::mfma_kc(t.mt, t.kw, t.depth), t.nw)) return false;
     } else {
         if (M < 1 || M > 8) return false;
         t.mt = M;
@@ -81,7 +84,7 @@ bool complete_tiling(Tiling& t, int M, int64_t N, int64_t K) {
             return true;
         }
         t.chunked = (int64_t)M * width * 2 > kern::kSingleBytes;
-        if (t.chunked && !kern::chunk_ok(M, kern::gemv_kc(M, t.kw, t.depth))) return false;
+        if (t.chunked && !kern::chunk_ok(M, kern::gemv_kc(M, t.kw, t.depth), t.nw)) return false;
     }
     return true;
 }
@@ -104,43 +107,55 @@ void bind_split(GemmArgs& a, const Tiling& t, void* ws) {
 }
 
 // Defaults measured on MI355X over the QKV (7168x5120), O (5120x5120),
-// gate+up (34816x5120) and down (5120x17408) shapes at M = 1-32.  M = 1 runs
-// the wavefront-reduction GEMV with x read directly (no x barrier), four
-// groups in flight per wave, and two K-waves per 16-row tile on weights of
-// 256-1024 tiles, four otherwise (QKV 10.9 us against 11.3 us with x staged
-// in LDS, O 9.3 against 10.2; gate+up 43.0 us with four K-waves against 46.3
-// with two; N = 896: 5.8 us against 7.4), and K is never split across
-// workgroups: no split factor 2-16 was faster on any weight measured (N =
-// 640-34816, K = 2176-17408; down 24.4 us unsplit against 25.2 in three).  From M = 2 each extra x row costs the GEMV four more dot2 per 8
-// weights, and the MFMA, whose cost does not grow until 16 rows, measured
-// faster on all shapes (QKV M = 4: 12.9 us against 14.6 us): up to M = 8 it
-// reads its A fragments straight from memory with two tiles per wave and
-// four K-waves (no x barrier).  So does M = 9-32 on weights of at most 1024
-// tiles and 64 groups per row (QKV M = 16: 13.4 us against 15.4 us with x
-// in LDS; M = 32: 18.7 against 19.2; O M = 16: 12.7 against 13.7).  On
-// larger weights x goes through LDS from M = 9, shared by the waves of a
-// workgroup, with two K-waves or, above 16 rows, one when the grid has
-// >= 1024 row blocks anyway (gate+up M = 32: 64 us against 69.5 us).
+// gate+up (34816x5120) and down (5120x17408) shapes and N = 1024-2048 at
+// K = 5120, M = 1-32.
 //
-// Splitting K across workgroups (the _ws entry points, MFMA only): slices of at
-// least 40 groups (5120 weights) keep each workgroup's prologue and
-// epilogue small against its stream, up to ~2048 workgroups -- three
-// slices on the down shape (M = 16-32: 31-38 us instead of 40-51 us).  The
-// LDS path from M = 9 also splits until it has ~480 workgroups, with slices
-// of at least 13 groups: its x chunks make few large workgroups slow (O,
-// 160 row blocks, three slices: M = 12-24 5-7% faster; QKV, 224 row
-// blocks, two slices at M = 24-32; three were 30% slower).
+// M = 1 runs the wavefront-reduction GEMV with x read directly (no x
+// barrier), four groups in flight per wave, and two K-waves per 16-row tile
+// on weights of 256-1024 tiles, four otherwise (QKV 10.9 us against 11.3 us
+// with x staged in LDS, O 9.3 against 10.2; gate+up 43.0 us with four
+// K-waves against 46.3 with two; N = 896: 5.8 us against 7.4), and K is
+// never split across workgroups: no split factor 2-16 was faster on any
+// weight measured (down 24.4 us unsplit against 25.2 in three).
+//
+// M = 2-8: each extra x row costs the GEMV four more dot2 per 8 weights,
+// while the MFMA's cost does not grow until 16 rows (QKV M = 4: 12.9 us
+// against 14.6 us).  It reads its A fragments straight from memory, two
+// tiles per wave, four K-waves (no x barrier); x staged in LDS was 2-7%
+// slower on QKV and gate+up.  So is M = 9-12 on weights of 385-1024 tiles
+// and at most 64 groups per row (QKV M = 9: 12.1 us against 12.8).
+//
+// Otherwise from M = 9 x is staged in LDS and shared by eight waves of a
+// 512-thread workgroup, with four K-waves (two tiles per workgroup) when K
+// is not split and M <= 16, two K-waves (four tiles) otherwise -- O M = 16:
+// 11.4 us against 12.7 us with x read directly; N = 1024-2048: 4-14%
+// faster; down M = 16 split in three: 27.4 us against 30.1 us with
+// 256-thread workgroups; gate+up M = 32: 58.2 against 60.6.  Above 16 rows
+// a weight of fewer than 128 row blocks that K does not split keeps four
+// K-waves, its 128 KB x double buffer included (down M = 24: 41.3 us
+// against 46.5 with 256 threads).
+//
+// Splitting K across workgroups (the _ws entry points, MFMA only): slices of
+// at least 40 groups (5120 weights) keep each workgroup's prologue and
+// epilogue small against its stream, up to ~2048 workgroups -- three slices
+// on the down shape.  Above 16 rows the LDS path also takes the fewest
+// slices that give it >= 1280 waves, with slices of at least 13 groups (QKV:
+// two slices, M = 32 16.9 us against 19.5 unsplit and 20.6 in three; O: two,
+// 15.3 us against 15.8 in three; N = 2048: three, 14.0 against 18.1
+// unsplit and 14.2 in two).
 Tiling choose_tiling(int M, int64_t N, int64_t K, bool allow_splitk) {
     Tiling t{};
     t.r = 1;
     t.splitk = 1;
+    t.nw = 4;
     const int64_t ntiles = (N + 15) / 16;
+    const int64_t G = K / 128;
     if (M == 1) {
         t.mfma = 0;
         t.kw = ntiles >= 256 && ntiles <= 1024 ? 2 : 4;
         t.depth = 4;
         t.xdirect = 1;
-    } else if (M <= 8 || (ntiles <= 1024 && K / 128 <= 64)) {
+    } else if (M <= 8 || (M <= 12 && ntiles > 384 && ntiles <= 1024 && G <= 64)) {
         t.mfma = 1;
         t.r = 2;
         t.kw = 4;
@@ -148,24 +163,25 @@ Tiling choose_tiling(int M, int64_t N, int64_t K, bool allow_splitk) {
         t.xdirect = 1;
     } else {
         t.mfma = 1;
-        t.kw = 2;
+        t.nw = 8;
         t.depth = 2;
-        if (M > 16 && row_blocks(t, N) >= 1024) t.kw = 1;
+        t.kw = 2;
     }
+    const int64_t nb = row_blocks(t, N);
     if (allow_splitk && t.mfma) {
-        const int64_t G = K / 128;
-        const int64_t nb = row_blocks(t, N);
         int64_t s = G / 40;
         const int64_t fill = (2048 + nb - 1) / nb;
         s = s < fill ? s : fill;
-        if (t.mfma && !t.xdirect) {
-            int64_t s2 = 480 / nb;
+        if (!t.xdirect && M > 16) {
+            const int64_t waves = nb * t.nw;
+            int64_t s2 = (1280 + waves - 1) / waves;
             s2 = s2 < G / 13 ? s2 : G / 13;
             s = s > s2 ? s : s2;
         }
         s = s < kMaxSplitK ? s : kMaxSplitK;
         t.splitk = s > 1 ? (int)s : 1;
     }
+    if (t.nw == 8 && t.splitk == 1 && (M <= 16 || nb < 128)) t.kw = 4;
     // Step down to a built combination (a chunked x buffer must fit LDS).
     while (!complete_tiling(t, M, N, K)) {
         if (t.depth > 2)
@@ -185,13 +201,14 @@ const char* tiling_name(const Tiling& t, bool is_w12) {
     n += t.mfma ? "mfma_mt" : "gemv_m";
     n += std::to_string(t.mt) + "_r" + std::to_string(t.r) + "_kw" + std::to_string(t.kw) + "_d" +
          std::to_string(t.depth) + (t.xdirect ? "_xdirect" : t.chunked ? "_chunked" : "_single");
+    if (t.nw == 8) n += "_w8";
     if (t.splitk > 1) n += "_s" + std::to_string(t.splitk);
     std::lock_guard<std::mutex> lock(mu);
     return names.insert(std::move(n)).first->c_str();
 }
 
 hipError_t launch_gemm(const GemmArgs& a, const Tiling& t, bool is_w12, hipStream_t s) {
-    if (t.mfma) return launch_mfma_mt(t.mt, a, t, is_w12, s);
+    if (t.mfma) return t.nw == 8 ? launch_mfma8_mt(t.mt, a, t, is_w12, s) : launch_mfma_mt(t.mt, a, t, is_w12, s);
     return launch_gemv_m(t.mt, a, t, is_w12, s);
 }
 

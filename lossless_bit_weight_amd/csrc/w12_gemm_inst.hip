@@ -24,8 +24,18 @@ hipError_t launch_mfma_mt(int MT, const GemmArgs& a, const Tiling& t, bool is_w1
         default: return hipErrorInvalidValue;
     }
 }
+#elif defined(W12_INST_MFMA8)
+hipError_t launch_mfma8_mt(int MT, const GemmArgs& a, const Tiling& t, bool is_w12, hipStream_t s) {
+    switch (MT) {
+        case 16: return is_w12 ? kern::dispatch8<kern::FetchW12, 16>(a, t, s)
+                               : kern::dispatch8<kern::FetchBF16, 16>(a, t, s);
+        case 32: return is_w12 ? kern::dispatch8<kern::FetchW12, 32>(a, t, s)
+                               : kern::dispatch8<kern::FetchBF16, 32>(a, t, s);
+        default: return hipErrorInvalidValue;
+    }
+}
 #else
-#error "define W12_INST_M or W12_INST_MFMA"
+#error "define W12_INST_M, W12_INST_MFMA or W12_INST_MFMA8"
 #endif
 
 }  // namespace w12

@@ -53,8 +53,6 @@
 namespace w12 {
 namespace kern {
 
-constexpr int kThreads = 256;
-
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
@@ -119,7 +117,7 @@ __device__ __forceinline__ void out_value(const GemmArgs& g, int m, int64_t n, f
 // workgroup that sees the count reach S - 1 therefore reads complete sums.
 // (A release/acquire fence here would write back and invalidate the whole
 // L2 of the XCD once per workgroup, which serialised the launch.)
-template <int kTilesPerWG>
+template <int kTilesPerWG, int NT>
 __device__ __forceinline__ void split_finish(const GemmArgs& g) {
     __shared__ int last;
     __builtin_amdgcn_s_waitcnt(0);   // this wave's partial-sum stores are complete
@@ -133,7 +131,7 @@ __device__ __forceinline__ void split_finish(const GemmArgs& g) {
     const int64_t np = (g.N + 15) / 16 * 16;
     const int64_t n0 = (int64_t)blockIdx.x * kRows;
     const int64_t slice = (int64_t)g.M * np;
-    for (int i = threadIdx.x; i < kRows * g.M; i += kThreads) {
+    for (int i = threadIdx.x; i < kRows * g.M; i += NT) {
         const int m = i / kRows;
         const int64_t n = n0 + i % kRows;
         if (n >= g.N) continue;
@@ -319,11 +317,11 @@ struct FetchBF16 {
 // x[0:MROWS][k0:k0+KC] -> LDS in 16-byte units (8 BF16); rows >= M and
 // columns >= K are zero.  Layout::phys(row, unit) is the LDS slot.
 
-template <int MROWS, int KC>
+template <int MROWS, int KC, int NT>
 struct XChunk {
     static constexpr int kUnitsPerRow = KC / 8;
     static constexpr int kUnits = MROWS * kUnitsPerRow;
-    static constexpr int kPerThread = (kUnits + kThreads - 1) / kThreads;
+    static constexpr int kPerThread = (kUnits + NT - 1) / NT;
     uint4 v[kPerThread];
 
     // Every lane issues every load (addresses clamped into x), and values
@@ -332,7 +330,7 @@ struct XChunk {
     __device__ __forceinline__ void load(const GemmArgs& g, int64_t k0) {
 #pragma unroll
         for (int j = 0; j < kPerThread; ++j) {
-            const int id = threadIdx.x + kThreads * j;
+            const int id = threadIdx.x + NT * j;
             const int m = id / kUnitsPerRow;
             const int64_t k = k0 + 8 * (id % kUnitsPerRow);
             const bool ok = id < kUnits && m < g.M && k < g.K;
@@ -346,7 +344,7 @@ struct XChunk {
     __device__ __forceinline__ void store(uint4* buf) const {
 #pragma unroll
         for (int j = 0; j < kPerThread; ++j) {
-            const int id = threadIdx.x + kThreads * j;
+            const int id = threadIdx.x + NT * j;
             if (id < kUnits) buf[Layout::phys(id / kUnitsPerRow, id % kUnitsPerRow)] = v[j];
         }
     }
@@ -355,15 +353,16 @@ struct XChunk {
 // Whole-x staging when all of x fits (at most kSingleBytes): loaded into
 // registers before the weight ring is primed, stored to LDS after it, so
 // waiting for x never waits for weights.  The registers die after the store.
-constexpr int kSingleBytes = 40 * 1024;
-constexpr int kSingleUnits = kSingleBytes / 16 / kThreads;  // per thread
+constexpr int kSingleBytes = 40 * 1024;   // a multiple of 16 * 512
 
+template <int NT>
 struct XAll {
+    static constexpr int kSingleUnits = kSingleBytes / 16 / NT;  // per thread
     uint4 v[kSingleUnits];
     int units, units_per_row;
 
     // Columns [k0, k0 + 8 * upr) of rows 0..mrows-1 (mrows * upr <=
-    // kSingleUnits * kThreads, checked on the host).
+    // kSingleUnits * NT, checked on the host).
     __device__ __forceinline__ void load(const GemmArgs& g, int mrows, int64_t k0, int upr) {
         units_per_row = upr;
         units = mrows * units_per_row;
@@ -372,8 +371,8 @@ struct XAll {
             // The guard is uniform over the workgroup (it depends on j and
             // the shape only), so the loads of a round are all issued or all
             // skipped and the count of later loads stays known.
-            if (kThreads * j < units) {
-                const int id = threadIdx.x + kThreads * j;
+            if (NT * j < units) {
+                const int id = threadIdx.x + NT * j;
                 const int m = id / units_per_row;
                 const int64_t k = k0 + 8 * (int64_t)(id % units_per_row);
                 const bool ok = id < units && m < g.M;
@@ -387,7 +386,7 @@ struct XAll {
     __device__ __forceinline__ void store(uint4* buf) const {
 #pragma unroll
         for (int j = 0; j < kSingleUnits; ++j) {
-            const int id = threadIdx.x + kThreads * j;
+            const int id = threadIdx.x + NT * j;
             if (id < units)
                 buf[Layout::phys(id / units_per_row, id % units_per_row, units_per_row)] = v[j];
         }
@@ -424,10 +423,11 @@ __host__ __device__ constexpr int mfma_kc(int MT, int KW, int D) {
     const int window = 128 * KW * D;
     return base < window ? window : base;
 }
-// A chunked variant is built only if its double buffer fits 64 KB of LDS
-// (x rows * KC <= 16384), which also caps the x registers at 8 x 16 bytes
-// per thread.
-__host__ __device__ constexpr bool chunk_ok(int rows, int kc) { return rows * kc <= 16384; }
+// A chunked variant is built only if each thread stages at most 8 x 16
+// bytes of a chunk (x rows * KC <= 64 * threads): a double buffer of 64 KB
+// of LDS for 256 threads, 128 KB for 512 (of the 160 KB a workgroup may
+// hold).
+__host__ __device__ constexpr bool chunk_ok(int rows, int kc, int nw) { return rows * kc <= 4096 * nw; }
 __host__ __device__ constexpr int kc_of(bool mfma, int rows, int KW, int D) {
     return mfma ? mfma_kc(rows, KW, D) : gemv_kc(rows, KW, D);
 }
@@ -495,22 +495,22 @@ __host__ __device__ constexpr int kc_of(bool mfma, int rows, int KW, int D) {
 
 // Bytes of LDS a launch needs (x buffers of one K slice of gs groups; the
 // reductions reuse them).
-template <bool MFMA, int MR, int R, int KW, int D, bool CHUNKED, bool XD>
+template <bool MFMA, int MR, int R, int KW, int D, bool CHUNKED, bool XD, int NW>
 __host__ __device__ size_t lds_bytes(int gs) {
     const size_t x = XD ? 0
                      : CHUNKED ? 2 * (size_t)MR * kc_of(MFMA, MR, KW, D) * 2
                                : (size_t)MR * gs * 128 * 2;
     const size_t red = KW == 1 ? 0
-                       : MFMA ? (size_t)(KW - 1) * (4 / KW) * 64 * R * (MR / 16) * 16
-                              : (size_t)(KW - 1) * (4 / KW) * 16 * R * MR * 4;
+                       : MFMA ? (size_t)(KW - 1) * (NW / KW) * 64 * R * (MR / 16) * 16
+                              : (size_t)(KW - 1) * (NW / KW) * 16 * R * MR * 4;
     const size_t m = x > red ? x : red;
     return (m + 15) / 16 * 16;
 }
 // With an exception list the owner waves also stage correction batches, in
 // an area after everything else (so it never meets x or the reductions).
-template <bool MFMA, int MR, int KW>
+template <bool MFMA, int MR, int KW, int NW>
 __host__ __device__ constexpr size_t exc_lds_bytes() {
-    return (size_t)(4 / KW) * ExcStage<MFMA ? 16 * (MR / 16) : MR>::kBytes;
+    return (size_t)(NW / KW) * ExcStage<MFMA ? 16 * (MR / 16) : MR>::kBytes;
 }
 
 // ---- the kernel ----------------------------------------------------------------------
@@ -525,11 +525,11 @@ __host__ __device__ constexpr size_t exc_lds_bytes() {
 // broadcast within the quad (DPP).  MFMA: each lane loads its own A
 // fragments (row 16 mt + col); rows past M repeat row M - 1 instead of being
 // zero -- they only feed output rows that are never stored.
-template <class F, bool MFMA, int MR, int R, int KW, int D, bool CHUNKED, bool XD>
-__global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
+template <class F, bool MFMA, int MR, int R, int KW, int D, bool CHUNKED, bool XD, int NW>
+__global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs g) {
     static_assert(!(XD && CHUNKED), "direct x is never chunked");
     constexpr int KC = kc_of(MFMA, MR, KW, D);
-    constexpr int kRowWaves = 4 / KW;
+    constexpr int kRowWaves = NW / KW;
     constexpr int kBuf = MR * KC / 8;                 // uint4 per x chunk buffer
     constexpr int L = KC / (128 * KW);                // wave groups per chunk (multiple of D)
     constexpr int kMT = MR / 16;                      // MFMA: 16-row tiles of x
@@ -545,7 +545,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
     const int64_t G = g.K / 128;
     const int64_t ntiles = (g.N + 15) / 16;
     // start of the exception staging area (after the x buffers / reductions)
-    const size_t exc_base = lds_bytes<MFMA, MR, R, KW, D, CHUNKED, XD>(g.gs);
+    const size_t exc_base = lds_bytes<MFMA, MR, R, KW, D, CHUNKED, XD, NW>(g.gs);
     const int64_t tile0 = ((int64_t)blockIdx.x * kRowWaves + nw) * R;  // tile r: tile0 + r
 
     int64_t tload[R];  // tiles past the end are clamped for loading
@@ -701,8 +701,8 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
     };
 
     // Prologue: x first, then the ring, so the barrier waits for x only.
-    XChunk<MR, KC> xr;
-    XAll xa;
+    XChunk<MR, KC, NW * 64> xr;
+    XAll<NW * 64> xa;
     if constexpr (CHUNKED)
         xr.load(g, kbase);
     else if constexpr (!XD)
@@ -841,19 +841,20 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
             }
         }
     }
-    if (gridDim.y > 1) split_finish<kRowWaves * R>(g);
+    if (gridDim.y > 1) split_finish<kRowWaves * R, NW * 64>(g);
 }
 
 // ---- launch helpers ----------------------------------------------------------------------
 
-template <class F, bool MFMA, int MR, int R, int KW, int D, bool CHUNKED, bool XD>
+template <class F, bool MFMA, int MR, int R, int KW, int D, bool CHUNKED, bool XD, int NW>
 hipError_t launch_one(const GemmArgs& a, hipStream_t s) {
-    constexpr int kTilesPerWG = (4 / KW) * R;
+    constexpr int kTilesPerWG = (NW / KW) * R;
     const int64_t ntiles = (a.N + 15) / 16;
     const dim3 grid((unsigned)((ntiles + kTilesPerWG - 1) / kTilesPerWG), (unsigned)a.S);
-    size_t lds = lds_bytes<MFMA, MR, R, KW, D, CHUNKED, XD>(a.gs);
-    if (F::kHasExceptions && a.exc_off != nullptr) lds += exc_lds_bytes<MFMA, MR, KW>();
-    hipLaunchKernelGGL((gemm_kernel<F, MFMA, MR, R, KW, D, CHUNKED, XD>), grid, dim3(kThreads), lds, s, a);
+    size_t lds = lds_bytes<MFMA, MR, R, KW, D, CHUNKED, XD, NW>(a.gs);
+    if (F::kHasExceptions && a.exc_off != nullptr) lds += exc_lds_bytes<MFMA, MR, KW, NW>();
+    hipLaunchKernelGGL((gemm_kernel<F, MFMA, MR, R, KW, D, CHUNKED, XD, NW>), grid, dim3(NW * 64), lds, s,
+                       a);
     return hipGetLastError();
 }
 
@@ -864,15 +865,16 @@ __host__ __device__ constexpr bool xd_ok(bool mfma, int mr, int r, int d) {
     return mfma ? d * 16 * (r + mr / 16) <= 192 : (mr <= 4 && d * (16 * r + 4 * mr) <= 192);
 }
 
-template <class F, bool MFMA, int MR, int R, int KW, int D>
+template <class F, bool MFMA, int MR, int R, int KW, int D, int NW = 4>
 hipError_t launch_ch(const GemmArgs& a, const Tiling& t, hipStream_t s) {
     if (t.xdirect) {
-        if constexpr (xd_ok(MFMA, MR, R, D)) return launch_one<F, MFMA, MR, R, KW, D, false, true>(a, s);
+        if constexpr (NW == 4 && xd_ok(MFMA, MR, R, D))
+            return launch_one<F, MFMA, MR, R, KW, D, false, true, NW>(a, s);
         return hipErrorInvalidValue;
     }
-    if (!t.chunked) return launch_one<F, MFMA, MR, R, KW, D, false, false>(a, s);
-    if constexpr (chunk_ok(MR, kc_of(MFMA, MR, KW, D)))
-        return launch_one<F, MFMA, MR, R, KW, D, true, false>(a, s);
+    if (!t.chunked) return launch_one<F, MFMA, MR, R, KW, D, false, false, NW>(a, s);
+    if constexpr (chunk_ok(MR, kc_of(MFMA, MR, KW, D), NW))
+        return launch_one<F, MFMA, MR, R, KW, D, true, false, NW>(a, s);
     return hipErrorInvalidValue;
 }
 
@@ -882,6 +884,21 @@ hipError_t launch_kw(const GemmArgs& a, const Tiling& t, hipStream_t s) {
         case 1: return launch_ch<F, MFMA, MR, R, 1, D>(a, t, s);
         case 2: return launch_ch<F, MFMA, MR, R, 2, D>(a, t, s);
         case 4: return launch_ch<F, MFMA, MR, R, 4, D>(a, t, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+// Eight-wave workgroups (512 threads): the MFMA kernels with x staged in LDS,
+// one tile per wave, ring depth 2 -- eight waves share each x chunk, which
+// halves the x traffic of the two-K-wave tiling on long-K weights.
+template <class F, int MR>
+hipError_t dispatch8(const GemmArgs& a, const Tiling& t, hipStream_t s) {
+    if (t.r != 1 || t.depth != 2 || t.xdirect) return hipErrorInvalidValue;
+    switch (t.kw) {
+        case 1: return launch_ch<F, true, MR, 1, 1, 2, 8>(a, t, s);
+        case 2: return launch_ch<F, true, MR, 1, 2, 2, 8>(a, t, s);
+        case 4: return launch_ch<F, true, MR, 1, 4, 2, 8>(a, t, s);
+        case 8: return launch_ch<F, true, MR, 1, 8, 2, 8>(a, t, s);
         default: return hipErrorInvalidValue;
     }
 }

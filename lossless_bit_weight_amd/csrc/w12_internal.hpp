@@ -40,7 +40,8 @@ struct GemmArgs {
 //   mfma    = 0: GEMV (v_dot2c_f32_bf16); 1: MFMA 16x16x32 bf16.
 //   r       = 16-row weight tiles per wave (1 or 2).
 //   mt      = GEMV: M (1..8); MFMA: x rows padded to 16 or 32.
-//   kw      = waves of a workgroup that split K between them (1, 2 or 4).
+//   kw      = waves of a workgroup that split K between them (1, 2, 4; 8
+//             with nw = 8).
 //   depth   = 32-weight slices each lane keeps in flight (2, 4 or 8).
 //   xdirect = 1: x is read by each lane with its weights instead of being
 //             staged in LDS (GEMV up to M = 4, MFMA; within a register
@@ -50,6 +51,8 @@ struct GemmArgs {
 //   chunked = 0 if the x columns of a K slice are staged in LDS at once, 1 if
 //             they are streamed through LDS in double-buffered chunks (set
 //             from the shape).
+//   nw      = waves per workgroup: 4 (256 threads) or 8 (512 threads; MFMA
+//             with x in LDS, r = 1, depth = 2 only).
 struct Tiling {
     int mfma;
     int mt;
@@ -60,6 +63,7 @@ struct Tiling {
     int splitk;
     int gs;
     int chunked;
+    int nw;
 };
 
 constexpr int kMaxSplitK = 64;
@@ -90,6 +94,7 @@ hipError_t launch_gemm(const GemmArgs& a, const Tiling& t, bool is_w12, hipStrea
 // Per-M (GEMV) and per-MT (MFMA) launchers, one object file each.
 hipError_t launch_gemv_m(int M, const GemmArgs& a, const Tiling& t, bool is_w12, hipStream_t s);
 hipError_t launch_mfma_mt(int MT, const GemmArgs& a, const Tiling& t, bool is_w12, hipStream_t s);
+hipError_t launch_mfma8_mt(int MT, const GemmArgs& a, const Tiling& t, bool is_w12, hipStream_t s);
 hipError_t launch_pack(const uint16_t* w, int64_t N, int64_t K, void* p0, void* p1,
                        void* p2, uint8_t* meta, uint32_t* bad, hipStream_t s);
 hipError_t launch_unpack(const void* p0, const void* p1, const void* p2,

@@ -46,26 +46,30 @@ class W12UnencodableError(ValueError):
 
 class Tiling(ctypes.Structure):
     """w12_tiling_t: kind (0 GEMV, 1 MFMA), r, kw, depth, x_direct, splitk
-    (0 or 1 = K not split across workgroups)."""
+    (0 or 1 = K not split across workgroups), waves (0 or 4 = 256-thread
+    workgroups, 8 = 512 threads)."""
     _fields_ = [("kind", ctypes.c_int32), ("r", ctypes.c_int32), ("kw", ctypes.c_int32),
                 ("depth", ctypes.c_int32), ("x_direct", ctypes.c_int32),
-                ("splitk", ctypes.c_int32)]
+                ("splitk", ctypes.c_int32), ("waves", ctypes.c_int32)]
 
     def astuple(self):
-        return (self.kind, self.r, self.kw, self.depth, self.x_direct, self.splitk)
+        return (self.kind, self.r, self.kw, self.depth, self.x_direct, self.splitk, self.waves)
 
     def __repr__(self):
-        return "Tiling(kind=%d, r=%d, kw=%d, depth=%d, x_direct=%d, splitk=%d)" % self.astuple()
+        return ("Tiling(kind=%d, r=%d, kw=%d, depth=%d, x_direct=%d, splitk=%d, waves=%d)"
+                % self.astuple())
 
 
 # Every tiling the library instantiates: (kind, r, kw, depth, x_direct); any
-# of them may add a sixth entry, the split-K factor (1..64).  x_direct needs a
+# of them may add a sixth entry, the split-K factor (1..64).  The 512-thread
+# MFMA tilings (x in LDS, r = 1, depth 2) also carry the wave count 8.  x_direct needs a
 # ring of at most 192 registers: depth * (16 * r + 4 * M) for the GEMV
 # (M <= 4), depth * 16 * (r + A tiles) for the MFMA (1 tile up to M = 16, 2
 # above); see x_direct_fits.
 _PAIRS = ((1, 2), (1, 4), (1, 8), (2, 2), (2, 4))
 GEMV_TILINGS = [(0, r, kw, d, xd) for (r, d) in _PAIRS for kw in (1, 2, 4) for xd in (0, 1)]
 MFMA_TILINGS = [(1, r, kw, d, xd) for (r, d) in _PAIRS for kw in (1, 2, 4) for xd in (0, 1)]
+MFMA8_TILINGS = [(1, 1, kw, 2, 0, 1, 8) for kw in (1, 2, 4, 8)]
 
 
 def x_direct_fits(M: int, r: int, depth: int, kind: int = 0) -> bool:
@@ -428,7 +432,8 @@ def w12_gemm(x: torch.Tensor, wt: W12Weight, out_dtype: torch.dtype = torch.floa
     """y[m, n] = sum_k x[m, k] W[n, k] with W rebuilt from the container.
     Default: w12_gemm_ws (K may be split over workgroups, using `workspace`
     or the binding's own); split_k=False: w12_gemm.  `tiling` (a Tiling or a
-    (kind, r, kw, depth, x_direct[, splitk]) tuple) selects w12_gemm_ex."""
+    (kind, r, kw, depth, x_direct[, splitk[, waves]]) tuple) selects
+    w12_gemm_ex."""
     M, ldx = _x_args(x)
     if y is None:
         y, _ = _out_tensor(M, wt.N, out_dtype, x.device)

@@ -21,7 +21,7 @@ def test_loads_and_exports_every_declared_symbol():
                           "w12_exceptions", "w12_exceptions_workspace_bytes"}
     for n in names:
         assert hasattr(L, n), n
-    assert w12.w12_abi_version() == 4
+    assert w12.w12_abi_version() == 5
 
 
 def test_sizes():
@@ -212,10 +212,56 @@ def test_default_tiling():
         assert t.kind == 0 and t.astuple()[:5] in w12.GEMV_TILINGS and t.splitk >= 1
         t = w12.w12_default_tiling(16, 34816, 5120, split)
         assert t.kind == 1 and t.astuple()[:5] in w12.MFMA_TILINGS and t.splitk >= 1
+        assert t.waves in (4, 8)
         if not split:
             assert t.splitk == 1
     with pytest.raises(w12.W12Error):
         w12.w12_default_tiling(40, 64, 512)
+
+
+def test_default_waves_rule():
+    """M = 2-8, and M = 9-12 on weights of 385-1024 tiles and <= 64 groups per
+    row, read x directly in 256-thread workgroups; otherwise from M = 9 x is
+    staged in LDS for 512-thread workgroups: four K-waves when K is not split
+    and M <= 16 (or the weight has < 128 row blocks), else two."""
+    for M in (1, 4, 8):
+        assert w12.w12_default_tiling(M, 5120, 17408).waves == 4
+    for M in (9, 16, 24, 32):
+        t = w12.w12_default_tiling(M, 5120, 17408)
+        assert (t.waves, t.kw, t.x_direct, t.splitk) == (8, 2, 0, 3)
+        t = w12.w12_default_tiling(M, 34816, 5120)
+        assert (t.waves, t.kw, t.x_direct, t.splitk) == (8, 4 if M <= 16 else 2, 0, 1)
+    for M in (9, 12):
+        t = w12.w12_default_tiling(M, 7168, 5120)
+        assert (t.waves, t.x_direct) == (4, 1)
+        t = w12.w12_default_tiling(M, 5120, 5120)
+        assert (t.waves, t.kw, t.x_direct, t.splitk) == (8, 4, 0, 1)
+    t = w12.w12_default_tiling(16, 7168, 5120)
+    assert (t.waves, t.kw, t.x_direct, t.splitk) == (8, 4, 0, 1)
+    for M in (24, 32):
+        for N in (7168, 5120):
+            t = w12.w12_default_tiling(M, N, 5120)
+            assert (t.waves, t.kw, t.splitk) == (8, 2, 2)
+        t = w12.w12_default_tiling(M, 2048, 5120)
+        assert (t.waves, t.kw, t.splitk) == (8, 2, 3)
+        t = w12.w12_default_tiling(M, 7168, 5120, False)
+        assert (t.waves, t.kw, t.x_direct, t.splitk) == (8, 4, 0, 1)
+        t = w12.w12_default_tiling(M, 5120, 17408, False)
+        assert (t.waves, t.kw, t.splitk) == (8, 4, 1)
+
+
+def test_tiling_waves_rejects():
+    """512-thread workgroups are built only for the MFMA with x in LDS, r = 1,
+    depth 2 and kw <= 8; 4 and 0 (= 4) are the other wave counts."""
+    L = w12.lib()
+    nbytes = ctypes.c_size_t()
+    ok = (1, 1, 2, 2, 0, 1, 8)
+    assert L.w12_gemm_workspace_bytes(16, 5120, 5120, w12._tiling_arg(ok), ctypes.byref(nbytes)) == 0
+    for bad in ((0, 1, 2, 2, 0, 1, 8), (1, 2, 2, 2, 0, 1, 8), (1, 1, 2, 4, 0, 1, 8),
+                (1, 1, 2, 2, 1, 1, 8), (1, 1, 8, 2, 0, 1, 4), (1, 1, 2, 2, 0, 1, 6),
+                (1, 1, 16, 2, 0, 1, 8)):
+        rc = L.w12_gemm_workspace_bytes(16, 5120, 5120, w12._tiling_arg(bad), ctypes.byref(nbytes))
+        assert rc == -6, bad
 
 
 def test_read_probe_rejects():

@@ -96,7 +96,8 @@ def test_capacity_short_and_count_only(oracle):
 
 GEMM_SHAPES = [(1000, 640), (45, 5120), (77, 17408), (130, 1152)]
 TILINGS = [None, "plain", (0, 1, 4, 2, 0), (0, 2, 1, 2, 1), (1, 2, 4, 2, 1), (1, 1, 2, 2, 0),
-           (1, 1, 1, 2, 0, 3), (0, 1, 4, 4, 0, 5), (1, 2, 4, 2, 1, 2)]
+           (1, 1, 1, 2, 0, 3), (0, 1, 4, 4, 0, 5), (1, 2, 4, 2, 1, 2),
+           (1, 1, 1, 2, 0, 1, 8), (1, 1, 2, 2, 0, 3, 8), (1, 1, 8, 2, 0, 64, 8)]
 
 
 def _gemm(x, wt, tiling):
@@ -137,7 +138,8 @@ def test_gemm_on_raw_weights(oracle, shape, tiling):
 
 
 @pytest.mark.parametrize("tiling", [None, "plain", (0, 1, 4, 2, 0), (1, 2, 4, 2, 1),
-                                    (1, 1, 2, 2, 0), (1, 1, 1, 2, 0, 3)], ids=lambda t: str(t))
+                                    (1, 1, 2, 2, 0), (1, 1, 1, 2, 0, 3), (1, 1, 1, 2, 0, 1, 8),
+                                    (1, 1, 4, 2, 0, 2, 8)], ids=lambda t: str(t))
 def test_one_hot_rows_give_original_words(oracle, tiling):
     """x rows = unit vectors at columns that hold exceptions: y[m, n] is the
     original weight w[n, k_m] exactly (the clamp is taken back exactly and the

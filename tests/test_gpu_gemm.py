@@ -182,8 +182,12 @@ def test_ieee_specials(oracle):
         assert np.array_equal(yh[fin], ref[fin])
 
 
-@pytest.mark.parametrize("tiling", w12.GEMV_TILINGS + w12.MFMA_TILINGS,
-                         ids=lambda t: "k%d_r%d_kw%d_d%d_x%d" % t)
+def _tiling_id(t):
+    return "k%d_r%d_kw%d_d%d_x%d" % t[:5] + ("_w%d" % t[6] if len(t) > 6 else "")
+
+
+@pytest.mark.parametrize("tiling", w12.GEMV_TILINGS + w12.MFMA_TILINGS + w12.MFMA8_TILINGS,
+                         ids=_tiling_id)
 def test_every_tiling(oracle, tiling):
     """Every instantiated variant, single-chunk and chunked x, ragged rows and
     a K tail, against the oracle; W12 and BF16 bitwise equal per tiling."""
@@ -215,17 +219,20 @@ def test_every_tiling(oracle, tiling):
             assert_gemm_close(y12h, oracle.gemm_bf16_f64(x, w_ref), oracle.tolerance(x, w_ref), what)
 
 
+# (kind, r, kw, depth, x_direct[, waves])
 SPLIT_BASES = [(0, 1, 4, 2, 0), (0, 2, 1, 2, 0), (0, 1, 2, 4, 1),
-               (1, 1, 1, 2, 0), (1, 2, 4, 2, 0), (1, 1, 2, 4, 0), (1, 1, 2, 2, 1), (1, 2, 1, 2, 1)]
+               (1, 1, 1, 2, 0), (1, 2, 4, 2, 0), (1, 1, 2, 4, 0), (1, 1, 2, 2, 1), (1, 2, 1, 2, 1),
+               (1, 1, 2, 2, 0, 8), (1, 1, 8, 2, 0, 8)]
 
 
-@pytest.mark.parametrize("base", SPLIT_BASES, ids=lambda t: "k%d_r%d_kw%d_d%d_x%d" % t)
+@pytest.mark.parametrize("base", SPLIT_BASES,
+                         ids=lambda t: "k%d_r%d_kw%d_d%d_x%d" % t[:5] + ("_w%d" % t[5] if len(t) > 5 else ""))
 @pytest.mark.parametrize("splitk", [2, 3, 7, 64])
 def test_split_k(oracle, base, splitk):
     """K split over workgroups: ragged slices (G not a multiple of the
     factor), one group per slice (64 > G), chunked x inside a slice (K =
     17408 at 32 rows); W12 and BF16 bitwise equal, oracle tolerance."""
-    tiling = base + (splitk,)
+    tiling = base[:5] + (splitk,) + base[5:]
     Ms = ([1, 2, 4] if base[4] else [1, 3, 8]) if base[0] == 0 else [9, 16, 17, 32]
     for shape in ((301, 640), (33, 2688), (45, 5120), (77, 17408)):
         P = prepared(shape)
