@@ -276,7 +276,48 @@ def summarize_trace(path, variant, command):
         lines += ["", "Average duration of `%s` (%s): %.3f us over %s calls (graph-replayed "
                   "launches plus warm-up launches)." % (variant, want, float(hit[0]["AverageNs"]) / 1e3,
                                                         hit[0]["Calls"])]
+    st = dispatch_stats(path, want)
+    if st:
+        lines += ["", "Per-dispatch durations of that kernel (the kernel-trace file beside the "
+                  "stats, first %d dispatches dropped as warm-up): n = %d, mean %.3f us (95%% "
+                  "bootstrap CI %.3f-%.3f us, %d resamples), median %.3f us (CI %.3f-%.3f us), "
+                  "p10 %.3f us, p90 %.3f us."
+                  % (st["skipped"], st["n"], st["mean"] / 1e3,
+                     st["mean_ci"][0] / 1e3, st["mean_ci"][1] / 1e3, st["resamples"],
+                     st["median"] / 1e3, st["median_ci"][0] / 1e3, st["median_ci"][1] / 1e3,
+                     st["p10"] / 1e3, st["p90"] / 1e3)]
     print("\n".join(lines))
+
+
+def dispatch_stats(stats_path, want, skip=20, resamples=2000):
+    """Mean, median, p10/p90 and 95% bootstrap confidence intervals of the
+    mean and the median of one kernel's per-dispatch durations, from the
+    rocprofv3 kernel-trace CSV written beside the --stats table (None if
+    there is none)."""
+    import numpy as np
+    d = os.path.dirname(os.path.abspath(stats_path))
+    names = sorted(f for f in os.listdir(d) if f.endswith("kernel_trace.csv"))
+    if not names:
+        return None
+    rows = _read_csv(os.path.join(d, names[0]))
+    if not rows or "Start_Timestamp" not in rows[0] or "Kernel_Name" not in rows[0]:
+        return None
+    durs = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+            for r in rows if want in r["Kernel_Name"]][skip:]
+    if len(durs) < 50:
+        return None
+    a = np.asarray(durs, dtype=np.float64)
+    rng = np.random.default_rng(0)
+    means, meds = [], []
+    for _ in range(resamples // 200):
+        r = rng.choice(a, size=(200, a.size))
+        means.append(r.mean(axis=1))
+        meds.append(np.median(r, axis=1))
+    ci = lambda v: tuple(float(c) for c in np.percentile(np.concatenate(v), [2.5, 97.5]))
+    return {"n": int(a.size), "skipped": skip, "median": float(np.median(a)),
+            "p10": float(np.percentile(a, 10)), "p90": float(np.percentile(a, 90)),
+            "mean": float(a.mean()), "mean_ci": ci(means), "median_ci": ci(meds),
+            "resamples": resamples}
 
 
 def summarize_pmc(fetch_path, write_path, variant, command):
@@ -471,9 +512,22 @@ def measure_exceptions(torch, w12, case, ms, steps, warmup):
     return out
 
 
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(case, M, seconds):
     """The CPU oracle as it stands: container decode + fp64 GEMM over the whole
-    headline weight on all host threads, repeated until ~`seconds` passed."""
+    headline weight on all host threads, repeated until ~`seconds` passed;
+    beside it the same on one thread (~seconds / 4) and one oracle pack of
+    the weight."""
     import oracle
     nthreads = len(os.sched_getaffinity(0))
     raw = case.weights_raw()
@@ -481,22 +535,68 @@ def cpu_baseline(case, M, seconds):
     # Oracle-side projection and container (no input from the HIP path).
     p0, p1, p2, meta, _ = oracle.pack(raw)
     w = oracle.unpack(p0, p1, p2, meta, case.N, case.K)
-    q = oracle.pack(w)
-    del raw, w
-    reps = 0
     t0 = time.perf_counter()
-    while True:
-        oracle.gemm_w12_f64(x, *q[:4], case.N, nthreads=nthreads)
-        reps += 1
-        dt = time.perf_counter() - t0
-        if dt >= seconds or reps >= 10000:
-            break
-    wbytes = reps * (3 * oracle.plane_bytes(case.N, case.K) + oracle.meta_bytes(case.N, case.K))
+    q = oracle.pack(w)
+    pack_s = time.perf_counter() - t0
+    del raw, w
+    wb = 3 * oracle.plane_bytes(case.N, case.K) + oracle.meta_bytes(case.N, case.K)
+
+    def run(threads, budget):
+        reps = 0
+        t0 = time.perf_counter()
+        while True:
+            oracle.gemm_w12_f64(x, *q[:4], case.N, nthreads=threads)
+            reps += 1
+            dt = time.perf_counter() - t0
+            if dt >= budget or reps >= 10000:
+                return reps, dt
+
+    reps, dt = run(nthreads, seconds)
+    reps1, dt1 = run(1, seconds / 4)
     return {
-        "value": wbytes / dt / 1e9, "unit": "GB/s", "cores": nthreads, "kind": "oracle",
+        "value": reps * wb / dt / 1e9, "unit": "GB/s", "cores": nthreads, "kind": "oracle",
         "sample": "%d full passes over %s, M=%d (decode + fp64 GEMM), %.1f s"
                   % (reps, case.name, M, dt),
+        "cpu_model": _cpu_model(), "nproc": os.cpu_count(),
+        "single_thread": {"value": reps1 * wb / dt1 / 1e9, "unit": "GB/s",
+                          "sample": "%d passes, %.1f s" % (reps1, dt1)},
+        "pack": {"seconds": pack_s, "bf16_gbps": 2 * case.N * case.K / pack_s / 1e9,
+                 "sample": "one oracle pack of %s" % case.name},
     }
+
+
+# hipDeviceAttribute_t values (ROCm 7 headers) of the memory clock (kHz) and
+# the memory bus width (bits).
+_HIP_ATTR_MEM_CLOCK_KHZ = 60
+_HIP_ATTR_MEM_BUS_BITS = 59
+
+
+def device_memory_peak():
+    """Peak HBM bandwidth recomputed from the device's reported memory clock
+    and bus width, beside the published 8 TB/s.  MI355X reports a 2 GHz
+    clock on 8192 bits; its HBM3E moves 8 Gb/s per pin, four transfers per
+    reported clock."""
+    import ctypes
+    # The HIP runtime torch has loaded (opening it by path again returns the
+    # same handle; a second runtime in the process is never loaded).
+    path = None
+    with open("/proc/self/maps") as f:
+        for line in f:
+            if "libamdhip64" in line:
+                path = line.split()[-1]
+                break
+    if path is None:
+        return None
+    hip = ctypes.CDLL(path)
+    clk, bus = ctypes.c_int(0), ctypes.c_int(0)
+    if (hip.hipDeviceGetAttribute(ctypes.byref(clk), _HIP_ATTR_MEM_CLOCK_KHZ, 0) != 0
+            or hip.hipDeviceGetAttribute(ctypes.byref(bus), _HIP_ATTR_MEM_BUS_BITS, 0) != 0):
+        return None
+    per_clock = clk.value * 1e3 * bus.value / 8 / 1e9
+    return {"memory_clock_khz": clk.value, "bus_width_bits": bus.value,
+            "gbps_one_transfer_per_clock": per_clock,
+            "gbps_four_transfers_per_clock": 4 * per_clock,
+            "published_gbps": HBM_PEAK_GBPS}
 
 
 def main():
@@ -609,6 +709,8 @@ def main():
                    "N": head_case.N, "K": head_case.K, "M": head_m, "group": 128,
                    "rotation_copies": rotation},
         "pct_hbm_peak": round(100.0 * head["w12_weight_gbps"] / HBM_PEAK_GBPS, 2),
+        "device": {"name": props.name, "cus": props.multi_processor_count,
+                   "memory": device_memory_peak()},
         "read_ceiling": {"w12_bytes": ceilings[args.workload][0]["bytes"],
                          "w12_bytes_gbps": round(ceilings[args.workload][0]["gbps"], 1),
                          "bf16_bytes": ceilings[args.workload][1]["bytes"],
