@@ -67,6 +67,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU-oracle work to time")
     ap.add_argument("--sweep-ms", type=str, default="1,2,4,8,16,32")
+    ap.add_argument("--shard-ms", type=str, default="1,4,16,32",
+                    help="x rows for the 8-way tensor-parallel shard shapes ('' to skip)")
     ap.add_argument("--workload", default="qkv", choices=["qkv", "o", "gate_up", "down"],
                     help="headline weight (default: the QKV projection)")
     ap.add_argument("--m", type=int, default=1, help="headline x rows (default 1)")
@@ -667,6 +669,22 @@ def main():
                 del wlc
                 torch.cuda.empty_cache()
 
+    shards = []
+    if not args.no_sweep:
+        for name, case in inputs.SHARD_CASES.items():
+            ms = [int(m) for m in args.shard_ms.split(",") if m]
+            if not ms:
+                break
+            wlc = Workload(case, torch, w12)
+            for M in ms:
+                r = measure(torch, w12, wlc, M, args.steps, args.warmup, torch.float32)
+                shards.append(r)
+                print("shard: %s M=%d w12 %.2f us (%.0f GB/s) bf16 %.2f us speedup %.3f"
+                      % (name, M, r["w12_us"], r["w12_weight_gbps"], r["bf16_us"],
+                         r["speedup_vs_bf16"]), file=sys.stderr, flush=True)
+            del wlc
+            torch.cuda.empty_cache()
+
     codec = time_codec(torch, w12, wl, args.steps)
     print("codec: %s" % json.dumps(codec), file=sys.stderr, flush=True)
 
@@ -730,6 +748,8 @@ def main():
         "cpu_baseline": cpu,
         "sweep": [{k: (round(v, 3) if isinstance(v, float) else v) for k, v in r.items()}
                   for r in sweep],
+        "tp8_shards": [{k: (round(v, 3) if isinstance(v, float) else v) for k, v in r.items()}
+                       for r in shards],
         "codec": codec,
         "exceptions": exc,
         "stack": stack,

@@ -155,9 +155,9 @@ Tiling choose_tiling(int M, int64_t N, int64_t K, bool allow_splitk) {
         t.kw = ntiles >= 256 && ntiles <= 1024 ? 2 : 4;
         t.depth = 4;
         t.xdirect = 1;
-    } else if (M <= 8 || (M <= 12 && ntiles > 384 && ntiles <= 1024 && G <= 64)) {
+    } else if (M <= 8 || ntiles <= 256 || (M <= 12 && ntiles > 384 && ntiles <= 1024 && G <= 64)) {
         t.mfma = 1;
-        t.r = 2;
+        t.r = ntiles <= 256 || (ntiles > 512 && M <= 6) ? 1 : 2;
         t.kw = 4;
         t.depth = 2;
         t.xdirect = 1;
@@ -176,6 +176,11 @@ Tiling choose_tiling(int M, int64_t N, int64_t K, bool allow_splitk) {
             const int64_t waves = nb * t.nw;
             int64_t s2 = (1280 + waves - 1) / waves;
             s2 = s2 < G / 13 ? s2 : G / 13;
+            s = s > s2 ? s : s2;
+        }
+        if (t.xdirect && t.r == 1 && M > 8) {
+            int64_t s2 = 256 / ntiles;
+            s2 = s2 < G / 10 ? s2 : G / 10;
             s = s > s2 ? s : s2;
         }
         s = s < kMaxSplitK ? s : kMaxSplitK;

@@ -99,6 +99,14 @@ O_PROJ = GemmCase("o 5120x5120", 5120, 5120, 1, 0.02, 1.0, 501, 502, 503)
 
 CASES = {c.name.split()[0]: c for c in (TINY, QKV, GATE_UP, DOWN, O_PROJ)}
 
+# One GPU's share of the same four weights under 8-way tensor parallelism:
+# QKV and gate+up split along N (their output rows), O and down along K.
+SHARD_CASES = {c.name.split()[0]: c for c in (
+    GemmCase("qkv_tp8 896x5120", 896, 5120, 1, 0.02, 1.0, 601, 602, 603),
+    GemmCase("o_tp8 5120x640", 5120, 640, 1, 0.02, 1.0, 611, 612, 613),
+    GemmCase("gate_up_tp8 4352x5120", 4352, 5120, 1, 0.02, 1.0, 621, 622, 623),
+    GemmCase("down_tp8 5120x2176", 5120, 2176, 1, 0.015, 0.5, 631, 632, 633))}
+
 # 64-layer stack: per layer QKV, O, gate+up, down (N, K).
 STACK_LAYERS = 64
 STACK_SHAPES = ((7168, 5120), (5120, 5120), (34816, 5120), (5120, 17408))

@@ -220,10 +220,12 @@ def test_default_tiling():
 
 
 def test_default_waves_rule():
-    """M = 2-8, and M = 9-12 on weights of 385-1024 tiles and <= 64 groups per
-    row, read x directly in 256-thread workgroups; otherwise from M = 9 x is
-    staged in LDS for 512-thread workgroups: four K-waves when K is not split
-    and M <= 16 (or the weight has < 128 row blocks), else two."""
+    """M = 2-8, any M on weights of <= 256 tiles, and M = 9-12 on weights of
+    385-1024 tiles and <= 64 groups per row, read x directly in 256-thread
+    workgroups (one tile per wave on <= 256 tiles, two above); otherwise from
+    M = 9 x is staged in LDS for 512-thread workgroups: four K-waves when K
+    is not split and M <= 16 (or the weight has < 128 row blocks), else
+    two."""
     for M in (1, 4, 8):
         assert w12.w12_default_tiling(M, 5120, 17408).waves == 4
     for M in (9, 16, 24, 32):
@@ -243,11 +245,35 @@ def test_default_waves_rule():
             t = w12.w12_default_tiling(M, N, 5120)
             assert (t.waves, t.kw, t.splitk) == (8, 2, 2)
         t = w12.w12_default_tiling(M, 2048, 5120)
-        assert (t.waves, t.kw, t.splitk) == (8, 2, 3)
+        assert (t.waves, t.r, t.kw, t.x_direct, t.splitk) == (4, 1, 4, 1, 2)
         t = w12.w12_default_tiling(M, 7168, 5120, False)
         assert (t.waves, t.kw, t.x_direct, t.splitk) == (8, 4, 0, 1)
         t = w12.w12_default_tiling(M, 5120, 17408, False)
         assert (t.waves, t.kw, t.splitk) == (8, 4, 1)
+
+
+def test_default_small_weights():
+    """Weights of <= 256 tiles: x direct, one tile per wave, four K-waves;
+    from M = 9 K is split into up to 256 / tiles slices of >= 10 groups.
+    Up to M = 6 weights of more than 512 tiles also take one tile per wave."""
+    for M in (2, 4, 8):
+        t = w12.w12_default_tiling(M, 896, 5120)
+        assert (t.kind, t.r, t.kw, t.x_direct, t.waves, t.splitk) == (1, 1, 4, 1, 4, 1)
+    for M in (9, 16, 32):
+        assert w12.w12_default_tiling(M, 896, 5120).splitk == 4
+        assert w12.w12_default_tiling(M, 896, 5120, False).splitk == 1
+        assert w12.w12_default_tiling(M, 1536, 5120).splitk == 2
+        assert w12.w12_default_tiling(M, 4096, 5120).splitk == 1
+        assert w12.w12_default_tiling(M, 896, 2176).splitk == 1    # 17 groups
+        assert w12.w12_default_tiling(M, 1024, 17408).splitk == 4
+    # 257-512 tiles: two tiles per wave (at most 256 workgroups); above 512
+    # tiles one again up to M = 6
+    assert w12.w12_default_tiling(4, 4112, 5120).r == 2
+    assert w12.w12_default_tiling(4, 4096, 5120).r == 1
+    assert w12.w12_default_tiling(4, 8192, 5120).r == 2
+    assert w12.w12_default_tiling(4, 8208, 5120).r == 1
+    assert w12.w12_default_tiling(6, 34816, 5120).r == 1
+    assert w12.w12_default_tiling(7, 34816, 5120).r == 2
 
 
 def test_tiling_waves_rejects():

@@ -114,6 +114,18 @@ def test_workloads_sampled(oracle, name, M):
     _check(oracle, P, x, _sample_rows(P.N, seed=M), "%s M=%d" % (name, M))
 
 
+@pytest.mark.parametrize("shape", [(896, 5120), (1536, 5120), (1024, 17408), (896, 2176),
+                                   (4352, 5120), (5120, 640)])
+@pytest.mark.parametrize("M", [2, 9, 16, 32])
+def test_shard_shapes_default(oracle, shape, M):
+    """One GPU's share of the QKV, gate+up, O and down weights under 8-way
+    tensor parallelism and nearby small weights, with the default tilings
+    (one tile per wave and K split across workgroups on <= 256 tiles)."""
+    P = prepared(shape)
+    x = inputs.gaussian_bf16((M, shape[1]), 1.0, 13 * M + shape[0])
+    _check(oracle, P, x, _sample_rows(P.N, seed=M), "shard %s M=%d" % (shape, M))
+
+
 @pytest.mark.parametrize("M", [1, 5, 8, 16, 32])
 def test_bf16_output_is_rounded_fp32(M):
     P = prepared("tiny")
