@@ -77,6 +77,26 @@ def _load():
     lib.w12o_apply_exceptions.argtypes = [p, i64, i64, p, p]
     lib.w12o_apply_exceptions.restype = i32
     lib.w12o_gemm_w12_f64.restype = i32
+    lib.w12o_b_base_for_emax.argtypes = [i32]
+    lib.w12o_b_base_for_emax.restype = i32
+    lib.w12o_b_encodable.argtypes = [ctypes.c_uint16, i32]
+    lib.w12o_b_encodable.restype = i32
+    lib.w12o_b_encode.argtypes = [ctypes.c_uint16, i32, ctypes.POINTER(ctypes.c_int)]
+    lib.w12o_b_encode.restype = ctypes.c_uint16
+    lib.w12o_b_decode.argtypes = [ctypes.c_uint16, i32]
+    lib.w12o_b_decode.restype = ctypes.c_uint16
+    lib.w12o_b_encode_many.argtypes = [p, i64, i32, p, p]
+    lib.w12o_b_encode_many.restype = None
+    lib.w12o_b_decode_many.argtypes = [p, i64, i32, p]
+    lib.w12o_b_decode_many.restype = None
+    lib.w12o_pack_fmt.argtypes = [i32, p, i64, i64, p, p, p, p]
+    lib.w12o_pack_fmt.restype = i64
+    lib.w12o_unpack_fmt.argtypes = [i32, p, p, p, p, i64, i64, p]
+    lib.w12o_unpack_fmt.restype = i32
+    lib.w12o_exceptions_fmt.argtypes = [i32, p, i64, i64, p, p]
+    lib.w12o_exceptions_fmt.restype = i64
+    lib.w12o_gemm_w12_f64_fmt.argtypes = [i32, p, i64, i64, p, p, p, p, i64, p, i32]
+    lib.w12o_gemm_w12_f64_fmt.restype = i32
     _lib = lib
     return lib
 
@@ -90,6 +110,17 @@ def _u16(a) -> np.ndarray:
     if a.dtype != np.uint16:
         raise TypeError("expected BF16 bit patterns as uint16, got %s" % a.dtype)
     return a
+
+
+# Allocations: "v1" = W12-v1 (3-bit offset of E[7:1] from an even base, low
+# byte verbatim); "b" = W12-b (4-bit offset of E from a base of any value).
+FORMATS = {"v1": 0, "b": 1}
+
+
+def _fmt(fmt: str) -> int:
+    if fmt not in FORMATS:
+        raise ValueError("unknown W12 format %r" % (fmt,))
+    return FORMATS[fmt]
 
 
 # ---- element level ---------------------------------------------------------
@@ -128,6 +159,41 @@ def decode_many(code: np.ndarray, beta: int) -> np.ndarray:
     return v
 
 
+# W12-b element level (base b, code = c << 8 | s << 7 | m)
+
+def b_base_for_emax(emax: int) -> int:
+    return int(_load().w12o_b_base_for_emax(int(emax)))
+
+
+def b_encodable(v: int, b: int) -> bool:
+    return bool(_load().w12o_b_encodable(int(v), int(b)))
+
+
+def b_encode(v: int, b: int) -> tuple[int, bool]:
+    ok = ctypes.c_int(0)
+    code = _load().w12o_b_encode(int(v), int(b), ctypes.byref(ok))
+    return int(code), bool(ok.value)
+
+
+def b_decode(code: int, b: int) -> int:
+    return int(_load().w12o_b_decode(int(code), int(b)))
+
+
+def b_encode_many(v: np.ndarray, b: int):
+    v = _u16(v)
+    code = np.empty(v.shape, np.uint16)
+    ok = np.empty(v.shape, np.uint8)
+    _load().w12o_b_encode_many(_ptr(v), v.size, int(b), _ptr(code), _ptr(ok))
+    return code, ok.astype(bool)
+
+
+def b_decode_many(code: np.ndarray, b: int) -> np.ndarray:
+    code = _u16(code)
+    v = np.empty(code.shape, np.uint16)
+    _load().w12o_b_decode_many(_ptr(code), code.size, int(b), _ptr(v))
+    return v
+
+
 # ---- tensor level ----------------------------------------------------------
 
 def padded_rows(N: int) -> int:
@@ -151,11 +217,12 @@ def meta_of(meta: np.ndarray, N: int, K: int) -> np.ndarray:
     return m.transpose(0, 2, 1).reshape(-1, G)[:N]
 
 
-def pack(w: np.ndarray):
+def pack(w: np.ndarray, fmt: str = "v1"):
     """BF16 bits [N, K] -> (p0, p1, p2, meta, bad_groups).
 
     p0/p1/p2 are flat uint8 arrays of plane_bytes(N, K); meta is a flat uint8
-    array of meta_bytes(N, K) (tiled layout, see w12_oracle.c)."""
+    array of meta_bytes(N, K) (tiled layout, see w12_oracle.c).  fmt selects
+    the allocation ("v1" or "b")."""
     w = _u16(w)
     N, K = w.shape
     if K % GROUP:
@@ -164,37 +231,40 @@ def pack(w: np.ndarray):
     p1 = np.zeros(plane_bytes(N, K), np.uint8)
     p2 = np.zeros(plane_bytes(N, K), np.uint8)
     meta = np.zeros(meta_bytes(N, K), np.uint8)
-    bad = _load().w12o_pack(_ptr(w), N, K, _ptr(p0), _ptr(p1), _ptr(p2), _ptr(meta))
+    bad = _load().w12o_pack_fmt(_fmt(fmt), _ptr(w), N, K, _ptr(p0), _ptr(p1), _ptr(p2),
+                                _ptr(meta))
     if bad < 0:
         raise ValueError("oracle pack rejected shape %r" % ((N, K),))
     return p0, p1, p2, meta, int(bad)
 
 
-def unpack(p0, p1, p2, meta, N: int, K: int) -> np.ndarray:
+def unpack(p0, p1, p2, meta, N: int, K: int, fmt: str = "v1") -> np.ndarray:
     arrs = [np.ascontiguousarray(a, dtype=np.uint8).reshape(-1) for a in (p0, p1, p2, meta)]
     for a, n in zip(arrs, (plane_bytes(N, K),) * 3 + (meta_bytes(N, K),)):
         if a.size != n:
             raise ValueError("container size mismatch")
     w = np.empty((N, K), np.uint16)
-    if _load().w12o_unpack(*(_ptr(a) for a in arrs), N, K, _ptr(w)) != 0:
+    if _load().w12o_unpack_fmt(_fmt(fmt), *(_ptr(a) for a in arrs), N, K, _ptr(w)) != 0:
         raise ValueError("oracle unpack rejected shape %r" % ((N, K),))
     return w
 
 
-def exceptions(w: np.ndarray):
+def exceptions(w: np.ndarray, fmt: str = "v1"):
     """BF16 bits [N, K] -> (offsets, entries): the exception list of the
     elements that fall below their group's window (see w12_oracle.c).
     offsets: uint32[padded_rows(N)/16 + 1]; entries: uint32[count, 2] with
-    word 0 = (row in tile) << 24 | k and word 1 = the original BF16 word."""
+    word 0 = (row in tile) << 24 | k and word 1 = base << 16 | the original
+    BF16 word."""
     w = _u16(w)
     N, K = w.shape
     lib = _load()
-    count = lib.w12o_exceptions(_ptr(w), N, K, None, None)
+    f = _fmt(fmt)
+    count = lib.w12o_exceptions_fmt(f, _ptr(w), N, K, None, None)
     if count < 0:
         raise ValueError("oracle exceptions rejected shape %r" % ((N, K),))
     offsets = np.zeros(padded_rows(N) // 16 + 1, np.uint32)
     entries = np.zeros((count, 2), np.uint32)
-    lib.w12o_exceptions(_ptr(w), N, K, _ptr(offsets), _ptr(entries) if count else None)
+    lib.w12o_exceptions_fmt(f, _ptr(w), N, K, _ptr(offsets), _ptr(entries) if count else None)
     return offsets, entries
 
 
@@ -234,7 +304,8 @@ def gemm_bf16_f64(x: np.ndarray, w: np.ndarray) -> np.ndarray:
     return y
 
 
-def gemm_w12_f64(x: np.ndarray, p0, p1, p2, meta, N: int, nthreads: int = 1) -> np.ndarray:
+def gemm_w12_f64(x: np.ndarray, p0, p1, p2, meta, N: int, nthreads: int = 1,
+                 fmt: str = "v1") -> np.ndarray:
     """Decode the container row by row and form y = x . W^T in fp64."""
     x = _u16(x)
     M, K = x.shape
@@ -243,8 +314,8 @@ def gemm_w12_f64(x: np.ndarray, p0, p1, p2, meta, N: int, nthreads: int = 1) -> 
         if a.size != n:
             raise ValueError("container size mismatch")
     y = np.empty((M, N), np.float64)
-    rc = _load().w12o_gemm_w12_f64(_ptr(x), M, K, *(_ptr(a) for a in arrs), N,
-                                   _ptr(y), int(nthreads))
+    rc = _load().w12o_gemm_w12_f64_fmt(_fmt(fmt), _ptr(x), M, K, *(_ptr(a) for a in arrs), N,
+                                       _ptr(y), int(nthreads))
     if rc != 0:
         raise ValueError("oracle gemm rejected shape")
     return y

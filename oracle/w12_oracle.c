@@ -43,6 +43,21 @@
  * (w12o_bf16_tile): block (T, g) of 2048 words, sub-block b of 512 words,
  * 8 words per piece L, words k = 128*g + 32*b + 8*q + e in natural order.
  *
+ * A second allocation, format "W12-b" (fmt = 1 in the *_fmt functions), is
+ * the arbitrary-base alternative: a 4-bit exponent offset c from a
+ * per-group base b that may take any value, instead of W12-v1's 3-bit offset
+ * of E[7:1] from an even base:
+ *   P0 = m[3:0];  P1 = (s << 3) | m[6:4];  P2 = c, where c = 0 when E = 0
+ *   (zeros and subnormals) and c = E - b in 1..15 otherwise.
+ *   b is the smallest value >= 0 with b + 15 >= the group's largest
+ *   exponent (0 <= b <= 240); exponents {0} and [b+1, b+15] are stored
+ *   exactly (15 + 1 per group, any alignment), anything else is written as
+ *   the window floor +-2^(b+1-127) (c = 1, mantissa 0, sign kept).
+ *   The meta byte is b itself (no flag bit: b needs all 8 bits); flagged
+ *   groups are counted, and their elements are listed in the exception
+ *   list with word 1 = (b << 16) | original.
+ * Same planes, tiles, split-nibble order and exception-list order as W12-v1.
+ *
  * Build: gcc -O2 -std=c11 -shared -fPIC w12_oracle.c -o libw12_oracle.so -lpthread
  * (no -ffast-math: the GEMM must keep IEEE semantics).
  */
@@ -70,6 +85,9 @@ static double bf16_to_double(uint16_t v)
 }
 
 /* ---- per-group base (reading of "three 4-bit planes": beta rule) ------- */
+
+#define W12O_FMT_V1 0
+#define W12O_FMT_B 1
 
 /* Smallest beta >= 0 whose window [2*beta+2, 2*beta+15] reaches emax.
  * Written as a search, not a closed form, so it can be read off the rule. */
@@ -130,6 +148,93 @@ uint16_t w12o_decode(uint16_t code, int beta)
     return (uint16_t)((s << 15) | (e_hi << 8) | lo);
 }
 
+/* ---- W12-b: the arbitrary-base allocation ------------------------------ */
+
+/* Smallest b >= 0 whose window [b+1, b+15] reaches emax (a search again). */
+int w12o_b_base_for_emax(int emax)
+{
+    int b = 0;
+    while (b + 15 < emax)
+        b++;
+    return b;
+}
+
+int w12o_b_encodable(uint16_t v, int b)
+{
+    int e = bf16_exponent(v);
+    return e == 0 || (e >= b + 1 && e <= b + 15);
+}
+
+/* code bits 11..8 = P2 nibble (c), 7..4 = P1 nibble (s, m6..m4), 3..0 = P0
+ * nibble (m3..m0). */
+uint16_t w12o_b_encode(uint16_t v, int b, int *ok)
+{
+    int s = bf16_sign(v);
+    int e = bf16_exponent(v);
+    int m = v & 0x7F;
+    int c;
+    int good = 1;
+
+    if (e == 0) {
+        c = 0;                        /* zeros and subnormals */
+    } else if (e >= b + 1 && e <= b + 15) {
+        c = e - b;                    /* 1..15 */
+    } else if (e < b + 1) {
+        good = 0;                     /* below the window: clamp up */
+        c = 1;
+        m = 0;                        /* E = b+1, mantissa 0 */
+    } else {
+        good = 0;                     /* above the window: saturate */
+        c = 15;
+        m = 0x7F;
+    }
+    if (ok)
+        *ok = good;
+    return (uint16_t)((c << 8) | (s << 7) | m);
+}
+
+uint16_t w12o_b_decode(uint16_t code, int b)
+{
+    int c = (code >> 8) & 0xF;
+    int s = (code >> 7) & 1;
+    int m = code & 0x7F;
+    int e = (c == 0) ? 0 : b + c;
+    return (uint16_t)((s << 15) | (e << 7) | m);
+}
+
+/* ---- the two allocations behind one interface -------------------------- */
+
+static int fmt_base_for_emax(int fmt, int emax)
+{
+    return fmt == W12O_FMT_B ? w12o_b_base_for_emax(emax) : w12o_beta_for_emax(emax);
+}
+
+static int fmt_encodable(int fmt, uint16_t v, int base)
+{
+    return fmt == W12O_FMT_B ? w12o_b_encodable(v, base) : w12o_encodable(v, base);
+}
+
+static uint16_t fmt_encode(int fmt, uint16_t v, int base, int *ok)
+{
+    return fmt == W12O_FMT_B ? w12o_b_encode(v, base, ok) : w12o_encode(v, base, ok);
+}
+
+static uint16_t fmt_decode(int fmt, uint16_t code, int base)
+{
+    return fmt == W12O_FMT_B ? w12o_b_decode(code, base) : w12o_decode(code, base);
+}
+
+/* meta byte <-> base: W12-v1 keeps a flag in bit 7, W12-b the base only */
+static uint8_t fmt_meta(int fmt, int base, int bad)
+{
+    return fmt == W12O_FMT_B ? (uint8_t)base : (uint8_t)(base | (bad ? 0x80 : 0));
+}
+
+static int fmt_base_of_meta(int fmt, uint8_t meta)
+{
+    return fmt == W12O_FMT_B ? meta : (meta & 0x7F);
+}
+
 /* Element-wise loops over the two functions above (for exhaustive tests). */
 void w12o_encode_many(const uint16_t *v, int64_t n, int beta,
                       uint16_t *code, uint8_t *ok)
@@ -145,6 +250,21 @@ void w12o_decode_many(const uint16_t *code, int64_t n, int beta, uint16_t *v)
 {
     for (int64_t i = 0; i < n; i++)
         v[i] = w12o_decode(code[i], beta);
+}
+
+void w12o_b_encode_many(const uint16_t *v, int64_t n, int b, uint16_t *code, uint8_t *ok)
+{
+    for (int64_t i = 0; i < n; i++) {
+        int good;
+        code[i] = w12o_b_encode(v[i], b, &good);
+        ok[i] = (uint8_t)good;
+    }
+}
+
+void w12o_b_decode_many(const uint16_t *code, int64_t n, int b, uint16_t *v)
+{
+    for (int64_t i = 0; i < n; i++)
+        v[i] = w12o_b_decode(code[i], b);
 }
 
 /* ---- plane addressing (16 x 128 tiles, split-nibble order) ------------- */
@@ -190,8 +310,8 @@ static int get_nibble(const uint8_t *plane, int64_t n, int64_t K, int64_t k)
 /* Returns the number of unencodable (flagged) groups, or -1 on bad shape. */
 /* The planes and meta must hold w12o_padded_rows(N) rows; padding rows are
  * written as zeros. */
-int64_t w12o_pack(const uint16_t *w, int64_t N, int64_t K,
-                  uint8_t *p0, uint8_t *p1, uint8_t *p2, uint8_t *meta)
+int64_t w12o_pack_fmt(int fmt, const uint16_t *w, int64_t N, int64_t K,
+                      uint8_t *p0, uint8_t *p1, uint8_t *p2, uint8_t *meta)
 {
     if (N < 0 || K < 0 || K % W12O_GROUP != 0)
         return -1;
@@ -210,42 +330,54 @@ int64_t w12o_pack(const uint16_t *w, int64_t N, int64_t K,
                 if (e > emax)
                     emax = e;
             }
-            int beta = w12o_beta_for_emax(emax);
+            int beta = fmt_base_for_emax(fmt, emax);
             int bad = 0;
             for (int i = 0; i < W12O_GROUP; i++) {
                 int64_t k = g * W12O_GROUP + i;
                 int ok;
-                uint16_t code = w12o_encode(w[n * K + k], beta, &ok);
+                uint16_t code = fmt_encode(fmt, w[n * K + k], beta, &ok);
                 if (!ok)
                     bad = 1;
                 put_nibble(p0, n, K, k, code & 0xF);
                 put_nibble(p1, n, K, k, (code >> 4) & 0xF);
                 put_nibble(p2, n, K, k, (code >> 8) & 0xF);
             }
-            meta[meta_byte(n, K, g * W12O_GROUP)] = (uint8_t)(beta | (bad ? 0x80 : 0));
+            meta[meta_byte(n, K, g * W12O_GROUP)] = fmt_meta(fmt, beta, bad);
             bad_groups += bad;
         }
     }
     return bad_groups;
 }
 
+int64_t w12o_pack(const uint16_t *w, int64_t N, int64_t K,
+                  uint8_t *p0, uint8_t *p1, uint8_t *p2, uint8_t *meta)
+{
+    return w12o_pack_fmt(W12O_FMT_V1, w, N, K, p0, p1, p2, meta);
+}
+
 /* Returns 0, or -1 on bad shape. Flagged groups decode to their clamped
  * values (the flag bit is ignored by the decoder). */
-int w12o_unpack(const uint8_t *p0, const uint8_t *p1, const uint8_t *p2,
-                const uint8_t *meta, int64_t N, int64_t K, uint16_t *w)
+int w12o_unpack_fmt(int fmt, const uint8_t *p0, const uint8_t *p1, const uint8_t *p2,
+                    const uint8_t *meta, int64_t N, int64_t K, uint16_t *w)
 {
     if (N < 0 || K < 0 || K % W12O_GROUP != 0)
         return -1;
     for (int64_t n = 0; n < N; n++) {
         for (int64_t k = 0; k < K; k++) {
-            int beta = meta[meta_byte(n, K, k)] & 0x7F;
+            int beta = fmt_base_of_meta(fmt, meta[meta_byte(n, K, k)]);
             uint16_t code = (uint16_t)((get_nibble(p2, n, K, k) << 8) |
                                        (get_nibble(p1, n, K, k) << 4) |
                                        get_nibble(p0, n, K, k));
-            w[n * K + k] = w12o_decode(code, beta);
+            w[n * K + k] = fmt_decode(fmt, code, beta);
         }
     }
     return 0;
+}
+
+int w12o_unpack(const uint8_t *p0, const uint8_t *p1, const uint8_t *p2,
+                const uint8_t *meta, int64_t N, int64_t K, uint16_t *w)
+{
+    return w12o_unpack_fmt(W12O_FMT_V1, p0, p1, p2, meta, N, K, w);
 }
 
 /* ---- exception list: the escape path for unencodable groups --------------
@@ -267,8 +399,8 @@ int w12o_unpack(const uint8_t *p0, const uint8_t *p1, const uint8_t *p2,
  * read a container).  offsets and entries may be NULL (then only the count is
  * returned).  Returns the number of entries, or -1 on bad shape (K must be a
  * multiple of 128 and below 2^24). */
-int64_t w12o_exceptions(const uint16_t *w, int64_t N, int64_t K,
-                        uint32_t *offsets, uint32_t *entries)
+int64_t w12o_exceptions_fmt(int fmt, const uint16_t *w, int64_t N, int64_t K,
+                            uint32_t *offsets, uint32_t *entries)
 {
     if (N < 0 || K < 0 || K % W12O_GROUP != 0 || K >= ((int64_t)1 << 24))
         return -1;
@@ -288,7 +420,7 @@ int64_t w12o_exceptions(const uint16_t *w, int64_t N, int64_t K,
                     if (e > emax)
                         emax = e;
                 }
-                beta[c] = w12o_beta_for_emax(emax);
+                beta[c] = fmt_base_for_emax(fmt, emax);
             }
             for (int L = 0; L < 64; L++) {
                 int q = L / 16, c = L % 16;
@@ -299,7 +431,7 @@ int64_t w12o_exceptions(const uint16_t *w, int64_t N, int64_t K,
                     for (int e = 0; e < 8; e++) {
                         int64_t k = g * W12O_GROUP + 32 * bb + 8 * q + e;
                         uint16_t v = w[n * K + k];
-                        if (w12o_encodable(v, beta[c]))
+                        if (fmt_encodable(fmt, v, beta[c]))
                             continue;
                         if (entries) {
                             entries[2 * count] = ((uint32_t)c << 24) | (uint32_t)k;
@@ -313,6 +445,12 @@ int64_t w12o_exceptions(const uint16_t *w, int64_t N, int64_t K,
     if (offsets)
         offsets[ntiles] = (uint32_t)count;
     return count;
+}
+
+int64_t w12o_exceptions(const uint16_t *w, int64_t N, int64_t K,
+                        uint32_t *offsets, uint32_t *entries)
+{
+    return w12o_exceptions_fmt(W12O_FMT_V1, w, N, K, offsets, entries);
 }
 
 /* Write the exceptions' original words over an unpacked [N, K] weight. */
@@ -380,6 +518,7 @@ int w12o_gemm_bf16_f64(const uint16_t *x, int64_t M, int64_t K,
  * CPU baseline that the benchmark times; the arithmetic per output is the
  * same ascending-k fp64 sum as above). */
 struct gemm_w12_job {
+    int fmt;
     const uint16_t *x;
     const uint8_t *p0, *p1, *p2, *meta;
     int64_t M, N, K, n_begin, n_end;
@@ -393,12 +532,12 @@ static void *gemm_w12_rows(void *arg)
         for (int64_t m = 0; m < j->M; m++) {
             double acc = 0.0;
             for (int64_t k = 0; k < j->K; k++) {
-                int beta = j->meta[meta_byte(n, j->K, k)] & 0x7F;
+                int beta = fmt_base_of_meta(j->fmt, j->meta[meta_byte(n, j->K, k)]);
                 uint16_t code = (uint16_t)((get_nibble(j->p2, n, j->K, k) << 8) |
                                            (get_nibble(j->p1, n, j->K, k) << 4) |
                                            get_nibble(j->p0, n, j->K, k));
                 acc += bf16_to_double(j->x[m * j->K + k]) *
-                       bf16_to_double(w12o_decode(code, beta));
+                       bf16_to_double(fmt_decode(j->fmt, code, beta));
             }
             j->y[m * j->N + n] = acc;
         }
@@ -408,9 +547,9 @@ static void *gemm_w12_rows(void *arg)
 
 #define W12O_MAX_THREADS 256
 
-int w12o_gemm_w12_f64(const uint16_t *x, int64_t M, int64_t K,
-                      const uint8_t *p0, const uint8_t *p1, const uint8_t *p2,
-                      const uint8_t *meta, int64_t N, double *y, int nthreads)
+int w12o_gemm_w12_f64_fmt(int fmt, const uint16_t *x, int64_t M, int64_t K,
+                          const uint8_t *p0, const uint8_t *p1, const uint8_t *p2,
+                          const uint8_t *meta, int64_t N, double *y, int nthreads)
 {
     if (M < 0 || N < 0 || K < 0 || K % W12O_GROUP != 0)
         return -1;
@@ -425,6 +564,7 @@ int w12o_gemm_w12_f64(const uint16_t *x, int64_t M, int64_t K,
     pthread_t tids[W12O_MAX_THREADS];
     int started[W12O_MAX_THREADS];
     for (int t = 0; t < nthreads; t++) {
+        jobs[t].fmt = fmt;
         jobs[t].x = x;
         jobs[t].p0 = p0;
         jobs[t].p1 = p1;
@@ -448,4 +588,11 @@ int w12o_gemm_w12_f64(const uint16_t *x, int64_t M, int64_t K,
             gemm_w12_rows(&jobs[t]);   /* thread creation failed: run inline */
     }
     return 0;
+}
+
+int w12o_gemm_w12_f64(const uint16_t *x, int64_t M, int64_t K,
+                      const uint8_t *p0, const uint8_t *p1, const uint8_t *p2,
+                      const uint8_t *meta, int64_t N, double *y, int nthreads)
+{
+    return w12o_gemm_w12_f64_fmt(W12O_FMT_V1, x, M, K, p0, p1, p2, meta, N, y, nthreads);
 }
