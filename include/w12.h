@@ -72,7 +72,7 @@
 extern "C" {
 #endif
 
-#define W12_ABI_VERSION 5
+#define W12_ABI_VERSION 6
 #define W12_GROUP 128
 #define W12_TILE_ROWS 16
 #define W12_MAX_M 32
@@ -314,10 +314,61 @@ int bf16_gemm_ex(const uint16_t *x, int64_t M, int64_t ldx,
 /*
  * Name of the kernel variant the GEMMs launch for this shape (static string,
  * for reports and profiles), or NULL if the shape is rejected.  `is_w12`
- * selects the weight fetch, `allow_splitk` the w12_gemm_ws default.
+ * selects the weight fetch (0 = BF16 control, 1 = W12-v1, 2 = W12-b),
+ * `allow_splitk` the w12_gemm_ws default.
  */
 const char *w12_gemm_variant(int64_t M, int64_t N, int64_t K, int is_w12,
                              int allow_splitk);
+
+/*
+ * W12-b: the arbitrary-base bit allocation (the alternative to W12-v1 that
+ * gives each group one more stored exponent at about 1.6x the decode
+ * instructions; same pages as W12-v1: 12 bits per weight in three 4-bit
+ * planes, rebuilt bit-exactly in the GEMM).  Per group:
+ *   b        = smallest b >= 0 with b + 15 >= the group's largest biased
+ *              exponent E (0 <= b <= 240);
+ *   stored   = exponents {0} and [b+1, b+15] (4096 values);
+ *   nibbles  = P0 = m[3:0], P1 = sign<<3 | m[6:4], P2 = c with c = 0 for
+ *              E = 0, else c = E - b (1..15);
+ *   layout   = the W12-v1 tiles, blocks and split-nibble order;
+ *   meta     = the byte b itself (no flag bit: b needs 8 bits); flagged
+ *              groups are only counted (bad_groups);
+ *   clamp    = an exponent in [1, b] is stored as +-2^(b+1-127);
+ *   list     = the W12-v1 exception-list layout, word 1 = (b << 16 | the
+ *              original BF16 word).
+ * The calls below take and return W12-b containers with exactly the
+ * arguments, sizes, conventions and errors of the W12-v1 call of the same
+ * name without the "b"; a W12-b container must not be passed to a W12-v1
+ * call or the other way round (the meta bytes are read differently).
+ */
+int w12b_pack(const uint16_t *w, int64_t N, int64_t K,
+              void *p0, void *p1, void *p2, uint8_t *meta,
+              uint32_t *bad_groups, void *stream);
+int w12b_exceptions(const uint16_t *w, int64_t N, int64_t K,
+                    void *workspace, size_t workspace_bytes,
+                    uint32_t *exc_offsets, uint32_t *exc_entries,
+                    int64_t capacity, uint32_t *total, void *stream);
+int w12b_unpack(const void *p0, const void *p1, const void *p2,
+                const uint8_t *meta, const uint32_t *exc_offsets,
+                const uint32_t *exc_entries, int64_t N, int64_t K,
+                uint16_t *w_out, void *stream);
+int w12b_gemm(const uint16_t *x, int64_t M, int64_t ldx,
+              const void *p0, const void *p1, const void *p2,
+              const uint8_t *meta, const uint32_t *exc_offsets,
+              const uint32_t *exc_entries, int64_t N, int64_t K,
+              void *y, int64_t ldy, int y_type, void *stream);
+int w12b_gemm_ws(const uint16_t *x, int64_t M, int64_t ldx,
+                 const void *p0, const void *p1, const void *p2,
+                 const uint8_t *meta, const uint32_t *exc_offsets,
+                 const uint32_t *exc_entries, int64_t N, int64_t K,
+                 void *y, int64_t ldy, int y_type,
+                 void *workspace, size_t workspace_bytes, void *stream);
+int w12b_gemm_ex(const uint16_t *x, int64_t M, int64_t ldx,
+                 const void *p0, const void *p1, const void *p2,
+                 const uint8_t *meta, const uint32_t *exc_offsets,
+                 const uint32_t *exc_entries, int64_t N, int64_t K,
+                 void *y, int64_t ldy, int y_type, const w12_tiling_t *tiling,
+                 void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * w12_read_probe -- measurement aid, not part of the W12 operation: reads

@@ -112,14 +112,28 @@ int w12_bf16_tile(const uint16_t* w, int64_t N, int64_t K, uint16_t* w_tiled, vo
     return status_of(w12::launch_bf16_tile(w, N, K, w_tiled, static_cast<hipStream_t>(stream)));
 }
 
-int w12_pack(const uint16_t* w, int64_t N, int64_t K, void* p0, void* p1, void* p2, uint8_t* meta,
-             uint32_t* bad_groups, void* stream) {
+}  // extern "C"
+
+static int pack_fmt(int fmt, const uint16_t* w, int64_t N, int64_t K, void* p0, void* p1, void* p2,
+                    uint8_t* meta, uint32_t* bad_groups, void* stream) {
     if (!w || !p0 || !p1 || !p2 || !meta) return W12_ERR_NULL;
     if (int rc = check_weight_shape(N, K)) return rc;
     if (!aligned16(w) || !aligned16(p0) || !aligned16(p1) || !aligned16(p2)) return W12_ERR_ALIGN;
     if (bad_groups && (reinterpret_cast<uintptr_t>(bad_groups) & 3u)) return W12_ERR_ALIGN;
-    return status_of(w12::launch_pack(w, N, K, p0, p1, p2, meta, bad_groups,
+    return status_of(w12::launch_pack(fmt, w, N, K, p0, p1, p2, meta, bad_groups,
                                       static_cast<hipStream_t>(stream)));
+}
+
+extern "C" {
+
+int w12_pack(const uint16_t* w, int64_t N, int64_t K, void* p0, void* p1, void* p2, uint8_t* meta,
+             uint32_t* bad_groups, void* stream) {
+    return pack_fmt(w12::kFmtV1, w, N, K, p0, p1, p2, meta, bad_groups, stream);
+}
+
+int w12b_pack(const uint16_t* w, int64_t N, int64_t K, void* p0, void* p1, void* p2, uint8_t* meta,
+              uint32_t* bad_groups, void* stream) {
+    return pack_fmt(w12::kFmtB, w, N, K, p0, p1, p2, meta, bad_groups, stream);
 }
 
 size_t w12_exceptions_workspace_bytes(int64_t N, int64_t K) {
@@ -127,9 +141,11 @@ size_t w12_exceptions_workspace_bytes(int64_t N, int64_t K) {
     return (size_t)((N + W12_TILE_ROWS - 1) / W12_TILE_ROWS * (K / W12_GROUP) * 4);
 }
 
-int w12_exceptions(const uint16_t* w, int64_t N, int64_t K, void* workspace, size_t workspace_bytes,
-                   uint32_t* exc_offsets, uint32_t* exc_entries, int64_t capacity, uint32_t* total,
-                   void* stream) {
+}  // extern "C"
+
+static int exceptions_fmt(int fmt, const uint16_t* w, int64_t N, int64_t K, void* workspace,
+                          size_t workspace_bytes, uint32_t* exc_offsets, uint32_t* exc_entries,
+                          int64_t capacity, uint32_t* total, void* stream) {
     if (!w || !exc_offsets || !total) return W12_ERR_NULL;
     if (int rc = check_weight_shape(N, K)) return rc;
     if (K >= kExcMaxK || (N + W12_TILE_ROWS) * K >= kExcMaxElems) return W12_ERR_SHAPE;
@@ -140,22 +156,50 @@ int w12_exceptions(const uint16_t* w, int64_t N, int64_t K, void* workspace, siz
     if (workspace == nullptr || workspace_bytes < w12_exceptions_workspace_bytes(N, K) ||
         !aligned4(workspace))
         return W12_ERR_WORKSPACE;
-    return status_of(w12::launch_exceptions(w, N, K, static_cast<uint32_t*>(workspace), exc_offsets,
-                                            exc_entries, capacity, total,
+    return status_of(w12::launch_exceptions(fmt, w, N, K, static_cast<uint32_t*>(workspace),
+                                            exc_offsets, exc_entries, capacity, total,
                                             static_cast<hipStream_t>(stream)));
 }
 
-int w12_unpack(const void* p0, const void* p1, const void* p2, const uint8_t* meta,
-               const uint32_t* exc_offsets, const uint32_t* exc_entries, int64_t N, int64_t K,
-               uint16_t* w_out, void* stream) {
+static int unpack_fmt(int fmt, const void* p0, const void* p1, const void* p2, const uint8_t* meta,
+                      const uint32_t* exc_offsets, const uint32_t* exc_entries, int64_t N,
+                      int64_t K, uint16_t* w_out, void* stream) {
     if (!p0 || !p1 || !p2 || !meta || !w_out) return W12_ERR_NULL;
     if (int rc = check_weight_shape(N, K)) return rc;
     if (!aligned16(p0) || !aligned16(p1) || !aligned16(p2) || !aligned16(w_out)) return W12_ERR_ALIGN;
     if (int rc = check_exceptions(exc_offsets, exc_entries, N, K)) return rc;
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    if (int rc = status_of(w12::launch_unpack(p0, p1, p2, meta, N, K, w_out, s))) return rc;
+    if (int rc = status_of(w12::launch_unpack(fmt, p0, p1, p2, meta, N, K, w_out, s))) return rc;
     if (exc_offsets == nullptr) return W12_OK;
     return status_of(w12::launch_apply_exceptions(exc_offsets, exc_entries, N, K, w_out, s));
+}
+
+extern "C" {
+
+int w12_exceptions(const uint16_t* w, int64_t N, int64_t K, void* workspace, size_t workspace_bytes,
+                   uint32_t* exc_offsets, uint32_t* exc_entries, int64_t capacity, uint32_t* total,
+                   void* stream) {
+    return exceptions_fmt(w12::kFmtV1, w, N, K, workspace, workspace_bytes, exc_offsets, exc_entries,
+                          capacity, total, stream);
+}
+
+int w12b_exceptions(const uint16_t* w, int64_t N, int64_t K, void* workspace,
+                    size_t workspace_bytes, uint32_t* exc_offsets, uint32_t* exc_entries,
+                    int64_t capacity, uint32_t* total, void* stream) {
+    return exceptions_fmt(w12::kFmtB, w, N, K, workspace, workspace_bytes, exc_offsets, exc_entries,
+                          capacity, total, stream);
+}
+
+int w12_unpack(const void* p0, const void* p1, const void* p2, const uint8_t* meta,
+               const uint32_t* exc_offsets, const uint32_t* exc_entries, int64_t N, int64_t K,
+               uint16_t* w_out, void* stream) {
+    return unpack_fmt(w12::kFmtV1, p0, p1, p2, meta, exc_offsets, exc_entries, N, K, w_out, stream);
+}
+
+int w12b_unpack(const void* p0, const void* p1, const void* p2, const uint8_t* meta,
+                const uint32_t* exc_offsets, const uint32_t* exc_entries, int64_t N, int64_t K,
+                uint16_t* w_out, void* stream) {
+    return unpack_fmt(w12::kFmtB, p0, p1, p2, meta, exc_offsets, exc_entries, N, K, w_out, stream);
 }
 
 static int resolve_tiling(const w12_tiling_t* tiling, bool allow_splitk, int64_t M, int64_t N,
@@ -186,7 +230,7 @@ static int check_workspace(const w12::Tiling& t, int64_t M, int64_t N, void* ws,
     return W12_OK;
 }
 
-static int gemm_w12(const uint16_t* x, int64_t M, int64_t ldx, const void* p0, const void* p1,
+static int gemm_w12(int fetch, const uint16_t* x, int64_t M, int64_t ldx, const void* p0, const void* p1,
                     const void* p2, const uint8_t* meta, const uint32_t* exc_off,
                     const uint32_t* exc_ent, int64_t N, int64_t K, void* y,
                     int64_t ldy, int y_type, const w12_tiling_t* tiling, bool allow_splitk,
@@ -206,7 +250,7 @@ static int gemm_w12(const uint16_t* x, int64_t M, int64_t ldx, const void* p0, c
     a.exc_off = exc_off;
     a.exc_ent = exc_ent;
     w12::bind_split(a, t, ws);
-    return status_of(w12::launch_gemm(a, t, true, static_cast<hipStream_t>(stream)));
+    return status_of(w12::launch_gemm(a, t, fetch, static_cast<hipStream_t>(stream)));
 }
 
 static int gemm_bf16(const uint16_t* x, int64_t M, int64_t ldx, const uint16_t* w, int64_t N,
@@ -221,7 +265,7 @@ static int gemm_bf16(const uint16_t* x, int64_t M, int64_t ldx, const uint16_t* 
     w12::GemmArgs a = make_args(x, M, ldx, N, K, y, ldy, y_type);
     a.w = w;
     w12::bind_split(a, t, ws);
-    return status_of(w12::launch_gemm(a, t, false, static_cast<hipStream_t>(stream)));
+    return status_of(w12::launch_gemm(a, t, w12::kFetchBF16, static_cast<hipStream_t>(stream)));
 }
 
 int w12_gemm_ex(const uint16_t* x, int64_t M, int64_t ldx, const void* p0, const void* p1,
@@ -229,8 +273,17 @@ int w12_gemm_ex(const uint16_t* x, int64_t M, int64_t ldx, const void* p0, const
                 const uint32_t* exc_entries, int64_t N, int64_t K, void* y, int64_t ldy,
                 int y_type, const w12_tiling_t* tiling, void* workspace, size_t workspace_bytes,
                 void* stream) {
-    return gemm_w12(x, M, ldx, p0, p1, p2, meta, exc_offsets, exc_entries, N, K, y, ldy, y_type,
-                    tiling, workspace != nullptr, workspace, workspace_bytes, stream);
+    return gemm_w12(w12::kFetchW12, x, M, ldx, p0, p1, p2, meta, exc_offsets, exc_entries, N, K, y,
+                    ldy, y_type, tiling, workspace != nullptr, workspace, workspace_bytes, stream);
+}
+
+int w12b_gemm_ex(const uint16_t* x, int64_t M, int64_t ldx, const void* p0, const void* p1,
+                 const void* p2, const uint8_t* meta, const uint32_t* exc_offsets,
+                 const uint32_t* exc_entries, int64_t N, int64_t K, void* y, int64_t ldy,
+                 int y_type, const w12_tiling_t* tiling, void* workspace, size_t workspace_bytes,
+                 void* stream) {
+    return gemm_w12(w12::kFetchW12B, x, M, ldx, p0, p1, p2, meta, exc_offsets, exc_entries, N, K, y,
+                    ldy, y_type, tiling, workspace != nullptr, workspace, workspace_bytes, stream);
 }
 
 int bf16_gemm_ex(const uint16_t* x, int64_t M, int64_t ldx, const uint16_t* w, int64_t N,
@@ -244,8 +297,16 @@ int w12_gemm(const uint16_t* x, int64_t M, int64_t ldx, const void* p0, const vo
              const void* p2, const uint8_t* meta, const uint32_t* exc_offsets,
              const uint32_t* exc_entries, int64_t N, int64_t K, void* y, int64_t ldy, int y_type,
              void* stream) {
-    return gemm_w12(x, M, ldx, p0, p1, p2, meta, exc_offsets, exc_entries, N, K, y, ldy, y_type,
-                    nullptr, false, nullptr, 0, stream);
+    return gemm_w12(w12::kFetchW12, x, M, ldx, p0, p1, p2, meta, exc_offsets, exc_entries, N, K, y,
+                    ldy, y_type, nullptr, false, nullptr, 0, stream);
+}
+
+int w12b_gemm(const uint16_t* x, int64_t M, int64_t ldx, const void* p0, const void* p1,
+              const void* p2, const uint8_t* meta, const uint32_t* exc_offsets,
+              const uint32_t* exc_entries, int64_t N, int64_t K, void* y, int64_t ldy, int y_type,
+              void* stream) {
+    return gemm_w12(w12::kFetchW12B, x, M, ldx, p0, p1, p2, meta, exc_offsets, exc_entries, N, K, y,
+                    ldy, y_type, nullptr, false, nullptr, 0, stream);
 }
 
 int bf16_gemm(const uint16_t* x, int64_t M, int64_t ldx, const uint16_t* w, int64_t N, int64_t K,
@@ -257,8 +318,16 @@ int w12_gemm_ws(const uint16_t* x, int64_t M, int64_t ldx, const void* p0, const
                 const void* p2, const uint8_t* meta, const uint32_t* exc_offsets,
                 const uint32_t* exc_entries, int64_t N, int64_t K, void* y, int64_t ldy,
                 int y_type, void* workspace, size_t workspace_bytes, void* stream) {
-    return gemm_w12(x, M, ldx, p0, p1, p2, meta, exc_offsets, exc_entries, N, K, y, ldy, y_type,
-                    nullptr, true, workspace, workspace_bytes, stream);
+    return gemm_w12(w12::kFetchW12, x, M, ldx, p0, p1, p2, meta, exc_offsets, exc_entries, N, K, y,
+                    ldy, y_type, nullptr, true, workspace, workspace_bytes, stream);
+}
+
+int w12b_gemm_ws(const uint16_t* x, int64_t M, int64_t ldx, const void* p0, const void* p1,
+                 const void* p2, const uint8_t* meta, const uint32_t* exc_offsets,
+                 const uint32_t* exc_entries, int64_t N, int64_t K, void* y, int64_t ldy,
+                 int y_type, void* workspace, size_t workspace_bytes, void* stream) {
+    return gemm_w12(w12::kFetchW12B, x, M, ldx, p0, p1, p2, meta, exc_offsets, exc_entries, N, K, y,
+                    ldy, y_type, nullptr, true, workspace, workspace_bytes, stream);
 }
 
 int bf16_gemm_ws(const uint16_t* x, int64_t M, int64_t ldx, const uint16_t* w, int64_t N,
@@ -299,7 +368,8 @@ int w12_default_tiling(int64_t M, int64_t N, int64_t K, int allow_splitk, w12_ti
 
 const char* w12_gemm_variant(int64_t M, int64_t N, int64_t K, int is_w12, int allow_splitk) {
     if (check_weight_shape(N, K) != W12_OK || M < 1 || M > W12_MAX_M) return nullptr;
-    return w12::tiling_name(w12::choose_tiling((int)M, N, K, allow_splitk != 0), is_w12 != 0);
+    const int fetch = is_w12 == 2 ? w12::kFetchW12B : is_w12 != 0 ? w12::kFetchW12 : w12::kFetchBF16;
+    return w12::tiling_name(w12::choose_tiling((int)M, N, K, allow_splitk != 0), fetch);
 }
 
 }  // extern "C"

@@ -1,4 +1,5 @@
-// w12_decode.hpp -- in-register W12-v1 -> BF16 reassembly for gfx950.
+// w12_decode.hpp -- in-register W12 -> BF16 reassembly for gfx950 (both
+// bit allocations: W12-v1 and the arbitrary-base W12-b).
 //
 // The pages describe W12 as BF16 split into three 4-bit planes and rebuilt
 // bit by bit in GEMM registers (AI Radar summary of SpecPilot, English
@@ -66,6 +67,42 @@ __device__ __forceinline__ void decode8(uint32_t p0, uint32_t p1, uint32_t p2,
     const uint32_t hi_a = ((p2 << 4) & 0x80808080u) | x_a;
     const uint32_t hi_b = (p2 & 0x80808080u) | x_b;
     // interleave {hi, lo} byte pairs into BF16 pairs
+    out[0] = perm(hi_a, lo_a, 0x05010400u);
+    out[1] = perm(hi_a, lo_a, 0x07030602u);
+    out[2] = perm(hi_b, lo_b, 0x05010400u);
+    out[3] = perm(hi_b, lo_b, 0x07030602u);
+}
+
+// ---- W12-b (arbitrary base) ------------------------------------------------
+// P0 = m[3:0], P1 = s << 3 | m[6:4], P2 = c; E = c ? b + c : 0 with b the
+// group's base (0..240, so b + c <= 255 and no byte carries).  Per dword of
+// four weights:
+//   sign|mantissa byte        = P1 nibble << 4 | P0 nibble          (v_bfi_b32)
+//   E                         = (c + b) & keep, keep = 0xFF unless c == 0
+//   high BF16 byte (s|E[7:1]) = bit 7 of the sign|mantissa byte, E >> 1
+//   low BF16 byte  (E0|m)     = E << 7 into bit 7, the mantissa below
+// keep comes from v_perm_b32, whose selector 12 gives 0x00 and selectors
+// 13..255 give 0xFF: c + 12 is 12 exactly when c = 0.  About 26 VALU
+// instructions per 8 weights (W12-v1: 16).
+
+__device__ __forceinline__ uint32_t exps_b(uint32_t c, uint32_t b4) {
+    const uint32_t keep = perm(0u, 0u, c + 0x0C0C0C0Cu);
+    return (c + b4) & keep;
+}
+
+// b4 = b * 0x01010101 (the base in every byte).
+__device__ __forceinline__ void decode8b(uint32_t p0, uint32_t p1, uint32_t p2, uint32_t b4,
+                                         uint32_t out[4]) {
+    const uint32_t sm_a = bfi(0xF0F0F0F0u, p1 << 4, p0);   // k0..k3
+    const uint32_t sm_b = bfi(0xF0F0F0F0u, p1, p0 >> 4);   // k4..k7
+    const uint32_t e_a = exps_b(p2 & 0x0F0F0F0Fu, b4);
+    const uint32_t e_b = exps_b((p2 >> 4) & 0x0F0F0F0Fu, b4);
+    // E >> 1 and E << 7 spill bits into the neighbouring bytes; the bit
+    // inserts keep only the bits of each byte that belong to it
+    const uint32_t hi_a = bfi(0x80808080u, sm_a, e_a >> 1);
+    const uint32_t hi_b = bfi(0x80808080u, sm_b, e_b >> 1);
+    const uint32_t lo_a = bfi(0x80808080u, e_a << 7, sm_a);
+    const uint32_t lo_b = bfi(0x80808080u, e_b << 7, sm_b);
     out[0] = perm(hi_a, lo_a, 0x05010400u);
     out[1] = perm(hi_a, lo_a, 0x07030602u);
     out[2] = perm(hi_b, lo_b, 0x05010400u);

@@ -3,11 +3,12 @@
 //
 // The pages call the format lossless (AI Radar summary of SpecPilot, English
 // edition, "Reasons"; HotRepo digest of StargazerX0/SpecPilot, project
-// introduction).  W12-v1 stores 16 exponents per group; an element outside
-// them is written to the planes as the window floor (the group is flagged)
-// and, here, also as one exception entry (format in w12.h): tile-grouped,
-// in the order the tiled layout stores the weights (group, piece, dword,
-// element).  Three launches build the list: a count per (tile, group) block,
+// introduction).  Each allocation stores 16 exponents per group (W12-v1:
+// {0, 1} and 14 above an even base; W12-b: {0} and 15 above any base); an
+// element outside them is written to the planes as the window floor (the
+// group is flagged) and, here, also as one exception entry (format in
+// w12.h): tile-grouped, in the order the tiled layout stores the weights
+// (group, piece, dword, element).  Three launches build the list: a count per (tile, group) block,
 // one scan over the blocks, and a write pass in which each wave places its
 // block's entries at the scanned offset, lanes in piece order.
 #include <hip/hip_runtime.h>
@@ -34,6 +35,7 @@ struct LaneWeights {
     int64_t kbase;  // k of bit 0: 128 g + 8 q
 };
 
+template <int FMT>
 __device__ __forceinline__ LaneWeights lane_weights(const uint16_t* __restrict__ w, int64_t N,
                                                     int64_t K, int64_t blk, int lane) {
     LaneWeights r;
@@ -61,15 +63,20 @@ __device__ __forceinline__ LaneWeights lane_weights(const uint16_t* __restrict__
     }
     emax = max_u32(emax, (uint32_t)__shfl_xor((int)emax, 16));
     emax = max_u32(emax, (uint32_t)__shfl_xor((int)emax, 32));
-    const uint32_t beta = emax <= 15u ? 0u : (emax - 14u) >> 1;
-    const uint32_t floor_e = 2u * beta + 2u;
+    // the group base and the lowest stored normal exponent: W12-v1
+    // [2 beta + 2, 2 beta + 15] (E <= 1 always stored), W12-b [b + 1, b + 15]
+    // (E = 0 always stored)
+    const uint32_t beta = FMT == kFmtB ? (emax <= 15u ? 0u : emax - 15u)
+                                       : (emax <= 15u ? 0u : (emax - 14u) >> 1);
+    const uint32_t floor_e = FMT == kFmtB ? beta + 1u : 2u * beta + 2u;
+    const uint32_t low_e = FMT == kFmtB ? 1u : 2u;
     r.beta = beta;
     r.mask = 0;
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
         const uint32_t word = (r.v[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
         const uint32_t ex = (word >> 7) & 0xFFu;
-        if (ex >= 2u && ex < floor_e) r.mask |= 1u << i;
+        if (ex >= low_e && ex < floor_e) r.mask |= 1u << i;
     }
     return r;
 }
@@ -85,13 +92,14 @@ __device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
     return v;
 }
 
+template <int FMT>
 __global__ __launch_bounds__(kThreads) void exc_count_kernel(const uint16_t* __restrict__ w, int64_t N,
                                                              int64_t K, int64_t nblocks,
                                                              uint32_t* __restrict__ cnt) {
     const int64_t blk = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
     if (blk >= nblocks) return;  // whole waves only
     const int lane = threadIdx.x & 63;
-    const LaneWeights r = lane_weights(w, N, K, blk, lane);
+    const LaneWeights r = lane_weights<FMT>(w, N, K, blk, lane);
     const uint32_t total = wave_sum((uint32_t)__popc(r.mask));
     if (lane == 0) cnt[blk] = total;
 }
@@ -132,6 +140,7 @@ __global__ __launch_bounds__(kScanThreads) void exc_scan_kernel(uint32_t* __rest
     }
 }
 
+template <int FMT>
 __global__ __launch_bounds__(kThreads) void exc_write_kernel(const uint16_t* __restrict__ w, int64_t N,
                                                              int64_t K, int64_t nblocks,
                                                              const uint32_t* __restrict__ off,
@@ -140,7 +149,7 @@ __global__ __launch_bounds__(kThreads) void exc_write_kernel(const uint16_t* __r
     const int64_t blk = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
     if (blk >= nblocks) return;
     const int lane = threadIdx.x & 63;
-    const LaneWeights r = lane_weights(w, N, K, blk, lane);
+    const LaneWeights r = lane_weights<FMT>(w, N, K, blk, lane);
     // Exclusive prefix of the lane counts in lane (= piece) order.
     const uint32_t mine = (uint32_t)__popc(r.mask);
     uint32_t incl = mine;
@@ -179,20 +188,28 @@ __global__ __launch_bounds__(kThreads) void exc_apply_kernel(const uint32_t* __r
     }
 }
 
-}  // namespace
-
-hipError_t launch_exceptions(const uint16_t* w, int64_t N, int64_t K, uint32_t* ws,
-                             uint32_t* offsets, uint32_t* entries, int64_t capacity,
-                             uint32_t* total, hipStream_t s) {
+template <int FMT>
+hipError_t exceptions_fmt(const uint16_t* w, int64_t N, int64_t K, uint32_t* ws, uint32_t* offsets,
+                          uint32_t* entries, int64_t capacity, uint32_t* total, hipStream_t s) {
     const int64_t nb = (N + 15) / 16 * (K / 128);
     const int64_t grid = (nb + 3) / 4;
-    hipLaunchKernelGGL(exc_count_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, w, N, K, nb, ws);
+    hipLaunchKernelGGL(exc_count_kernel<FMT>, dim3((unsigned)grid), dim3(kThreads), 0, s, w, N, K,
+                       nb, ws);
     hipLaunchKernelGGL(exc_scan_kernel, dim3(1), dim3(kScanThreads), 0, s, ws, nb, K / 128, offsets,
                        total);
     if (entries != nullptr && capacity > 0)
-        hipLaunchKernelGGL(exc_write_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, w, N, K, nb,
-                           ws, entries, capacity);
+        hipLaunchKernelGGL(exc_write_kernel<FMT>, dim3((unsigned)grid), dim3(kThreads), 0, s, w, N,
+                           K, nb, ws, entries, capacity);
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_exceptions(int fmt, const uint16_t* w, int64_t N, int64_t K, uint32_t* ws,
+                             uint32_t* offsets, uint32_t* entries, int64_t capacity,
+                             uint32_t* total, hipStream_t s) {
+    return fmt == kFmtB ? exceptions_fmt<kFmtB>(w, N, K, ws, offsets, entries, capacity, total, s)
+                        : exceptions_fmt<kFmtV1>(w, N, K, ws, offsets, entries, capacity, total, s);
 }
 
 hipError_t launch_apply_exceptions(const uint32_t* offsets, const uint32_t* entries, int64_t N,

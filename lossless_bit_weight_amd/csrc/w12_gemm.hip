@@ -10,25 +10,25 @@
 
 namespace w12 {
 
-hipError_t launch_gemv_m1(const GemmArgs&, const Tiling&, bool, hipStream_t);
-hipError_t launch_gemv_m2(const GemmArgs&, const Tiling&, bool, hipStream_t);
-hipError_t launch_gemv_m3(const GemmArgs&, const Tiling&, bool, hipStream_t);
-hipError_t launch_gemv_m4(const GemmArgs&, const Tiling&, bool, hipStream_t);
-hipError_t launch_gemv_m5(const GemmArgs&, const Tiling&, bool, hipStream_t);
-hipError_t launch_gemv_m6(const GemmArgs&, const Tiling&, bool, hipStream_t);
-hipError_t launch_gemv_m7(const GemmArgs&, const Tiling&, bool, hipStream_t);
-hipError_t launch_gemv_m8(const GemmArgs&, const Tiling&, bool, hipStream_t);
+hipError_t launch_gemv_m1(const GemmArgs&, const Tiling&, int, hipStream_t);
+hipError_t launch_gemv_m2(const GemmArgs&, const Tiling&, int, hipStream_t);
+hipError_t launch_gemv_m3(const GemmArgs&, const Tiling&, int, hipStream_t);
+hipError_t launch_gemv_m4(const GemmArgs&, const Tiling&, int, hipStream_t);
+hipError_t launch_gemv_m5(const GemmArgs&, const Tiling&, int, hipStream_t);
+hipError_t launch_gemv_m6(const GemmArgs&, const Tiling&, int, hipStream_t);
+hipError_t launch_gemv_m7(const GemmArgs&, const Tiling&, int, hipStream_t);
+hipError_t launch_gemv_m8(const GemmArgs&, const Tiling&, int, hipStream_t);
 
-hipError_t launch_gemv_m(int M, const GemmArgs& a, const Tiling& t, bool is_w12, hipStream_t s) {
+hipError_t launch_gemv_m(int M, const GemmArgs& a, const Tiling& t, int fetch, hipStream_t s) {
     switch (M) {
-        case 1: return launch_gemv_m1(a, t, is_w12, s);
-        case 2: return launch_gemv_m2(a, t, is_w12, s);
-        case 3: return launch_gemv_m3(a, t, is_w12, s);
-        case 4: return launch_gemv_m4(a, t, is_w12, s);
-        case 5: return launch_gemv_m5(a, t, is_w12, s);
-        case 6: return launch_gemv_m6(a, t, is_w12, s);
-        case 7: return launch_gemv_m7(a, t, is_w12, s);
-        case 8: return launch_gemv_m8(a, t, is_w12, s);
+        case 1: return launch_gemv_m1(a, t, fetch, s);
+        case 2: return launch_gemv_m2(a, t, fetch, s);
+        case 3: return launch_gemv_m3(a, t, fetch, s);
+        case 4: return launch_gemv_m4(a, t, fetch, s);
+        case 5: return launch_gemv_m5(a, t, fetch, s);
+        case 6: return launch_gemv_m6(a, t, fetch, s);
+        case 7: return launch_gemv_m7(a, t, fetch, s);
+        case 8: return launch_gemv_m8(a, t, fetch, s);
         default: return hipErrorInvalidValue;
     }
 }
@@ -199,10 +199,10 @@ Tiling choose_tiling(int M, int64_t N, int64_t K, bool allow_splitk) {
     return t;
 }
 
-const char* tiling_name(const Tiling& t, bool is_w12) {
+const char* tiling_name(const Tiling& t, int fetch) {
     static std::mutex mu;
     static std::unordered_set<std::string> names;  // node-based: c_str() stays valid
-    std::string n = is_w12 ? "w12_" : "bf16_";
+    std::string n = fetch == kFetchW12 ? "w12_" : fetch == kFetchW12B ? "w12b_" : "bf16_";
     n += t.mfma ? "mfma_mt" : "gemv_m";
     n += std::to_string(t.mt) + "_r" + std::to_string(t.r) + "_kw" + std::to_string(t.kw) + "_d" +
          std::to_string(t.depth) + (t.xdirect ? "_xdirect" : t.chunked ? "_chunked" : "_single");
@@ -212,9 +212,10 @@ const char* tiling_name(const Tiling& t, bool is_w12) {
     return names.insert(std::move(n)).first->c_str();
 }
 
-hipError_t launch_gemm(const GemmArgs& a, const Tiling& t, bool is_w12, hipStream_t s) {
-    if (t.mfma) return t.nw == 8 ? launch_mfma8_mt(t.mt, a, t, is_w12, s) : launch_mfma_mt(t.mt, a, t, is_w12, s);
-    return launch_gemv_m(t.mt, a, t, is_w12, s);
+hipError_t launch_gemm(const GemmArgs& a, const Tiling& t, int fetch, hipStream_t s) {
+    if (t.mfma)
+        return t.nw == 8 ? launch_mfma8_mt(t.mt, a, t, fetch, s) : launch_mfma_mt(t.mt, a, t, fetch, s);
+    return launch_gemv_m(t.mt, a, t, fetch, s);
 }
 
 }  // namespace w12

@@ -1,7 +1,9 @@
 // w12_gemm_inst.hip -- instantiates the GEMM kernel templates for one x
 // height, chosen at compile time (-DW12_INST_M=1..8 for the GEMV, or
-// -DW12_INST_MFMA for the 16- and 32-row MFMA tiles).  One object file per
-// height keeps the build parallel.
+// -DW12_INST_MFMA / -DW12_INST_MFMA8 for the 16- and 32-row MFMA tiles in
+// 256- and 512-thread workgroups), for the three weight fetches (BF16
+// control, W12-v1, W12-b).  One object file per height keeps the build
+// parallel.
 #include "w12_gemm_kernels.hpp"
 
 namespace w12 {
@@ -9,28 +11,43 @@ namespace w12 {
 #if defined(W12_INST_M)
 #define W12_CAT2(a, b) a##b
 #define W12_CAT(a, b) W12_CAT2(a, b)
-hipError_t W12_CAT(launch_gemv_m, W12_INST_M)(const GemmArgs& a, const Tiling& t, bool is_w12,
+hipError_t W12_CAT(launch_gemv_m, W12_INST_M)(const GemmArgs& a, const Tiling& t, int fetch,
                                               hipStream_t s) {
-    return is_w12 ? kern::dispatch<kern::FetchW12, false, W12_INST_M>(a, t, s)
-                  : kern::dispatch<kern::FetchBF16, false, W12_INST_M>(a, t, s);
+    switch (fetch) {
+        case kFetchW12: return kern::dispatch<kern::FetchW12, false, W12_INST_M>(a, t, s);
+        case kFetchW12B: return kern::dispatch<kern::FetchW12B, false, W12_INST_M>(a, t, s);
+        default: return kern::dispatch<kern::FetchBF16, false, W12_INST_M>(a, t, s);
+    }
 }
 #elif defined(W12_INST_MFMA)
-hipError_t launch_mfma_mt(int MT, const GemmArgs& a, const Tiling& t, bool is_w12, hipStream_t s) {
+template <int MT>
+static hipError_t mfma_fetch(const GemmArgs& a, const Tiling& t, int fetch, hipStream_t s) {
+    switch (fetch) {
+        case kFetchW12: return kern::dispatch<kern::FetchW12, true, MT>(a, t, s);
+        case kFetchW12B: return kern::dispatch<kern::FetchW12B, true, MT>(a, t, s);
+        default: return kern::dispatch<kern::FetchBF16, true, MT>(a, t, s);
+    }
+}
+hipError_t launch_mfma_mt(int MT, const GemmArgs& a, const Tiling& t, int fetch, hipStream_t s) {
     switch (MT) {
-        case 16: return is_w12 ? kern::dispatch<kern::FetchW12, true, 16>(a, t, s)
-                               : kern::dispatch<kern::FetchBF16, true, 16>(a, t, s);
-        case 32: return is_w12 ? kern::dispatch<kern::FetchW12, true, 32>(a, t, s)
-                               : kern::dispatch<kern::FetchBF16, true, 32>(a, t, s);
+        case 16: return mfma_fetch<16>(a, t, fetch, s);
+        case 32: return mfma_fetch<32>(a, t, fetch, s);
         default: return hipErrorInvalidValue;
     }
 }
 #elif defined(W12_INST_MFMA8)
-hipError_t launch_mfma8_mt(int MT, const GemmArgs& a, const Tiling& t, bool is_w12, hipStream_t s) {
+template <int MT>
+static hipError_t mfma8_fetch(const GemmArgs& a, const Tiling& t, int fetch, hipStream_t s) {
+    switch (fetch) {
+        case kFetchW12: return kern::dispatch8<kern::FetchW12, MT>(a, t, s);
+        case kFetchW12B: return kern::dispatch8<kern::FetchW12B, MT>(a, t, s);
+        default: return kern::dispatch8<kern::FetchBF16, MT>(a, t, s);
+    }
+}
+hipError_t launch_mfma8_mt(int MT, const GemmArgs& a, const Tiling& t, int fetch, hipStream_t s) {
     switch (MT) {
-        case 16: return is_w12 ? kern::dispatch8<kern::FetchW12, 16>(a, t, s)
-                               : kern::dispatch8<kern::FetchBF16, 16>(a, t, s);
-        case 32: return is_w12 ? kern::dispatch8<kern::FetchW12, 32>(a, t, s)
-                               : kern::dispatch8<kern::FetchBF16, 32>(a, t, s);
+        case 16: return mfma8_fetch<16>(a, t, fetch, s);
+        case 32: return mfma8_fetch<32>(a, t, fetch, s);
         default: return hipErrorInvalidValue;
     }
 }

@@ -145,8 +145,8 @@ __device__ __forceinline__ void split_finish(const GemmArgs& g) {
 }
 
 // Exception corrections (W12 containers with an exception list): the main
-// loop multiplied each exception element's stored clamp (sign | window floor
-// 2^(2 beta + 2 - 127)); for every entry of `tile` whose group lies in this
+// loop multiplied each exception element's stored clamp (sign | window floor:
+// 2^(2 beta + 2 - 127) in W12-v1, 2^(b + 1 - 127) in W12-b); for every entry of `tile` whose group lies in this
 // workgroup's K slice [g0, g0 + gn), the sum first takes back x[m][k] * clamp
 // and then adds x[m][k] * original (two fused multiply-adds; a precomputed
 // difference would round away originals far below the clamp).
@@ -165,8 +165,9 @@ struct ExcStage {
 };
 
 // apply(j, orig, clamp, xs) runs on the lanes of entry j's row; xs(m) reads
-// that entry's x[m][k] from LDS.
-template <int XR, class Apply>
+// that entry's x[m][k] from LDS.  F::clamp_word(entry word 1) gives the
+// BF16 clamp the planes hold for the entry.
+template <class F, int XR, class Apply>
 __device__ __forceinline__ void exc_corrections(const GemmArgs& g, int64_t tile, int g0, int gn,
                                                 int lane, int col, uint8_t* area, Apply apply) {
     float* orig = reinterpret_cast<float*>(area + 256);
@@ -186,7 +187,7 @@ __device__ __forceinline__ void exc_corrections(const GemmArgs& g, int64_t tile,
             if (grp >= g0 && grp < g0 + gn) {
                 c = (int)(pos >> 24);
                 o = bf16_to_f32(val & 0xFFFFu);
-                cl = bf16_to_f32((val & 0x8000u) | ((2u * ((val >> 16) & 0x7Fu) + 2u) << 7));
+                cl = bf16_to_f32(F::clamp_word(val));
             }
         }
         orig[lane] = o;
@@ -284,6 +285,26 @@ struct FetchW12 {
         const uint32_t pb = b == 0 ? r.b.x : b == 1 ? r.b.y : b == 2 ? r.b.z : r.b.w;
         const uint32_t pc = b == 0 ? r.c.x : b == 1 ? r.c.y : b == 2 ? r.c.z : r.c.w;
         decode8(pa, pb, pc, t, out);
+    }
+    // Exception entry word 1 = beta << 16 | original: the clamp is the
+    // window floor 2^(2 beta + 2 - 127) with the original's sign.
+    __device__ __forceinline__ static uint32_t clamp_word(uint32_t val) {
+        return (val & 0x8000u) | ((2u * ((val >> 16) & 0x7Fu) + 2u) << 7);
+    }
+};
+
+// The arbitrary-base allocation W12-b: same planes and loads, the meta byte
+// is the base b itself (0..240), decode8b rebuilds E = b + c.
+struct FetchW12B : FetchW12 {
+    __device__ __forceinline__ static void block(const Raw& r, int b, uint32_t out[4]) {
+        const uint32_t pa = b == 0 ? r.a.x : b == 1 ? r.a.y : b == 2 ? r.a.z : r.a.w;
+        const uint32_t pb = b == 0 ? r.b.x : b == 1 ? r.b.y : b == 2 ? r.b.z : r.b.w;
+        const uint32_t pc = b == 0 ? r.c.x : b == 1 ? r.c.y : b == 2 ? r.c.z : r.c.w;
+        decode8b(pa, pb, pc, (r.beta & 0xFFu) * 0x01010101u, out);
+    }
+    // Entry word 1 = b << 16 | original: the clamp is 2^(b + 1 - 127).
+    __device__ __forceinline__ static uint32_t clamp_word(uint32_t val) {
+        return (val & 0x8000u) | ((((val >> 16) & 0xFFu) + 1u) << 7);
     }
 };
 
@@ -752,7 +773,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs g) {
 #pragma unroll
                 for (int r = 0; r < R; ++r) {
                     if (tile0 + r >= ntiles) continue;
-                    exc_corrections<16 * kMT>(g, tile0 + r, g0, gn, lane, col, area,
+                    exc_corrections<F, 16 * kMT>(g, tile0 + r, g0, gn, lane, col, area,
                                               [&](float orig, float clamp, auto xs) {
 #pragma unroll
                         for (int mt = 0; mt < kMT; ++mt)
@@ -819,7 +840,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs g) {
 #pragma unroll
                 for (int r = 0; r < R; ++r) {
                     if (tile0 + r >= ntiles) continue;
-                    exc_corrections<MR>(g, tile0 + r, g0, gn, lane, col, area,
+                    exc_corrections<F, MR>(g, tile0 + r, g0, gn, lane, col, area,
                                         [&](float orig, float clamp, auto xs) {
 #pragma unroll
                         for (int m = 0; m < MR; ++m) {

@@ -6,6 +6,13 @@
 
 namespace w12 {
 
+// Bit allocations of the planes: W12-v1 (3-bit offset of E[7:1] from an
+// even base, low byte verbatim) and W12-b (4-bit offset of E from a base of
+// any value).
+enum Format { kFmtV1 = 0, kFmtB = 1 };
+// Weight fetch of a GEMM launch: the BF16 control or a W12 container.
+enum Fetch { kFetchBF16 = 0, kFetchW12 = 1, kFetchW12B = 2 };
+
 // Everything a GEMM launch needs.  Exactly one of {p0,p1,p2,meta} (W12
 // container) or w (plain BF16) is used, by the weight-fetch policy.
 struct GemmArgs {
@@ -81,7 +88,7 @@ Tiling choose_tiling(int M, int64_t N, int64_t K, bool allow_splitk);
 // false if the combination is not built (or splits K over more than
 // kMaxSplitRowBlocks row blocks).
 bool complete_tiling(Tiling& t, int M, int64_t N, int64_t K);
-const char* tiling_name(const Tiling& t, bool is_w12);
+const char* tiling_name(const Tiling& t, int fetch);
 // Workgroups along N (grid x) of a launch with this tiling.
 int64_t row_blocks(const Tiling& t, int64_t N);
 // Workspace a completed tiling needs: 0 without split-K, else the counter
@@ -90,19 +97,19 @@ size_t workspace_bytes(const Tiling& t, int M, int64_t N);
 // Point the split-K fields of `a` at `ws` (which holds workspace_bytes).
 void bind_split(GemmArgs& a, const Tiling& t, void* ws);
 
-hipError_t launch_gemm(const GemmArgs& a, const Tiling& t, bool is_w12, hipStream_t s);
+hipError_t launch_gemm(const GemmArgs& a, const Tiling& t, int fetch, hipStream_t s);
 // Per-M (GEMV) and per-MT (MFMA) launchers, one object file each.
-hipError_t launch_gemv_m(int M, const GemmArgs& a, const Tiling& t, bool is_w12, hipStream_t s);
-hipError_t launch_mfma_mt(int MT, const GemmArgs& a, const Tiling& t, bool is_w12, hipStream_t s);
-hipError_t launch_mfma8_mt(int MT, const GemmArgs& a, const Tiling& t, bool is_w12, hipStream_t s);
-hipError_t launch_pack(const uint16_t* w, int64_t N, int64_t K, void* p0, void* p1,
+hipError_t launch_gemv_m(int M, const GemmArgs& a, const Tiling& t, int fetch, hipStream_t s);
+hipError_t launch_mfma_mt(int MT, const GemmArgs& a, const Tiling& t, int fetch, hipStream_t s);
+hipError_t launch_mfma8_mt(int MT, const GemmArgs& a, const Tiling& t, int fetch, hipStream_t s);
+hipError_t launch_pack(int fmt, const uint16_t* w, int64_t N, int64_t K, void* p0, void* p1,
                        void* p2, uint8_t* meta, uint32_t* bad, hipStream_t s);
-hipError_t launch_unpack(const void* p0, const void* p1, const void* p2,
+hipError_t launch_unpack(int fmt, const void* p0, const void* p1, const void* p2,
                          const uint8_t* meta, int64_t N, int64_t K, uint16_t* w,
                          hipStream_t s);
 // Exception list: count per block into ws (nblocks words), scan, write the
 // tile offsets, the total and at most `capacity` entries.
-hipError_t launch_exceptions(const uint16_t* w, int64_t N, int64_t K, uint32_t* ws,
+hipError_t launch_exceptions(int fmt, const uint16_t* w, int64_t N, int64_t K, uint32_t* ws,
                              uint32_t* offsets, uint32_t* entries, int64_t capacity,
                              uint32_t* total, hipStream_t s);
 // Write the exceptions' original words over an unpacked [N, K] weight.

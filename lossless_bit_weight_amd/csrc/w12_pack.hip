@@ -1,5 +1,6 @@
-// w12_pack.hip -- W12-v1 encoder (pack), streaming decoder (unpack) and the
-// BF16 control layout (bf16_tile).
+// w12_pack.hip -- W12 encoders (pack), streaming decoders (unpack) for both
+// bit allocations (W12-v1 and the arbitrary-base W12-b), and the BF16
+// control layout (bf16_tile).
 //
 // Format: see w12.h.  The pages say only that BF16 is split into three 4-bit
 // planes and that the format is lossless (AI Radar summary of SpecPilot,
@@ -23,6 +24,7 @@ constexpr int kThreads = 256;
 
 __device__ __forceinline__ uint32_t max_u32(uint32_t a, uint32_t b) { return a > b ? a : b; }
 
+template <int FMT>
 __global__ __launch_bounds__(kThreads) void pack_kernel(const uint16_t* __restrict__ w, int64_t N,
                                                         int64_t K, int64_t nblocks,
                                                         uint4* __restrict__ p0,
@@ -60,10 +62,15 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(const uint16_t* __restri
     }
     emax = max_u32(emax, (uint32_t)__shfl_xor((int)emax, 16));
     emax = max_u32(emax, (uint32_t)__shfl_xor((int)emax, 32));
-    const uint32_t beta = emax <= 15u ? 0u : (emax - 14u) >> 1;
-    const uint32_t floor_e = 2u * beta + 2u;
+    // W12-v1: even base 2 beta, window [2 beta + 2, 2 beta + 15] plus E <= 1.
+    // W12-b: base b, window [b + 1, b + 15] plus E = 0.
+    const uint32_t beta = FMT == kFmtB ? (emax <= 15u ? 0u : emax - 15u)
+                                       : (emax <= 15u ? 0u : (emax - 14u) >> 1);
+    const uint32_t floor_e = FMT == kFmtB ? beta + 1u : 2u * beta + 2u;
 
-    // Per weight: low byte kept, high byte -> sign<<3 | h.
+    // Per weight: lo = the byte that becomes planes P1:P0, code = the P2
+    // nibble.  W12-v1: the BF16 low byte and sign<<3 | h.  W12-b: sign<<7 |
+    // mantissa and the exponent offset c.
     uint32_t lo[32], code[32];
     uint32_t bad = 0;
 #pragma unroll
@@ -71,19 +78,35 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(const uint16_t* __restri
         const uint32_t word = (v[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
         const uint32_t ex = (word >> 7) & 0xFFu;
         const uint32_t s = word >> 15;
-        uint32_t l = word & 0xFFu;
-        uint32_t h;
-        if (ex <= 1u) {
-            h = 0u;
-        } else if (ex >= floor_e) {
-            h = (ex >> 1) - beta;
-        } else {  // below the window: store the window floor, flag the group
-            h = 1u;
-            l = 0u;
-            bad = 1u;
+        if constexpr (FMT == kFmtB) {
+            uint32_t m = word & 0x7Fu;
+            uint32_t c;
+            if (ex == 0u) {
+                c = 0u;
+            } else if (ex >= floor_e) {
+                c = ex - beta;
+            } else {  // below the window: store the window floor, flag the group
+                c = 1u;
+                m = 0u;
+                bad = 1u;
+            }
+            lo[i] = (s << 7) | m;
+            code[i] = c;
+        } else {
+            uint32_t l = word & 0xFFu;
+            uint32_t h;
+            if (ex <= 1u) {
+                h = 0u;
+            } else if (ex >= floor_e) {
+                h = (ex >> 1) - beta;
+            } else {  // below the window: store the window floor, flag the group
+                h = 1u;
+                l = 0u;
+                bad = 1u;
+            }
+            lo[i] = l;
+            code[i] = (s << 3) | h;
         }
-        lo[i] = l;
-        code[i] = (s << 3) | h;
     }
 
     // Split-nibble order: dword b holds weights 8b..8b+7 of the lane; byte j
@@ -109,7 +132,8 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(const uint16_t* __restri
     p0[blk * 64 + lane] = make_uint4(o0[0], o0[1], o0[2], o0[3]);
     p1[blk * 64 + lane] = make_uint4(o1[0], o1[1], o1[2], o1[3]);
     p2[blk * 64 + lane] = make_uint4(o2[0], o2[1], o2[2], o2[3]);
-    if (q == 0) meta[blk * 16 + c] = (uint8_t)(beta | (bad << 7));
+    // W12-b's base needs all 8 bits: its groups are flagged through the count
+    if (q == 0) meta[blk * 16 + c] = (uint8_t)(FMT == kFmtB ? beta : (beta | (bad << 7)));
 
     // One atomic per wave: the flagged groups of this block.
     const uint64_t flagged = __ballot(q == 0 && valid && bad);
@@ -117,6 +141,7 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(const uint16_t* __restri
         atomicAdd(bad_count, (uint32_t)__popcll(flagged));
 }
 
+template <int FMT>
 __global__ __launch_bounds__(kThreads) void unpack_kernel(const uint4* __restrict__ p0,
                                                           const uint4* __restrict__ p1,
                                                           const uint4* __restrict__ p2,
@@ -132,7 +157,9 @@ __global__ __launch_bounds__(kThreads) void unpack_kernel(const uint4* __restric
     const int64_t n = (blk / G) * 16 + c;
     const int64_t g = blk % G;
     const uint4 a = p0[blk * 64 + lane], b4 = p1[blk * 64 + lane], c4 = p2[blk * 64 + lane];
-    const Lut t = make_lut(meta[blk * 16 + c] & 0x7Fu);
+    const uint32_t mb = meta[blk * 16 + c];
+    const Lut t = make_lut(mb & 0x7Fu);
+    const uint32_t base4 = mb * 0x01010101u;
     if (n >= N) return;
     const uint32_t pa[4] = {a.x, a.y, a.z, a.w};
     const uint32_t pb[4] = {b4.x, b4.y, b4.z, b4.w};
@@ -140,7 +167,10 @@ __global__ __launch_bounds__(kThreads) void unpack_kernel(const uint4* __restric
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
         uint32_t o[4];
-        decode8(pa[b], pb[b], pc[b], t, o);
+        if constexpr (FMT == kFmtB)
+            decode8b(pa[b], pb[b], pc[b], base4, o);
+        else
+            decode8(pa[b], pb[b], pc[b], t, o);
         *reinterpret_cast<uint4*>(w + n * K + 128 * g + 32 * b + 8 * q) = make_uint4(o[0], o[1], o[2], o[3]);
     }
 }
@@ -170,23 +200,33 @@ int64_t blocks_of(int64_t N, int64_t K) { return (N + 15) / 16 * (K / 128); }
 
 }  // namespace
 
-hipError_t launch_pack(const uint16_t* w, int64_t N, int64_t K, void* p0, void* p1, void* p2,
-                       uint8_t* meta, uint32_t* bad, hipStream_t s) {
+hipError_t launch_pack(int fmt, const uint16_t* w, int64_t N, int64_t K, void* p0, void* p1,
+                       void* p2, uint8_t* meta, uint32_t* bad, hipStream_t s) {
     const int64_t nb = blocks_of(N, K);
     const int64_t grid = (nb + 3) / 4;
-    hipLaunchKernelGGL(pack_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, w, N, K, nb,
-                       reinterpret_cast<uint4*>(p0), reinterpret_cast<uint4*>(p1),
-                       reinterpret_cast<uint4*>(p2), meta, bad);
+    if (fmt == kFmtB)
+        hipLaunchKernelGGL(pack_kernel<kFmtB>, dim3((unsigned)grid), dim3(kThreads), 0, s, w, N, K,
+                           nb, reinterpret_cast<uint4*>(p0), reinterpret_cast<uint4*>(p1),
+                           reinterpret_cast<uint4*>(p2), meta, bad);
+    else
+        hipLaunchKernelGGL(pack_kernel<kFmtV1>, dim3((unsigned)grid), dim3(kThreads), 0, s, w, N, K,
+                           nb, reinterpret_cast<uint4*>(p0), reinterpret_cast<uint4*>(p1),
+                           reinterpret_cast<uint4*>(p2), meta, bad);
     return hipGetLastError();
 }
 
-hipError_t launch_unpack(const void* p0, const void* p1, const void* p2, const uint8_t* meta,
-                         int64_t N, int64_t K, uint16_t* w, hipStream_t s) {
+hipError_t launch_unpack(int fmt, const void* p0, const void* p1, const void* p2,
+                         const uint8_t* meta, int64_t N, int64_t K, uint16_t* w, hipStream_t s) {
     const int64_t nb = blocks_of(N, K);
     const int64_t grid = (nb + 3) / 4;
-    hipLaunchKernelGGL(unpack_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s,
-                       reinterpret_cast<const uint4*>(p0), reinterpret_cast<const uint4*>(p1),
-                       reinterpret_cast<const uint4*>(p2), meta, N, K, nb, w);
+    if (fmt == kFmtB)
+        hipLaunchKernelGGL(unpack_kernel<kFmtB>, dim3((unsigned)grid), dim3(kThreads), 0, s,
+                           reinterpret_cast<const uint4*>(p0), reinterpret_cast<const uint4*>(p1),
+                           reinterpret_cast<const uint4*>(p2), meta, N, K, nb, w);
+    else
+        hipLaunchKernelGGL(unpack_kernel<kFmtV1>, dim3((unsigned)grid), dim3(kThreads), 0, s,
+                           reinterpret_cast<const uint4*>(p0), reinterpret_cast<const uint4*>(p1),
+                           reinterpret_cast<const uint4*>(p2), meta, N, K, nb, w);
     return hipGetLastError();
 }
 

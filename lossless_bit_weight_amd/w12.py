@@ -142,6 +142,10 @@ def lib() -> ctypes.CDLL:
     L.w12_read_probe.restype = i32
     L.w12_gemm_variant.argtypes = [i64, i64, i64, i32, i32]
     L.w12_gemm_variant.restype = ctypes.c_char_p
+    # W12-b entry points: the W12-v1 signatures
+    for name in ("pack", "unpack", "exceptions", "gemm", "gemm_ws", "gemm_ex"):
+        fb, fv = getattr(L, "w12b_" + name), getattr(L, "w12_" + name)
+        fb.argtypes, fb.restype = fv.argtypes, fv.restype
     _lib = L
     return L
 
@@ -155,6 +159,17 @@ def header_functions() -> list[str]:
 
 
 # ---- marshalling helpers ---------------------------------------------------
+
+# Bit allocations: "v1" (W12-v1) and "b" (W12-b, arbitrary base); the W12-b
+# calls carry a "w12b_" prefix and the W12-v1 signatures.
+FORMATS = ("v1", "b")
+
+
+def _fmt_fn(fmt: str, name: str):
+    if fmt not in FORMATS:
+        raise ValueError("unknown W12 format %r" % (fmt,))
+    return getattr(lib(), name if fmt == "v1" else "w12b_" + name[len("w12_"):]), \
+        (name if fmt == "v1" else "w12b_" + name[len("w12_"):])
 
 _BF16_TYPES = (torch.bfloat16, torch.int16, torch.uint16)
 
@@ -215,9 +230,11 @@ def w12_default_tiling(M: int, N: int, K: int, allow_splitk: bool = True) -> Til
     return t
 
 
-def w12_gemm_variant(M: int, N: int, K: int, is_w12: bool = True,
+def w12_gemm_variant(M: int, N: int, K: int, is_w12: bool | int = True,
                      allow_splitk: bool = True) -> str | None:
-    r = lib().w12_gemm_variant(int(M), int(N), int(K), int(bool(is_w12)), int(bool(allow_splitk)))
+    """Variant name; is_w12: False/0 = BF16 control, True/1 = W12-v1, 2 = W12-b."""
+    fetch = 2 if (not isinstance(is_w12, bool) and int(is_w12) == 2) else int(bool(is_w12))
+    r = lib().w12_gemm_variant(int(M), int(N), int(K), fetch, int(bool(allow_splitk)))
     return None if r is None else r.decode()
 
 
@@ -262,6 +279,7 @@ class W12Weight:
     K: int
     exc_offsets: torch.Tensor | None = None
     exc_entries: torch.Tensor | None = None
+    fmt: str = "v1"     # "v1" (W12-v1) or "b" (W12-b)
 
     @property
     def nbytes(self) -> int:
@@ -288,12 +306,15 @@ class BF16Tiled:
         return 2 * self.w.numel()
 
 
-def empty_weight(N: int, K: int, device="cuda") -> W12Weight:
+def empty_weight(N: int, K: int, device="cuda", fmt: str = "v1") -> W12Weight:
     pb, mb = w12_plane_bytes(N, K), w12_meta_bytes(N, K)
     if pb == 0:
         raise W12Error(-2, "empty_weight(%d, %d)" % (N, K))
+    if fmt not in FORMATS:
+        raise ValueError("unknown W12 format %r" % (fmt,))
     mk = lambda: torch.empty(pb, dtype=torch.uint8, device=device)
-    return W12Weight(mk(), mk(), mk(), torch.empty(mb, dtype=torch.uint8, device=device), N, K)
+    return W12Weight(mk(), mk(), mk(), torch.empty(mb, dtype=torch.uint8, device=device), N, K,
+                     fmt=fmt)
 
 
 def w12_bf16_tile(w: torch.Tensor) -> BF16Tiled:
@@ -312,28 +333,30 @@ def w12_bf16_tile(w: torch.Tensor) -> BF16Tiled:
 
 
 def w12_pack(w: torch.Tensor, out: W12Weight | None = None,
-             bad_groups: torch.Tensor | None = None) -> W12Weight:
-    """Pack BF16 [N, K] (contiguous) into W12.  If `bad_groups` (int32/uint32
-    GPU tensor with one element) is given, the count of unencodable groups is
-    added to it on the stream."""
+             bad_groups: torch.Tensor | None = None, fmt: str = "v1") -> W12Weight:
+    """Pack BF16 [N, K] (contiguous) into W12 (fmt "v1": w12_pack, "b":
+    w12b_pack).  If `bad_groups` (int32/uint32 GPU tensor with one element)
+    is given, the count of unencodable groups is added to it on the
+    stream."""
     w = _bf16_2d(w, "w")
     if not w.is_contiguous():
         raise ValueError("w must be contiguous")
     N, K = w.shape
     if out is None:
-        out = empty_weight(N, K, w.device)
+        out = empty_weight(N, K, w.device, fmt)
+    out.fmt = fmt
     bad_ptr = None
     if bad_groups is not None:
         if bad_groups.dtype not in (torch.int32, torch.uint32) or bad_groups.numel() < 1:
             raise TypeError("bad_groups must be a 32-bit integer GPU tensor")
         bad_ptr = _dev_ptr(bad_groups, "bad_groups")
-    _check(lib().w12_pack(_dev_ptr(w, "w"), N, K, _dev_ptr(out.p0, "p0"), _dev_ptr(out.p1, "p1"),
-                          _dev_ptr(out.p2, "p2"), _dev_ptr(out.meta, "meta"), bad_ptr, _stream()),
-           "w12_pack")
+    fn, name = _fmt_fn(fmt, "w12_pack")
+    _check(fn(_dev_ptr(w, "w"), N, K, _dev_ptr(out.p0, "p0"), _dev_ptr(out.p1, "p1"),
+              _dev_ptr(out.p2, "p2"), _dev_ptr(out.meta, "meta"), bad_ptr, _stream()), name)
     return out
 
 
-def w12_exceptions(w: torch.Tensor) -> tuple[torch.Tensor, torch.Tensor]:
+def w12_exceptions(w: torch.Tensor, fmt: str = "v1") -> tuple[torch.Tensor, torch.Tensor]:
     """The exception list of BF16 [N, K] (contiguous): (tile offsets,
     entries [count, 2]) as int32 tensors.  Counts first, reads the count
     (a stream synchronisation), then writes the entries."""
@@ -348,29 +371,30 @@ def w12_exceptions(w: torch.Tensor) -> tuple[torch.Tensor, torch.Tensor]:
     off = torch.empty(w12_padded_rows(N) // 16 + 1, dtype=torch.int32, device=w.device)
     total = torch.zeros(1, dtype=torch.int32, device=w.device)
     args = (_dev_ptr(w, "w"), N, K, _dev_ptr(ws, "workspace"), wsb, _dev_ptr(off, "exc_offsets"))
-    _check(lib().w12_exceptions(*args, None, 0, _dev_ptr(total, "total"), _stream()), "w12_exceptions")
+    fn, name = _fmt_fn(fmt, "w12_exceptions")
+    _check(fn(*args, None, 0, _dev_ptr(total, "total"), _stream()), name)
     count = int(total.item())
     ent = torch.empty((max(count, 1), 2), dtype=torch.int32, device=w.device)
     if count:
-        _check(lib().w12_exceptions(*args, _dev_ptr(ent, "exc_entries"), count,
-                                    _dev_ptr(total, "total"), _stream()), "w12_exceptions")
+        _check(fn(*args, _dev_ptr(ent, "exc_entries"), count, _dev_ptr(total, "total"), _stream()),
+               name)
     return off, ent
 
 
-def pack(w: torch.Tensor, strict: bool = False,
-         exceptions: bool = False) -> tuple[W12Weight, int]:
+def pack(w: torch.Tensor, strict: bool = False, exceptions: bool = False,
+         fmt: str = "v1") -> tuple[W12Weight, int]:
     """Pack and return (container, number of unencodable groups).  Reading the
     count synchronises the stream; with strict=True a non-zero count raises;
     with exceptions=True a container with unencodable groups also gets its
-    exception list, which makes it lossless."""
+    exception list, which makes it lossless.  fmt: "v1" or "b"."""
     bad = torch.zeros(1, dtype=torch.int32, device=w.device)
-    out = w12_pack(w, bad_groups=bad)
+    out = w12_pack(w, bad_groups=bad, fmt=fmt)
     n_bad = int(bad.item())
     if strict and n_bad:
         raise W12UnencodableError("%d of %d groups cannot be stored losslessly"
                                   % (n_bad, w.numel() // GROUP))
     if exceptions and n_bad:
-        out.exc_offsets, out.exc_entries = w12_exceptions(w)
+        out.exc_offsets, out.exc_entries = w12_exceptions(w, fmt)
     return out, n_bad
 
 
@@ -379,10 +403,10 @@ def w12_unpack(wt: W12Weight, out: torch.Tensor | None = None) -> torch.Tensor:
     if out is None:
         out = torch.empty((wt.N, wt.K), dtype=torch.bfloat16, device=wt.p0.device)
     _bf16_2d(out, "out")
-    _check(lib().w12_unpack(_dev_ptr(wt.p0, "p0"), _dev_ptr(wt.p1, "p1"), _dev_ptr(wt.p2, "p2"),
-                            _dev_ptr(wt.meta, "meta"), *wt.exc_ptrs(), wt.N, wt.K,
-                            _dev_ptr(out, "out"), _stream()),
-           "w12_unpack")
+    fn, name = _fmt_fn(wt.fmt, "w12_unpack")
+    _check(fn(_dev_ptr(wt.p0, "p0"), _dev_ptr(wt.p1, "p1"), _dev_ptr(wt.p2, "p2"),
+              _dev_ptr(wt.meta, "meta"), *wt.exc_ptrs(), wt.N, wt.K, _dev_ptr(out, "out"),
+              _stream()), name)
     return out
 
 
@@ -443,11 +467,14 @@ def w12_gemm(x: torch.Tensor, wt: W12Weight, out_dtype: torch.dtype = torch.floa
             _dev_ptr(y, "y"), ldy, yt)
     wsp, wsb = _ws_args(M, wt.N, wt.K, tiling, split_k, workspace)
     if tiling is not None:
-        _check(lib().w12_gemm_ex(*args, _tiling_arg(tiling), wsp, wsb, _stream()), "w12_gemm_ex")
+        fn, name = _fmt_fn(wt.fmt, "w12_gemm_ex")
+        _check(fn(*args, _tiling_arg(tiling), wsp, wsb, _stream()), name)
     elif split_k:
-        _check(lib().w12_gemm_ws(*args, wsp, wsb, _stream()), "w12_gemm_ws")
+        fn, name = _fmt_fn(wt.fmt, "w12_gemm_ws")
+        _check(fn(*args, wsp, wsb, _stream()), name)
     else:
-        _check(lib().w12_gemm(*args, _stream()), "w12_gemm")
+        fn, name = _fmt_fn(wt.fmt, "w12_gemm")
+        _check(fn(*args, _stream()), name)
     return y
 
 

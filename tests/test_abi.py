@@ -21,7 +21,7 @@ def test_loads_and_exports_every_declared_symbol():
                           "w12_exceptions", "w12_exceptions_workspace_bytes"}
     for n in names:
         assert hasattr(L, n), n
-    assert w12.w12_abi_version() == 5
+    assert w12.w12_abi_version() == 6
 
 
 def test_sizes():
