@@ -67,6 +67,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU-oracle work to time")
     ap.add_argument("--sweep-ms", type=str, default="1,2,4,8,16,32")
+    ap.add_argument("--w12b-ms", type=str, default="1,4,16,32",
+                    help="x rows for the W12-b (arbitrary-base) comparison ('' to skip)")
     ap.add_argument("--shard-ms", type=str, default="1,4,16,32",
                     help="x rows for the 8-way tensor-parallel shard shapes ('' to skip)")
     ap.add_argument("--workload", default="qkv", choices=["qkv", "o", "gate_up", "down"],
@@ -97,18 +99,20 @@ def source_sha() -> str:
 
 
 class Workload:
-    """One weight on the GPU in R rotated copies, W12 and BF16."""
+    """One weight on the GPU in R rotated copies, W12 (allocation `fmt`) and
+    BF16."""
 
-    def __init__(self, case, torch, w12):
+    def __init__(self, case, torch, w12, fmt="v1"):
         from lossless_bit_weight_amd.inputs import GemmCase  # noqa: F401
         self.case = case
+        self.fmt = fmt
         self.N, self.K = case.N, case.K
         raw = case.weights_raw()
         wd = torch.from_numpy(raw.view(np.int16)).cuda()
         # project onto the encodable set with the library itself, then repack
-        first, self.raw_bad = w12.pack(wd)
+        first, self.raw_bad = w12.pack(wd, fmt=fmt)
         w_bf16 = w12.w12_unpack(first)
-        wt, bad = w12.pack(w_bf16)
+        wt, bad = w12.pack(w_bf16, fmt=fmt)
         if bad:
             raise RuntimeError("projected weights still have unencodable groups")
         self.w_tiled = w12.w12_bf16_tile(w_bf16)
@@ -118,7 +122,7 @@ class Workload:
         r12 = max(2, math.ceil(ROTATE_BYTES / self.w12_bytes))
         r16 = max(2, math.ceil(ROTATE_BYTES / self.bf16_bytes))
         self.w12_copies = [wt] + [w12.W12Weight(wt.p0.clone(), wt.p1.clone(), wt.p2.clone(),
-                                                wt.meta.clone(), self.N, self.K)
+                                                wt.meta.clone(), self.N, self.K, fmt=fmt)
                                   for _ in range(r12 - 1)]
         self.bf16_copies = [self.w_tiled] + [w12.BF16Tiled(self.w_tiled.w.clone(), self.N, self.K)
                                              for _ in range(r16 - 1)]
@@ -183,7 +187,7 @@ def measure(torch, w12, wl: Workload, M, steps, warmup, out_dtype, settle_s=0.05
     b16 = gemm_bytes(wl.N, wl.K, M, out_b, wl.bf16_bytes)
     return {
         "workload": wl.case.name, "M": M,
-        "w12_kernel": w12.w12_gemm_variant(M, wl.N, wl.K, True),
+        "w12_kernel": w12.w12_gemm_variant(M, wl.N, wl.K, 2 if wl.fmt == "b" else 1),
         "bf16_kernel": w12.w12_gemm_variant(M, wl.N, wl.K, False),
         "w12_us": ms12 * 1e3, "bf16_us": ms16 * 1e3,
         "w12_weight_gbps": wl.w12_bytes / (ms12 * 1e-3) / 1e9,
@@ -479,22 +483,22 @@ def stack_step(torch, w12, inputs, ms, steps, warmup):
     return out
 
 
-def measure_exceptions(torch, w12, case, ms, steps, warmup):
+def measure_exceptions(torch, w12, case, ms, steps, warmup, fmt="v1"):
     """The raw (unprojected) weight packed with its exception list, so the
     container is lossless: list size, and the W12 GEMM against the BF16
     control on the same raw weight (same protocol as the headline)."""
     raw = torch.from_numpy(case.weights_raw().view(np.int16)).cuda()
-    wt, bad = w12.pack(raw, exceptions=True)
+    wt, bad = w12.pack(raw, exceptions=True, fmt=fmt)
     w_tiled = w12.w12_bf16_tile(raw)
     count = int(wt.exc_offsets[-1].item()) if wt.exc_offsets is not None else 0
     r = max(2, math.ceil(ROTATE_BYTES / wt.nbytes))
     clone = lambda t: None if t is None else t.clone()
     copies = [wt] + [w12.W12Weight(wt.p0.clone(), wt.p1.clone(), wt.p2.clone(), wt.meta.clone(),
-                                   wt.N, wt.K, clone(wt.exc_offsets), clone(wt.exc_entries))
+                                   wt.N, wt.K, clone(wt.exc_offsets), clone(wt.exc_entries), fmt=fmt)
                      for _ in range(r - 1)]
     b16 = [w_tiled] + [w12.BF16Tiled(w_tiled.w.clone(), wt.N, wt.K)
                        for _ in range(max(2, math.ceil(ROTATE_BYTES / w_tiled.nbytes)) - 1)]
-    out = {"workload": case.name + " raw (unprojected)", "flagged_groups": bad,
+    out = {"workload": case.name + " raw (unprojected)", "format": fmt, "flagged_groups": bad,
            "exceptions": count, "list_bytes": wt.nbytes - 3 * wt.p0.numel() - wt.meta.numel(),
            "by_m": []}
     for M in ms:
@@ -685,6 +689,46 @@ def main():
             del wlc
             torch.cuda.empty_cache()
 
+    # W12-b, the arbitrary-base allocation: unencodable groups and exception
+    # counts of the raw weights beside W12-v1's, and its GEMMs on its own
+    # projection of the same weights.
+    w12b = None
+    bms = [int(m) for m in args.w12b_ms.split(",") if m]
+    if not args.no_sweep and bms:
+        w12b = {"by_workload": [], "gemm": []}
+        v1_rows = {(r["workload"], r["M"]): r for r in sweep}
+        for name in ("qkv", "o", "gate_up", "down"):
+            case = inputs.CASES[name]
+            raw = torch.from_numpy(case.weights_raw().view(np.int16)).cuda()
+            groups = case.N * case.K // 128
+            enc = {"workload": case.name, "groups": groups}
+            for fmt in ("v1", "b"):
+                wt, bad = w12.pack(raw, exceptions=True, fmt=fmt)
+                count = int(wt.exc_offsets[-1].item()) if wt.exc_offsets is not None else 0
+                enc[fmt] = {"flagged_groups": bad, "flagged_frac": round(bad / groups, 5),
+                            "exceptions": count}
+                del wt
+            del raw
+            w12b["by_workload"].append(enc)
+            wlb = Workload(case, torch, w12, fmt="b")
+            for M in bms:
+                r = measure(torch, w12, wlb, M, args.steps, args.warmup, torch.float32)
+                v1 = v1_rows.get((case.name, M))
+                row = {"workload": case.name, "M": M, "w12b_kernel": r["w12_kernel"],
+                       "w12b_us": round(r["w12_us"], 3), "bf16_us": round(r["bf16_us"], 3),
+                       "w12b_weight_gbps": round(r["w12_weight_gbps"], 1),
+                       "speedup_vs_bf16": round(r["speedup_vs_bf16"], 4),
+                       "w12_v1_us": round(v1["w12_us"], 3) if v1 else None}
+                w12b["gemm"].append(row)
+                print("w12b: %s M=%d w12b %.2f us (v1 %s) bf16 %.2f us"
+                      % (name, M, r["w12_us"], row["w12_v1_us"], r["bf16_us"]),
+                      file=sys.stderr, flush=True)
+            del wlb
+            torch.cuda.empty_cache()
+        w12b["exceptions"] = measure_exceptions(torch, w12, head_case, [1, 16], args.steps,
+                                                args.warmup, fmt="b")
+        print("w12b: %s" % json.dumps(w12b["by_workload"]), file=sys.stderr, flush=True)
+
     codec = time_codec(torch, w12, wl, args.steps)
     print("codec: %s" % json.dumps(codec), file=sys.stderr, flush=True)
 
@@ -748,6 +792,7 @@ def main():
         "cpu_baseline": cpu,
         "sweep": [{k: (round(v, 3) if isinstance(v, float) else v) for k, v in r.items()}
                   for r in sweep],
+        "w12b": w12b,
         "tp8_shards": [{k: (round(v, 3) if isinstance(v, float) else v) for k, v in r.items()}
                        for r in shards],
         "codec": codec,
