@@ -75,7 +75,7 @@ extern "C" {
 #define W12_ABI_VERSION 6
 #define W12_GROUP 128
 #define W12_TILE_ROWS 16
-#define W12_MAX_M 32
+#define W12_MAX_M 128
 
 typedef enum {
     W12_OK = 0,
@@ -84,7 +84,7 @@ typedef enum {
                                  N*K >= 2^40, M < 1, ld < K/N               */
     W12_ERR_ALIGN = -3,       /* pointer or leading dimension misaligned     */
     W12_ERR_DTYPE = -4,       /* unknown output type                         */
-    W12_ERR_UNSUPPORTED = -6, /* M > 32                                      */
+    W12_ERR_UNSUPPORTED = -6, /* M > 128, or a tiling not built             */
     W12_ERR_HIP = -7,         /* the HIP launch reported an error            */
     W12_ERR_WORKSPACE = -8    /* split-K workspace NULL, short or misaligned */
 } w12_status_t;
@@ -171,7 +171,7 @@ int w12_unpack(const void *p0, const void *p1, const void *p2,
  * w12_gemm -- y[m, n] = sum_k x[m, k] * W[n, k] with W read from a W12
  * container and rebuilt in registers (a2-a6), fp32 accumulation.
  *   x      : device BF16 [M, K], row stride ldx elements (ldx >= K,
- *            ldx % 8 == 0), 16-byte aligned.  1 <= M <= 32.
+ *            ldx % 8 == 0), 16-byte aligned.  1 <= M <= 128.
  *   p0..meta: the container of an [N, K] weight as written by w12_pack.
  *   exc_offsets, exc_entries: its exception list (w12_exceptions) or both
  *            NULL; with a list the result is the GEMM of the original
@@ -180,12 +180,13 @@ int w12_unpack(const void *p0, const void *p1, const void *p2,
  *   y      : device output [M, N], row stride ldy elements (ldy >= N),
  *            BF16 bits (2-byte aligned) or fp32 (4-byte aligned) per y_type.
  * By default M = 1 runs a wavefront-reduction GEMV (v_dot2c_f32_bf16) and
- * 2 <= M <= 32 runs bf16 MFMA with x padded to 16 or 32 rows (measured
- * crossover); w12_gemm_ex selects either explicitly (GEMV up to M = 8).
+ * 2 <= M <= 128 runs bf16 MFMA with x padded to 16, 32, 64 or 128 rows
+ * (measured crossover; above 32 rows with x in LDS, 512-thread
+ * workgroups); w12_gemm_ex selects either explicitly (GEMV up to M = 8).
  * Each workgroup covers all of K for its rows, so no workspace is needed;
  * w12_gemm_ws adds the split-K tilings.
  * Errors: W12_ERR_NULL, W12_ERR_SHAPE, W12_ERR_ALIGN, W12_ERR_DTYPE,
- *         W12_ERR_UNSUPPORTED (M > 32), W12_ERR_HIP.
+ *         W12_ERR_UNSUPPORTED (M > 128), W12_ERR_HIP.
  */
 int w12_gemm(const uint16_t *x, int64_t M, int64_t ldx,
              const void *p0, const void *p1, const void *p2,
@@ -220,7 +221,8 @@ int bf16_gemm(const uint16_t *x, int64_t M, int64_t ldx,
 
 /*
  * Explicit tiling, for callers that tune the kernels on their own shapes.
- *   kind  : 0 = wavefront-reduction GEMV (M <= 8), 1 = bf16 MFMA (M <= 32).
+ *   kind  : 0 = wavefront-reduction GEMV (M <= 8), 1 = bf16 MFMA (M <= 128;
+ *           above 32 rows only with waves = 8).
  *   r     : 16-row weight tiles per wave (1, 2).
  *   kw    : waves of a workgroup that split K (1, 2, 4; 8 with waves = 8);
  *           the workgroup's other waves take further weight tiles.

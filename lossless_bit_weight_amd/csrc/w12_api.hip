@@ -81,7 +81,7 @@ const char* w12_status_string(int status) {
         case W12_ERR_SHAPE: return "bad shape (need N >= 1, K a positive multiple of 128, M >= 1, ldx >= K, ldy >= N)";
         case W12_ERR_ALIGN: return "misaligned pointer or leading dimension (16-byte tensors, ldx % 8 == 0)";
         case W12_ERR_DTYPE: return "unknown output type";
-        case W12_ERR_UNSUPPORTED: return "unsupported size or tiling (M > 32, or a tiling that is not built for this shape)";
+        case W12_ERR_UNSUPPORTED: return "unsupported size or tiling (M > 128, or a tiling that is not built for this shape)";
         case W12_ERR_HIP: return "HIP launch failed";
         case W12_ERR_WORKSPACE: return "workspace missing, too small or not 256-byte aligned for this split-K tiling";
         default: return "unknown status";

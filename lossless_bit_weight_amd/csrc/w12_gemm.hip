@@ -64,8 +64,10 @@ bool complete_tiling(Tiling& t, int M, int64_t N, int64_t K) {
     if (t.splitk > 1 && row_blocks(t, N) > kMaxSplitRowBlocks) return false;
     const int64_t width = gs * 128;  // x columns one workgroup reads
     if (t.mfma) {
-        if (M > 32) return false;
-        t.mt = M <= 16 ? 16 : 32;
+        if (M > 128) return false;
+        t.mt = M <= 16 ? 16 : M <= 32 ? 32 : M <= 64 ? 64 : 128;
+        // 64 and 128 rows: eight-wave workgroups with x in LDS only
+        if (t.mt > 32 && t.nw != 8) return false;
         if (!pair_built(t.r, t.depth)) return false;
         if (t.xdirect) {
             if (!kern::xd_ok(true, t.mt, t.r, t.depth)) return false;
@@ -155,7 +157,8 @@ Tiling choose_tiling(int M, int64_t N, int64_t K, bool allow_splitk) {
         t.kw = ntiles >= 256 && ntiles <= 1024 ? 2 : 4;
         t.depth = 4;
         t.xdirect = 1;
-    } else if (M <= 8 || ntiles <= 256 || (M <= 12 && ntiles > 384 && ntiles <= 1024 && G <= 64)) {
+    } else if (M <= 8 ||
+               (M <= 32 && (ntiles <= 256 || (M <= 12 && ntiles > 384 && ntiles <= 1024 && G <= 64)))) {
         t.mfma = 1;
         t.r = ntiles <= 256 || (ntiles > 512 && M <= 6) ? 1 : 2;
         t.kw = 4;
@@ -213,6 +216,7 @@ const char* tiling_name(const Tiling& t, int fetch) {
 }
 
 hipError_t launch_gemm(const GemmArgs& a, const Tiling& t, int fetch, hipStream_t s) {
+    if (t.mfma && t.mt > 32) return launch_mfma8_big_mt(t.mt, a, t, fetch, s);
     if (t.mfma)
         return t.nw == 8 ? launch_mfma8_mt(t.mt, a, t, fetch, s) : launch_mfma_mt(t.mt, a, t, fetch, s);
     return launch_gemv_m(t.mt, a, t, fetch, s);

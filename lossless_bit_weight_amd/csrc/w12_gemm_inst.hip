@@ -1,8 +1,8 @@
 // w12_gemm_inst.hip -- instantiates the GEMM kernel templates for one x
 // height, chosen at compile time (-DW12_INST_M=1..8 for the GEMV, or
 // -DW12_INST_MFMA / -DW12_INST_MFMA8 for the 16- and 32-row MFMA tiles in
-// 256- and 512-thread workgroups), for the three weight fetches (BF16
-// control, W12-v1, W12-b).  One object file per height keeps the build
+// 256- and 512-thread workgroups, -DW12_INST_MFMA8_BIG for 64 and 128 rows),
+// for the three weight fetches (BF16 control, W12-v1, W12-b).  One object file per height keeps the build
 // parallel.
 #include "w12_gemm_kernels.hpp"
 
@@ -51,8 +51,25 @@ hipError_t launch_mfma8_mt(int MT, const GemmArgs& a, const Tiling& t, int fetch
         default: return hipErrorInvalidValue;
     }
 }
+#elif defined(W12_INST_MFMA8_BIG)
+template <int MT>
+static hipError_t mfma8_fetch(const GemmArgs& a, const Tiling& t, int fetch, hipStream_t s) {
+    switch (fetch) {
+        case kFetchW12: return kern::dispatch8<kern::FetchW12, MT>(a, t, s);
+        case kFetchW12B: return kern::dispatch8<kern::FetchW12B, MT>(a, t, s);
+        default: return kern::dispatch8<kern::FetchBF16, MT>(a, t, s);
+    }
+}
+hipError_t launch_mfma8_big_mt(int MT, const GemmArgs& a, const Tiling& t, int fetch,
+                               hipStream_t s) {
+    switch (MT) {
+        case 64: return mfma8_fetch<64>(a, t, fetch, s);
+        case 128: return mfma8_fetch<128>(a, t, fetch, s);
+        default: return hipErrorInvalidValue;
+    }
+}
 #else
-#error "define W12_INST_M, W12_INST_MFMA or W12_INST_MFMA8"
+#error "define W12_INST_M, W12_INST_MFMA, W12_INST_MFMA8 or W12_INST_MFMA8_BIG"
 #endif
 
 }  // namespace w12

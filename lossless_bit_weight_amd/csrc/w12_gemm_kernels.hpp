@@ -163,13 +163,21 @@ template <int XR>
 struct ExcStage {
     static constexpr int kBytes = 64 * 3 * 4 + XR * 64 * 2;
 };
+// x rows one pass of the corrections stages: all of them for the GEMV and
+// MFMA tiles up to 32 rows, 16 at a time above (so that eight staging areas
+// fit beside a 128 KB x double buffer).
+__host__ __device__ constexpr int exc_rows(bool mfma, int mr) {
+    return !mfma || mr <= 32 ? mr : 16;
+}
 
 // apply(j, orig, clamp, xs) runs on the lanes of entry j's row; xs(m) reads
-// that entry's x[m][k] from LDS.  F::clamp_word(entry word 1) gives the
-// BF16 clamp the planes hold for the entry.
+// that entry's x[mb + m][k] from LDS (XR rows from row mb < M).
+// F::clamp_word(entry word 1) gives the BF16 clamp the planes hold for the
+// entry.
 template <class F, int XR, class Apply>
 __device__ __forceinline__ void exc_corrections(const GemmArgs& g, int64_t tile, int g0, int gn,
-                                                int lane, int col, uint8_t* area, Apply apply) {
+                                                int lane, int col, uint8_t* area, int mb,
+                                                Apply apply) {
     float* orig = reinterpret_cast<float*>(area + 256);
     float* clamp = reinterpret_cast<float*>(area + 512);
     uint16_t* xs = reinterpret_cast<uint16_t*>(area + 768);
@@ -195,7 +203,8 @@ __device__ __forceinline__ void exc_corrections(const GemmArgs& g, int64_t tile,
         // x[m][k] for the batch, sixteen rows of loads in flight at a time;
         // rows past M and lanes without an entry store zero (a zero x adds
         // nothing, so the consumers need no row test)
-        const uint16_t* px = g.x + (c >= 0 ? k : 0);   // a per-lane running row pointer
+        // a per-lane running row pointer, from row mb
+        const uint16_t* px = g.x + (int64_t)mb * g.ldx + (c >= 0 ? k : 0);
         const uint32_t keep = c >= 0 ? 0xFFFFu : 0u;
         constexpr int kRound = XR < 16 ? XR : 16;
 #pragma unroll 1
@@ -204,9 +213,9 @@ __device__ __forceinline__ void exc_corrections(const GemmArgs& g, int64_t tile,
 #pragma unroll
             for (int d = 0; d < kRound; ++d) {
                 xv[d] = *px;
-                px += m0 + d + 1 < g.M ? g.ldx : 0;   // stays on the last row of x
+                px += mb + m0 + d + 1 < g.M ? g.ldx : 0;   // stays on the last row of x
             }
-            const int valid = g.M - m0;
+            const int valid = g.M - mb - m0;
 #pragma unroll
             for (int d = 0; d < kRound; ++d)
                 xs[(m0 + d) * 64 + lane] = (uint16_t)(d < valid ? xv[d] & keep : 0u);
@@ -531,7 +540,7 @@ __host__ __device__ size_t lds_bytes(int gs) {
 // an area after everything else (so it never meets x or the reductions).
 template <bool MFMA, int MR, int KW, int NW>
 __host__ __device__ constexpr size_t exc_lds_bytes() {
-    return (size_t)(NW / KW) * ExcStage<MFMA ? 16 * (MR / 16) : MR>::kBytes;
+    return (size_t)(NW / KW) * ExcStage<exc_rows(MFMA, MR)>::kBytes;
 }
 
 // ---- the kernel ----------------------------------------------------------------------
@@ -769,20 +778,29 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs g) {
         // split K the values go to this slice's partial sums instead.
         if constexpr (F::kHasExceptions) {
             if (kw == 0 && g.exc_off != nullptr) {
-                uint8_t* area = reinterpret_cast<uint8_t*>(lds) + exc_base + nw * ExcStage<16 * kMT>::kBytes;
+                // above 32 rows x is staged 16 rows at a time (the list is
+                // walked once per 16 rows): each output still takes its
+                // entries in list order
+                constexpr int kXR = exc_rows(MFMA, MR);
+                uint8_t* area = reinterpret_cast<uint8_t*>(lds) + exc_base + nw * ExcStage<kXR>::kBytes;
 #pragma unroll
                 for (int r = 0; r < R; ++r) {
                     if (tile0 + r >= ntiles) continue;
-                    exc_corrections<F, 16 * kMT>(g, tile0 + r, g0, gn, lane, col, area,
-                                              [&](float orig, float clamp, auto xs) {
 #pragma unroll
-                        for (int mt = 0; mt < kMT; ++mt)
+                    for (int mb = 0; mb < 16 * kMT; mb += kXR) {
+                        if (mb >= g.M) break;
+                        exc_corrections<F, kXR>(g, tile0 + r, g0, gn, lane, col, area, mb,
+                                                [&](float orig, float clamp, auto xs) {
 #pragma unroll
-                            for (int e = 0; e < 4; ++e) {
-                                const float xv = xs(16 * mt + 4 * q + e);
-                                macc[r][mt][e] = fmaf(xv, orig, fmaf(-xv, clamp, macc[r][mt][e]));
-                            }
-                    });
+                            for (int t = 0; t < kXR / 16; ++t)
+#pragma unroll
+                                for (int e = 0; e < 4; ++e) {
+                                    const int mt = mb / 16 + t;
+                                    const float xv = xs(16 * t + 4 * q + e);
+                                    macc[r][mt][e] = fmaf(xv, orig, fmaf(-xv, clamp, macc[r][mt][e]));
+                                }
+                        });
+                    }
                 }
             }
         }
@@ -840,7 +858,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs g) {
 #pragma unroll
                 for (int r = 0; r < R; ++r) {
                     if (tile0 + r >= ntiles) continue;
-                    exc_corrections<F, MR>(g, tile0 + r, g0, gn, lane, col, area,
+                    exc_corrections<F, MR>(g, tile0 + r, g0, gn, lane, col, area, 0,
                                         [&](float orig, float clamp, auto xs) {
 #pragma unroll
                         for (int m = 0; m < MR; ++m) {

@@ -46,7 +46,8 @@ struct GemmArgs {
 // Tiling of one GEMM launch.
 //   mfma    = 0: GEMV (v_dot2c_f32_bf16); 1: MFMA 16x16x32 bf16.
 //   r       = 16-row weight tiles per wave (1 or 2).
-//   mt      = GEMV: M (1..8); MFMA: x rows padded to 16 or 32.
+//   mt      = GEMV: M (1..8); MFMA: x rows padded to 16, 32, 64 or 128 (64
+//             and 128 with nw = 8 only).
 //   kw      = waves of a workgroup that split K between them (1, 2, 4; 8
 //             with nw = 8).
 //   depth   = 32-weight slices each lane keeps in flight (2, 4 or 8).
@@ -102,6 +103,8 @@ hipError_t launch_gemm(const GemmArgs& a, const Tiling& t, int fetch, hipStream_
 hipError_t launch_gemv_m(int M, const GemmArgs& a, const Tiling& t, int fetch, hipStream_t s);
 hipError_t launch_mfma_mt(int MT, const GemmArgs& a, const Tiling& t, int fetch, hipStream_t s);
 hipError_t launch_mfma8_mt(int MT, const GemmArgs& a, const Tiling& t, int fetch, hipStream_t s);
+hipError_t launch_mfma8_big_mt(int MT, const GemmArgs& a, const Tiling& t, int fetch,
+                               hipStream_t s);
 hipError_t launch_pack(int fmt, const uint16_t* w, int64_t N, int64_t K, void* p0, void* p1,
                        void* p2, uint8_t* meta, uint32_t* bad, hipStream_t s);
 hipError_t launch_unpack(int fmt, const void* p0, const void* p1, const void* p2,

@@ -22,7 +22,7 @@ LIB_PATH = os.path.join(_HERE, "libw12.so")
 HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "w12.h")
 
 GROUP = 128
-MAX_M = 32
+MAX_M = 128
 OUT_BF16 = 0
 OUT_F32 = 1
 

@@ -56,7 +56,7 @@ def _gemm(**kw):
     (dict(K=500), -2), (dict(K=0), -2), (dict(N=0), -2), (dict(M=0), -2),
     (dict(K=1 << 24, ldx=1 << 24), -2), (dict(N=1 << 26, K=1 << 14, ldx=1 << 14, ldy=1 << 26), -2),
     (dict(ldx=256), -2), (dict(ldy=63), -2),
-    (dict(M=33), -6), (dict(yt=2), -4),
+    (dict(M=129), -6), (dict(yt=2), -4),
     (dict(x=MIS), -3), (dict(ldx=516), -3), (dict(p2=MIS), -3),
     (dict(yt=1, y=P(4098)), -3),
     (dict(eo=A16), -1), (dict(ee=A16), -1), (dict(eo=P(4098), ee=A16), -3),
@@ -70,7 +70,7 @@ def test_bf16_gemm_rejects():
     L = w12.lib()
     assert L.bf16_gemm(A16, 1, 512, None, 64, 512, A16, 64, 0, None) == -1
     assert L.bf16_gemm(A16, 1, 512, MIS, 64, 512, A16, 64, 0, None) == -3
-    assert L.bf16_gemm(A16, 40, 512, A16, 64, 512, A16, 64, 0, None) == -6
+    assert L.bf16_gemm(A16, 129, 512, A16, 64, 512, A16, 64, 0, None) == -6
     assert L.bf16_gemm(A16, 1, 512, A16, 64, 384 + 1, A16, 64, 0, None) == -2
 
 
@@ -121,7 +121,10 @@ def test_variant_selection():
     assert w12.w12_gemm_variant(9, 7168, 5120).startswith("w12_mfma_mt16_")
     assert w12.w12_gemm_variant(16, 34816, 5120).startswith("w12_mfma_mt16_")
     assert w12.w12_gemm_variant(17, 5120, 17408).startswith("w12_mfma_mt32_")
-    assert w12.w12_gemm_variant(33, 5120, 17408) is None
+    assert w12.w12_gemm_variant(33, 5120, 17408).startswith("w12_mfma_mt64_r1_kw2_d2_chunked_w8")
+    assert w12.w12_gemm_variant(65, 7168, 5120).startswith("w12_mfma_mt128_r1_kw1_d2_chunked_w8")
+    assert w12.w12_gemm_variant(128, 896, 5120).startswith("w12_mfma_mt128_")
+    assert w12.w12_gemm_variant(129, 5120, 17408) is None
     assert w12.w12_gemm_variant(1, 5120, 100) is None
 
 
@@ -188,7 +191,7 @@ def test_workspace_rejects():
     assert L.bf16_gemm_ws(A16, 4, K, A16, 64, K, A16, 64, 0, None, 0, None) == -8
     # argument errors still come first
     assert L.w12_gemm_ws(None, 4, K, A16, A16, A16, A16, None, None, 64, K, A16, 64, 0, None, 0, None) == -1
-    assert L.w12_gemm_ws(A16, 33, K, A16, A16, A16, A16, None, None, 64, K, A16, 64, 0, None, 0, None) == -6
+    assert L.w12_gemm_ws(A16, 129, K, A16, A16, A16, A16, None, None, 64, K, A16, 64, 0, None, 0, None) == -6
 
 
 def test_default_split_rule():
@@ -216,7 +219,7 @@ def test_default_tiling():
         if not split:
             assert t.splitk == 1
     with pytest.raises(w12.W12Error):
-        w12.w12_default_tiling(40, 64, 512)
+        w12.w12_default_tiling(129, 64, 512)
 
 
 def test_default_waves_rule():

@@ -110,7 +110,7 @@ def _gemm(x, wt, tiling):
 
 def _ms(tiling):
     if tiling is None or tiling == "plain":
-        return [1, 3, 8, 16, 32]
+        return [1, 3, 8, 16, 32, 64, 128]
     if tiling[0] == 0:
         return [1, 2] if tiling[4] else [1, 4, 8]
     return [5, 16] if tiling[4] else [9, 32]
@@ -148,10 +148,10 @@ def test_one_hot_rows_give_original_words(oracle, tiling):
     wt, _ = _pack_exc(bits)
     off, ent = oracle.exceptions(bits)
     ks = np.unique(ent[:, 0] & 0xFFFFFF)
-    for M in ([1, 4] if tiling not in (None, "plain") and tiling[0] == 0 else [8, 32]):
-        pick = ks[np.random.default_rng(M).choice(ks.size, size=M, replace=False)]
-        x = np.zeros((M, 640), np.uint16)
-        x[np.arange(M), pick] = 0x3F80
+    for M in ([1, 4] if tiling not in (None, "plain") and tiling[0] == 0 else [8, 32, 64]):
+        pick = ks[np.random.default_rng(M).choice(ks.size, size=min(M, ks.size), replace=False)]
+        x = np.zeros((pick.size, 640), np.uint16)
+        x[np.arange(pick.size), pick] = 0x3F80
         try:
             y = _gemm(to_dev(x), wt, tiling)
         except w12.W12Error as e:

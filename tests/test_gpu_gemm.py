@@ -126,6 +126,45 @@ def test_shard_shapes_default(oracle, shape, M):
     _check(oracle, P, x, _sample_rows(P.N, seed=M), "shard %s M=%d" % (shape, M))
 
 
+@pytest.mark.parametrize("shape", [(301, 640), (45, 5120), (77, 17408), (1000, 1152)])
+@pytest.mark.parametrize("M", [33, 48, 64, 65, 100, 128])
+def test_large_m_default(oracle, shape, M):
+    """M = 33-128: x padded to 64 or 128 rows, staged in LDS for 512-thread
+    workgroups, with and without split K; W12 and BF16 bitwise equal."""
+    P = prepared(shape)
+    x = inputs.gaussian_bf16((M, shape[1]), 1.0, 17 * M + shape[0])
+    _check(oracle, P, x, np.arange(P.N), "large M %s M=%d" % (shape, M))
+
+
+@pytest.mark.parametrize("tiling", [(1, 1, 1, 2, 0, 1, 8), (1, 1, 2, 2, 0, 1, 8),
+                                    (1, 1, 1, 2, 0, 3, 8), (1, 1, 2, 2, 0, 7, 8),
+                                    (1, 1, 1, 2, 0, 64, 8)],
+                         ids=lambda t: "kw%d_s%d_w%d" % (t[2], t[5], t[6]))
+def test_large_m_tilings(oracle, tiling):
+    """Every 64- and 128-row tiling that is built, ragged shapes, split K
+    down to one group per slice; a tiling that is not built for a shape is
+    rejected (a chunk beyond 128 KB of LDS)."""
+    for shape in ((301, 640), (33, 2688), (77, 17408)):
+        P = prepared(shape)
+        w_ref = P.ref_rows(oracle, np.arange(P.N))
+        for M in (40, 64, 97, 128):
+            what = "large M tiling %s %s M=%d" % (tiling, shape, M)
+            print(what, flush=True)
+            x = inputs.gaussian_bf16((M, shape[1]), 1.0, 3 * M + shape[1])
+            xd = to_dev(x)
+            try:
+                y12 = w12.w12_gemm(xd, P.wt, tiling=tiling)
+            except w12.W12Error as e:
+                mt = 64 if M <= 64 else 128
+                assert e.status == -6 and mt * 128 * tiling[2] * 2 > 32768, what
+                continue
+            y16 = w12.bf16_gemm(xd, P.w_tiled, tiling=tiling)
+            torch.cuda.synchronize()
+            y12h, y16h = y12.cpu().numpy(), y16.cpu().numpy()
+            assert np.array_equal(y12h.view(np.uint32), y16h.view(np.uint32)), what
+            assert_gemm_close(y12h, oracle.gemm_bf16_f64(x, w_ref), oracle.tolerance(x, w_ref), what)
+
+
 @pytest.mark.parametrize("M", [1, 5, 8, 16, 32])
 def test_bf16_output_is_rounded_fp32(M):
     P = prepared("tiny")

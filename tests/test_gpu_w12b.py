@@ -138,7 +138,7 @@ def _bf16(x, tiled, tiling):
 
 def _ms(tiling):
     if tiling is None or tiling == "plain":
-        return [1, 2, 9, 16, 32]
+        return [1, 2, 9, 16, 32, 128]
     if tiling[0] == 0:
         return [1, 3] if tiling[4] else [1, 8]
     return [4, 16] if tiling[4] else [9, 32]
@@ -197,7 +197,7 @@ def test_raw_weights_with_list(oracle, tiling):
     wt, bad = w12.pack(to_dev(bits), exceptions=True, fmt="b")
     torch.cuda.synchronize()
     assert bad > 0
-    for M in ([1, 8] if tiling not in (None, "plain") and tiling[0] == 0 else [8, 32]):
+    for M in ([1, 8] if tiling not in (None, "plain") and tiling[0] == 0 else [8, 32, 100]):
         x = inputs.gaussian_bf16((M, 640), 1.0, M + 640)
         try:
             y = _gemm(to_dev(x), wt, tiling)
