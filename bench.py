@@ -63,10 +63,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stack", action="store_true",
                     help="skip the 64-layer linear-stack decode step")
-    ap.add_argument("--stack-ms", type=str, default="1,4,8,16,32")
+    ap.add_argument("--stack-ms", type=str, default="1,4,8,16,32,64,128")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU-oracle work to time")
-    ap.add_argument("--sweep-ms", type=str, default="1,2,4,8,16,32")
+    ap.add_argument("--sweep-ms", type=str, default="1,2,4,8,16,32,64,128")
     ap.add_argument("--w12b-ms", type=str, default="1,4,16,32",
                     help="x rows for the W12-b (arbitrary-base) comparison ('' to skip)")
     ap.add_argument("--shard-ms", type=str, default="1,4,16,32",

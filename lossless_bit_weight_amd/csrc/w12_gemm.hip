@@ -137,6 +137,11 @@ void bind_split(GemmArgs& a, const Tiling& t, void* ws) {
 // K-waves, its 128 KB x double buffer included (down M = 24: 41.3 us
 // against 46.5 with 256 threads).
 //
+// M = 33-128: x padded to 64 or 128 rows, in LDS, eight waves, two K-waves
+// (64 rows) or one (128 rows: a 128 KB double buffer holds 256 columns); a
+// weight of >= 512 row blocks that K does not split takes one K-wave at 64
+// rows too (gate+up M = 64: 75.7 us against 84.7 with two).
+//
 // Splitting K across workgroups (the _ws entry points, MFMA only): slices of
 // at least 40 groups (5120 weights) keep each workgroup's prologue and
 // epilogue small against its stream, up to ~2048 workgroups -- three slices
@@ -190,6 +195,9 @@ Tiling choose_tiling(int M, int64_t N, int64_t K, bool allow_splitk) {
         t.splitk = s > 1 ? (int)s : 1;
     }
     if (t.nw == 8 && t.splitk == 1 && (M <= 16 || nb < 128)) t.kw = 4;
+    // above 32 rows a grid of >= 512 row blocks unsplit keeps eight tiles per
+    // workgroup (one K-wave each): x is staged once for eight tiles
+    if (t.nw == 8 && t.splitk == 1 && M > 32 && nb >= 512) t.kw = 1;
     // Step down to a built combination (a chunked x buffer must fit LDS).
     while (!complete_tiling(t, M, N, K)) {
         if (t.depth > 2)

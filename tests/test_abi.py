@@ -279,6 +279,22 @@ def test_default_small_weights():
     assert w12.w12_default_tiling(7, 34816, 5120).r == 2
 
 
+def test_default_large_m():
+    """M = 33-128: 64 or 128 padded rows in 512-thread workgroups with x in
+    LDS; one K-wave at 128 rows, and at 64 rows on an unsplit grid of >= 512
+    row blocks; K split as above 16 rows."""
+    t = w12.w12_default_tiling(64, 34816, 5120)
+    assert (t.kind, t.waves, t.kw, t.x_direct, t.splitk) == (1, 8, 1, 0, 1)
+    t = w12.w12_default_tiling(64, 7168, 5120)
+    assert (t.waves, t.kw, t.splitk) == (8, 2, 2)
+    t = w12.w12_default_tiling(48, 5120, 17408)
+    assert (t.waves, t.kw, t.splitk) == (8, 2, 3)
+    for N, K in ((34816, 5120), (7168, 5120), (5120, 17408), (896, 5120)):
+        t = w12.w12_default_tiling(128, N, K)
+        assert (t.waves, t.kw, t.x_direct) == (8, 1, 0)
+        assert w12.w12_gemm_variant(100, N, K).startswith("w12_mfma_mt128_")
+
+
 def test_tiling_waves_rejects():
     """512-thread workgroups are built only for the MFMA with x in LDS, r = 1,
     depth 2 and kw <= 8; 4 and 0 (= 4) are the other wave counts."""
