@@ -52,8 +52,10 @@ bool complete_tiling(Tiling& t, int M, int64_t N, int64_t K) {
     if (t.nw != 4 && t.nw != 8) return false;
     if (t.kw != 1 && t.kw != 2 && t.kw != 4 && t.kw != 8) return false;
     if (t.kw > t.nw) return false;
-    // eight-wave workgroups: MFMA with x in LDS, one tile per wave, depth 2
-    if (t.nw == 8 && (!t.mfma || t.xdirect || t.r != 1 || t.depth != 2)) return false;
+    // eight-wave workgroups: MFMA with x in LDS, depth 2, one tile per wave
+    // (two with one K-wave above 32 rows)
+    if (t.nw == 8 && (!t.mfma || t.xdirect || t.depth != 2)) return false;
+    if (t.nw == 8 && t.r != 1 && !(t.r == 2 && t.kw == 1 && M > 32)) return false;
     if (t.splitk < 1 || t.splitk > kMaxSplitK) return false;
     // Slices of gs groups; a request above the group count gives one group
     // per slice.
@@ -140,7 +142,10 @@ void bind_split(GemmArgs& a, const Tiling& t, void* ws) {
 // M = 33-128: x padded to 64 or 128 rows, in LDS, eight waves, two K-waves
 // (64 rows) or one (128 rows: a 128 KB double buffer holds 256 columns); a
 // weight of >= 512 row blocks that K does not split takes one K-wave at 64
-// rows too (gate+up M = 64: 75.7 us against 84.7 with two).
+// rows too (gate+up M = 64: 75.7 us against 84.7 with two) and, at 128
+// rows, two tiles per wave, which read each A fragment from LDS once for
+// both (gate+up M = 128: 94.9 us against 130.7; on smaller grids the halved
+// workgroup count loses: QKV 87.7 against 48.3).
 //
 // Splitting K across workgroups (the _ws entry points, MFMA only): slices of
 // at least 40 groups (5120 weights) keep each workgroup's prologue and
@@ -197,7 +202,10 @@ Tiling choose_tiling(int M, int64_t N, int64_t K, bool allow_splitk) {
     if (t.nw == 8 && t.splitk == 1 && (M <= 16 || nb < 128)) t.kw = 4;
     // above 32 rows a grid of >= 512 row blocks unsplit keeps eight tiles per
     // workgroup (one K-wave each): x is staged once for eight tiles
-    if (t.nw == 8 && t.splitk == 1 && M > 32 && nb >= 512) t.kw = 1;
+    if (t.nw == 8 && t.splitk == 1 && M > 32 && nb >= 512) {
+        t.kw = 1;
+        if (M > 64) t.r = 2;   // 128 rows: two tiles per wave share A
+    }
     // Step down to a built combination (a chunked x buffer must fit LDS).
     while (!complete_tiling(t, M, N, K)) {
         if (t.depth > 2)

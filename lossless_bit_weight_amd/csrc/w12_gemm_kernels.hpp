@@ -928,11 +928,20 @@ hipError_t launch_kw(const GemmArgs& a, const Tiling& t, hipStream_t s) {
 }
 
 // Eight-wave workgroups (512 threads): the MFMA kernels with x staged in LDS,
-// one tile per wave, ring depth 2 -- eight waves share each x chunk, which
-// halves the x traffic of the two-K-wave tiling on long-K weights.
+// one tile per wave (two at 64 and 128 rows with one K-wave), ring depth 2
+// -- eight waves share each x chunk, which halves the x traffic of the
+// two-K-wave tiling on long-K weights.
 template <class F, int MR>
 hipError_t dispatch8(const GemmArgs& a, const Tiling& t, hipStream_t s) {
-    if (t.r != 1 || t.depth != 2 || t.xdirect) return hipErrorInvalidValue;
+    if (t.depth != 2 || t.xdirect) return hipErrorInvalidValue;
+    if (t.r == 2) {
+        // two tiles per wave read each A fragment once for both: 64 and 128
+        // rows, one K-wave
+        if constexpr (MR >= 64)
+            if (t.kw == 1) return launch_ch<F, true, MR, 2, 1, 2, 8>(a, t, s);
+        return hipErrorInvalidValue;
+    }
+    if (t.r != 1) return hipErrorInvalidValue;
     switch (t.kw) {
         case 1: return launch_ch<F, true, MR, 1, 1, 2, 8>(a, t, s);
         case 2: return launch_ch<F, true, MR, 1, 2, 2, 8>(a, t, s);

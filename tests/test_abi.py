@@ -289,9 +289,12 @@ def test_default_large_m():
     assert (t.waves, t.kw, t.splitk) == (8, 2, 2)
     t = w12.w12_default_tiling(48, 5120, 17408)
     assert (t.waves, t.kw, t.splitk) == (8, 2, 3)
+    t = w12.w12_default_tiling(128, 34816, 5120)
+    assert (t.waves, t.r, t.kw, t.splitk) == (8, 2, 1, 1)
     for N, K in ((34816, 5120), (7168, 5120), (5120, 17408), (896, 5120)):
         t = w12.w12_default_tiling(128, N, K)
         assert (t.waves, t.kw, t.x_direct) == (8, 1, 0)
+        assert t.r == (2 if N == 34816 else 1)
         assert w12.w12_gemm_variant(100, N, K).startswith("w12_mfma_mt128_")
 
 
@@ -302,7 +305,7 @@ def test_tiling_waves_rejects():
     nbytes = ctypes.c_size_t()
     ok = (1, 1, 2, 2, 0, 1, 8)
     assert L.w12_gemm_workspace_bytes(16, 5120, 5120, w12._tiling_arg(ok), ctypes.byref(nbytes)) == 0
-    for bad in ((0, 1, 2, 2, 0, 1, 8), (1, 2, 2, 2, 0, 1, 8), (1, 1, 2, 4, 0, 1, 8),
+    for bad in ((0, 1, 2, 2, 0, 1, 8), (1, 2, 2, 2, 0, 1, 8), (1, 2, 1, 2, 0, 1, 8), (1, 1, 2, 4, 0, 1, 8),
                 (1, 1, 2, 2, 1, 1, 8), (1, 1, 8, 2, 0, 1, 4), (1, 1, 2, 2, 0, 1, 6),
                 (1, 1, 16, 2, 0, 1, 8)):
         rc = L.w12_gemm_workspace_bytes(16, 5120, 5120, w12._tiling_arg(bad), ctypes.byref(nbytes))

@@ -138,8 +138,9 @@ def test_large_m_default(oracle, shape, M):
 
 @pytest.mark.parametrize("tiling", [(1, 1, 1, 2, 0, 1, 8), (1, 1, 2, 2, 0, 1, 8),
                                     (1, 1, 1, 2, 0, 3, 8), (1, 1, 2, 2, 0, 7, 8),
-                                    (1, 1, 1, 2, 0, 64, 8)],
-                         ids=lambda t: "kw%d_s%d_w%d" % (t[2], t[5], t[6]))
+                                    (1, 1, 1, 2, 0, 64, 8), (1, 2, 1, 2, 0, 1, 8),
+                                    (1, 2, 1, 2, 0, 3, 8)],
+                         ids=lambda t: "r%d_kw%d_s%d_w%d" % (t[1], t[2], t[5], t[6]))
 def test_large_m_tilings(oracle, tiling):
     """Every 64- and 128-row tiling that is built, ragged shapes, split K
     down to one group per slice; a tiling that is not built for a shape is
@@ -155,6 +156,7 @@ def test_large_m_tilings(oracle, tiling):
             try:
                 y12 = w12.w12_gemm(xd, P.wt, tiling=tiling)
             except w12.W12Error as e:
+                # only a chunk beyond 128 KB of LDS is rejected here
                 mt = 64 if M <= 64 else 128
                 assert e.status == -6 and mt * 128 * tiling[2] * 2 > 32768, what
                 continue
