@@ -166,10 +166,13 @@ FORMATS = ("v1", "b")
 
 
 def _fmt_fn(fmt: str, name: str):
+    """(library function, its name) of the W12-v1 call `name` ("w12_...") for
+    containers of allocation `fmt`."""
     if fmt not in FORMATS:
         raise ValueError("unknown W12 format %r" % (fmt,))
-    return getattr(lib(), name if fmt == "v1" else "w12b_" + name[len("w12_"):]), \
-        (name if fmt == "v1" else "w12b_" + name[len("w12_"):])
+    full = name if fmt == "v1" else "w12b_" + name[len("w12_"):]
+    return getattr(lib(), full), full
+
 
 _BF16_TYPES = (torch.bfloat16, torch.int16, torch.uint16)
 
