@@ -320,3 +320,23 @@ def test_read_probe_rejects():
     assert L.w12_read_probe(A16, 24, A16, None) == -3
     assert L.w12_read_probe(A16, 16, P(4097), None) == -3
     assert L.w12_read_probe(A16, 0, A16, None) == -2
+
+
+def test_w12b_entry_points_and_routing():
+    """Every W12-v1 container call has its W12-b twin with the same
+    signature, and the binding routes a W12-b container to it."""
+    L = w12.lib()
+    for name in ("pack", "unpack", "exceptions", "gemm", "gemm_ws", "gemm_ex"):
+        fb, fv = getattr(L, "w12b_" + name), getattr(L, "w12_" + name)
+        assert fb.argtypes == fv.argtypes and fb.restype == fv.restype
+        assert w12._fmt_fn("b", "w12_" + name)[1] == "w12b_" + name
+        assert w12._fmt_fn("v1", "w12_" + name)[1] == "w12_" + name
+    with pytest.raises(ValueError):
+        w12._fmt_fn("v2", "w12_gemm")
+    # argument errors of the W12-b calls are the W12-v1 ones
+    assert L.w12b_pack(None, 4, 128, A16, A16, A16, A16, None, None) == -1
+    assert L.w12b_pack(A16, 4, 100, A16, A16, A16, A16, None, None) == -2
+    assert L.w12b_unpack(A16, A16, A16, A16, None, None, 4, 128, MIS, None) == -3
+    assert L.w12b_gemm(A16, 129, 512, A16, A16, A16, A16, None, None, 64, 512, A16, 64, 0,
+                       None) == -6
+    assert w12.w12_gemm_variant(1, 7168, 5120, 2).startswith("w12b_gemv_m1_")
