@@ -37,6 +37,16 @@ class Prepared:
         self.w_tiled = w12.w12_bf16_tile(self.w_bf16)
         torch.cuda.synchronize()
 
+    def container(self, fmt: str):
+        """The projected weight as a container of allocation fmt (W12-v1's
+        projection holds no exponent W12-b cannot store for these inputs)."""
+        if fmt == "v1":
+            return self.wt
+        if not hasattr(self, "wt_b"):
+            self.wt_b, bad = w12.pack(self.w_bf16, fmt="b")
+            assert bad == 0
+        return self.wt_b
+
     def ref_rows(self, oracle, rows):
         """Oracle projection of the raw rows (groups never span rows)."""
         sub = np.ascontiguousarray(self.raw[rows])
@@ -239,23 +249,25 @@ def _tiling_id(t):
     return "k%d_r%d_kw%d_d%d_x%d" % t[:5] + ("_w%d" % t[6] if len(t) > 6 else "")
 
 
+@pytest.mark.parametrize("fmt", ["v1", "b"])
 @pytest.mark.parametrize("tiling", w12.GEMV_TILINGS + w12.MFMA_TILINGS + w12.MFMA8_TILINGS,
                          ids=_tiling_id)
-def test_every_tiling(oracle, tiling):
+def test_every_tiling(oracle, tiling, fmt):
     """Every instantiated variant, single-chunk and chunked x, ragged rows and
-    a K tail, against the oracle; W12 and BF16 bitwise equal per tiling."""
+    a K tail, against the oracle; W12 (both allocations) and BF16 bitwise
+    equal per tiling."""
     Ms = ([1, 2, 4] if tiling[4] else [1, 3, 8]) if tiling[0] == 0 else [9, 16, 17, 32]
     for shape in ((301, 640), (33, 2688), (45, 5120), (77, 17408)):
         P = prepared(shape)
         rows = np.arange(P.N)
         w_ref = P.ref_rows(oracle, rows)
         for M in Ms:
-            what = "tiling %s %s M=%d" % (tiling, shape, M)
+            what = "tiling %s %s %s M=%d" % (fmt, tiling, shape, M)
             print(what, flush=True)
             x = inputs.gaussian_bf16((M, shape[1]), 1.0, 3 * M + shape[1])
             xd = to_dev(x)
             try:
-                y12 = w12.w12_gemm(xd, P.wt, tiling=tiling)
+                y12 = w12.w12_gemm(xd, P.container(fmt), tiling=tiling)
             except w12.W12Error as e:
                 # only a chunked x buffer that would not fit LDS is rejected
                 rows = M if tiling[0] == 0 else (16 if M <= 16 else 32)
@@ -281,7 +293,8 @@ SPLIT_BASES = [(0, 1, 4, 2, 0), (0, 2, 1, 2, 0), (0, 1, 2, 4, 1),
 @pytest.mark.parametrize("base", SPLIT_BASES,
                          ids=lambda t: "k%d_r%d_kw%d_d%d_x%d" % t[:5] + ("_w%d" % t[5] if len(t) > 5 else ""))
 @pytest.mark.parametrize("splitk", [2, 3, 7, 64])
-def test_split_k(oracle, base, splitk):
+@pytest.mark.parametrize("fmt", ["v1", "b"])
+def test_split_k(oracle, base, splitk, fmt):
     """K split over workgroups: ragged slices (G not a multiple of the
     factor), one group per slice (64 > G), chunked x inside a slice (K =
     17408 at 32 rows); W12 and BF16 bitwise equal, oracle tolerance."""
@@ -292,14 +305,14 @@ def test_split_k(oracle, base, splitk):
         rows = np.arange(P.N)
         w_ref = P.ref_rows(oracle, rows)
         for M in Ms:
-            what = "split tiling %s %s M=%d" % (tiling, shape, M)
+            what = "split tiling %s %s %s M=%d" % (fmt, tiling, shape, M)
             print(what, flush=True)
             if base[4] and not w12.x_direct_fits(M, base[1], base[3], base[0]):
                 continue
             x = inputs.gaussian_bf16((M, shape[1]), 1.0, 5 * M + shape[1])
             xd = to_dev(x)
             try:
-                y12 = w12.w12_gemm(xd, P.wt, tiling=tiling)
+                y12 = w12.w12_gemm(xd, P.container(fmt), tiling=tiling)
             except w12.W12Error as e:
                 assert e.status == -6, what   # a chunked x buffer too large for LDS
                 continue
