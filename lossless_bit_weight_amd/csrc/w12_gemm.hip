@@ -124,10 +124,16 @@ void bind_split(GemmArgs& a, const Tiling& t, void* ws) {
 //
 // M = 2-8: each extra x row costs the GEMV four more dot2 per 8 weights,
 // while the MFMA's cost does not grow until 16 rows (QKV M = 4: 12.9 us
-// against 14.6 us).  It reads its A fragments straight from memory, two
-// tiles per wave, four K-waves (no x barrier); x staged in LDS was 2-7%
-// slower on QKV and gate+up.  So is M = 9-12 on weights of 385-1024 tiles
-// and at most 64 groups per row (QKV M = 9: 12.1 us against 12.8).
+// against 14.6 us).  It reads its A fragments straight from memory, four
+// K-waves (no x barrier); x staged in LDS was 2-7% slower on QKV and
+// gate+up.  So is M = 9-12 on weights of 385-1024 tiles and at most 64
+// groups per row (QKV M = 9: 12.1 us against 12.8), and M <= 32 on weights
+// of at most 256 tiles (N = 512-4096, K = 5120: 13-48% faster than any
+// other tiling), where K is split from M = 9 into up to 256 / tiles slices
+// of >= 10 groups.  Two tiles per wave at 257-512 tiles (at most 256
+// workgroups; O M = 4: 10.2 us against 10.9 with one), one otherwise, and
+// two again above 512 tiles from M = 7 (gate+up M = 4: 43.3 us with one
+// against 45.0; M = 8: 46.6 with two against 48.1).
 //
 // Otherwise from M = 9 x is staged in LDS and shared by eight waves of a
 // 512-thread workgroup, with four K-waves (two tiles per workgroup) when K

@@ -223,7 +223,7 @@ def test_default_tiling():
 
 
 def test_default_waves_rule():
-    """M = 2-8, any M on weights of <= 256 tiles, and M = 9-12 on weights of
+    """M = 2-8, M <= 32 on weights of <= 256 tiles, and M = 9-12 on weights of
     385-1024 tiles and <= 64 groups per row, read x directly in 256-thread
     workgroups (one tile per wave on <= 256 tiles, two above); otherwise from
     M = 9 x is staged in LDS for 512-thread workgroups: four K-waves when K
