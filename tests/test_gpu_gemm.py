@@ -383,3 +383,26 @@ def test_ex_null_tiling_follows_workspace(oracle):
         outs.append(y)
     torch.cuda.synchronize()
     assert torch.equal(outs[0], ref_ws) and torch.equal(outs[1], ref_plain)
+
+
+def test_two_streams_split_k():
+    """Split-K GEMMs issued on two streams at once: each stream gets its own
+    workspace from the binding, and every result equals the one computed
+    alone on the default stream, bit for bit."""
+    P = prepared((301, 17408))
+    xs = [to_dev(inputs.gaussian_bf16((16, 17408), 1.0, 900 + i)) for i in range(8)]
+    ref = []
+    for x in xs:
+        ref.append(w12.w12_gemm(x, P.wt))
+    torch.cuda.synchronize()
+    ref = [r.cpu() for r in ref]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = [None] * len(xs)
+    for rep in range(3):
+        for i, x in enumerate(xs):
+            with torch.cuda.stream(streams[i % 2]):
+                outs[i] = w12.w12_gemm(x, P.wt)
+        torch.cuda.synchronize()
+        for i in range(len(xs)):
+            assert torch.equal(outs[i].cpu().view(torch.int32), ref[i].view(torch.int32)), (rep, i)
+    assert w12.w12_default_tiling(16, 301, 17408).splitk > 1
