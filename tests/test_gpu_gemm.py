@@ -177,7 +177,7 @@ def test_large_m_tilings(oracle, tiling):
             assert_gemm_close(y12h, oracle.gemm_bf16_f64(x, w_ref), oracle.tolerance(x, w_ref), what)
 
 
-@pytest.mark.parametrize("M", [1, 5, 8, 16, 32])
+@pytest.mark.parametrize("M", [1, 5, 8, 16, 32, 64, 128])
 def test_bf16_output_is_rounded_fp32(M):
     P = prepared("tiny")
     xd = to_dev(inputs.TINY.activations(M))
@@ -189,7 +189,7 @@ def test_bf16_output_is_rounded_fp32(M):
         assert torch.equal(yb.cpu().view(torch.int16), expect)
 
 
-@pytest.mark.parametrize("M", [1, 8, 16, 32])
+@pytest.mark.parametrize("M", [1, 8, 16, 32, 64, 128])
 def test_strided_x_and_y(oracle, M):
     P = prepared((1000, 640))
     x_full = inputs.gaussian_bf16((M, 640 + 64), 1.0, 5 + M)
@@ -205,11 +205,14 @@ def test_strided_x_and_y(oracle, M):
     assert torch.all(y_full[:, 1000:] == -7.0)
 
 
-@pytest.mark.parametrize("M", [1, 4, 8, 16, 32])
-def test_one_hot_rows_rebuild_weights_exactly(oracle, M):
+@pytest.mark.parametrize("name,M", [("qkv", M) for M in (1, 4, 8, 16, 32, 64, 128)]
+                         + [("gate_up", 128), ("down", 100)])
+def test_one_hot_rows_rebuild_weights_exactly(oracle, name, M):
     """x rows = unit vectors: y[m, :] is column k_m of W, bit for bit, i.e.
-    the in-register reassembly reproduces the BF16 weights exactly."""
-    P = prepared("qkv")
+    the in-register reassembly reproduces the BF16 weights exactly (every
+    kernel family the defaults reach, two tiles per wave at gate+up M =
+    128 included)."""
+    P = prepared(name)
     K = P.K
     ks = np.random.default_rng(M).choice(K, size=M, replace=False)
     x = np.zeros((M, K), np.uint16)
