@@ -559,6 +559,24 @@ def cpu_baseline(case, M, seconds):
 
     reps, dt = run(nthreads, seconds)
     reps1, dt1 = run(1, seconds / 4)
+    del q
+    # One layer of the 64-layer stack at M = 1 on host-generated weights of
+    # the stack's shapes, one decode + fp64 GEMM pass each, times 64.
+    from lossless_bit_weight_amd import inputs
+    layer_s = 0.0
+    layer_bytes = 0
+    for j, (N, K) in enumerate(inputs.STACK_SHAPES):
+        ql = oracle.pack(inputs.gaussian_bf16((N, K), 0.02, 30000 + j))
+        xl = inputs.gaussian_bf16((1, K), 1.0, 30100 + j)
+        t0 = time.perf_counter()
+        oracle.gemm_w12_f64(xl, *ql[:4], N, nthreads=nthreads)
+        layer_s += time.perf_counter() - t0
+        layer_bytes += 3 * oracle.plane_bytes(N, K) + oracle.meta_bytes(N, K)
+        del ql
+    stack = {"layer_s": layer_s, "step_s_extrapolated": 64 * layer_s,
+             "gbps": layer_bytes / layer_s / 1e9,
+             "sample": "one pass over each of the 4 weights of one stack layer at M=1, "
+                       "x64 (an extrapolation, not a measured 64-layer step)"}
     return {
         "value": reps * wb / dt / 1e9, "unit": "GB/s", "cores": nthreads, "kind": "oracle",
         "sample": "%d full passes over %s, M=%d (decode + fp64 GEMM), %.1f s"
@@ -568,6 +586,7 @@ def cpu_baseline(case, M, seconds):
                           "sample": "%d passes, %.1f s" % (reps1, dt1)},
         "pack": {"seconds": pack_s, "bf16_gbps": 2 * case.N * case.K / pack_s / 1e9,
                  "sample": "one oracle pack of %s" % case.name},
+        "stack_m1": stack,
     }
 
 
