@@ -123,3 +123,20 @@ def test_bf16_control_layout(oracle, N, K):
     t = w12.w12_bf16_tile(to_dev(bits))
     torch.cuda.synchronize()
     assert np.array_equal(to_host_u16(t.w), oracle.bf16_tile(bits))
+
+
+def test_readme_example():
+    """The usage example of the README, as written there."""
+    require_gpu()
+    torch.manual_seed(0)
+    w = torch.randn(7168, 5120, device="cuda").to(torch.bfloat16)
+    wt, flagged = w12.pack(w, exceptions=True)
+    x = torch.randn(4, 5120, device="cuda").to(torch.bfloat16)
+    y = w12.w12_gemm(x, wt)
+    assert torch.equal(w12.w12_unpack(wt).view(torch.int16), w.view(torch.int16))
+    wt_b, _ = w12.pack(w, exceptions=True, fmt="b")
+    assert torch.equal(w12.w12_unpack(wt_b).view(torch.int16), w.view(torch.int16))
+    ref = x.float() @ w.float().t()
+    assert flagged > 0 and y.shape == (4, 7168)
+    assert torch.allclose(y, ref, rtol=0, atol=1e-3 * float(x.float().norm(dim=1).max())
+                          * float(w.float().norm(dim=1).max()) + 1e-6)
