@@ -144,6 +144,82 @@ __device__ __forceinline__ void split_finish(const GemmArgs& g) {
     if (threadIdx.x == 0) __hip_atomic_store(g.cnt + blockIdx.x, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// The same protocol for the 64- and 128-row MFMA tiles, whose workgroups
+// hold up to 16K outputs: split_arrive counts the workgroup in (true in every
+// thread of the last one, which also resets the counter), and split_sum then
+// lets each lane finish the outputs it stored itself, taking its own slice
+// from registers and issuing the loads of the other slices together instead
+// of one output (and one memory round trip) after another.  (In the 16- and
+// 32-row kernels this form measured slower than split_finish.)
+__device__ __forceinline__ bool split_arrive(const GemmArgs& g) {
+    __shared__ int last;
+    __builtin_amdgcn_s_waitcnt(0);   // this wave's partial-sum stores are complete
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const bool l = __hip_atomic_fetch_add(g.cnt + blockIdx.x, 1u, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT) == gridDim.y - 1;
+        // all S workgroups have counted: nothing else touches the counter in
+        // this launch
+        if (l) __hip_atomic_store(g.cnt + blockIdx.x, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        last = l;
+    }
+    __syncthreads();
+    return last;
+}
+
+// Output (m, n) of y held in a lane's register i; ok = false: no output.
+struct OutPos {
+    int m;
+    bool ok;
+    int64_t n;
+};
+
+// In the last workgroup of a row block: v[i] holds this slice's sum of the
+// output pos(i) (an OutPos); it becomes the sum of the S slices' partial sums, added in slice order
+// 0, 1, ..., S-1 (the same order whichever workgroup is last, so y is
+// deterministic).  This slice's term comes from v itself; the loads of the
+// other slices are issued kP slices x kC outputs at a time, so that they
+// are in flight together.
+template <int NO, class Pos>
+__device__ __forceinline__ void split_sum(const GemmArgs& g, float (&v)[NO], Pos pos) {
+    constexpr int kC = NO < 32 ? NO : 32;
+    constexpr int kP = kC <= 16 ? 2 : 1;
+    static_assert(NO % kC == 0, "outputs come in whole chunks");
+    const int S = (int)gridDim.y;
+    const int me = (int)blockIdx.y;
+    const int64_t np = (g.N + 15) / 16 * 16;
+    const int64_t slice = (int64_t)g.M * np;
+#pragma unroll
+    for (int c0 = 0; c0 < NO; c0 += kC) {
+        float acc[kC];
+        for (int s0 = 0; s0 < S; s0 += kP) {
+            float t[kP][kC];
+#pragma unroll
+            for (int p = 0; p < kP; ++p) {
+                const int s = s0 + p;
+#pragma unroll
+                for (int i = 0; i < kC; ++i) {
+                    const OutPos o = pos(c0 + i);
+                    if (s == me)
+                        t[p][i] = v[c0 + i];
+                    else if (s < S && o.ok)
+                        t[p][i] = __hip_atomic_load(g.ws + s * slice + (int64_t)o.m * np + o.n,
+                                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    else
+                        t[p][i] = 0.f;
+                }
+            }
+#pragma unroll
+            for (int p = 0; p < kP; ++p)
+#pragma unroll
+                for (int i = 0; i < kC; ++i)
+                    if (s0 + p < S) acc[i] = s0 + p == 0 ? t[p][i] : acc[i] + t[p][i];
+        }
+#pragma unroll
+        for (int i = 0; i < kC; ++i) v[c0 + i] = acc[i];
+    }
+}
+
 // Exception corrections (W12 containers with an exception list): the main
 // loop multiplied each exception element's stored clamp (sign | window floor:
 // 2^(2 beta + 2 - 127) in W12-v1, 2^(b + 1 - 127) in W12-b); for every entry of `tile` whose group lies in this
@@ -818,6 +894,27 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs g) {
                     }
             }
         }
+        // 64 and 128 rows: each lane of the last workgroup finishes the
+        // outputs it stored
+        if constexpr (MR >= 64) {
+            if (gridDim.y > 1 && split_arrive(g) && kw == 0) {
+                constexpr int kNO = R * kMT * 4;
+                auto pos = [&](int i) {
+                    const int64_t n = (tile0 + i / (kMT * 4)) * 16 + col;
+                    const int m = 16 * (i / 4 % kMT) + 4 * q + i % 4;
+                    return OutPos{m, n < g.N && m < g.M, n};
+                };
+                float v[kNO];
+#pragma unroll
+                for (int i = 0; i < kNO; ++i) v[i] = macc[i / (kMT * 4)][i / 4 % kMT][i % 4];
+                split_sum(g, v, pos);
+#pragma unroll
+                for (int i = 0; i < kNO; ++i) {
+                    const OutPos o = pos(i);
+                    if (o.ok) store_y(g, o.m, o.n, v[i]);
+                }
+            }
+        }
     } else {
         // Add the 4 quarter sums of each row (fixed butterfly order).
 #pragma unroll
@@ -880,7 +977,8 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs g) {
             }
         }
     }
-    if (gridDim.y > 1) split_finish<kRowWaves * R, NW * 64>(g);
+    if constexpr (!(MFMA && MR >= 64))
+        if (gridDim.y > 1) split_finish<kRowWaves * R, NW * 64>(g);
 }
 
 // ---- launch helpers ----------------------------------------------------------------------
