@@ -145,13 +145,18 @@ void bind_split(GemmArgs& a, const Tiling& t, void* ws) {
 // K-waves, its 128 KB x double buffer included (down M = 24: 41.3 us
 // against 46.5 with 256 threads).
 //
-// M = 33-128: x padded to 64 or 128 rows, in LDS, eight waves, two K-waves
-// (64 rows) or one (128 rows: a 128 KB double buffer holds 256 columns); a
-// weight of >= 512 row blocks that K does not split takes one K-wave at 64
-// rows too (gate+up M = 64: 75.7 us against 84.7 with two) and, at 128
-// rows, two tiles per wave, which read each A fragment from LDS once for
-// both (gate+up M = 128: 94.9 us against 130.7; on smaller grids the halved
-// workgroup count loses: QKV 87.7 against 48.3).
+// M = 33-128: x padded to 64 or 128 rows, in LDS, eight waves.  With a
+// workspace, on weights of >= 256 tiles: one K-wave (eight tiles per
+// workgroup, x staged once for all of them) and K split into as many slices
+// of >= 10 groups as fill 256 workgroups -- QKV and O four slices, down six
+// (QKV M = 64: 21.1 us against 22.9 with two K-waves in two slices; M = 128:
+// 30.6 against 41.1 in two slices; down M = 128: 55.5 against 80.1 in three).
+// Otherwise two K-waves (64 rows) or one (128 rows: a 128 KB double buffer
+// holds 256 columns); a weight of >= 512 row blocks that K does not split
+// takes one K-wave and two tiles per wave, which read each A fragment from
+// LDS once for both (gate+up M = 64: 74.2 us against 80.5 with one tile;
+// M = 128: 93.6 against 130.7; on smaller grids the halved workgroup count
+// loses: QKV M = 128 87.7 against 48.3).
 //
 // Splitting K across workgroups (the _ws entry points, MFMA only): slices of
 // at least 40 groups (5120 weights) keep each workgroup's prologue and
@@ -204,13 +209,26 @@ Tiling choose_tiling(int M, int64_t N, int64_t K, bool allow_splitk) {
         }
         s = s < kMaxSplitK ? s : kMaxSplitK;
         t.splitk = s > 1 ? (int)s : 1;
+        // above 32 rows, on weights of >= 256 tiles: one K-wave (eight tiles
+        // per workgroup, x staged once for all eight) and as many slices of
+        // >= 10 groups as fill 256 workgroups
+        if (M > 32 && ntiles >= 256) {
+            const int64_t nb1 = (ntiles + 7) / 8;
+            int64_t s1 = 256 / nb1;
+            s1 = s1 < G / 10 ? s1 : G / 10;
+            if (s1 >= 2) {
+                t.kw = 1;
+                t.splitk = (int)(s1 < kMaxSplitK ? s1 : kMaxSplitK);
+            }
+        }
     }
     if (t.nw == 8 && t.splitk == 1 && (M <= 16 || nb < 128)) t.kw = 4;
     // above 32 rows a grid of >= 512 row blocks unsplit keeps eight tiles per
-    // workgroup (one K-wave each): x is staged once for eight tiles
+    // workgroup (one K-wave each): x is staged once for eight tiles, and two
+    // tiles per wave share each A fragment
     if (t.nw == 8 && t.splitk == 1 && M > 32 && nb >= 512) {
         t.kw = 1;
-        if (M > 64) t.r = 2;   // 128 rows: two tiles per wave share A
+        t.r = 2;
     }
     // Step down to a built combination (a chunked x buffer must fit LDS).
     while (!complete_tiling(t, M, N, K)) {

@@ -121,7 +121,8 @@ def test_variant_selection():
     assert w12.w12_gemm_variant(9, 7168, 5120).startswith("w12_mfma_mt16_")
     assert w12.w12_gemm_variant(16, 34816, 5120).startswith("w12_mfma_mt16_")
     assert w12.w12_gemm_variant(17, 5120, 17408).startswith("w12_mfma_mt32_")
-    assert w12.w12_gemm_variant(33, 5120, 17408).startswith("w12_mfma_mt64_r1_kw2_d2_chunked_w8")
+    assert w12.w12_gemm_variant(33, 5120, 17408).startswith("w12_mfma_mt64_r1_kw1_d2_chunked_w8_s6")
+    assert w12.w12_gemm_variant(33, 2048, 5120).startswith("w12_mfma_mt64_r1_kw2_d2_chunked_w8")
     assert w12.w12_gemm_variant(65, 7168, 5120).startswith("w12_mfma_mt128_r1_kw1_d2_chunked_w8")
     assert w12.w12_gemm_variant(128, 896, 5120).startswith("w12_mfma_mt128_")
     assert w12.w12_gemm_variant(129, 5120, 17408) is None
@@ -281,16 +282,23 @@ def test_default_small_weights():
 
 def test_default_large_m():
     """M = 33-128: 64 or 128 padded rows in 512-thread workgroups with x in
-    LDS; one K-wave at 128 rows, and at 64 rows on an unsplit grid of >= 512
-    row blocks; K split as above 16 rows."""
+    LDS.  On weights of >= 256 tiles one K-wave, K split into as many slices
+    of >= 10 groups as fill 256 workgroups; a grid of >= 512 row blocks that
+    K does not split takes two tiles per wave; smaller weights split K as
+    above 16 rows."""
     t = w12.w12_default_tiling(64, 34816, 5120)
-    assert (t.kind, t.waves, t.kw, t.x_direct, t.splitk) == (1, 8, 1, 0, 1)
+    assert (t.kind, t.waves, t.r, t.kw, t.x_direct, t.splitk) == (1, 8, 2, 1, 0, 1)
     t = w12.w12_default_tiling(64, 7168, 5120)
-    assert (t.waves, t.kw, t.splitk) == (8, 2, 2)
+    assert (t.waves, t.kw, t.splitk) == (8, 1, 4)
     t = w12.w12_default_tiling(48, 5120, 17408)
+    assert (t.waves, t.kw, t.splitk) == (8, 1, 6)
+    t = w12.w12_default_tiling(64, 2048, 5120)
     assert (t.waves, t.kw, t.splitk) == (8, 2, 3)
     t = w12.w12_default_tiling(128, 34816, 5120)
     assert (t.waves, t.r, t.kw, t.splitk) == (8, 2, 1, 1)
+    # without a workspace K is never split
+    t = w12.w12_default_tiling(128, 7168, 5120, False)
+    assert (t.waves, t.splitk) == (8, 1)
     for N, K in ((34816, 5120), (7168, 5120), (5120, 17408), (896, 5120)):
         t = w12.w12_default_tiling(128, N, K)
         assert (t.waves, t.kw, t.x_direct) == (8, 1, 0)
