@@ -146,6 +146,20 @@ def test_large_m_default(oracle, shape, M):
     _check(oracle, P, x, np.arange(P.N), "large M %s M=%d" % (shape, M))
 
 
+@pytest.mark.parametrize("shape", [(7168, 5120), (5120, 17408), (4100, 5120)])
+@pytest.mark.parametrize("M", [64, 100, 128])
+def test_large_m_split_default(oracle, shape, M):
+    """Weights of >= 256 tiles above 32 rows: the default takes one K-wave
+    and K split into four to six slices, which the last workgroup of each
+    row block finishes from its lanes' registers (full QKV and down shapes,
+    and a ragged 257-tile weight)."""
+    t = w12.w12_default_tiling(M, *shape)
+    assert (t.kw, t.waves) == (1, 8) and t.splitk >= 4
+    P = prepared(shape)
+    x = inputs.gaussian_bf16((M, shape[1]), 1.0, 29 * M + shape[0])
+    _check(oracle, P, x, _sample_rows(P.N, n=256, seed=M), "large M split %s M=%d" % (shape, M))
+
+
 @pytest.mark.parametrize("tiling", [(1, 1, 1, 2, 0, 1, 8), (1, 1, 2, 2, 0, 1, 8),
                                     (1, 1, 1, 2, 0, 3, 8), (1, 1, 2, 2, 0, 7, 8),
                                     (1, 1, 1, 2, 0, 64, 8), (1, 2, 1, 2, 0, 1, 8),
