@@ -3,11 +3,16 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-sweep] [--no-stack]
                     [--no-cpu-baseline] [--workload qkv|gate_up|down] [--m M]
 
-Prints ONE JSON line.  The headline workload is the attention QKV projection
-of a ~27B dense decoder at single-request decode: W [7168, 5120] packed to
-W12 (group 128), x [1, 5120], y fp32.  One step = one w12_gemm launch over
-that weight (x staged in LDS, the three planes streamed, BF16 rebuilt in
-registers, fp32 dot products, epilogue).  `value` is the effective weight
+Prints ONE compact JSON line on stdout (the headline, its roofline and the
+CPU oracle's rate); the full record -- sweep, shard shapes, W12-b, codec,
+exception-list and stack figures -- goes to stderr as one "detail:" line and,
+with --detail-out PATH, to a file.
+
+The headline workload is the attention QKV projection of a ~27B dense
+decoder at single-request decode: W [7168, 5120] packed to W12 (group 128),
+x [1, 5120], y fp32.  One step = one w12_gemm launch over that weight (the
+three planes streamed with x, BF16 rebuilt in registers, fp32 dot products,
+epilogue).  `value` is the effective weight
 stream rate: stored W12 bytes (planes + meta) per launch x launches / time.
 
 Timing protocol (the pages warm up before timing and tune kernels against
@@ -81,6 +86,8 @@ def parse():
     ap.add_argument("--summarize-counters", nargs=2, metavar=("COUNTER_CSV", "VARIANT"),
                     help="print a markdown summary of any rocprofv3 --pmc run")
     ap.add_argument("--command", default="", help="command line recorded in a summary")
+    ap.add_argument("--detail-out", default="",
+                    help="also write the full record (sweep, shards, codec, stack...) to this file")
     ap.add_argument("--pmc-calibration", action="store_true",
                     help="also run a plain elementwise kernel over 256 MiB (bitwise not: "
                          "reads and writes 256 MiB) 4 times, the known-size reference for "
@@ -769,45 +776,14 @@ def main():
         print("cpu baseline: %s" % json.dumps(cpu), file=sys.stderr, flush=True)
 
     kernel = head["w12_kernel"]
-    achieved = head["w12_alg_gbps"]
     traffic = stored_traffic(kernel)
-    out = {
-        "metric": METRIC,
-        "value": round(head["w12_weight_gbps"], 2),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": head["launches"],
-        "warmup": args.warmup,
-        "ms_per_step": head["w12_us"] / 1e3,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": "%s: W[%d,%d] as W12 (group 128), x[%d,%d] BF16, y fp32%s"
-                               % (WORKLOAD_NAMES[args.workload], head_case.N, head_case.K, head_m,
-                                  head_case.K, "; single-request decode GEMV" if head_m == 1 else ""),
-                   "N": head_case.N, "K": head_case.K, "M": head_m, "group": 128,
-                   "rotation_copies": rotation},
-        "pct_hbm_peak": round(100.0 * head["w12_weight_gbps"] / HBM_PEAK_GBPS, 2),
+    detail = {
         "device": {"name": props.name, "cus": props.multi_processor_count,
                    "memory": device_memory_peak()},
-        "read_ceiling": {"w12_bytes": ceilings[args.workload][0]["bytes"],
-                         "w12_bytes_gbps": round(ceilings[args.workload][0]["gbps"], 1),
-                         "bf16_bytes": ceilings[args.workload][1]["bytes"],
-                         "bf16_bytes_gbps": round(ceilings[args.workload][1]["gbps"], 1),
-                         "w12_frac": round(head["w12_frac_of_read_ceiling"], 4),
-                         "bf16_frac": round(head["bf16_frac_of_read_ceiling"], 4),
-                         "by_workload": {k: {"w12_bytes_gbps": round(v[0]["gbps"], 1),
-                                             "bf16_bytes_gbps": round(v[1]["gbps"], 1)}
-                                         for k, v in ceilings.items()}},
-        "w12_us": round(head["w12_us"], 3),
-        "bf16_us": round(head["bf16_us"], 3),
-        "speedup_vs_bf16": round(head["speedup_vs_bf16"], 4),
-        "roofline": {"bound": "hbm", "kernel": kernel, "achieved": round(achieved, 1),
-                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": traffic, "alg_bytes_per_launch": head["w12_alg_bytes"]},
+        "headline": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in head.items()},
+        "read_ceiling": {k: {"w12_bytes_gbps": round(v[0]["gbps"], 1),
+                             "bf16_bytes_gbps": round(v[1]["gbps"], 1)}
+                         for k, v in ceilings.items()},
         "cpu_baseline": cpu,
         "sweep": [{k: (round(v, 3) if isinstance(v, float) else v) for k, v in r.items()}
                   for r in sweep],
@@ -819,7 +795,68 @@ def main():
         "stack": stack,
         "source_sha": source_sha(),
     }
-    print(json.dumps(out), flush=True)
+    # The full record goes to stderr (one line) and, if asked, to a file; the
+    # one stdout line is the compact headline.
+    print("detail: %s" % json.dumps(detail), file=sys.stderr, flush=True)
+    if args.detail_out:
+        os.makedirs(os.path.dirname(os.path.abspath(args.detail_out)), exist_ok=True)
+        with open(args.detail_out, "w") as f:
+            json.dump(detail, f, indent=1)
+    out = headline_record(head, args.workload, head_case, head_m, args.warmup, rotation,
+                          ceilings[args.workload], traffic, cpu, sweep, stack)
+    print(json.dumps(out, separators=(",", ":")), flush=True)
+
+
+def headline_record(head, workload, case, M, warmup, rotation, ceiling, traffic, cpu, sweep,
+                    stack):
+    """The one JSON line bench.py prints on stdout (kept well under 2 KB):
+    the headline launch's rate, its roofline and the CPU oracle's rate, plus
+    the smallest W12 / BF16 speedup of the sweep at M = 1-32 and the stack
+    step at M = 1.  Everything else is in the detail record."""
+    achieved = head["w12_alg_gbps"]
+    small = [r for r in sweep if r["M"] <= 32]
+    worst = min(small, key=lambda r: r["speedup_vs_bf16"]) if small else None
+    st1 = None
+    if stack:
+        st1 = next((r for r in stack["by_m"] if r["M"] == 1), None)
+    cpu_short = None
+    if cpu is not None:
+        cpu_short = {"value": round(cpu["value"], 3), "unit": cpu["unit"], "cores": cpu["cores"],
+                     "kind": cpu["kind"], "sample": cpu["sample"], "nproc": cpu["nproc"],
+                     "cpu_model": cpu["cpu_model"],
+                     "single_thread": round(cpu["single_thread"]["value"], 3)}
+    return {
+        "metric": METRIC,
+        "value": round(head["w12_weight_gbps"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": head["launches"],
+        "warmup": warmup,
+        "ms_per_step": round(head["w12_us"] / 1e3, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "%s W[%d,%d] W12 group 128, x[%d,%d] bf16, y fp32"
+                               % (WORKLOAD_NAMES[workload], case.N, case.K, M, case.K),
+                   "N": case.N, "K": case.K, "M": M, "rotation_copies": rotation},
+        "pct_hbm_peak": round(100.0 * head["w12_weight_gbps"] / HBM_PEAK_GBPS, 2),
+        "w12_us": round(head["w12_us"], 3),
+        "bf16_us": round(head["bf16_us"], 3),
+        "speedup_vs_bf16": round(head["speedup_vs_bf16"], 4),
+        "read_ceiling_gbps": round(ceiling[0]["gbps"], 1),
+        "roofline": {"bound": "hbm", "kernel": head["w12_kernel"], "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic, "alg_bytes_per_launch": head["w12_alg_bytes"]},
+        "cpu_baseline": cpu_short,
+        "sweep_min_speedup_m1_32": None if worst is None else
+            {"workload": worst["workload"], "M": worst["M"],
+             "speedup": round(worst["speedup_vs_bf16"], 4)},
+        "stack_m1": None if st1 is None else {"w12_ms": st1["w12_ms"],
+                                              "speedup_vs_bf16": st1["speedup_vs_bf16"]},
+    }
 
 
 if __name__ == "__main__":
