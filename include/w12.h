@@ -103,8 +103,10 @@ const char *w12_status_string(int status);
 /* Rows of the container: N rounded up to a multiple of 16 (0 if N < 1). */
 int64_t w12_padded_rows(int64_t N);
 
-/* Bytes of ONE nibble plane for an [N, K] weight: Np*K/2, i.e. exactly 0.75x
- * the BF16 bytes / 3 when N % 16 == 0 (0 on bad shape). */
+/* Bytes of ONE nibble plane for an [N, K] weight: Np*K/2, so the three
+ * planes hold exactly 0.75x the BF16 bytes when N % 16 == 0 -- 12 of every
+ * 16 bits, in three 4-bit planes (AI Radar paper summary of SpecPilot,
+ * English edition, "Reasons", mechanisms item).  0 on bad shape. */
 size_t w12_plane_bytes(int64_t N, int64_t K);
 
 /* Bytes of the metadata array: Np*K/128 (0 on bad shape). */
@@ -115,7 +117,13 @@ size_t w12_bf16_tiled_bytes(int64_t N, int64_t K);
 
 /*
  * w12_pack -- BF16 [N, K] (row-major, contiguous) -> three planes + meta.
- * The format's encoder (a1): one 128-weight group at a time, integer only.
+ * The format's encoder: it splits every BF16 weight into three 4-bit planes
+ * (AI Radar paper summary of SpecPilot, English edition, "Reasons",
+ * mechanisms item: W12 keeps 12 of the 16 bits of each weight, as three
+ * nibble planes; HotRepo digest "StargazerX0/SpecPilot", project
+ * introduction, second paragraph).  One 128-weight
+ * group at a time, integer only; a group it cannot store exactly is flagged,
+ * never silently rounded.
  *   w          : device, N*K BF16 words, 16-byte aligned.
  *   p0, p1, p2 : device outputs, w12_plane_bytes(N, K) bytes each, 16-byte
  *                aligned; padding rows are written as zeros.
@@ -129,9 +137,12 @@ int w12_pack(const uint16_t *w, int64_t N, int64_t K,
              uint32_t *bad_groups, void *stream);
 
 /*
- * w12_exceptions -- the exception list of a BF16 [N, K] weight (the escape
- * path that makes the container lossless; format above).  Three launches:
- * per-block counts into `workspace`, one scan, and the entries.
+ * w12_exceptions -- the exception list of a BF16 [N, K] weight: the escape
+ * path that keeps the container lossless for every input, since the pages
+ * call W12 lossless (AI Radar paper summary of SpecPilot, English edition,
+ * "Reasons", mechanisms item) without saying how values outside a group's
+ * 12-bit range are kept.  Format above.  Three launches: per-block counts
+ * into `workspace`, one scan, and the entries.
  *   w           : device, the same N*K BF16 words given to w12_pack, 16-byte
  *                 aligned.
  *   workspace   : device, w12_exceptions_workspace_bytes(N, K) bytes, 4-byte
@@ -153,9 +164,11 @@ int w12_exceptions(const uint16_t *w, int64_t N, int64_t K,
                    uint32_t *total, void *stream);
 
 /*
- * w12_unpack -- planes + meta (+ exception list) -> BF16 [N, K] (a7, the
- * inverse of w12_pack on every unflagged group, and on every group when the
- * exception list is given; same in-register decode as the GEMMs).
+ * w12_unpack -- planes + meta (+ exception list) -> BF16 [N, K]: the
+ * lossless inverse of w12_pack (AI Radar paper summary of SpecPilot, English
+ * edition, "Reasons", mechanisms item: W12 is lossless and rebuilt bit by
+ * bit), exact on every unflagged group, and on every group when the
+ * exception list is given; same in-register decode as the GEMMs.
  *   p0, p1, p2 : device, w12_plane_bytes(N, K) bytes each, 16-byte aligned.
  *   meta       : device, w12_meta_bytes(N, K) bytes.
  *   exc_offsets, exc_entries : the container's exception list, or both NULL.
@@ -169,7 +182,11 @@ int w12_unpack(const void *p0, const void *p1, const void *p2,
 
 /*
  * w12_gemm -- y[m, n] = sum_k x[m, k] * W[n, k] with W read from a W12
- * container and rebuilt in registers (a2-a6), fp32 accumulation.
+ * container and rebuilt bit by bit in registers inside the GEMM (AI Radar
+ * paper summary of SpecPilot, English edition, "Reasons", mechanisms item;
+ * HotRepo digest "StargazerX0/SpecPilot", project introduction, second
+ * paragraph: decoded bit-exactly inside the GEMM at batch 1-32), fp32
+ * accumulation.
  *   x      : device BF16 [M, K], row stride ldx elements (ldx >= K,
  *            ldx % 8 == 0), 16-byte aligned.  1 <= M <= 128.
  *   p0..meta: the container of an [N, K] weight as written by w12_pack.
@@ -195,8 +212,10 @@ int w12_gemm(const uint16_t *x, int64_t M, int64_t ldx,
              void *y, int64_t ldy, int y_type, void *stream);
 
 /*
- * w12_bf16_tile -- row-major BF16 [N, K] -> the layout of the BF16 control
- * (a8): the same (tile, group) blocks and lane order as the W12 planes,
+ * w12_bf16_tile -- row-major BF16 [N, K] -> the layout of the BF16 control,
+ * the plain BF16 decoding W12 is measured against (HotRepo digest
+ * "StargazerX0/SpecPilot", project introduction, second paragraph): the
+ * same (tile, group) blocks and lane order as the W12 planes,
  * with whole BF16 words: block (T, g) of 2048 words, 1 KB sub-block b, lane
  * L's 8 words k = 128*g + 32*b + 8*q + e in natural order; padding rows zero.
  *   w       : device, N*K words, 16-byte aligned.
@@ -207,8 +226,12 @@ int w12_bf16_tile(const uint16_t *w, int64_t N, int64_t K, uint16_t *w_tiled,
                   void *stream);
 
 /*
- * bf16_gemm -- the control: the same kernels, tiling, memory access order and
- * summation order as w12_gemm, with W read as plain BF16 words (a8).  For
+ * bf16_gemm -- the control: plain BF16 decoding, the baseline W12 is said to
+ * speed up by 1.15-1.26x at batch 1-32 (HotRepo digest
+ * "StargazerX0/SpecPilot", project introduction, second paragraph; AI Radar
+ * paper summary of SpecPilot, English edition, "Reasons", mechanisms item).
+ * The same kernels, tiling, memory access order and summation order as
+ * w12_gemm, with W read as plain BF16 words.  For
  * w_tiled = w12_bf16_tile(unpack(pack(W))) the two calls return bitwise
  * identical y.
  *   w_tiled : device, the [N, K] weight in the control layout (see
@@ -280,7 +303,8 @@ int w12_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K,
 
 /*
  * w12_gemm / bf16_gemm with the default tiling including split K, which
- * fills the GPU on shapes with few row blocks (small N, long K).
+ * fills the GPU on shapes with few row blocks (small N, long K).  Same
+ * operation and passages as w12_gemm and bf16_gemm.
  *   workspace       : device, at least w12_gemm_workspace_bytes(M, N, K,
  *                     NULL) bytes, 256-byte aligned, zero-filled before its
  *                     first use (every call leaves its counters at zero);
@@ -298,7 +322,8 @@ int bf16_gemm_ws(const uint16_t *x, int64_t M, int64_t ldx,
                  void *y, int64_t ldy, int y_type,
                  void *workspace, size_t workspace_bytes, void *stream);
 
-/* The GEMMs with an explicit tiling.  tiling = NULL selects the default of
+/* The GEMMs with an explicit tiling (same operation and passages as w12_gemm
+ * and bf16_gemm).  tiling = NULL selects the default of
  * w12_gemm_ws if a workspace is given, else that of w12_gemm.  A tiling with
  * splitk > 1 needs the workspace w12_gemm_workspace_bytes reports for it.
  * Additional errors: W12_ERR_UNSUPPORTED for a tiling that is not built or
