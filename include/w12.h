@@ -72,7 +72,7 @@
 extern "C" {
 #endif
 
-#define W12_ABI_VERSION 6
+#define W12_ABI_VERSION 7
 #define W12_GROUP 128
 #define W12_TILE_ROWS 16
 #define W12_MAX_M 128
@@ -86,7 +86,8 @@ typedef enum {
     W12_ERR_DTYPE = -4,       /* unknown output type                         */
     W12_ERR_UNSUPPORTED = -6, /* M > 128, or a tiling not built             */
     W12_ERR_HIP = -7,         /* the HIP launch reported an error            */
-    W12_ERR_WORKSPACE = -8    /* split-K workspace NULL, short or misaligned */
+    W12_ERR_WORKSPACE = -8,   /* split-K workspace NULL, short or misaligned */
+    W12_ERR_SCRATCH = -9      /* w12_gemm_noalloc: partial sums over 16 MiB   */
 } w12_status_t;
 
 typedef enum {
@@ -347,6 +348,35 @@ int bf16_gemm_ex(const uint16_t *x, int64_t M, int64_t ldx,
  */
 const char *w12_gemm_variant(int64_t M, int64_t N, int64_t K, int is_w12,
                              int allow_splitk);
+
+/*
+ * w12_gemm_noalloc -- w12_gemm_ws for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same operation, default tiling (K split over
+ * workgroups where that is faster) and result, bit for bit, as w12_gemm_ws,
+ * with the split-K counters and partial sums kept in a fixed array inside
+ * the library instead of a caller workspace.  The call allocates and frees
+ * nothing, neither does any library routine it calls.
+ *   arguments : as w12_gemm (the caller still owns x, the container and y).
+ *   limit     : the shape's split-K partial sums, splitk * M * Np * 4 bytes
+ *               of the w12_gemm_ws default tiling (w12_gemm_workspace_bytes
+ *               minus its 64 KB counter area), must fit 16 MiB -- every M up
+ *               to 128 on weights up to 7168 x 5120 and 5120 x 17408 does;
+ *               larger ones return W12_ERR_SCRATCH before any launch.
+ *   scratch   : 16 MiB + 64 KB of device memory per GPU the call runs on,
+ *               held from its first call on that GPU until the process ends
+ *               (that first call also enqueues one small kernel that clears
+ *               the counters).  Every call on one GPU shares that GPU's
+ *               array, so calls that may overlap on one GPU -- on different
+ *               streams, or from different threads -- race and must be
+ *               ordered by the caller.
+ * Errors: those of w12_gemm, W12_ERR_SCRATCH, W12_ERR_HIP.
+ */
+int w12_gemm_noalloc(const uint16_t *x, int64_t M, int64_t ldx,
+                     const void *p0, const void *p1, const void *p2,
+                     const uint8_t *meta, const uint32_t *exc_offsets,
+                     const uint32_t *exc_entries, int64_t N, int64_t K,
+                     void *y, int64_t ldy, int y_type, void *stream);
 
 /*
  * W12-b: the arbitrary-base bit allocation (the alternative to W12-v1 that

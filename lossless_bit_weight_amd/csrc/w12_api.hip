@@ -1,8 +1,12 @@
 // w12_api.hip -- the C ABI declared in include/w12.h: host-side argument
 // checks, tiling choice, and launches on the caller's stream.  Nothing here
-// allocates, synchronises or keeps state (split-K launches keep their
-// counters in the caller's workspace).
+// allocates or synchronises.  Split-K launches keep their counters in the
+// caller's workspace -- except w12_gemm_noalloc, which uses the library's
+// own fixed device array `scratch` (defined below with its set-up), for
+// callers that cannot allocate.
 #include <stdint.h>
+
+#include <mutex>
 
 #include "../../include/w12.h"
 #include "w12_internal.hpp"
@@ -84,6 +88,7 @@ const char* w12_status_string(int status) {
         case W12_ERR_UNSUPPORTED: return "unsupported size or tiling (M > 128, or a tiling that is not built for this shape)";
         case W12_ERR_HIP: return "HIP launch failed";
         case W12_ERR_WORKSPACE: return "workspace missing, too small or not 256-byte aligned for this split-K tiling";
+        case W12_ERR_SCRATCH: return "the split-K partial sums of this shape exceed the library's fixed 16 MiB scratch (w12_gemm_noalloc); use w12_gemm_ws with a workspace";
         default: return "unknown status";
     }
 }
@@ -370,6 +375,77 @@ const char* w12_gemm_variant(int64_t M, int64_t N, int64_t K, int is_w12, int al
     if (check_weight_shape(N, K) != W12_OK || M < 1 || M > W12_MAX_M) return nullptr;
     const int fetch = is_w12 == 2 ? w12::kFetchW12B : is_w12 != 0 ? w12::kFetchW12 : w12::kFetchBF16;
     return w12::tiling_name(w12::choose_tiling((int)M, N, K, allow_splitk != 0), fetch);
+}
+
+}  // extern "C"
+
+// ---- w12_gemm_noalloc: split-K scratch in a fixed device array ---------------
+// The counters (kCounterBytes, one per row block) followed by room for
+// kScratchPartialBytes of fp32 partial sums.  Each GPU the library runs on
+// holds its own copy for the life of the process.  In host code `scratch`
+// names a host-side stand-in, never the device copy: kernels and copies
+// take the address hipGetSymbolAddress returns for the current device.
+namespace {
+constexpr size_t kScratchPartialBytes = (size_t)16 << 20;
+constexpr size_t kScratchBytes = (size_t)w12::kCounterBytes + kScratchPartialBytes;
+}  // namespace
+
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+__global__ void zero_words(uint32_t* p, int n) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0u;
+}
+
+// Device address of `scratch` on the current device.  The first call on a
+// device looks it up and clears the counter area on `s` (a fill kernel, so
+// the call may also be captured in a graph); every split-K launch leaves the
+// counters at zero again, and the partial sums are written before they are
+// read, so nothing else needs clearing.
+int scratch_on_device(hipStream_t s, void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return W12_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr)
+            return W12_ERR_HIP;
+        constexpr int kWords = (int)(w12::kCounterBytes / 4);
+        hipLaunchKernelGGL(zero_words, dim3((kWords + 255) / 256), dim3(256), 0, s,
+                           static_cast<uint32_t*>(ptr), kWords);
+        if (hipGetLastError() != hipSuccess) return W12_ERR_HIP;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return W12_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int w12_gemm_noalloc(const uint16_t* x, int64_t M, int64_t ldx, const void* p0, const void* p1,
+                     const void* p2, const uint8_t* meta, const uint32_t* exc_offsets,
+                     const uint32_t* exc_entries, int64_t N, int64_t K, void* y, int64_t ldy,
+                     int y_type, void* stream) {
+    // the argument checks of w12_gemm_ws, then the scratch limit, all before
+    // any HIP call
+    if (!p0 || !p1 || !p2 || !meta) return W12_ERR_NULL;
+    if (int rc = check_gemm_common(x, M, ldx, N, K, y, ldy, y_type)) return rc;
+    if (!aligned16(p0) || !aligned16(p1) || !aligned16(p2)) return W12_ERR_ALIGN;
+    if (int rc = check_exceptions(exc_offsets, exc_entries, N, K)) return rc;
+    const w12::Tiling t = w12::choose_tiling((int)M, N, K, true);
+    if (w12::workspace_bytes(t, (int)M, N) > kScratchBytes) return W12_ERR_SCRATCH;
+    void* ws = nullptr;
+    if (int rc = scratch_on_device(static_cast<hipStream_t>(stream), &ws)) return rc;
+    return gemm_w12(w12::kFetchW12, x, M, ldx, p0, p1, p2, meta, exc_offsets, exc_entries, N, K, y,
+                    ldy, y_type, nullptr, true, ws, kScratchBytes, stream);
 }
 
 }  // extern "C"

@@ -29,7 +29,7 @@ OUT_F32 = 1
 STATUS = {
     0: "W12_OK", -1: "W12_ERR_NULL", -2: "W12_ERR_SHAPE", -3: "W12_ERR_ALIGN",
     -4: "W12_ERR_DTYPE", -6: "W12_ERR_UNSUPPORTED", -7: "W12_ERR_HIP",
-    -8: "W12_ERR_WORKSPACE",
+    -8: "W12_ERR_WORKSPACE", -9: "W12_ERR_SCRATCH",
 }
 
 
@@ -134,6 +134,8 @@ def lib() -> ctypes.CDLL:
     L.w12_gemm_ws.restype = i32
     L.bf16_gemm_ws.argtypes = [p, i64, i64, p, i64, i64, p, i64, i32, p, sz, p]
     L.bf16_gemm_ws.restype = i32
+    L.w12_gemm_noalloc.argtypes = [p, i64, i64, p, p, p, p, p, p, i64, i64, p, i64, i32, p]
+    L.w12_gemm_noalloc.restype = i32
     L.w12_gemm_workspace_bytes.argtypes = [i64, i64, i64, p, ctypes.POINTER(sz)]
     L.w12_gemm_workspace_bytes.restype = i32
     L.w12_default_tiling.argtypes = [i64, i64, i64, i32, ctypes.POINTER(Tiling)]
@@ -478,6 +480,24 @@ def w12_gemm(x: torch.Tensor, wt: W12Weight, out_dtype: torch.dtype = torch.floa
     else:
         fn, name = _fmt_fn(wt.fmt, "w12_gemm")
         _check(fn(*args, _stream()), name)
+    return y
+
+
+def w12_gemm_noalloc(x: torch.Tensor, wt: W12Weight, out_dtype: torch.dtype = torch.float32,
+                     y: torch.Tensor | None = None) -> torch.Tensor:
+    """w12_gemm_noalloc: the w12_gemm_ws operation with its split-K scratch
+    in the library's fixed device array (no workspace, no allocation by the
+    library; y is allocated here only if not given).  W12-v1 containers."""
+    if wt.fmt != "v1":
+        raise ValueError("w12_gemm_noalloc takes W12-v1 containers")
+    M, ldx = _x_args(x)
+    if y is None:
+        y, _ = _out_tensor(M, wt.N, out_dtype, x.device)
+    ldy, yt = _y_args(y)
+    _check(lib().w12_gemm_noalloc(_dev_ptr(x, "x"), M, ldx, _dev_ptr(wt.p0, "p0"),
+                                  _dev_ptr(wt.p1, "p1"), _dev_ptr(wt.p2, "p2"),
+                                  _dev_ptr(wt.meta, "meta"), *wt.exc_ptrs(), wt.N, wt.K,
+                                  _dev_ptr(y, "y"), ldy, yt, _stream()), "w12_gemm_noalloc")
     return y
 
 

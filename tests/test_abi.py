@@ -18,10 +18,11 @@ def test_loads_and_exports_every_declared_symbol():
                           "w12_plane_bytes", "w12_meta_bytes", "w12_status_string",
                           "w12_abi_version", "w12_gemm_variant", "w12_gemm_ws", "bf16_gemm_ws",
                           "w12_gemm_workspace_bytes", "w12_gemm_ex", "bf16_gemm_ex",
-                          "w12_exceptions", "w12_exceptions_workspace_bytes"}
+                          "w12_exceptions", "w12_exceptions_workspace_bytes",
+                          "w12_gemm_noalloc"}
     for n in names:
         assert hasattr(L, n), n
-    assert w12.w12_abi_version() == 6
+    assert w12.w12_abi_version() == 7
 
 
 def test_sizes():
@@ -38,7 +39,7 @@ def test_sizes():
 
 
 def test_status_strings():
-    for s in (0, -1, -2, -3, -4, -6, -7, -8, 99):
+    for s in (0, -1, -2, -3, -4, -6, -7, -8, -9, 99):
         assert isinstance(w12.w12_status_string(s), str) and w12.w12_status_string(s)
 
 
@@ -348,3 +349,35 @@ def test_w12b_entry_points_and_routing():
     assert L.w12b_gemm(A16, 129, 512, A16, A16, A16, A16, None, None, 64, 512, A16, 64, 0,
                        None) == -6
     assert w12.w12_gemm_variant(1, 7168, 5120, 2).startswith("w12b_gemv_m1_")
+
+
+def _noalloc(**kw):
+    a = dict(x=A16, M=1, ldx=512, p0=A16, p1=A16, p2=A16, meta=A16, N=64, K=512, y=A16,
+             ldy=64, yt=0)
+    a.update(kw)
+    return w12.lib().w12_gemm_noalloc(a["x"], a["M"], a["ldx"], a["p0"], a["p1"], a["p2"],
+                                      a["meta"], a.get("eo"), a.get("ee"), a["N"], a["K"], a["y"],
+                                      a["ldy"], a["yt"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), -1), (dict(meta=None), -1), (dict(K=500), -2), (dict(M=0), -2),
+    (dict(M=129), -6), (dict(yt=2), -4), (dict(x=MIS), -3), (dict(eo=A16), -1),
+    # a default tiling whose split-K partial sums exceed the fixed 16 MiB
+    # scratch: M = 32, N = 64000, K = 15360 splits K in three,
+    # 3 * 32 * 64000 * 4 bytes = 23.4 MiB
+    (dict(M=32, N=64000, K=15360, ldx=15360, ldy=64000), -9),
+])
+def test_noalloc_rejects_before_any_launch(kw, status):
+    assert _noalloc(**kw) == status
+
+
+def test_noalloc_scratch_covers_the_workloads():
+    """Every M up to 128 on the four layer shapes fits the 16 MiB scratch
+    (the default split-K partial sums, without the 64 KB counter area)."""
+    for N, K in ((7168, 5120), (5120, 5120), (34816, 5120), (5120, 17408)):
+        for M in (1, 2, 4, 8, 16, 32, 64, 128):
+            need = w12.w12_gemm_workspace_bytes(M, N, K)
+            assert need == 0 or need - 65536 <= 16 << 20, (N, K, M, need)
+    assert w12.w12_gemm_workspace_bytes(128, 16384, 5120) - 65536 == 16 << 20   # fits exactly
+    assert w12.w12_gemm_workspace_bytes(32, 64000, 15360) - 65536 > 16 << 20
