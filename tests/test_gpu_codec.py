@@ -140,3 +140,25 @@ def test_readme_example():
     assert flagged > 0 and y.shape == (4, 7168)
     assert torch.allclose(y, ref, rtol=0, atol=1e-3 * float(x.float().norm(dim=1).max())
                           * float(w.float().norm(dim=1).max()) + 1e-6)
+
+
+def test_layout_worked_example2_on_gpu():
+    """The hand-derived second layout example (tests/golden/
+    w12_layout_example2.txt) packed by the GPU: the same non-zero plane and
+    meta bytes, flag count, unpacked words and exception list."""
+    from tests.test_oracle_codec import layout_example2_weight
+    w, rec = layout_example2_weight()
+    wt, bad = _gpu_pack(w)
+    for name, plane in (("p0", wt.p0), ("p1", wt.p1), ("p2", wt.p2)):
+        h = to_host_u8(plane)
+        assert {int(i): int(h[i]) for i in np.flatnonzero(h)} == rec[name], name
+    hm = to_host_u8(wt.meta)
+    assert {int(i): int(hm[i]) for i in np.flatnonzero(hm)} == rec["meta"]
+    assert bad == rec["bad"][0]
+    want = w.copy()
+    for n, k, v in rec["unpacked"]:
+        want[n, k] = v
+    assert np.array_equal(to_host_u16(w12.w12_unpack(wt)), want)
+    off, ent = w12.w12_exceptions(to_dev(w))
+    assert list(off.cpu().numpy()) == rec["offsets"]
+    assert [tuple(int(v) for v in e) for e in ent.cpu().numpy().view(np.uint32)] == rec["entry"]

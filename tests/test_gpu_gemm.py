@@ -12,6 +12,8 @@ kernels, same summation order; only the weight fetch differs).
 The binding's default GEMM is the split-K capable w12_gemm_ws; the checks
 below also run the plain w12_gemm (split_k=False) on every case.
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -423,3 +425,21 @@ def test_two_streams_split_k():
         for i in range(len(xs)):
             assert torch.equal(outs[i].cpu().view(torch.int32), ref[i].view(torch.int32)), (rep, i)
     assert w12.w12_default_tiling(16, 301, 17408).splitk > 1
+
+
+@pytest.mark.parametrize("name,M", [("tiny", 1), ("qkv", 1), ("gate_up", 16), ("down", 32)])
+def test_headline_configs_every_row(oracle, name, M):
+    """The four benchmark configurations at their own M, every output row
+    against the oracle's container GEMM (decode + fp64, threaded), in the
+    default tiling the benchmark times."""
+    case = inputs.CASES[name]
+    P = prepared(name)
+    x = case.activations(M)
+    print("gemm parity every row:", name, M, flush=True)
+    y12, y16 = _run_both(x, P)
+    yh = y12.cpu().numpy()
+    assert np.array_equal(yh.view(np.uint32), y16.cpu().numpy().view(np.uint32))
+    p0, p1, p2, meta, _ = oracle.pack(P.raw)
+    y_ref = oracle.gemm_w12_f64(x, p0, p1, p2, meta, P.N, nthreads=min(16, os.cpu_count() or 1))
+    w_ref = oracle.unpack(p0, p1, p2, meta, P.N, P.K)
+    assert_gemm_close(yh, y_ref, oracle.tolerance(x, w_ref), "%s M=%d every row" % (name, M))

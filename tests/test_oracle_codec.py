@@ -227,3 +227,53 @@ def test_bf16_control_layout_is_the_same_permutation(oracle):
         b, j = divmod(within, 4)
         e = j + (4 if p0[byte] >= 16 else 0)
         assert t[block * 2048 + b * 512 + lane * 8 + e] == w[n, k], (n, k)
+
+
+def read_layout_example2():
+    """Records of tests/golden/w12_layout_example2.txt (hand-derived)."""
+    path = os.path.join(os.path.dirname(__file__), "golden", "w12_layout_example2.txt")
+    rec = {"planted": [], "p0": {}, "p1": {}, "p2": {}, "meta": {}, "unpacked": [], "entry": []}
+    with open(path) as f:
+        for line in f:
+            t = line.split()
+            if not t or t[0].startswith("#"):
+                continue
+            v = [int(s, 0) for s in t[1:]]
+            if t[0] in ("p0", "p1", "p2", "meta"):
+                rec[t[0]][v[0]] = v[1]
+            elif t[0] in ("planted", "unpacked", "entry"):
+                rec[t[0]].append(tuple(v))
+            else:
+                rec[t[0]] = v
+    return rec
+
+
+def layout_example2_weight():
+    rec = read_layout_example2()
+    w = np.zeros((21, 256), np.uint16)
+    for n, k, v in rec["planted"]:
+        w[n, k] = v
+    return w, rec
+
+
+def test_layout_worked_example2(oracle):
+    """Second hand-derived example: a second tile and group, rows c > 0,
+    quarters q > 0, dwords b > 0, high nibbles, a flagged group with two
+    elements below its window, and the exception list they produce."""
+    w, rec = layout_example2_weight()
+    p0, p1, p2, meta, bad = oracle.pack(w)
+    for name, plane in (("p0", p0), ("p1", p1), ("p2", p2)):
+        assert plane.shape == (4096,)
+        nz = {int(i): int(plane[i]) for i in np.flatnonzero(plane)}
+        assert nz == rec[name], name
+    assert meta.shape == (64,)
+    assert {int(i): int(meta[i]) for i in np.flatnonzero(meta)} == rec["meta"]
+    assert bad == rec["bad"][0]
+    out = oracle.unpack(p0, p1, p2, meta, 21, 256)
+    want = w.copy()
+    for n, k, v in rec["unpacked"]:
+        want[n, k] = v
+    assert np.array_equal(out, want)
+    off, ent = oracle.exceptions(w)
+    assert list(off) == rec["offsets"]
+    assert [tuple(int(v) for v in e) for e in ent] == rec["entry"]
