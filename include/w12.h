@@ -308,7 +308,8 @@ int w12_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K,
  * operation and passages as w12_gemm and bf16_gemm.
  *   workspace       : device, at least w12_gemm_workspace_bytes(M, N, K,
  *                     NULL) bytes, 256-byte aligned, zero-filled before its
- *                     first use (every call leaves its counters at zero);
+ *                     first use (every call leaves it ready for the next:
+ *                     counters zero, two-slice slots empty);
  *                     may be NULL when that size is 0.
  * Additional error: W12_ERR_WORKSPACE.
  */
@@ -366,7 +367,7 @@ const char *w12_gemm_variant(int64_t M, int64_t N, int64_t K, int is_w12,
  *   scratch   : 16 MiB + 64 KB of device memory per GPU the call runs on,
  *               held from its first call on that GPU until the process ends
  *               (that first call also enqueues one small kernel that clears
- *               the counters).  Every call on one GPU shares that GPU's
+ *               it; every call leaves it ready for the next).  Every call on one GPU shares that GPU's
  *               array, so calls that may overlap on one GPU -- on different
  *               streams, or from different threads -- race and must be
  *               ordered by the caller.

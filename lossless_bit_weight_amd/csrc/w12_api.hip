@@ -404,10 +404,9 @@ __global__ void zero_words(uint32_t* p, int n) {
 }
 
 // Device address of `scratch` on the current device.  The first call on a
-// device looks it up and clears the counter area on `s` (a fill kernel, so
-// the call may also be captured in a graph); every split-K launch leaves the
-// counters at zero again, and the partial sums are written before they are
-// read, so nothing else needs clearing.
+// device looks it up and clears the whole array on `s` (a fill kernel, so
+// the call may also be captured in a graph); every split-K launch leaves
+// the counters at zero and no two-slice slot tagged.
 int scratch_on_device(hipStream_t s, void** out) {
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return W12_ERR_HIP;
@@ -416,7 +415,7 @@ int scratch_on_device(hipStream_t s, void** out) {
         void* ptr = nullptr;
         if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr)
             return W12_ERR_HIP;
-        constexpr int kWords = (int)(w12::kCounterBytes / 4);
+        constexpr int kWords = (int)(kScratchBytes / 4);
         hipLaunchKernelGGL(zero_words, dim3((kWords + 255) / 256), dim3(256), 0, s,
                            static_cast<uint32_t*>(ptr), kWords);
         if (hipGetLastError() != hipSuccess) return W12_ERR_HIP;

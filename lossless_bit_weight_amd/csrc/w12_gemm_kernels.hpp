@@ -103,8 +103,40 @@ __device__ __forceinline__ void out_value(const GemmArgs& g, int m, int64_t n, f
     }
 }
 
-// Split-K epilogue, run by every thread of a workgroup after its partial
-// sums are stored.  The workgroups of one row block count themselves in
+// K split in exactly two slices (MFMA and GEMV tiles up to 32 rows): each
+// output is published with ONE 64-bit atomic exchange of (kPairTag << 32 |
+// its fp32 bits) into its slot, ws64[m][n] (Np columns; the slots occupy the
+// bytes the two slices' partial sums would).  The workgroup that gets its
+// partner's tagged value back adds the two in slice order -- slice 0's sum
+// plus slice 1's, whichever arrives second, so y never depends on the order
+// of arrival -- stores y and clears the slot; the other gets back anything
+// else and is done.  One memory round trip per output batch, against the
+// store, completion wait, counter round trip and reload of split_finish.
+// The tag is a word no fp32 partial sum of BF16 products can be (a NaN
+// whose low 16 payload bits are ones: NaNs from BF16 operands carry zero
+// low bits, NaNs made by invalid operations are the default quiet NaN), so
+// the partial sums that other launches leave in the workspace (three or
+// more slices, or 64- and 128-row tiles) never read as a published slot,
+// and a zero-filled workspace starts with every slot empty.
+constexpr uint32_t kPairTag = 0xFFFFFFFFu;
+__device__ __forceinline__ uint64_t pair_publish(const GemmArgs& g, int m, int64_t n, float v) {
+    const int64_t np = (g.N + 15) / 16 * 16;
+    uint64_t* slot = reinterpret_cast<uint64_t*>(g.ws) + (int64_t)m * np + n;
+    return __hip_atomic_exchange(slot, ((uint64_t)kPairTag << 32) | __builtin_bit_cast(uint32_t, v),
+                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void pair_complete(const GemmArgs& g, int m, int64_t n, float v,
+                                              uint64_t old) {
+    if ((uint32_t)(old >> 32) != kPairTag) return;   // the partner finishes this output
+    const float o = __builtin_bit_cast(float, (uint32_t)old);
+    store_y(g, m, n, blockIdx.y == 0 ? v + o : o + v);
+    const int64_t np = (g.N + 15) / 16 * 16;
+    __hip_atomic_store(reinterpret_cast<uint64_t*>(g.ws) + (int64_t)m * np + n, (uint64_t)0,
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Split-K epilogue for three or more slices, run by every thread of a
+// workgroup after its partial sums are stored.  The workgroups of one row block count themselves in
 // cnt[block]; the last one to arrive adds the S partial sums of the block in
 // slice order 0, 1, ..., S-1 (the same order whichever workgroup is last, so
 // y is deterministic) and resets the counter to zero for the next launch.
@@ -881,17 +913,42 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs g) {
             }
         }
         if (kw == 0) {
+            if (MR <= 32 && gridDim.y == 2) {
+                // all exchanges of the lane in flight together, then finish
+                uint64_t old[R][kMT][4];
 #pragma unroll
-            for (int r = 0; r < R; ++r) {
-                const int64_t n = (tile0 + r) * 16 + col;
-                if (n >= g.N) continue;
+                for (int r = 0; r < R; ++r)
 #pragma unroll
-                for (int mt = 0; mt < kMT; ++mt)
+                    for (int mt = 0; mt < kMT; ++mt)
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int m = 16 * mt + 4 * q + e;
-                        if (m < g.M) out_value(g, m, n, macc[r][mt][e]);
-                    }
+                        for (int e = 0; e < 4; ++e) {
+                            const int64_t n = (tile0 + r) * 16 + col;
+                            const int m = 16 * mt + 4 * q + e;
+                            old[r][mt][e] = n < g.N && m < g.M ? pair_publish(g, m, n, macc[r][mt][e]) : 0;
+                        }
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+#pragma unroll
+                    for (int mt = 0; mt < kMT; ++mt)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int64_t n = (tile0 + r) * 16 + col;
+                            const int m = 16 * mt + 4 * q + e;
+                            if (n < g.N && m < g.M) pair_complete(g, m, n, macc[r][mt][e], old[r][mt][e]);
+                        }
+            } else {
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    const int64_t n = (tile0 + r) * 16 + col;
+                    if (n >= g.N) continue;
+#pragma unroll
+                    for (int mt = 0; mt < kMT; ++mt)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int m = 16 * mt + 4 * q + e;
+                            if (m < g.M) out_value(g, m, n, macc[r][mt][e]);
+                        }
+                }
             }
         }
         // 64 and 128 rows: each lane of the last workgroup finishes the
@@ -968,17 +1025,35 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs g) {
         }
         // Lane (col, q) stores the outputs m with m % 4 == q.
         if (kw == 0) {
+            if (gridDim.y == 2) {
+                uint64_t old[R][MR];
 #pragma unroll
-            for (int r = 0; r < R; ++r) {
-                const int64_t n = (tile0 + r) * 16 + col;
+                for (int r = 0; r < R; ++r)
 #pragma unroll
-                for (int m = 0; m < MR; ++m)
-                    if ((m & 3) == q && n < g.N && m < g.M) out_value(g, m, n, gacc[r][m]);
+                    for (int m = 0; m < MR; ++m) {
+                        const int64_t n = (tile0 + r) * 16 + col;
+                        old[r][m] = (m & 3) == q && n < g.N && m < g.M ? pair_publish(g, m, n, gacc[r][m]) : 0;
+                    }
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+#pragma unroll
+                    for (int m = 0; m < MR; ++m) {
+                        const int64_t n = (tile0 + r) * 16 + col;
+                        if ((m & 3) == q && n < g.N && m < g.M) pair_complete(g, m, n, gacc[r][m], old[r][m]);
+                    }
+            } else {
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    const int64_t n = (tile0 + r) * 16 + col;
+#pragma unroll
+                    for (int m = 0; m < MR; ++m)
+                        if ((m & 3) == q && n < g.N && m < g.M) out_value(g, m, n, gacc[r][m]);
+                }
             }
         }
     }
     if constexpr (!(MFMA && MR >= 64))
-        if (gridDim.y > 1) split_finish<kRowWaves * R, NW * 64>(g);
+        if (gridDim.y > 2) split_finish<kRowWaves * R, NW * 64>(g);
 }
 
 // ---- launch helpers ----------------------------------------------------------------------

@@ -34,9 +34,13 @@ struct GemmArgs {
     int64_t ldy;
     int y_f32;
     // K split across workgroups (grid y): slice s holds groups
-    // [s * gs, min(G, (s + 1) * gs)); with S > 1 every workgroup writes its
-    // fp32 partial sums to ws[s][m][Np] and the last of the S workgroups of a
-    // row block (counted in cnt[block]) adds them in slice order and writes y.
+    // [s * gs, min(G, (s + 1) * gs)).  With S = 2 (up to 32 x rows) the two
+    // workgroups of a row block meet in 64-bit slots ws64[m][Np] (one atomic
+    // exchange per output; the second adds slice 0 + slice 1).  With S > 2
+    // every workgroup writes its fp32 partial sums to ws[s][m][Np] and the
+    // last of the S workgroups of a row block (counted in cnt[block]) adds
+    // them in slice order and writes y.  Every launch leaves the counters at
+    // zero and no slot tagged.
     int S;
     int gs;
     float* ws;

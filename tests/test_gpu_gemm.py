@@ -343,16 +343,23 @@ def test_split_k(oracle, base, splitk, fmt):
 
 
 def test_split_k_counters_reset(oracle):
-    """Every split-K launch leaves its row-block counters at zero, so the next
-    launch on the same workspace writes all of y again (y is prefilled with
-    NaN) and is correct -- also when a launch with many row blocks follows one
-    with few row blocks and large partial sums."""
+    """Every split-K launch leaves its row-block counters at zero and no
+    two-slice exchange slot tagged, so the next launch on the same workspace
+    writes all of y again (y is prefilled with NaN) and is correct, whatever
+    the previous launch's shape, slice count or kernel: two-slice launches
+    follow launches that stored many slices of partial sums over the same
+    bytes, and launches with many row blocks follow ones with few."""
     ws = torch.zeros(1 << 22, dtype=torch.uint8, device="cuda")
     seq = [((130, 1152), 16, (1, 1, 1, 2, 0, 8)),   # 3 row blocks, 5 slices
            ((4099, 384), 1, (0, 1, 4, 2, 0, 3)),    # 257 row blocks
            ((1000, 640), 16, (1, 1, 1, 2, 0, 8)),
+           ((1000, 640), 16, (1, 1, 1, 2, 0, 2)),   # two slices: exchange slots
            ((1000, 640), 16, (1, 1, 1, 2, 0, 8)),
-           ((4099, 384), 3, (0, 1, 4, 2, 0, 2))]
+           ((300, 2560), 64, (1, 1, 1, 2, 0, 4, 8)),   # 64-row tiles, 4 slices
+           ((1000, 640), 32, (1, 1, 2, 2, 0, 2, 8)),   # two slices, 32 rows
+           ((300, 2560), 128, (1, 1, 1, 2, 0, 5, 8)),
+           ((1000, 640), 9, (1, 1, 4, 2, 1, 2)),       # two slices, x direct
+           ((4099, 384), 3, (0, 1, 4, 2, 0, 2))]       # two slices, GEMV
     for i, (shape, M, tiling) in enumerate(seq):
         P = prepared(shape)
         x = inputs.gaussian_bf16((M, shape[1]), 1.0, 100 + i)
@@ -360,7 +367,9 @@ def test_split_k_counters_reset(oracle):
         w12.w12_gemm(to_dev(x), P.wt, y=y, tiling=tiling, workspace=ws)
         torch.cuda.synchronize()
         assert w12.w12_gemm_workspace_bytes(M, shape[0], shape[1], tiling) > 65536
-        assert int(ws[:65536].count_nonzero()) == 0, "counters not reset"
+        assert int(ws[:65536].count_nonzero()) == 0, "counters not reset (%s %s)" % (tiling, shape)
+        hi = ws[65536:].view(torch.int32)[1::2]
+        assert int((hi == -1).sum()) == 0, "a tagged slot left behind (%s %s)" % (tiling, shape)
         w_ref = P.ref_rows(oracle, np.arange(P.N))
         assert_gemm_close(y.cpu().numpy(), oracle.gemm_bf16_f64(x, w_ref),
                           oracle.tolerance(x, w_ref), "counters %s %s" % (tiling, shape))
