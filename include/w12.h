@@ -33,12 +33,16 @@
  * window floor +-2^(2*beta+2-127).  Unpack and GEMM ignore the flag and use
  * the stored (clamped) value -- unless the container carries an exception
  * list (w12_exceptions), which keeps it lossless for every input:
- *   exc_offsets = Np/16 + 1 uint32 words; tile T = n/16 owns entries
- *                 exc_offsets[T] .. exc_offsets[T+1]-1 (exc_offsets[0] = 0);
+ *   exc_offsets = (Np/16)*(K/128) + 1 uint32 words, one per (tile, group)
+ *                 block in block order and then the total: block
+ *                 t = T*(K/128) + g (tile T = n/16, group g = k/128) owns
+ *                 entries exc_offsets[t] .. exc_offsets[t+1]-1
+ *                 (exc_offsets[0] = 0), so a GEMM finds the entries of the
+ *                 block it is streaming without a search;
  *   exc_entries = two uint32 words per element below its window:
  *                 (c << 24 | k) with c = n % 16, and (beta << 16 | the
  *                 original BF16 word) with beta the group's base;
- *                 inside a tile in storage order (group g, piece L, dword b,
+ *                 inside a block in storage order (piece L, dword b,
  *                 element e).
  * Unpack writes the original words back; the GEMMs add x[m][k] * (original -
  * clamp) for each entry after their main loop.  Every call that takes a
@@ -72,7 +76,7 @@
 extern "C" {
 #endif
 
-#define W12_ABI_VERSION 7
+#define W12_ABI_VERSION 8
 #define W12_GROUP 128
 #define W12_TILE_ROWS 16
 #define W12_MAX_M 128
@@ -148,7 +152,7 @@ int w12_pack(const uint16_t *w, int64_t N, int64_t K,
  *                 aligned.
  *   workspace   : device, w12_exceptions_workspace_bytes(N, K) bytes, 4-byte
  *                 aligned (no initial contents needed).
- *   exc_offsets : device output, Np/16 + 1 uint32 words.
+ *   exc_offsets : device output, (Np/16)*(K/128) + 1 uint32 words.
  *   exc_entries : device output with room for `capacity` entries (2 words
  *                 each), or NULL with capacity 0 to count only.
  *   total       : device uint32 output: the number of entries.  Entries past

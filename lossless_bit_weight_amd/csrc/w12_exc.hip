@@ -7,10 +7,12 @@
 // {0, 1} and 14 above an even base; W12-b: {0} and 15 above any base); an
 // element outside them is written to the planes as the window floor (the
 // group is flagged) and, here, also as one exception entry (format in
-// w12.h): tile-grouped, in the order the tiled layout stores the weights
-// (group, piece, dword, element).  Three launches build the list: a count per (tile, group) block,
-// one scan over the blocks, and a write pass in which each wave places its
-// block's entries at the scanned offset, lanes in piece order.
+// w12.h): grouped by (tile, group) block in block order, inside a block in
+// the order the tiled layout stores the weights (piece, dword, element).
+// Three launches build the list: a count per block, one scan over the
+// blocks (whose exclusive sums are the block offsets), and a write pass in
+// which each wave places its block's entries at the scanned offset, lanes in
+// piece order.
 #include <hip/hip_runtime.h>
 
 #include "w12_internal.hpp"
@@ -105,9 +107,9 @@ __global__ __launch_bounds__(kThreads) void exc_count_kernel(const uint16_t* __r
 }
 
 // One workgroup: exclusive scan of the block counts in place, in chunks of
-// kScanThreads with a running carry; then the tile offsets and the total.
+// kScanThreads with a running carry; then the block offsets and the total.
 __global__ __launch_bounds__(kScanThreads) void exc_scan_kernel(uint32_t* __restrict__ cnt,
-                                                                int64_t nblocks, int64_t G,
+                                                                int64_t nblocks,
                                                                 uint32_t* __restrict__ offsets,
                                                                 uint32_t* __restrict__ total) {
     __shared__ uint32_t buf[kScanThreads];
@@ -132,10 +134,9 @@ __global__ __launch_bounds__(kScanThreads) void exc_scan_kernel(uint32_t* __rest
         if (threadIdx.x == kScanThreads - 1) carry = c0 + buf[threadIdx.x];
         __syncthreads();
     }
-    const int64_t ntiles = nblocks / G;
-    for (int64_t t = threadIdx.x; t < ntiles; t += kScanThreads) offsets[t] = cnt[t * G];
+    for (int64_t t = threadIdx.x; t < nblocks; t += kScanThreads) offsets[t] = cnt[t];
     if (threadIdx.x == 0) {
-        offsets[ntiles] = carry;
+        offsets[nblocks] = carry;
         *total = carry;
     }
 }
@@ -178,8 +179,11 @@ __global__ __launch_bounds__(kThreads) void exc_apply_kernel(const uint32_t* __r
                                                              const uint32_t* __restrict__ entries,
                                                              int64_t N, int64_t K,
                                                              uint16_t* __restrict__ w) {
+    // tile t: blocks t * G .. t * G + G - 1, entries of consecutive blocks
+    // are consecutive
     const int64_t t = blockIdx.x;
-    const uint32_t beg = offsets[t], end = offsets[t + 1];
+    const int64_t G = K / 128;
+    const uint32_t beg = offsets[t * G], end = offsets[(t + 1) * G];
     for (uint32_t i = beg + threadIdx.x; i < end; i += kThreads) {
         const uint32_t pos = entries[2 * (int64_t)i];
         const int64_t n = 16 * t + (pos >> 24);
@@ -195,8 +199,7 @@ hipError_t exceptions_fmt(const uint16_t* w, int64_t N, int64_t K, uint32_t* ws,
     const int64_t grid = (nb + 3) / 4;
     hipLaunchKernelGGL(exc_count_kernel<FMT>, dim3((unsigned)grid), dim3(kThreads), 0, s, w, N, K,
                        nb, ws);
-    hipLaunchKernelGGL(exc_scan_kernel, dim3(1), dim3(kScanThreads), 0, s, ws, nb, K / 128, offsets,
-                       total);
+    hipLaunchKernelGGL(exc_scan_kernel, dim3(1), dim3(kScanThreads), 0, s, ws, nb, offsets, total);
     if (entries != nullptr && capacity > 0)
         hipLaunchKernelGGL(exc_write_kernel<FMT>, dim3((unsigned)grid), dim3(kThreads), 0, s, w, N,
                            K, nb, ws, entries, capacity);

@@ -289,7 +289,9 @@ __device__ __forceinline__ void exc_corrections(const GemmArgs& g, int64_t tile,
     float* orig = reinterpret_cast<float*>(area + 256);
     float* clamp = reinterpret_cast<float*>(area + 512);
     uint16_t* xs = reinterpret_cast<uint16_t*>(area + 768);
-    const uint32_t beg = g.exc_off[tile], end = g.exc_off[tile + 1];
+    // the entries of the slice's blocks (tile, g0) .. (tile, g0 + gn - 1)
+    const int64_t blk0 = tile * (g.K / 128) + g0;
+    const uint32_t beg = g.exc_off[blk0], end = g.exc_off[blk0 + gn];
     for (uint32_t base = beg; base < end; base += 64) {
         const uint32_t i = base + (uint32_t)lane;
         int c = -1;

@@ -24,7 +24,8 @@ struct GemmArgs {
     const uint8_t* p2;
     const uint8_t* meta;
     // Optional exception list of the container (both NULL when it has none):
-    // tile T owns entries exc_off[T] .. exc_off[T+1]-1, two words each.
+    // block (tile T, group g) owns entries exc_off[T * G + g] ..
+    // exc_off[T * G + g + 1] - 1 (G = K / 128), two words each.
     const uint32_t* exc_off;
     const uint32_t* exc_ent;
     const uint16_t* w;

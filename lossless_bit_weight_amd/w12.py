@@ -274,8 +274,8 @@ def workspace(nbytes: int) -> torch.Tensor:
 class W12Weight:
     """A packed [N, K] weight: three flat uint8 planes of w12_plane_bytes(N, K)
     and a flat uint8 meta array of w12_meta_bytes(N, K) (tiled layout), plus
-    an optional exception list (int32 tensors: Np/16 + 1 tile offsets and
-    [count, 2] entries) that makes every group lossless."""
+    an optional exception list (int32 tensors: (Np/16)*(K/128) + 1 block
+    offsets and [count, 2] entries) that makes every group lossless."""
     p0: torch.Tensor
     p1: torch.Tensor
     p2: torch.Tensor
@@ -373,7 +373,8 @@ def w12_exceptions(w: torch.Tensor, fmt: str = "v1") -> tuple[torch.Tensor, torc
     if wsb == 0:
         raise W12Error(-2, "w12_exceptions(%d, %d)" % (N, K))
     ws = torch.empty(wsb // 4, dtype=torch.int32, device=w.device)
-    off = torch.empty(w12_padded_rows(N) // 16 + 1, dtype=torch.int32, device=w.device)
+    off = torch.empty(w12_padded_rows(N) // 16 * (K // GROUP) + 1, dtype=torch.int32,
+                      device=w.device)
     total = torch.zeros(1, dtype=torch.int32, device=w.device)
     args = (_dev_ptr(w, "w"), N, K, _dev_ptr(ws, "workspace"), wsb, _dev_ptr(off, "exc_offsets"))
     fn, name = _fmt_fn(fmt, "w12_exceptions")

@@ -252,7 +252,8 @@ def unpack(p0, p1, p2, meta, N: int, K: int, fmt: str = "v1") -> np.ndarray:
 def exceptions(w: np.ndarray, fmt: str = "v1"):
     """BF16 bits [N, K] -> (offsets, entries): the exception list of the
     elements that fall below their group's window (see w12_oracle.c).
-    offsets: uint32[padded_rows(N)/16 + 1]; entries: uint32[count, 2] with
+    offsets: uint32[(padded_rows(N)/16) * (K/128) + 1], one per (tile, group)
+    block in block order, then the total; entries: uint32[count, 2] with
     word 0 = (row in tile) << 24 | k and word 1 = base << 16 | the original
     BF16 word."""
     w = _u16(w)
@@ -262,7 +263,7 @@ def exceptions(w: np.ndarray, fmt: str = "v1"):
     count = lib.w12o_exceptions_fmt(f, _ptr(w), N, K, None, None)
     if count < 0:
         raise ValueError("oracle exceptions rejected shape %r" % ((N, K),))
-    offsets = np.zeros(padded_rows(N) // 16 + 1, np.uint32)
+    offsets = np.zeros(padded_rows(N) // 16 * (K // 128) + 1, np.uint32)
     entries = np.zeros((count, 2), np.uint32)
     lib.w12o_exceptions_fmt(f, _ptr(w), N, K, _ptr(offsets), _ptr(entries) if count else None)
     return offsets, entries
@@ -274,7 +275,7 @@ def apply_exceptions(w: np.ndarray, offsets: np.ndarray, entries: np.ndarray) ->
     N, K = out.shape
     offsets = np.ascontiguousarray(offsets, dtype=np.uint32)
     entries = np.ascontiguousarray(entries, dtype=np.uint32).reshape(-1, 2)
-    if offsets.size != padded_rows(N) // 16 + 1 or entries.shape[0] < int(offsets[-1]):
+    if offsets.size != padded_rows(N) // 16 * (K // 128) + 1 or entries.shape[0] < int(offsets[-1]):
         raise ValueError("exception list size mismatch")
     if _load().w12o_apply_exceptions(_ptr(out), N, K, _ptr(offsets),
                                      _ptr(entries) if entries.size else None) != 0:

@@ -388,12 +388,14 @@ int w12o_unpack(const uint8_t *p0, const uint8_t *p1, const uint8_t *p2,
  *   word 1 = (beta << 16) | the element's original BF16 word, beta being
  *            the base of the element's group (so an entry alone gives both
  *            the original and the clamp the planes hold)
- * Entries are grouped by tile T = n / 16: tile T owns entries
- * offsets[T] .. offsets[T+1]-1 (offsets has Np/16 + 1 words, offsets[0] = 0).
- * Inside a tile they follow the order in which the tiled layout stores the
- * weights: group g, then piece L = 16*q + c, then dword b, then element e
- * (k = 128*g + 32*b + 8*q + e).  With the list, unpack reproduces every
- * element exactly, whatever the input.
+ * Entries are grouped by block (T, g) -- 16-row tile T = n / 16, group
+ * g = k / 128 -- in the order of the blocks in the planes, (T, g) ascending:
+ * block t = T*G + g (G = K/128) owns entries offsets[t] .. offsets[t+1]-1
+ * (offsets has (Np/16)*G + 1 words, offsets[0] = 0).  Inside a block they
+ * follow the order in which the tiled layout stores the weights: piece
+ * L = 16*q + c, then dword b, then element e (k = 128*g + 32*b + 8*q + e).
+ * With the list, unpack reproduces every element exactly, whatever the
+ * input.
  *
  * w12o_exceptions recomputes each group's base from the weights (it does not
  * read a container).  offsets and entries may be NULL (then only the count is
@@ -408,9 +410,9 @@ int64_t w12o_exceptions_fmt(int fmt, const uint16_t *w, int64_t N, int64_t K,
     int64_t ntiles = w12o_padded_rows(N) / 16;
     int64_t count = 0;
     for (int64_t T = 0; T < ntiles; T++) {
-        if (offsets)
-            offsets[T] = (uint32_t)count;
         for (int64_t g = 0; g < groups; g++) {
+            if (offsets)
+                offsets[T * groups + g] = (uint32_t)count;
             int beta[16];
             for (int c = 0; c < 16; c++) {
                 int64_t n = 16 * T + c;
@@ -443,7 +445,7 @@ int64_t w12o_exceptions_fmt(int fmt, const uint16_t *w, int64_t N, int64_t K,
         }
     }
     if (offsets)
-        offsets[ntiles] = (uint32_t)count;
+        offsets[ntiles * groups] = (uint32_t)count;
     return count;
 }
 
@@ -459,13 +461,14 @@ int w12o_apply_exceptions(uint16_t *w, int64_t N, int64_t K,
 {
     if (N < 0 || K < 0 || K % W12O_GROUP != 0)
         return -1;
-    int64_t ntiles = w12o_padded_rows(N) / 16;
-    for (int64_t T = 0; T < ntiles; T++)
-        for (uint32_t i = offsets[T]; i < offsets[T + 1]; i++) {
+    int64_t groups = K / W12O_GROUP;
+    int64_t blocks = w12o_padded_rows(N) / 16 * groups;
+    for (int64_t t = 0; t < blocks; t++)
+        for (uint32_t i = offsets[t]; i < offsets[t + 1]; i++) {
             int64_t c = entries[2 * i] >> 24;
             int64_t k = entries[2 * i] & 0xFFFFFF;
-            int64_t n = 16 * T + c;
-            if (n >= N || k >= K)
+            int64_t n = 16 * (t / groups) + c;
+            if (n >= N || k >= K || k / W12O_GROUP != t % groups)
                 return -1;
             w[n * K + k] = (uint16_t)(entries[2 * i + 1] & 0xFFFF);
         }

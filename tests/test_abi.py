@@ -22,7 +22,7 @@ def test_loads_and_exports_every_declared_symbol():
                           "w12_gemm_noalloc"}
     for n in names:
         assert hasattr(L, n), n
-    assert w12.w12_abi_version() == 7
+    assert w12.w12_abi_version() == 8
 
 
 def test_sizes():

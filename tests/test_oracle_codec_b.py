@@ -144,11 +144,13 @@ def test_list_is_exactly_the_lossy_set(oracle, shape, sigma, seed):
     lossy = set(zip(*np.nonzero(back != w)))
     bases = oracle.meta_of(meta, *shape)
     off, ent = oracle.exceptions(w, fmt="b")
+    G = shape[1] // 128
     listed = {}
-    for T in range(len(off) - 1):
-        for i in range(off[T], off[T + 1]):
+    for t in range(len(off) - 1):
+        for i in range(off[t], off[t + 1]):
             c, k = int(ent[i, 0]) >> 24, int(ent[i, 0]) & 0xFFFFFF
-            listed[(16 * T + c, k)] = int(ent[i, 1])
+            assert k // 128 == t % G
+            listed[(16 * (t // G) + c, k)] = int(ent[i, 1])
     assert set(listed) == lossy
     assert all(w[n, k] == v & 0xFFFF for (n, k), v in listed.items())
     assert all(v >> 16 == bases[n, k // 128] for (n, k), v in listed.items())

@@ -55,11 +55,14 @@ def test_list_is_exactly_the_lossy_set(oracle, shape, sigma, seed):
     betas = oracle.meta_of(meta, *shape) & 0x7F
     off, ent = oracle.exceptions(w)
     N, K = shape
+    G = K // 128
+    assert len(off) == (N + 15) // 16 * G + 1
     listed = {}
-    for T in range(len(off) - 1):
-        for i in range(off[T], off[T + 1]):
+    for t in range(len(off) - 1):
+        for i in range(off[t], off[t + 1]):
             c, k = int(ent[i, 0]) >> 24, int(ent[i, 0]) & 0xFFFFFF
-            listed[(16 * T + c, k)] = int(ent[i, 1])
+            assert k // 128 == t % G          # the entry lies in its block's group
+            listed[(16 * (t // G) + c, k)] = int(ent[i, 1])
     assert set(listed) == lossy
     assert all(w[n, k] == v & 0xFFFF for (n, k), v in listed.items())
     # the base in each entry is the one the container holds for that group
@@ -72,9 +75,10 @@ def test_storage_order_inside_tiles(oracle):
     w = inputs.gaussian_bf16((256, 1024), 0.02, 31)
     off, ent = oracle.exceptions(w)
     assert len(ent) > 40
-    for T in range(len(off) - 1):
+    G = 1024 // 128
+    for T in range(len(off) // G):
         keys = []
-        for i in range(off[T], off[T + 1]):
+        for i in range(off[T * G], off[(T + 1) * G]):
             c, k = int(ent[i, 0]) >> 24, int(ent[i, 0]) & 0xFFFFFF
             r = k % 128
             keys.append((k // 128, 16 * ((r % 32) // 8) + c, r // 32, r % 8))
@@ -94,3 +98,14 @@ def test_long_k_rejected(oracle):
     lib = oracle._load()
     assert lib.w12o_exceptions(None, 0, 1 << 24, None, None) == -1
     assert lib.w12o_exceptions(None, 0, (1 << 24) - 128, None, None) == 0
+
+
+def test_apply_rejects_an_entry_outside_its_block(oracle):
+    """An entry listed under a block whose group does not hold its k is
+    refused, not written."""
+    w = np.full((16, 256), 0x3F80, np.uint16)
+    w[3, 200] = 0x3000                      # group 1, below the window
+    off, ent = oracle.exceptions(w)
+    assert off.tolist() == [0, 0, 1]
+    with pytest.raises(ValueError):
+        oracle.apply_exceptions(w, np.array([0, 1, 1], np.uint32), ent)
