@@ -45,10 +45,12 @@
  *                 inside a block in storage order (piece L, dword b,
  *                 element e).
  * Unpack writes the original words back; the GEMMs add x[m][k] * (original -
- * clamp) for each entry after their main loop.  Every call that takes a
+ * clamp) for each entry after their main loop (W12-v1: the owner waves
+ * load the first entries of their tiles at the start of the launch).  Every
+ * call that takes a
  * container accepts exc_offsets = exc_entries = NULL for "no list"; a list
  * must come from w12_exceptions for the same weight (it is not validated on
- * the device), and needs K < 2^24.
+ * the device), both arrays 8-byte aligned, and needs K < 2^24.
  *
  * Conventions for every call below:
  *   - all tensor pointers are DEVICE memory owned by the caller; the library
@@ -152,9 +154,11 @@ int w12_pack(const uint16_t *w, int64_t N, int64_t K,
  *                 aligned.
  *   workspace   : device, w12_exceptions_workspace_bytes(N, K) bytes, 4-byte
  *                 aligned (no initial contents needed).
- *   exc_offsets : device output, (Np/16)*(K/128) + 1 uint32 words.
+ *   exc_offsets : device output, (Np/16)*(K/128) + 1 uint32 words, 8-byte
+ *                 aligned.
  *   exc_entries : device output with room for `capacity` entries (2 words
- *                 each), or NULL with capacity 0 to count only.
+ *                 each), 8-byte aligned, or NULL with capacity 0 to count
+ *                 only.
  *   total       : device uint32 output: the number of entries.  Entries past
  *                 `capacity` are not written; a caller that finds
  *                 total > capacity calls again with more room.

@@ -71,7 +71,11 @@ def _compile(item) -> str:
                     and not l.lstrip().startswith(("|", "^")) and not re.match(r"^\s*\d+ \|", l))
     if r.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s" % (src, err))
-    _check_resources(name, remarks)
+    try:
+        _check_resources(name, remarks)
+    except RuntimeError:
+        os.remove(obj)   # never link, or later reuse, an object that spills
+        raise
     return obj
 
 

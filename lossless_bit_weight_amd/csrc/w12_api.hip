@@ -49,11 +49,14 @@ bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0
 constexpr int64_t kExcMaxK = (int64_t)1 << 24;
 constexpr int64_t kExcMaxElems = (int64_t)1 << 32;
 
-// Both list pointers or neither; 4-byte aligned; a shape the list can index.
+bool aligned8(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 7u) == 0; }
+
+// Both list pointers or neither; 8-byte aligned (the GEMMs read entries and
+// offset pairs as 8-byte words); a shape the list can index.
 int check_exceptions(const uint32_t* off, const uint32_t* ent, int64_t N, int64_t K) {
     if ((off == nullptr) != (ent == nullptr)) return W12_ERR_NULL;
     if (off == nullptr) return W12_OK;
-    if (!aligned4(off) || !aligned4(ent)) return W12_ERR_ALIGN;
+    if (!aligned8(off) || !aligned8(ent)) return W12_ERR_ALIGN;
     if (K >= kExcMaxK || (N + W12_TILE_ROWS) * K >= kExcMaxElems) return W12_ERR_SHAPE;
     return W12_OK;
 }
@@ -155,8 +158,8 @@ static int exceptions_fmt(int fmt, const uint16_t* w, int64_t N, int64_t K, void
     if (int rc = check_weight_shape(N, K)) return rc;
     if (K >= kExcMaxK || (N + W12_TILE_ROWS) * K >= kExcMaxElems) return W12_ERR_SHAPE;
     if (capacity < 0 || (capacity > 0 && exc_entries == nullptr)) return W12_ERR_NULL;
-    if (!aligned16(w) || !aligned4(exc_offsets) || !aligned4(total) ||
-        (exc_entries && !aligned4(exc_entries)))
+    if (!aligned16(w) || !aligned8(exc_offsets) || !aligned4(total) ||
+        (exc_entries && !aligned8(exc_entries)))
         return W12_ERR_ALIGN;
     if (workspace == nullptr || workspace_bytes < w12_exceptions_workspace_bytes(N, K) ||
         !aligned4(workspace))
@@ -246,6 +249,16 @@ static int gemm_w12(int fetch, const uint16_t* x, int64_t M, int64_t ldx, const 
     if (int rc = check_exceptions(exc_off, exc_ent, N, K)) return rc;
     w12::Tiling t;
     if (int rc = resolve_tiling(tiling, allow_splitk, M, N, K, &t)) return rc;
+    // With an exception list, the default x-direct MFMA tilings run one tile
+    // per wave: their workgroup's correction wave then has one tile's entries
+    // to prepare instead of two, and finishes within the main loop (the
+    // summation order of every output is unchanged).
+    if (tiling == nullptr && exc_off != nullptr && fetch == w12::kFetchW12 && t.mfma && t.xdirect &&
+        t.r == 2) {
+        w12::Tiling t1 = t;
+        t1.r = 1;
+        if (w12::complete_tiling(t1, (int)M, N, K)) t = t1;
+    }
     if (int rc = check_workspace(t, M, N, ws, ws_bytes)) return rc;
     w12::GemmArgs a = make_args(x, M, ldx, N, K, y, ldy, y_type);
     a.p0 = static_cast<const uint8_t*>(p0);

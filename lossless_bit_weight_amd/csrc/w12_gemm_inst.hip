@@ -2,7 +2,8 @@
 // height, chosen at compile time (-DW12_INST_M=1..8 for the GEMV, or
 // -DW12_INST_MFMA / -DW12_INST_MFMA8 for the 16- and 32-row MFMA tiles in
 // 256- and 512-thread workgroups, -DW12_INST_MFMA8_BIG for 64 and 128 rows),
-// for the three weight fetches (BF16 control, W12-v1, W12-b).  One object file per height keeps the build
+// for the weight fetches (BF16 control, W12-v1 without and with an exception
+// list, W12-b).  One object file per height keeps the build
 // parallel.
 #include "w12_gemm_kernels.hpp"
 
@@ -14,7 +15,9 @@ namespace w12 {
 hipError_t W12_CAT(launch_gemv_m, W12_INST_M)(const GemmArgs& a, const Tiling& t, int fetch,
                                               hipStream_t s) {
     switch (fetch) {
-        case kFetchW12: return kern::dispatch<kern::FetchW12, false, W12_INST_M>(a, t, s);
+        case kFetchW12:
+            return a.exc_off != nullptr ? kern::dispatch<kern::FetchW12X, false, W12_INST_M>(a, t, s)
+                                        : kern::dispatch<kern::FetchW12, false, W12_INST_M>(a, t, s);
         case kFetchW12B: return kern::dispatch<kern::FetchW12B, false, W12_INST_M>(a, t, s);
         default: return kern::dispatch<kern::FetchBF16, false, W12_INST_M>(a, t, s);
     }
@@ -23,7 +26,9 @@ hipError_t W12_CAT(launch_gemv_m, W12_INST_M)(const GemmArgs& a, const Tiling& t
 template <int MT>
 static hipError_t mfma_fetch(const GemmArgs& a, const Tiling& t, int fetch, hipStream_t s) {
     switch (fetch) {
-        case kFetchW12: return kern::dispatch<kern::FetchW12, true, MT>(a, t, s);
+        case kFetchW12:
+            return a.exc_off != nullptr ? kern::dispatch<kern::FetchW12X, true, MT>(a, t, s)
+                                        : kern::dispatch<kern::FetchW12, true, MT>(a, t, s);
         case kFetchW12B: return kern::dispatch<kern::FetchW12B, true, MT>(a, t, s);
         default: return kern::dispatch<kern::FetchBF16, true, MT>(a, t, s);
     }
@@ -39,7 +44,9 @@ hipError_t launch_mfma_mt(int MT, const GemmArgs& a, const Tiling& t, int fetch,
 template <int MT>
 static hipError_t mfma8_fetch(const GemmArgs& a, const Tiling& t, int fetch, hipStream_t s) {
     switch (fetch) {
-        case kFetchW12: return kern::dispatch8<kern::FetchW12, MT>(a, t, s);
+        case kFetchW12:
+            return a.exc_off != nullptr ? kern::dispatch8<kern::FetchW12X, MT>(a, t, s)
+                                        : kern::dispatch8<kern::FetchW12, MT>(a, t, s);
         case kFetchW12B: return kern::dispatch8<kern::FetchW12B, MT>(a, t, s);
         default: return kern::dispatch8<kern::FetchBF16, MT>(a, t, s);
     }
@@ -55,7 +62,9 @@ hipError_t launch_mfma8_mt(int MT, const GemmArgs& a, const Tiling& t, int fetch
 template <int MT>
 static hipError_t mfma8_fetch(const GemmArgs& a, const Tiling& t, int fetch, hipStream_t s) {
     switch (fetch) {
-        case kFetchW12: return kern::dispatch8<kern::FetchW12, MT>(a, t, s);
+        case kFetchW12:
+            return a.exc_off != nullptr ? kern::dispatch8<kern::FetchW12X, MT>(a, t, s)
+                                        : kern::dispatch8<kern::FetchW12, MT>(a, t, s);
         case kFetchW12B: return kern::dispatch8<kern::FetchW12B, MT>(a, t, s);
         default: return kern::dispatch8<kern::FetchBF16, MT>(a, t, s);
     }

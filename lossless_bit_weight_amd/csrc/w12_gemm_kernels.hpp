@@ -278,20 +278,62 @@ __host__ __device__ constexpr int exc_rows(bool mfma, int mr) {
     return !mfma || mr <= 32 ? mr : 16;
 }
 
+// The walk over one staged batch: lane i of the batch holds the entry of row
+// c_i (-1: none); its original and clamp are at area+256 / area+512 and its
+// x values at area+768, 64 per x row.  Each lane applies, in list order,
+// only the entries of its own row (col).
+template <class Apply>
+__device__ __forceinline__ void exc_walk(int lane, int col, const uint8_t* area, int c, Apply apply) {
+    const float* orig = reinterpret_cast<const float*>(area + 256);
+    const float* clamp = reinterpret_cast<const float*>(area + 512);
+    const uint16_t* xs = reinterpret_cast<const uint16_t*>(area + 768);
+    // LDS accesses of one wave complete in order; keep the compiler from
+    // moving the reads below above the writes.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // The batch entries of this lane's row, as a lane mask (list order =
+    // ascending bit); each lane then walks only its own entries.
+    uint64_t mine = 0;
+#pragma unroll 1
+    for (int cc = 0; cc < 16; ++cc) {
+        const uint64_t b = __ballot(c == cc);
+        if (col == cc) mine = b;
+    }
+    while (mine != 0) {
+        const int j = __ffsll((unsigned long long)mine) - 1;
+        mine &= mine - 1;
+        apply(orig[j], clamp[j], [&](int m) { return bf16_to_f32(xs[m * 64 + j]); });
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    (void)lane;
+}
+
 // apply(j, orig, clamp, xs) runs on the lanes of entry j's row; xs(m) reads
 // that entry's x[mb + m][k] from LDS (XR rows from row mb < M).
 // F::clamp_word(entry word 1) gives the BF16 clamp the planes hold for the
-// entry.
+// entry.  The entries walked are [beg, end) of the list (by default the
+// slice's blocks of `tile`).
 template <class F, int XR, class Apply>
 __device__ __forceinline__ void exc_corrections(const GemmArgs& g, int64_t tile, int g0, int gn,
                                                 int lane, int col, uint8_t* area, int mb,
-                                                Apply apply) {
+                                                Apply apply, int64_t beg_in = -1,
+                                                int64_t end_in = -1) {
     float* orig = reinterpret_cast<float*>(area + 256);
     float* clamp = reinterpret_cast<float*>(area + 512);
     uint16_t* xs = reinterpret_cast<uint16_t*>(area + 768);
     // the entries of the slice's blocks (tile, g0) .. (tile, g0 + gn - 1)
-    const int64_t blk0 = tile * (g.K / 128) + g0;
-    const uint32_t beg = g.exc_off[blk0], end = g.exc_off[blk0 + gn];
+    uint32_t beg, end;
+    if (beg_in >= 0) {
+        beg = (uint32_t)beg_in;
+        end = (uint32_t)end_in;
+    } else {
+        const int64_t blk0 = tile * (g.K / 128) + g0;
+        beg = g.exc_off[blk0];
+        end = g.exc_off[blk0 + gn];
+    }
     for (uint32_t base = beg; base < end; base += 64) {
         const uint32_t i = base + (uint32_t)lane;
         int c = -1;
@@ -330,27 +372,7 @@ __device__ __forceinline__ void exc_corrections(const GemmArgs& g, int64_t tile,
             for (int d = 0; d < kRound; ++d)
                 xs[(m0 + d) * 64 + lane] = (uint16_t)(d < valid ? xv[d] & keep : 0u);
         }
-        // LDS accesses of one wave complete in order; keep the compiler from
-        // moving the reads below above the writes.
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        // The batch entries of this lane's row, as a lane mask (list order =
-        // ascending bit); each lane then walks only its own entries.
-        uint64_t mine = 0;
-#pragma unroll 1
-        for (int cc = 0; cc < 16; ++cc) {
-            const uint64_t b = __ballot(c == cc);
-            if (col == cc) mine = b;
-        }
-        while (mine != 0) {
-            const int j = __ffsll((unsigned long long)mine) - 1;
-            mine &= mine - 1;
-            apply(orig[j], clamp[j], [&](int m) { return bf16_to_f32(xs[m * 64 + j]); });
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        exc_walk(lane, col, area, c, apply);
     }
 }
 
@@ -372,7 +394,12 @@ __device__ __forceinline__ uint4 load_stream(const uint8_t* p) {
 // BF16 pairs in natural k order.
 
 struct FetchW12 {
-    static constexpr bool kHasExceptions = true;
+    // kHasExceptions: the container may carry an exception list, whose
+    // corrections are added to the sums after the main loop.  kExcWave: in
+    // the kernels that read x directly, an extra wave of the workgroup
+    // prepares those corrections while the others stream the weights.
+    static constexpr bool kHasExceptions = false;
+    static constexpr bool kExcWave = false;
     static constexpr bool kHasMeta = true;
     struct Raw {
         uint4 a, b, c;
@@ -412,9 +439,16 @@ struct FetchW12 {
     }
 };
 
+// W12-v1 with an exception list (the same planes and decode).
+struct FetchW12X : FetchW12 {
+    static constexpr bool kHasExceptions = true;
+    static constexpr bool kExcWave = true;
+};
+
 // The arbitrary-base allocation W12-b: same planes and loads, the meta byte
 // is the base b itself (0..240), decode8b rebuilds E = b + c.
 struct FetchW12B : FetchW12 {
+    static constexpr bool kHasExceptions = true;
     __device__ __forceinline__ static void block(const Raw& r, int b, uint32_t out[4]) {
         const uint32_t pa = b == 0 ? r.a.x : b == 1 ? r.a.y : b == 2 ? r.a.z : r.a.w;
         const uint32_t pb = b == 0 ? r.b.x : b == 1 ? r.b.y : b == 2 ? r.b.z : r.b.w;
@@ -429,6 +463,7 @@ struct FetchW12B : FetchW12 {
 
 struct FetchBF16 {
     static constexpr bool kHasExceptions = false;
+    static constexpr bool kExcWave = false;
     static constexpr bool kHasMeta = false;
     struct Raw {
         uint4 q[4];
@@ -652,6 +687,14 @@ template <bool MFMA, int MR, int KW, int NW>
 __host__ __device__ constexpr size_t exc_lds_bytes() {
     return (size_t)(NW / KW) * ExcStage<exc_rows(MFMA, MR)>::kBytes;
 }
+// With a correction wave (F::kExcWave, x read directly): its one staging
+// area, then the two correction sums of every output of the workgroup's
+// tiles -- [tile of the workgroup][row in tile][x row][2] fp32.
+template <int MR, int R, int KW, int NW>
+__host__ __device__ constexpr size_t excwave_lds_bytes() {
+    return (size_t)ExcStage<MR>::kBytes + (size_t)(NW / KW) * R * 16 * MR * 2 * 4;
+}
+
 
 // ---- the kernel ----------------------------------------------------------------------
 // MFMA = false: GEMV, MR = M (1..8).  MFMA = true: MR = 16 or 32 (x rows,
@@ -666,7 +709,7 @@ __host__ __device__ constexpr size_t exc_lds_bytes() {
 // fragments (row 16 mt + col); rows past M repeat row M - 1 instead of being
 // zero -- they only feed output rows that are never stored.
 template <class F, bool MFMA, int MR, int R, int KW, int D, bool CHUNKED, bool XD, int NW>
-__global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs g) {
+__global__ __launch_bounds__(NW * 64 + (F::kExcWave && XD ? 64 : 0)) void gemm_kernel(GemmArgs g) {
     static_assert(!(XD && CHUNKED), "direct x is never chunked");
     constexpr int KC = kc_of(MFMA, MR, KW, D);
     constexpr int kRowWaves = NW / KW;
@@ -677,7 +720,9 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs g) {
     extern __shared__ uint4 lds[];
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    // wave-uniform by construction; readfirstlane tells the compiler, so the
+    // loop bounds derived from it stay scalar
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int col = lane & 15;   // weight row in the tile; A row for the MFMA
     const int q = lane >> 4;     // quarter: weights 8q..8q+7 of each 32
     const int kw = wave % KW;
@@ -707,6 +752,120 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs g) {
 #pragma unroll
     for (int r = 0; r < R; ++r) wbase[r] = F::base(g, tload[r]);
     const int glast = g0 + gn - 1;
+
+    // The correction wave (exception list, x read directly): wave NW of the
+    // workgroup walks the entries of every tile of the workgroup -- block
+    // offsets, entries, the x values they need: three dependent memory round
+    // trips, taken while the other waves stream the weights -- and leaves,
+    // for each output, the sum of x[m][k] * clamp and the sum of
+    // x[m][k] * original over its entries (list order, fp32) in LDS.  The
+    // owner waves read them after the K-wave reduction barrier and form
+    // (y - sum clamp) + sum original, so that a one-hot x row returns an
+    // original word exactly.  The wave then takes part in exactly the
+    // barriers the other waves still execute (the reduction, or its stand-in
+    // with one K-wave; the two of a split-K finish of three or more slices).
+    constexpr bool kExcWave = F::kExcWave && XD;
+    float* exc_corr = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(lds) + exc_base +
+                                               ExcStage<MR>::kBytes);
+    if constexpr (kExcWave) {
+        if (wave == NW) {
+            // T tiles; the x values of TB tiles' entries are loaded in one
+            // round (at most 64 values per lane)
+            constexpr int T = kRowWaves * R;
+            constexpr int TB = 64 / MR < 1 ? 1 : (64 / MR > T ? T : 64 / MR);
+            uint8_t* area = reinterpret_cast<uint8_t*>(lds) + exc_base;
+            const int64_t tbase = (int64_t)blockIdx.x * T;
+            // 1. the block offsets of every tile's slice (lanes 2t, 2t + 1)
+            int64_t tl = tbase + (lane >> 1 < T ? lane >> 1 : T - 1);
+            tl = tl < ntiles ? tl : ntiles - 1;
+            const uint32_t offw = g.exc_off[tl * G + g0 + ((lane & 1) ? gn : 0)];
+            // 2. the first 64 entries of every tile, all loads in flight at once
+            const uint2* ent = reinterpret_cast<const uint2*>(g.exc_ent);
+            uint32_t beg[T], end[T];
+            uint2 e[T];
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
+                beg[t] = (uint32_t)__builtin_amdgcn_readlane((int)offw, 2 * t);
+                end[t] = tbase + t < ntiles ? (uint32_t)__builtin_amdgcn_readlane((int)offw, 2 * t + 1)
+                                            : beg[t];
+                // lanes without an entry load nothing (every workgroup pointing
+                // its idle lanes at one shared word made that word's cache
+                // line a hot spot); this wave has no weight ring to pace
+                const uint32_t i = beg[t] + (uint32_t)lane;
+                e[t] = make_uint2(0u, 0u);
+                if (i < end[t]) e[t] = ent[i];
+            }
+            // 3. per round of TB tiles: the x values of their entries, then
+            // per tile the staged walk and the two sums of each output
+#pragma unroll
+            for (int t0 = 0; t0 < T; t0 += TB) {
+                uint16_t xv[TB][MR];
+                int cl_row[TB];
+#pragma unroll
+                for (int tb = 0; tb < TB; ++tb) {
+                    const int t = t0 + tb < T ? t0 + tb : T - 1;
+                    const bool has = beg[t] + (uint32_t)lane < end[t];
+                    const uint32_t kk = e[t].x & 0xFFFFFFu;
+                    const int grp = (int)(kk >> 7);
+                    cl_row[tb] = has && grp >= g0 && grp < g0 + gn ? (int)(e[t].x >> 24) : -1;
+                    const uint16_t* px = g.x + kk;
+#pragma unroll
+                    for (int m = 0; m < MR; ++m) xv[tb][m] = 0;
+                    if (cl_row[tb] >= 0) {
+#pragma unroll
+                        for (int m = 0; m < MR; ++m) {
+                            if (m < g.M) xv[tb][m] = *px;
+                            px += m + 1 < g.M ? g.ldx : 0;   // stays on the last row of x
+                        }
+                    }
+                }
+#pragma unroll
+                for (int tb = 0; tb < TB; ++tb) {
+                    const int t = t0 + tb;
+                    if (t >= T) break;
+                    float* orig = reinterpret_cast<float*>(area + 256);
+                    float* clamp = reinterpret_cast<float*>(area + 512);
+                    uint16_t* xs = reinterpret_cast<uint16_t*>(area + 768);
+                    const int c = cl_row[tb];
+                    orig[lane] = c >= 0 ? bf16_to_f32(e[t].y & 0xFFFFu) : 0.f;
+                    clamp[lane] = c >= 0 ? bf16_to_f32(F::clamp_word(e[t].y)) : 0.f;
+#pragma unroll
+                    for (int m = 0; m < MR; ++m)
+                        xs[m * 64 + lane] = (uint16_t)(c >= 0 && m < g.M ? xv[tb][m] : 0u);
+                    float cm[MR], cp[MR];
+#pragma unroll
+                    for (int m = 0; m < MR; ++m) cm[m] = cp[m] = 0.f;
+                    auto acc = [&](float o, float cl, auto xs_of) {
+#pragma unroll
+                        for (int m = 0; m < MR; ++m) {
+                            const float xm = xs_of(m);
+                            cm[m] = fmaf(xm, cl, cm[m]);
+                            cp[m] = fmaf(xm, o, cp[m]);
+                        }
+                    };
+                    exc_walk(lane, col, area, c, acc);
+                    // more than 64 entries in this tile's slice: the rest in
+                    // batches with their own loads
+                    if (end[t] - beg[t] > 64u)
+                        exc_corrections<F, MR>(g, tbase + t, g0, gn, lane, col, area, 0, acc,
+                                               (int64_t)beg[t] + 64, (int64_t)end[t]);
+                    if (q == 0) {
+#pragma unroll
+                        for (int m = 0; m < MR; ++m) {
+                            exc_corr[((t * 16 + col) * MR + m) * 2] = cm[m];
+                            exc_corr[((t * 16 + col) * MR + m) * 2 + 1] = cp[m];
+                        }
+                    }
+                }
+            }
+            __syncthreads();   // with the owners' K-wave reduction (or its stand-in)
+            if (gridDim.y > 2) {
+                __syncthreads();   // the two barriers of split_finish
+                __syncthreads();
+            }
+            return;
+        }
+    }
 
     constexpr int kXRows = XD ? (MFMA ? kMT : MR) : 1;  // x registers per slot
     constexpr int kXBlocks = MFMA ? 4 : 1;
@@ -886,7 +1045,21 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs g) {
         // D layout of the 16x16 MFMA: lane (col, q) holds rows 4q..4q+3 of
         // column col, i.e. y[m = 16 mt + 4q + e][n = 16 tile + col].  With a
         // split K the values go to this slice's partial sums instead.
-        if constexpr (F::kHasExceptions) {
+        if constexpr (kExcWave) {
+            if constexpr (KW == 1) __syncthreads();   // the correction wave's results are in
+            if (kw == 0) {
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+#pragma unroll
+                    for (int mt = 0; mt < kMT; ++mt)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int m = 16 * mt + 4 * q + e;
+                            const float* cc = exc_corr + (((nw * R + r) * 16 + col) * MR + m) * 2;
+                            macc[r][mt][e] = (macc[r][mt][e] - cc[0]) + cc[1];
+                        }
+            }
+        } else if constexpr (F::kHasExceptions) {
             if (kw == 0 && g.exc_off != nullptr) {
                 // above 32 rows x is staged 16 rows at a time (the list is
                 // walked once per 16 rows): each output still takes its
@@ -1008,7 +1181,18 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs g) {
                     }
             }
         }
-        if constexpr (F::kHasExceptions) {
+        if constexpr (kExcWave) {
+            if constexpr (KW == 1) __syncthreads();   // the correction wave's results are in
+            if (kw == 0) {
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+#pragma unroll
+                    for (int m = 0; m < MR; ++m) {
+                        const float* cc = exc_corr + (((nw * R + r) * 16 + col) * MR + m) * 2;
+                        gacc[r][m] = (gacc[r][m] - cc[0]) + cc[1];
+                    }
+            }
+        } else if constexpr (F::kHasExceptions) {
             if (kw == 0 && g.exc_off != nullptr) {
                 uint8_t* area = reinterpret_cast<uint8_t*>(lds) + exc_base + nw * ExcStage<MR>::kBytes;
 #pragma unroll
@@ -1066,9 +1250,13 @@ hipError_t launch_one(const GemmArgs& a, hipStream_t s) {
     const int64_t ntiles = (a.N + 15) / 16;
     const dim3 grid((unsigned)((ntiles + kTilesPerWG - 1) / kTilesPerWG), (unsigned)a.S);
     size_t lds = lds_bytes<MFMA, MR, R, KW, D, CHUNKED, XD, NW>(a.gs);
-    if (F::kHasExceptions && a.exc_off != nullptr) lds += exc_lds_bytes<MFMA, MR, KW, NW>();
-    hipLaunchKernelGGL((gemm_kernel<F, MFMA, MR, R, KW, D, CHUNKED, XD, NW>), grid, dim3(NW * 64), lds, s,
-                       a);
+    constexpr bool kExcWave = F::kExcWave && XD;
+    if (kExcWave)
+        lds += excwave_lds_bytes<MR, R, KW, NW>();
+    else if (F::kHasExceptions && a.exc_off != nullptr)
+        lds += exc_lds_bytes<MFMA, MR, KW, NW>();
+    hipLaunchKernelGGL((gemm_kernel<F, MFMA, MR, R, KW, D, CHUNKED, XD, NW>), grid,
+                       dim3(NW * 64 + (kExcWave ? 64 : 0)), lds, s, a);
     return hipGetLastError();
 }
 
@@ -1133,7 +1321,15 @@ hipError_t dispatch(const GemmArgs& a, const Tiling& t, hipStream_t s) {
     if (t.r == 1 && t.depth == 4) return launch_kw<F, MFMA, MR, 1, 4>(a, t, s);
     if (t.r == 1 && t.depth == 8) return launch_kw<F, MFMA, MR, 1, 8>(a, t, s);
     if (t.r == 2 && t.depth == 2) return launch_kw<F, MFMA, MR, 2, 2>(a, t, s);
-    if (t.r == 2 && t.depth == 4) return launch_kw<F, MFMA, MR, 2, 4>(a, t, s);
+    if (t.r == 2 && t.depth == 4) {
+        // with the exception-list code the two-tile ring of depth 4 does not
+        // fit the registers: depth 2 (the ring depth only moves loads;
+        // products and sums are the same)
+        if constexpr (F::kHasExceptions)
+            return launch_kw<F, MFMA, MR, 2, 2>(a, t, s);
+        else
+            return launch_kw<F, MFMA, MR, 2, 4>(a, t, s);
+    }
     return hipErrorInvalidValue;
 }
 

@@ -108,6 +108,15 @@ def _gemm(x, wt, tiling):
     return w12.w12_gemm(x, wt, tiling=tiling)
 
 
+def _control(x, bt, tiling):
+    """The BF16 control on the raw weights with the same tiling."""
+    if tiling is None:
+        return w12.bf16_gemm(x, bt)
+    if tiling == "plain":
+        return w12.bf16_gemm(x, bt, split_k=False)
+    return w12.bf16_gemm(x, bt, tiling=tiling)
+
+
 def _ms(tiling):
     if tiling is None or tiling == "plain":
         return [1, 3, 8, 16, 32, 64, 128]
@@ -119,10 +128,14 @@ def _ms(tiling):
 @pytest.mark.parametrize("shape", GEMM_SHAPES, ids=lambda s: "%dx%d" % s)
 @pytest.mark.parametrize("tiling", TILINGS, ids=lambda t: str(t))
 def test_gemm_on_raw_weights(oracle, shape, tiling):
+    """With its list the container multiplies as the raw weights: the oracle's
+    GEMM of the raw weights within the tolerance (and the BF16 control on the
+    raw weights with the same tiling within the same bound)."""
     N, K = shape
     bits = _raw(shape, 0.02, 17 * N + K)
     wt, bad = _pack_exc(bits)
     assert bad > 0
+    bt = w12.w12_bf16_tile(to_dev(bits))
     for M in _ms(tiling):
         what = "exc gemm %s %s M=%d" % (shape, tiling, M)
         print(what, flush=True)
@@ -132,9 +145,32 @@ def test_gemm_on_raw_weights(oracle, shape, tiling):
         except w12.W12Error as e:
             assert e.status == -6, what
             continue
+        yc = _control(to_dev(x), bt, tiling)
         torch.cuda.synchronize()
-        assert_gemm_close(y.cpu().numpy(), oracle.gemm_bf16_f64(x, bits),
-                          oracle.tolerance(x, bits), what)
+        yh = y.cpu().numpy()
+        ref = oracle.gemm_bf16_f64(x, bits)
+        tol = oracle.tolerance(x, bits)
+        assert_gemm_close(yh, ref, tol, what)
+        assert_gemm_close(yc.cpu().numpy(), ref, tol, what + " (control)")
+
+
+@pytest.mark.parametrize("M", [1, 2, 16, 32])
+def test_specials_with_list(oracle, M):
+    """NaN payloads, infinities, subnormals, arbitrary words and elements far
+    below their group's window: the GEMM of the raw weights (NaN and infinity
+    where the oracle has them, the rest within the tolerance), like the BF16
+    control on them."""
+    bits = _specials()
+    wt, _ = _pack_exc(bits)
+    bt = w12.w12_bf16_tile(to_dev(bits))
+    x = inputs.gaussian_bf16((M, bits.shape[1]), 1.0, 97 + M)
+    y = w12.w12_gemm(to_dev(x), wt)
+    yc = w12.bf16_gemm(to_dev(x), bt)
+    torch.cuda.synchronize()
+    ref = oracle.gemm_bf16_f64(x, bits)
+    tol = oracle.tolerance(x, bits)
+    assert_gemm_close(y.cpu().numpy(), ref, tol, "specials M=%d" % M)
+    assert_gemm_close(yc.cpu().numpy(), ref, tol, "specials M=%d (control)" % M)
 
 
 @pytest.mark.parametrize("tiling", [None, "plain", (0, 1, 4, 2, 0), (1, 2, 4, 2, 1),
