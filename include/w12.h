@@ -45,9 +45,9 @@
  *                 inside a block in storage order (piece L, dword b,
  *                 element e).
  * Unpack writes the original words back; the GEMMs add x[m][k] * (original -
- * clamp) for each entry after their main loop (W12-v1: the owner waves
- * load the first entries of their tiles at the start of the launch).  Every
- * call that takes a
+ * clamp) for each entry to their sums (W12-v1 with x read directly: an extra
+ * wave of each workgroup prepares those sums while the others stream the
+ * weights; otherwise after the main loop).  Every call that takes a
  * container accepts exc_offsets = exc_entries = NULL for "no list"; a list
  * must come from w12_exceptions for the same weight (it is not validated on
  * the device), both arrays 8-byte aligned, and needs K < 2^24.
