@@ -215,7 +215,7 @@ def read_ceiling(torch, w12, nbytes, steps, warmup):
     once can reach at this size on this device."""
     nbytes = (nbytes + 15) // 16 * 16
     R = max(2, math.ceil(ROTATE_BYTES / nbytes))
-    bufs = [torch.full((nbytes,), i, dtype=torch.uint8, device="cuda") for i in range(R)]
+    bufs = [torch.full((nbytes,), i & 255, dtype=torch.uint8, device="cuda") for i in range(R)]
     sink = torch.zeros(1, dtype=torch.int32, device="cuda")
     ms, n = time_graph(torch, [(lambda b=b: w12.w12_read_probe(b, sink)) for b in bufs], steps, warmup)
     del bufs

@@ -162,10 +162,17 @@ void bind_split(GemmArgs& a, const Tiling& t, void* ws) {
 // at least 40 groups (5120 weights) keep each workgroup's prologue and
 // epilogue small against its stream, up to ~2048 workgroups -- three slices
 // on the down shape.  Above 16 rows the LDS path also takes the fewest
-// slices that give it >= 1280 waves, with slices of at least 13 groups (QKV:
-// two slices, M = 32 16.9 us against 19.5 unsplit and 20.6 in three; O: two,
-// 15.3 us against 15.8 in three; N = 2048: three, 14.0 against 18.1
-// unsplit and 14.2 in two).
+// slices that give it >= 1280 waves, with slices of at least 13 groups, but
+// at most two: those meet in one atomic exchange per output (QKV M = 32: 16.9
+// us against 19.5 unsplit; O: 15.3 against 15.8 in three; 4352 x 5120 at
+// M = 32: 13.1 against 14.7 in three).
+//
+// Small shapes (measured per tensor-parallel shard, W12 and BF16 alike):
+// at most 128 tiles with 20-64 groups take two K slices at every M (896 x
+// 5120 at M = 2: 5.2 us against 6.3 unsplit); rows of <= 8 groups take two
+// K-waves per tile up to 16 rows (5120 x 640 at M = 8: 4.1 against 4.8);
+// 7-8 rows on 257-384 tiles with >= 40 groups stage x in LDS (5120 x 5120
+// at M = 8: 10.7 against 11.1).
 Tiling choose_tiling(int M, int64_t N, int64_t K, bool allow_splitk) {
     Tiling t{};
     t.r = 1;
@@ -173,16 +180,24 @@ Tiling choose_tiling(int M, int64_t N, int64_t K, bool allow_splitk) {
     t.nw = 4;
     const int64_t ntiles = (N + 15) / 16;
     const int64_t G = K / 128;
+    // small weights (at most 128 tiles, e.g. one GPU's QKV share under 8-way
+    // tensor parallelism, N = 896) with 20-64 groups per row: K split in two
+    // at every M -- the two slices meet in one atomic exchange per output,
+    // and the grid doubles
+    const bool small_pair = ntiles <= 128 && G >= 20 && G <= 64;
     if (M == 1) {
         t.mfma = 0;
         t.kw = ntiles >= 256 && ntiles <= 1024 ? 2 : 4;
-        t.depth = 4;
+        t.depth = small_pair ? 2 : 4;
         t.xdirect = 1;
-    } else if (M <= 8 ||
+    } else if ((M <= 8 && !(M > 6 && ntiles > 256 && ntiles <= 384 && G >= 40)) ||
+               (M <= 16 && G <= 8) ||
                (M <= 32 && (ntiles <= 256 || (M <= 12 && ntiles > 384 && ntiles <= 1024 && G <= 64)))) {
         t.mfma = 1;
-        t.r = ntiles <= 256 || (ntiles > 512 && M <= 6) ? 1 : 2;
-        t.kw = 4;
+        t.r = ntiles <= 256 || (ntiles > 512 && M <= 6) || G <= 20 ? 1 : 2;
+        // rows of at most 8 groups (one GPU's O share under 8-way tensor
+        // parallelism, K = 640): two K-waves per tile
+        t.kw = G <= 8 ? 2 : 4;
         t.depth = 2;
         t.xdirect = 1;
     } else {
@@ -192,7 +207,14 @@ Tiling choose_tiling(int M, int64_t N, int64_t K, bool allow_splitk) {
         t.kw = 2;
     }
     const int64_t nb = row_blocks(t, N);
-    if (allow_splitk && t.mfma) {
+    if (allow_splitk && small_pair && t.xdirect && t.r == 1) {
+        t.splitk = 2;
+    } else if (allow_splitk && t.mfma && t.xdirect && t.r == 1 && M <= 8 && ntiles > 256 &&
+               ntiles <= 512 && G >= 10 && G <= 20) {
+        // short rows on a mid-size grid (one GPU's down share under 8-way
+        // tensor parallelism, 5120 x 2176): two slices
+        t.splitk = 2;
+    } else if (allow_splitk && t.mfma) {
         int64_t s = G / 40;
         const int64_t fill = (2048 + nb - 1) / nb;
         s = s < fill ? s : fill;
@@ -200,6 +222,9 @@ Tiling choose_tiling(int M, int64_t N, int64_t K, bool allow_splitk) {
             const int64_t waves = nb * t.nw;
             int64_t s2 = (1280 + waves - 1) / waves;
             s2 = s2 < G / 13 ? s2 : G / 13;
+            // up to 32 rows two slices meet in one atomic exchange, more in
+            // a counted reduction: at most two for this purpose
+            if (M <= 32) s2 = s2 < 2 ? s2 : 2;
             s = s > s2 ? s : s2;
         }
         if (t.xdirect && t.r == 1 && M > 8) {

@@ -199,15 +199,28 @@ def test_workspace_rejects():
 def test_default_split_rule():
     """MFMA: slices of at least 40 groups, and none once ~2048 workgroups
     fill the grid: the 40-group shapes never split, the 136-group down shape
-    splits in three, a very tall long-K weight does not.  The GEMV (M = 1)
-    never splits."""
+    splits in three, a very tall long-K weight does not.  Small weights (at
+    most 128 tiles, at least 20 groups) split in two at every M, the GEMV
+    included; short rows (10-20 groups) on 257-512 tiles split in two up to
+    8 rows; the LDS path above 16 rows takes at most two slices for
+    filling the grid."""
     assert w12.w12_default_tiling(1, 7168, 5120).splitk == 1
     assert w12.w12_default_tiling(32, 34816, 5120).splitk == 1
     for M in (4, 8, 16, 32):
         assert w12.w12_default_tiling(M, 5120, 17408).splitk == 3
-    # the M = 1 GEMV never splits K
-    for N, K in ((5120, 17408), (896, 5120), (640, 17408)):
-        assert w12.w12_default_tiling(1, N, K).splitk == 1
+    # the M = 1 GEMV splits K only on small weights
+    assert w12.w12_default_tiling(1, 5120, 17408).splitk == 1
+    assert w12.w12_default_tiling(1, 640, 17408).splitk == 1     # 136 groups
+    for N, K in ((896, 5120), (640, 2560)):
+        for M in (1, 2, 8, 16, 32):
+            t = w12.w12_default_tiling(M, N, K)
+            assert t.splitk == 2 and t.x_direct == 1
+    for M in (2, 4, 8):
+        t = w12.w12_default_tiling(M, 5120, 2176)
+        assert (t.kind, t.splitk, t.x_direct) == (1, 2, 1)
+    assert w12.w12_default_tiling(16, 5120, 2176).splitk == 1
+    for M in (24, 32):
+        assert w12.w12_default_tiling(M, 4352, 5120).splitk == 2
     assert w12.w12_default_tiling(32, 5120 * 64, 17408).splitk == 1
 
 
@@ -231,11 +244,21 @@ def test_default_waves_rule():
     M = 9 x is staged in LDS for 512-thread workgroups: four K-waves when K
     is not split and M <= 16 (or the weight has < 128 row blocks), else
     two."""
-    for M in (1, 4, 8):
+    for M in (1, 4, 6):
         assert w12.w12_default_tiling(M, 5120, 17408).waves == 4
-    for M in (9, 16, 24, 32):
+    # 7-8 rows on 257-384 tiles with >= 40 groups stage x in LDS
+    for M in (7, 8):
+        assert w12.w12_default_tiling(M, 7168, 5120).waves == 4
+        assert w12.w12_default_tiling(M, 5120, 5120).waves == 8
+    # rows of <= 8 groups: two K-waves, x read directly, up to 16 rows
+    for M in (2, 8, 16):
+        t = w12.w12_default_tiling(M, 5120, 640)
+        assert (t.waves, t.kw, t.x_direct, t.splitk) == (4, 2, 1, 1)
+    for M in (8, 9, 16, 24, 32):
         t = w12.w12_default_tiling(M, 5120, 17408)
         assert (t.waves, t.kw, t.x_direct, t.splitk) == (8, 2, 0, 3)
+    assert w12.w12_default_tiling(8, 34816, 5120).waves == 4
+    for M in (9, 16, 24, 32):
         t = w12.w12_default_tiling(M, 34816, 5120)
         assert (t.waves, t.kw, t.x_direct, t.splitk) == (8, 4 if M <= 16 else 2, 0, 1)
     for M in (9, 12):
@@ -259,13 +282,14 @@ def test_default_waves_rule():
 
 def test_default_small_weights():
     """Weights of <= 256 tiles: x direct, one tile per wave, four K-waves;
+    at most 128 tiles with 20-64 groups split K in two at every M; otherwise
     from M = 9 K is split into up to 256 / tiles slices of >= 10 groups.
     Up to M = 6 weights of more than 512 tiles also take one tile per wave."""
     for M in (2, 4, 8):
         t = w12.w12_default_tiling(M, 896, 5120)
-        assert (t.kind, t.r, t.kw, t.x_direct, t.waves, t.splitk) == (1, 1, 4, 1, 4, 1)
+        assert (t.kind, t.r, t.kw, t.x_direct, t.waves, t.splitk) == (1, 1, 4, 1, 4, 2)
     for M in (9, 16, 32):
-        assert w12.w12_default_tiling(M, 896, 5120).splitk == 4
+        assert w12.w12_default_tiling(M, 896, 5120).splitk == 2
         assert w12.w12_default_tiling(M, 896, 5120, False).splitk == 1
         assert w12.w12_default_tiling(M, 1536, 5120).splitk == 2
         assert w12.w12_default_tiling(M, 4096, 5120).splitk == 1
