@@ -76,8 +76,14 @@ def parse():
                     help="x rows for the W12-b (arbitrary-base) comparison ('' to skip)")
     ap.add_argument("--shard-ms", type=str, default="1,4,16,32",
                     help="x rows for the 8-way tensor-parallel shard shapes ('' to skip)")
-    ap.add_argument("--workload", default="qkv", choices=["qkv", "o", "gate_up", "down"],
-                    help="headline weight (default: the QKV projection)")
+    ap.add_argument("--workload", default="qkv",
+                    choices=["qkv", "o", "gate_up", "down",
+                             "qkv_tp8", "o_tp8", "gate_up_tp8", "down_tp8"],
+                    help="headline weight (default: the QKV projection; *_tp8: one GPU's "
+                         "share under 8-way tensor parallelism)")
+    ap.add_argument("--exceptions-ms", type=str, default=None,
+                    help="x rows for the raw (unprojected) weight with its exception list "
+                         "(default: 1,16 with the sweep, none with --no-sweep)")
     ap.add_argument("--m", type=int, default=1, help="headline x rows (default 1)")
     ap.add_argument("--summarize-trace", nargs=2, metavar=("KERNEL_STATS_CSV", "VARIANT"),
                     help="print a markdown summary of a rocprofv3 --stats kernel table")
@@ -241,8 +247,11 @@ def template_of(variant: str) -> str:
     nw = 8 if "w8" in parts[7:] else 4
     mr = mr.replace("mt", "").replace("m", "")
     tf = lambda b: "true" if b else "false"
+    # w12x_: W12-v1 with an exception list (the kernel of a container that
+    # carries one); w12b_: the arbitrary-base allocation
+    fetch = {"w12": "FetchW12", "w12x": "FetchW12X", "w12b": "FetchW12B"}.get(f, "FetchBF16")
     return "gemm_kernel<w12::kern::%s, %s, %s, %s, %s, %s, %s, %s, %d>" % (
-        "FetchW12" if f == "w12" else "FetchBF16", tf(kind == "mfma"),
+        fetch, tf(kind == "mfma"),
         mr, r[1:], kw[2:], d[1:], tf(mode == "chunked"), tf(mode == "xdirect"), nw)
 
 
@@ -656,7 +665,7 @@ def main():
     print("device: %s, %d CUs" % (props.name, props.multi_processor_count), file=sys.stderr,
           flush=True)
 
-    head_case = inputs.CASES[args.workload]
+    head_case = inputs.CASES.get(args.workload) or inputs.SHARD_CASES[args.workload]
     head_m = args.m
     wl = Workload(head_case, torch, w12)
     print("headline workload ready (%s, raw unencodable groups %d)" % (head_case.name, wl.raw_bad),
@@ -759,8 +768,11 @@ def main():
     print("codec: %s" % json.dumps(codec), file=sys.stderr, flush=True)
 
     exc = None
-    if not args.no_sweep:
-        exc = measure_exceptions(torch, w12, head_case, [1, 16], args.steps, args.warmup)
+    exc_ms = args.exceptions_ms if args.exceptions_ms is not None else (
+        "" if args.no_sweep else "1,16")
+    exc_ms = [int(m) for m in exc_ms.split(",") if m]
+    if exc_ms:
+        exc = measure_exceptions(torch, w12, head_case, exc_ms, args.steps, args.warmup)
         print("exceptions: %s" % json.dumps(exc), file=sys.stderr, flush=True)
 
     stack = None
