@@ -40,6 +40,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import re
 import math
 import os
 import sys
@@ -57,6 +58,8 @@ CALIB_BYTES = 256 << 20          # size of the counter-calibration copy
 METRIC = "w12_gemm effective weight GB/s & % HBM peak; speedup vs BF16 GEMM, M=1–32"
 WORKLOAD_NAMES = {"qkv": "QKV projection", "o": "attention output projection",
                   "gate_up": "MLP fused gate+up projection", "down": "MLP down projection"}
+WORKLOAD_NAMES.update({k + "_tp8": v + ", one GPU's share under 8-way tensor parallelism"
+                       for k, v in list(WORKLOAD_NAMES.items())})
 
 
 def parse():
@@ -92,6 +95,10 @@ def parse():
     ap.add_argument("--summarize-counters", nargs=2, metavar=("COUNTER_CSV", "VARIANT"),
                     help="print a markdown summary of any rocprofv3 --pmc run")
     ap.add_argument("--command", default="", help="command line recorded in a summary")
+    ap.add_argument("--read-sizes", type=str, default="",
+                    help="only time the plain streaming-read kernel at these sizes (MB, "
+                         "comma-separated) and print a markdown table: the launch floor and "
+                         "the read rate a kernel reaching each byte once can reach")
     ap.add_argument("--detail-out", default="",
                     help="also write the full record (sweep, shards, codec, stack...) to this file")
     ap.add_argument("--pmc-calibration", action="store_true",
@@ -229,6 +236,32 @@ def read_ceiling(torch, w12, nbytes, steps, warmup):
     return {"bytes": nbytes, "us": ms * 1e3, "gbps": nbytes / (ms * 1e-3) / 1e9, "launches": n}
 
 
+def read_sizes_table(torch, w12, sizes_mb, steps, warmup):
+    """The read ceiling at each size, as a markdown table: time per launch
+    (graph-replayed, buffers rotated over >= 1 GiB), the rate, and a
+    least-squares line t = t0 + bytes / rate over the sizes >= 50 MB."""
+    rows = []
+    for mb in sizes_mb:
+        nbytes = max(4096, int(mb * 1e6) // 4096 * 4096)
+        r = read_ceiling(torch, w12, nbytes, steps, warmup)
+        rows.append(r)
+        print("read %.3f MB: %.3f us" % (nbytes / 1e6, r["us"]), file=sys.stderr, flush=True)
+    lines = ["| bytes | us per launch | GB/s | launches timed |", "|---|---|---|---|"]
+    for r in rows:
+        lines.append("| %d | %.3f | %.0f | %d |" % (r["bytes"], r["us"], r["gbps"], r["launches"]))
+    big = [r for r in rows if r["bytes"] >= 50e6]
+    if len(big) >= 2:
+        xs = [r["bytes"] for r in big]
+        ys = [r["us"] for r in big]
+        n = len(xs)
+        mx, my = sum(xs) / n, sum(ys) / n
+        slope = sum((a - mx) * (b - my) for a, b in zip(xs, ys)) / sum((a - mx) ** 2 for a in xs)
+        t0 = my - slope * mx
+        lines += ["", "Least-squares line over the sizes >= 50 MB: t = %.2f us + bytes / %.0f GB/s."
+                  % (t0, 1e-3 / slope)]
+    print("\n".join(lines))
+
+
 def attach_ceiling(r, c12, c16):
     """Fractions of the measured read ceiling (same bytes, same protocol)."""
     r["w12_frac_of_read_ceiling"] = r["w12_weight_gbps"] / c12["gbps"]
@@ -258,9 +291,10 @@ def template_of(variant: str) -> str:
 TRAFFIC_TAG = "traffic_record: "
 
 
-def stored_traffic(kernel: str):
-    """HBM bytes per launch from a committed counter summary under profiles/,
-    if it was taken on the current kernel sources; else None."""
+def stored_traffic(kernel: str, workload: str, M: int):
+    """HBM bytes per launch of `kernel` on `workload` at M x rows from a
+    committed counter summary under profiles/, if it was taken on the
+    current kernel sources; else None."""
     pdir = os.path.join(HERE, "profiles")
     if not os.path.isdir(pdir):
         return None
@@ -271,7 +305,8 @@ def stored_traffic(kernel: str):
             for line in f:
                 if line.startswith(TRAFFIC_TAG):
                     rec = json.loads(line[len(TRAFFIC_TAG):])
-                    if rec.get("kernel") == kernel and rec.get("source_sha") == source_sha():
+                    if (rec.get("kernel") == kernel and rec.get("workload") == workload
+                            and rec.get("M") == M and rec.get("source_sha") == source_sha()):
                         return rec.get("hbm_bytes_per_launch")
     return None
 
@@ -362,6 +397,11 @@ def summarize_pmc(fetch_path, write_path, variant, command):
     f_med = statistics.median(fetch[fk[0]])
     w_med = statistics.median(write[wk[0]])
     hbm = f_med * 1024 * f_scale + w_med * 1024 * w_scale
+    # the workload and x rows of the profiled run, from its command line
+    wm = re.search(r"--workload (\S+)", command)
+    mm = re.search(r"--m (\d+)", command)
+    workload = wm.group(1) if wm else "qkv"
+    m_rows = int(mm.group(1)) if mm else 1
     lines = ["# HBM bytes of %s (rocprofv3 FETCH_SIZE / WRITE_SIZE)" % variant, "",
              "Commands (run from the repository root on the GPU box, one counter per run):", "",
              "    " + command.replace("{CTR}", "FETCH_SIZE"),
@@ -379,7 +419,8 @@ def summarize_pmc(fetch_path, write_path, variant, command):
                                                           statistics.median(write[k])))
     lines += ["", "HBM bytes per launch of `%s`: %.0f (fetch %.0f + write %.0f)."
               % (variant, hbm, f_med * 1024 * f_scale, w_med * 1024 * w_scale), "",
-              TRAFFIC_TAG + json.dumps({"kernel": variant, "source_sha": source_sha(),
+              TRAFFIC_TAG + json.dumps({"kernel": variant, "workload": workload, "M": m_rows,
+                                        "source_sha": source_sha(),
                                         "hbm_bytes_per_launch": round(hbm),
                                         "fetch_kib": f_med, "write_kib": w_med,
                                         "fetch_scale": f_scale, "write_scale": w_scale})]
@@ -661,6 +702,10 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     w12.lib()
+    if args.read_sizes:
+        read_sizes_table(torch, w12, [float(v) for v in args.read_sizes.split(",") if v],
+                         args.steps, args.warmup)
+        return
     props = torch.cuda.get_device_properties(0)
     print("device: %s, %d CUs" % (props.name, props.multi_processor_count), file=sys.stderr,
           flush=True)
@@ -788,7 +833,7 @@ def main():
         print("cpu baseline: %s" % json.dumps(cpu), file=sys.stderr, flush=True)
 
     kernel = head["w12_kernel"]
-    traffic = stored_traffic(kernel)
+    traffic = stored_traffic(kernel, args.workload, head_m)
     detail = {
         "device": {"name": props.name, "cus": props.multi_processor_count,
                    "memory": device_memory_peak()},
