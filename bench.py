@@ -273,11 +273,11 @@ def template_of(variant: str) -> str:
     """rocprofv3's demangled name of the kernel a variant name refers to, e.g.
     w12_gemv_m1_r1_kw4_d2_single ->
     gemm_kernel<w12::kern::FetchW12, false, 1, 1, 4, 2, false, false, 4>
-    (the last argument is the wave count, 8 for a _w8 suffix; a split-K
+    (the last argument is the wave count, 8 or 16 for a _w8 or _w16 suffix; a split-K
     suffix _sN does not change the kernel)."""
     parts = variant.split("_")
     f, kind, mr, r, kw, d, mode = parts[:7]
-    nw = 8 if "w8" in parts[7:] else 4
+    nw = 16 if "w16" in parts[7:] else 8 if "w8" in parts[7:] else 4
     mr = mr.replace("mt", "").replace("m", "")
     tf = lambda b: "true" if b else "false"
     # w12x_: W12-v1 with an exception list (the kernel of a container that

@@ -274,7 +274,9 @@ int bf16_gemm(const uint16_t *x, int64_t M, int64_t ldx,
  *   waves : waves per workgroup: 0 or 4 = 256 threads; 8 = 512 threads,
  *           built for kind 1 with x in LDS and depth = 2, with r = 1, or
  *           r = 2 and kw = 1 above 32 rows (more waves share each x tile
- *           staged in LDS).
+ *           staged in LDS); 16 = 1024 threads, the same with r = 1,
+ *           2 <= kw <= 8 and at most 32 rows (twice the weight loads in
+ *           flight per x copy).
  * When the x columns of a slice do not fit LDS at once they are streamed in
  * chunks; some kw x depth combinations then need more than 64 KB of LDS
  * (128 KB with waves = 8) and are rejected.  The summation order depends

@@ -27,6 +27,7 @@ SOURCES = [("w12_api.hip", "w12_api", []), ("w12_pack.hip", "w12_pack", []),
 SOURCES += [("w12_gemm_inst.hip", "w12_gemv_m%d" % m, ["-DW12_INST_M=%d" % m]) for m in range(1, 9)]
 SOURCES += [("w12_gemm_inst.hip", "w12_mfma", ["-DW12_INST_MFMA"]),
             ("w12_gemm_inst.hip", "w12_mfma8", ["-DW12_INST_MFMA8"]),
+            ("w12_gemm_inst.hip", "w12_mfma16", ["-DW12_INST_MFMA16"]),
             ("w12_gemm_inst.hip", "w12_mfma8_big", ["-DW12_INST_MFMA8_BIG"])]
 ARCH = os.environ.get("W12_OFFLOAD_ARCH", "gfx950")
 

@@ -49,13 +49,17 @@ int64_t row_blocks(const Tiling& t, int64_t N) {
 
 bool complete_tiling(Tiling& t, int M, int64_t N, int64_t K) {
     if (t.nw == 0) t.nw = 4;
-    if (t.nw != 4 && t.nw != 8) return false;
+    if (t.nw != 4 && t.nw != 8 && t.nw != 16) return false;
     if (t.kw != 1 && t.kw != 2 && t.kw != 4 && t.kw != 8) return false;
     if (t.kw > t.nw) return false;
     // eight-wave workgroups: MFMA with x in LDS, depth 2, one tile per wave
     // (two with one K-wave above 32 rows)
     if (t.nw == 8 && (!t.mfma || t.xdirect || t.depth != 2)) return false;
     if (t.nw == 8 && t.r != 1 && !(t.r == 2 && t.kw == 1 && M > 32)) return false;
+    // sixteen-wave workgroups: the same, one tile per wave, up to 32 rows,
+    // two to eight K-waves
+    if (t.nw == 16 && (!t.mfma || t.xdirect || t.depth != 2 || t.r != 1 || M > 32 || t.kw < 2))
+        return false;
     if (t.splitk < 1 || t.splitk > kMaxSplitK) return false;
     // Slices of gs groups; a request above the group count gives one group
     // per slice.
@@ -247,6 +251,16 @@ Tiling choose_tiling(int M, int64_t N, int64_t K, bool allow_splitk) {
             }
         }
     }
+    // 9-32 rows on long rows (>= 100 groups) of 257-512 tiles with K split
+    // (the down projection, 5120 x 17408, in three slices): sixteen waves
+    // with four K-waves per workgroup -- the same four tiles and x copy,
+    // twice the weight loads in flight (M = 9: 25.7 us against 26.5; M = 32:
+    // 30.4 against 30.9)
+    if (t.nw == 8 && t.splitk > 1 && M > 8 && M <= 32 && G >= 100 && ntiles > 256 &&
+        ntiles <= 512) {
+        t.nw = 16;
+        t.kw = 4;
+    }
     if (t.nw == 8 && t.splitk == 1 && (M <= 16 || nb < 128)) t.kw = 4;
     // above 32 rows a grid of >= 512 row blocks unsplit keeps eight tiles per
     // workgroup (one K-wave each): x is staged once for eight tiles, and two
@@ -275,6 +289,7 @@ const char* tiling_name(const Tiling& t, int fetch) {
     n += std::to_string(t.mt) + "_r" + std::to_string(t.r) + "_kw" + std::to_string(t.kw) + "_d" +
          std::to_string(t.depth) + (t.xdirect ? "_xdirect" : t.chunked ? "_chunked" : "_single");
     if (t.nw == 8) n += "_w8";
+    if (t.nw == 16) n += "_w16";
     if (t.splitk > 1) n += "_s" + std::to_string(t.splitk);
     std::lock_guard<std::mutex> lock(mu);
     return names.insert(std::move(n)).first->c_str();
@@ -283,7 +298,9 @@ const char* tiling_name(const Tiling& t, int fetch) {
 hipError_t launch_gemm(const GemmArgs& a, const Tiling& t, int fetch, hipStream_t s) {
     if (t.mfma && t.mt > 32) return launch_mfma8_big_mt(t.mt, a, t, fetch, s);
     if (t.mfma)
-        return t.nw == 8 ? launch_mfma8_mt(t.mt, a, t, fetch, s) : launch_mfma_mt(t.mt, a, t, fetch, s);
+        return t.nw == 16  ? launch_mfma16_mt(t.mt, a, t, fetch, s)
+               : t.nw == 8 ? launch_mfma8_mt(t.mt, a, t, fetch, s)
+                           : launch_mfma_mt(t.mt, a, t, fetch, s);
     return launch_gemv_m(t.mt, a, t, fetch, s);
 }
 

@@ -532,7 +532,7 @@ constexpr int kSingleBytes = 40 * 1024;   // a multiple of 16 * 512
 
 template <int NT>
 struct XAll {
-    static constexpr int kSingleUnits = kSingleBytes / 16 / NT;  // per thread
+    static constexpr int kSingleUnits = (kSingleBytes / 16 + NT - 1) / NT;  // per thread
     uint4 v[kSingleUnits];
     int units, units_per_row;
 
@@ -599,10 +599,12 @@ __host__ __device__ constexpr int mfma_kc(int MT, int KW, int D) {
     return base < window ? window : base;
 }
 // A chunked variant is built only if each thread stages at most 8 x 16
-// bytes of a chunk (x rows * KC <= 64 * threads): a double buffer of 64 KB
-// of LDS for 256 threads, 128 KB for 512 (of the 160 KB a workgroup may
-// hold).
-__host__ __device__ constexpr bool chunk_ok(int rows, int kc, int nw) { return rows * kc <= 4096 * nw; }
+// bytes of a chunk (x rows * KC <= 64 * threads) and the double buffer
+// stays within 128 KB of LDS (of the 160 KB a workgroup may hold): 64 KB
+// for 256 threads, 128 KB for 512 and 1024.
+__host__ __device__ constexpr bool chunk_ok(int rows, int kc, int nw) {
+    return rows * kc <= 4096 * (nw < 8 ? nw : 8);
+}
 __host__ __device__ constexpr int kc_of(bool mfma, int rows, int KW, int D) {
     return mfma ? mfma_kc(rows, KW, D) : gemv_kc(rows, KW, D);
 }
@@ -1000,20 +1002,28 @@ __global__ __launch_bounds__(NW * 64 + (F::kExcWave && XD ? 64 : 0)) void gemm_k
     };
 
     // Prologue: x first, then the ring, so the barrier waits for x only.
+    // Chunked: chunks 0 and 1 are both loaded before the ring is primed, so
+    // that on entering the loop -- as after every chunk step -- the loads
+    // of the next x chunk are followed by one window of ring loads, and the
+    // compiler's wait for them at the first chunk step counts exactly (with
+    // chunk 1 loaded after the ring it waited for everything, either here
+    // or at every chunk step).
     XChunk<MR, KC, NW * 64> xr;
     XAll<NW * 64> xa;
-    if constexpr (CHUNKED)
-        xr.load(g, kbase);
-    else if constexpr (!XD)
-        xa.load(g, MR, kbase, units_per_row);
+    if constexpr (CHUNKED) {
+        XChunk<MR, KC, NW * 64> x0;
+        x0.load(g, kbase);
+        xr.load(g, kbase + (int64_t)(nchunks > 1 ? 1 : 0) * KC);
 #pragma unroll
-    for (int d = 0; d < D; ++d) fetch(d, ring[d], d);
-    if constexpr (CHUNKED)
-        xr.template store<FixedLayout<XLayout, KC / 8>>(lds);
-    else if constexpr (!XD)
-        xa.template store<XLayout>(lds);
+        for (int d = 0; d < D; ++d) fetch(d, ring[d], d);
+        x0.template store<FixedLayout<XLayout, KC / 8>>(lds);
+    } else {
+        if constexpr (!XD) xa.load(g, MR, kbase, units_per_row);
+#pragma unroll
+        for (int d = 0; d < D; ++d) fetch(d, ring[d], d);
+        if constexpr (!XD) xa.template store<XLayout>(lds);
+    }
     if constexpr (!XD) __syncthreads();
-    if constexpr (CHUNKED) xr.load(g, kbase + (int64_t)(nchunks > 1 ? 1 : 0) * KC);
 
     auto store_next = [&]() {
         xr.template store<FixedLayout<XLayout, KC / 8>>(lds + ((c + 1) & 1) * kBuf);
@@ -1310,6 +1320,21 @@ hipError_t dispatch8(const GemmArgs& a, const Tiling& t, hipStream_t s) {
         case 2: return launch_ch<F, true, MR, 1, 2, 2, 8>(a, t, s);
         case 4: return launch_ch<F, true, MR, 1, 4, 2, 8>(a, t, s);
         case 8: return launch_ch<F, true, MR, 1, 8, 2, 8>(a, t, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+// Sixteen-wave workgroups (1024 threads): the same MFMA kernels with x
+// staged in LDS, one tile per wave, ring depth 2, 16 and 32 rows -- twice the
+// waves (and weight bytes in flight) of an eight-wave workgroup on one x
+// copy, for grids with too few row blocks to fill the CUs twice.
+template <class F, int MR>
+hipError_t dispatch16(const GemmArgs& a, const Tiling& t, hipStream_t s) {
+    if (t.depth != 2 || t.xdirect || t.r != 1) return hipErrorInvalidValue;
+    switch (t.kw) {
+        case 2: return launch_ch<F, true, MR, 1, 2, 2, 16>(a, t, s);
+        case 4: return launch_ch<F, true, MR, 1, 4, 2, 16>(a, t, s);
+        case 8: return launch_ch<F, true, MR, 1, 8, 2, 16>(a, t, s);
         default: return hipErrorInvalidValue;
     }
 }

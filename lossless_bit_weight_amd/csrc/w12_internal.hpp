@@ -64,8 +64,9 @@ struct GemmArgs {
 //   chunked = 0 if the x columns of a K slice are staged in LDS at once, 1 if
 //             they are streamed through LDS in double-buffered chunks (set
 //             from the shape).
-//   nw      = waves per workgroup: 4 (256 threads) or 8 (512 threads; MFMA
-//             with x in LDS, r = 1, depth = 2 only).
+//   nw      = waves per workgroup: 4 (256 threads), 8 (512 threads; MFMA
+//             with x in LDS, r = 1, depth = 2 only) or 16 (1024 threads;
+//             the same, 16 and 32 rows, kw 2-8).
 struct Tiling {
     int mfma;
     int mt;
@@ -108,6 +109,7 @@ hipError_t launch_gemm(const GemmArgs& a, const Tiling& t, int fetch, hipStream_
 hipError_t launch_gemv_m(int M, const GemmArgs& a, const Tiling& t, int fetch, hipStream_t s);
 hipError_t launch_mfma_mt(int MT, const GemmArgs& a, const Tiling& t, int fetch, hipStream_t s);
 hipError_t launch_mfma8_mt(int MT, const GemmArgs& a, const Tiling& t, int fetch, hipStream_t s);
+hipError_t launch_mfma16_mt(int MT, const GemmArgs& a, const Tiling& t, int fetch, hipStream_t s);
 hipError_t launch_mfma8_big_mt(int MT, const GemmArgs& a, const Tiling& t, int fetch,
                                hipStream_t s);
 hipError_t launch_pack(int fmt, const uint16_t* w, int64_t N, int64_t K, void* p0, void* p1,

@@ -47,7 +47,7 @@ class W12UnencodableError(ValueError):
 class Tiling(ctypes.Structure):
     """w12_tiling_t: kind (0 GEMV, 1 MFMA), r, kw, depth, x_direct, splitk
     (0 or 1 = K not split across workgroups), waves (0 or 4 = 256-thread
-    workgroups, 8 = 512 threads)."""
+    workgroups, 8 = 512 threads, 16 = 1024 threads)."""
     _fields_ = [("kind", ctypes.c_int32), ("r", ctypes.c_int32), ("kw", ctypes.c_int32),
                 ("depth", ctypes.c_int32), ("x_direct", ctypes.c_int32),
                 ("splitk", ctypes.c_int32), ("waves", ctypes.c_int32)]
@@ -70,6 +70,8 @@ _PAIRS = ((1, 2), (1, 4), (1, 8), (2, 2), (2, 4))
 GEMV_TILINGS = [(0, r, kw, d, xd) for (r, d) in _PAIRS for kw in (1, 2, 4) for xd in (0, 1)]
 MFMA_TILINGS = [(1, r, kw, d, xd) for (r, d) in _PAIRS for kw in (1, 2, 4) for xd in (0, 1)]
 MFMA8_TILINGS = [(1, 1, kw, 2, 0, 1, 8) for kw in (1, 2, 4, 8)]
+# 1024-thread workgroups: the same, 16 and 32 rows, two to eight K-waves.
+MFMA16_TILINGS = [(1, 1, kw, 2, 0, 1, 16) for kw in (2, 4, 8)]
 
 
 def x_direct_fits(M: int, r: int, depth: int, kind: int = 0) -> bool:

@@ -254,9 +254,12 @@ def test_default_waves_rule():
     for M in (2, 8, 16):
         t = w12.w12_default_tiling(M, 5120, 640)
         assert (t.waves, t.kw, t.x_direct, t.splitk) == (4, 2, 1, 1)
-    for M in (8, 9, 16, 24, 32):
+    t = w12.w12_default_tiling(8, 5120, 17408)
+    assert (t.waves, t.kw, t.x_direct, t.splitk) == (8, 2, 0, 3)
+    # 9-32 rows on long rows of 257-512 tiles: sixteen waves, four K-waves
+    for M in (9, 16, 24, 32):
         t = w12.w12_default_tiling(M, 5120, 17408)
-        assert (t.waves, t.kw, t.x_direct, t.splitk) == (8, 2, 0, 3)
+        assert (t.waves, t.kw, t.x_direct, t.splitk) == (16, 4, 0, 3)
     assert w12.w12_default_tiling(8, 34816, 5120).waves == 4
     for M in (9, 16, 24, 32):
         t = w12.w12_default_tiling(M, 34816, 5120)
@@ -333,16 +336,25 @@ def test_default_large_m():
 
 def test_tiling_waves_rejects():
     """512-thread workgroups are built only for the MFMA with x in LDS, r = 1,
-    depth 2 and kw <= 8; 4 and 0 (= 4) are the other wave counts."""
+    depth 2 and kw <= 8; 1024-thread ones for the same with 2 <= kw <= 8 and
+    at most 32 rows; 4 and 0 (= 4) are the other wave counts."""
     L = w12.lib()
     nbytes = ctypes.c_size_t()
     ok = (1, 1, 2, 2, 0, 1, 8)
     assert L.w12_gemm_workspace_bytes(16, 5120, 5120, w12._tiling_arg(ok), ctypes.byref(nbytes)) == 0
     for bad in ((0, 1, 2, 2, 0, 1, 8), (1, 2, 2, 2, 0, 1, 8), (1, 2, 1, 2, 0, 1, 8), (1, 1, 2, 4, 0, 1, 8),
                 (1, 1, 2, 2, 1, 1, 8), (1, 1, 8, 2, 0, 1, 4), (1, 1, 2, 2, 0, 1, 6),
-                (1, 1, 16, 2, 0, 1, 8)):
+                (1, 1, 16, 2, 0, 1, 8), (1, 1, 1, 2, 0, 1, 16), (1, 2, 4, 2, 0, 1, 16),
+                (1, 1, 4, 2, 1, 1, 16), (0, 1, 4, 2, 0, 1, 16), (1, 1, 4, 4, 0, 1, 16),
+                (1, 1, 16, 2, 0, 1, 16), (1, 1, 4, 2, 0, 1, 12)):
         rc = L.w12_gemm_workspace_bytes(16, 5120, 5120, w12._tiling_arg(bad), ctypes.byref(nbytes))
         assert rc == -6, bad
+    for ok16 in ((1, 1, 2, 2, 0, 1, 16), (1, 1, 4, 2, 0, 3, 16), (1, 1, 8, 2, 0, 1, 16)):
+        assert L.w12_gemm_workspace_bytes(16, 5120, 5120, w12._tiling_arg(ok16),
+                                          ctypes.byref(nbytes)) == 0, ok16
+    # above 32 rows only 256- and 512-thread workgroups
+    assert L.w12_gemm_workspace_bytes(33, 5120, 5120, w12._tiling_arg((1, 1, 4, 2, 0, 1, 16)),
+                                      ctypes.byref(nbytes)) == -6
 
 
 def test_read_probe_rejects():

@@ -269,8 +269,8 @@ def _tiling_id(t):
 
 
 @pytest.mark.parametrize("fmt", ["v1", "b"])
-@pytest.mark.parametrize("tiling", w12.GEMV_TILINGS + w12.MFMA_TILINGS + w12.MFMA8_TILINGS,
-                         ids=_tiling_id)
+@pytest.mark.parametrize("tiling", w12.GEMV_TILINGS + w12.MFMA_TILINGS + w12.MFMA8_TILINGS +
+                         w12.MFMA16_TILINGS, ids=_tiling_id)
 def test_every_tiling(oracle, tiling, fmt):
     """Every instantiated variant, single-chunk and chunked x, ragged rows and
     a K tail, against the oracle; W12 (both allocations) and BF16 bitwise
@@ -306,7 +306,7 @@ def test_every_tiling(oracle, tiling, fmt):
 # (kind, r, kw, depth, x_direct[, waves])
 SPLIT_BASES = [(0, 1, 4, 2, 0), (0, 2, 1, 2, 0), (0, 1, 2, 4, 1),
                (1, 1, 1, 2, 0), (1, 2, 4, 2, 0), (1, 1, 2, 4, 0), (1, 1, 2, 2, 1), (1, 2, 1, 2, 1),
-               (1, 1, 2, 2, 0, 8), (1, 1, 8, 2, 0, 8)]
+               (1, 1, 2, 2, 0, 8), (1, 1, 8, 2, 0, 8), (1, 1, 4, 2, 0, 16), (1, 1, 8, 2, 0, 16)]
 
 
 @pytest.mark.parametrize("base", SPLIT_BASES,
