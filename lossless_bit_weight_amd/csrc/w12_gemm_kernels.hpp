@@ -755,6 +755,25 @@ __global__ __launch_bounds__(NW * 64 + (F::kExcWave && XD ? 64 : 0)) void gemm_k
     for (int r = 0; r < R; ++r) wbase[r] = F::base(g, tload[r]);
     const int glast = g0 + gn - 1;
 
+    // Exception list walked after the main loop (no correction wave): the
+    // entry range of each tile's blocks in this K slice is read here, before
+    // any other load, so the walk starts with the entries (one memory round
+    // trip fewer after the loop) and these loads are older than everything
+    // the ring's wait counts track.  Every wave loads (the address is
+    // uniform); without a list the loads read the first words of plane 0
+    // and the range stays empty.
+    uint32_t exc_b[R], exc_e[R];
+    if constexpr (F::kHasExceptions && !(F::kExcWave && XD)) {
+        const bool has = g.exc_off != nullptr;
+        const uint32_t* offp = has ? g.exc_off : reinterpret_cast<const uint32_t*>(g.p0);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int64_t blk0 = has ? tload[r] * G + g0 : 0;
+            exc_b[r] = offp[blk0];
+            exc_e[r] = offp[has ? blk0 + gn : 0];
+        }
+    }
+
     // The correction wave (exception list, x read directly): wave NW of the
     // workgroup walks the entries of every tile of the workgroup -- block
     // offsets, entries, the x values they need: three dependent memory round
@@ -1092,7 +1111,7 @@ __global__ __launch_bounds__(NW * 64 + (F::kExcWave && XD ? 64 : 0)) void gemm_k
                                     const float xv = xs(16 * t + 4 * q + e);
                                     macc[r][mt][e] = fmaf(xv, orig, fmaf(-xv, clamp, macc[r][mt][e]));
                                 }
-                        });
+                        }, exc_b[r], exc_e[r]);
                     }
                 }
             }
@@ -1215,7 +1234,7 @@ __global__ __launch_bounds__(NW * 64 + (F::kExcWave && XD ? 64 : 0)) void gemm_k
                             const float xv = xs(m);
                             gacc[r][m] = fmaf(xv, orig, fmaf(-xv, clamp, gacc[r][m]));
                         }
-                    });
+                    }, exc_b[r], exc_e[r]);
                 }
             }
         }
