@@ -796,19 +796,25 @@ __global__ __launch_bounds__(NW * 64 + (F::kExcWave && XD ? 64 : 0)) void gemm_k
             constexpr int TB = 64 / MR < 1 ? 1 : (64 / MR > T ? T : 64 / MR);
             uint8_t* area = reinterpret_cast<uint8_t*>(lds) + exc_base;
             const int64_t tbase = (int64_t)blockIdx.x * T;
-            // 1. the block offsets of every tile's slice (lanes 2t, 2t + 1)
-            int64_t tl = tbase + (lane >> 1 < T ? lane >> 1 : T - 1);
-            tl = tl < ntiles ? tl : ntiles - 1;
-            const uint32_t offw = g.exc_off[tl * G + g0 + ((lane & 1) ? gn : 0)];
-            // 2. the first 64 entries of every tile, all loads in flight at once
+            // 1. the block offsets of every tile's slice: uniform addresses,
+            // so scalar loads, which do not queue behind the vector loads of
+            // the weight streams on this CU
             const uint2* ent = reinterpret_cast<const uint2*>(g.exc_ent);
+            const __attribute__((address_space(4))) uint32_t* off4 =
+                (const __attribute__((address_space(4))) uint32_t*)g.exc_off;
             uint32_t beg[T], end[T];
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
+                const int64_t tl = tbase + t < ntiles ? tbase + t : ntiles - 1;
+                const uint32_t b0 = off4[tl * G + g0];
+                const uint32_t e0 = off4[tl * G + g0 + gn];
+                beg[t] = b0;
+                end[t] = tbase + t < ntiles ? e0 : b0;
+            }
+            // 2. the first 64 entries of every tile, all loads in flight at once
             uint2 e[T];
 #pragma unroll
             for (int t = 0; t < T; ++t) {
-                beg[t] = (uint32_t)__builtin_amdgcn_readlane((int)offw, 2 * t);
-                end[t] = tbase + t < ntiles ? (uint32_t)__builtin_amdgcn_readlane((int)offw, 2 * t + 1)
-                                            : beg[t];
                 // lanes without an entry load nothing (every workgroup pointing
                 // its idle lanes at one shared word made that word's cache
                 // line a hot spot); this wave has no weight ring to pace
