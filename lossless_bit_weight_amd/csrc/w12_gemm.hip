@@ -174,7 +174,9 @@ void bind_split(GemmArgs& a, const Tiling& t, void* ws) {
 // Small shapes (measured per tensor-parallel shard, W12 and BF16 alike):
 // at most 128 tiles with 20-64 groups take two K slices at every M (896 x
 // 5120 at M = 2: 5.2 us against 6.3 unsplit); rows of <= 8 groups take two
-// K-waves per tile up to 16 rows (5120 x 640 at M = 8: 4.1 against 4.8);
+// K-waves per tile up to 32 rows (5120 x 640 at M = 8: 4.1 against 4.8; at
+// M = 32: 5.9 against 6.0), and so do rows of 10-20 groups on 257-512 tiles
+// at 9-12 rows (5120 x 2176 at M = 9: 6.7 against 7.5 with x in LDS);
 // 7-8 rows on 257-384 tiles with >= 40 groups stage x in LDS (5120 x 5120
 // at M = 8: 10.7 against 11.1).
 Tiling choose_tiling(int M, int64_t N, int64_t K, bool allow_splitk) {
@@ -195,13 +197,15 @@ Tiling choose_tiling(int M, int64_t N, int64_t K, bool allow_splitk) {
         t.depth = small_pair ? 2 : 4;
         t.xdirect = 1;
     } else if ((M <= 8 && !(M > 6 && ntiles > 256 && ntiles <= 384 && G >= 40)) ||
-               (M <= 16 && G <= 8) ||
+               (M <= 32 && G <= 8) ||
+               (M <= 12 && G >= 10 && G <= 20 && ntiles > 256 && ntiles <= 512) ||
                (M <= 32 && (ntiles <= 256 || (M <= 12 && ntiles > 384 && ntiles <= 1024 && G <= 64)))) {
         t.mfma = 1;
         t.r = ntiles <= 256 || (ntiles > 512 && M <= 6) || G <= 20 ? 1 : 2;
         // rows of at most 8 groups (one GPU's O share under 8-way tensor
-        // parallelism, K = 640): two K-waves per tile
-        t.kw = G <= 8 ? 2 : 4;
+        // parallelism, K = 640), and of 10-20 groups on 257-512 tiles from
+        // 9 rows (the down share, K = 2176): two K-waves per tile
+        t.kw = G <= 8 || (M > 8 && G <= 20) ? 2 : 4;
         t.depth = 2;
         t.xdirect = 1;
     } else {

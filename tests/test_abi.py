@@ -250,10 +250,15 @@ def test_default_waves_rule():
     for M in (7, 8):
         assert w12.w12_default_tiling(M, 7168, 5120).waves == 4
         assert w12.w12_default_tiling(M, 5120, 5120).waves == 8
-    # rows of <= 8 groups: two K-waves, x read directly, up to 16 rows
-    for M in (2, 8, 16):
+    # rows of <= 8 groups: two K-waves, x read directly, up to 32 rows
+    for M in (2, 8, 16, 24, 32):
         t = w12.w12_default_tiling(M, 5120, 640)
         assert (t.waves, t.kw, t.x_direct, t.splitk) == (4, 2, 1, 1)
+    # rows of 10-20 groups on 257-512 tiles: the same at 9-12 rows, x in LDS above
+    for M in (9, 12):
+        t = w12.w12_default_tiling(M, 5120, 2176)
+        assert (t.waves, t.r, t.kw, t.x_direct, t.splitk) == (4, 1, 2, 1, 1)
+    assert w12.w12_default_tiling(13, 5120, 2176).x_direct == 0
     t = w12.w12_default_tiling(8, 5120, 17408)
     assert (t.waves, t.kw, t.x_direct, t.splitk) == (8, 2, 0, 3)
     # 9-32 rows on long rows of 257-512 tiles: sixteen waves, four K-waves
