@@ -403,7 +403,11 @@ struct FetchW12 {
     static constexpr bool kHasMeta = true;
     struct Raw {
         uint4 a, b, c;
-        uint32_t beta;
+        // the meta byte as loaded: widened only where a group is computed,
+        // so no arithmetic on it is placed right after its load (in the
+        // x-staged kernels that put a wait for the whole primed ring before
+        // the first x barrier)
+        uint8_t beta;
     };
     // Wave-uniform part of the addresses of tile `tile` (all groups); the
     // lane part is added per load.
@@ -422,7 +426,7 @@ struct FetchW12 {
     }
     // The meta byte of row (lane & 15) in group grp (each quarter of a wave
     // may ask for a different group).
-    __device__ __forceinline__ static uint32_t load_meta(const Base& b, int grp, int lane) {
+    __device__ __forceinline__ static uint8_t load_meta(const Base& b, int grp, int lane) {
         return b.meta[(uint32_t)grp * 16u + (uint32_t)(lane & 15)];
     }
     __device__ __forceinline__ static void block(const Raw& r, int b, uint32_t out[4]) {
