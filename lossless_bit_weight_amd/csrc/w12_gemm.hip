@@ -177,8 +177,11 @@ void bind_split(GemmArgs& a, const Tiling& t, void* ws) {
 // K-waves per tile up to 32 rows (5120 x 640 at M = 8: 4.1 against 4.8; at
 // M = 32: 5.9 against 6.0), and so do rows of 10-20 groups on 257-512 tiles
 // at 9-12 rows (5120 x 2176 at M = 9: 6.7 against 7.5 with x in LDS);
-// 7-8 rows on 257-384 tiles with >= 40 groups stage x in LDS (5120 x 5120
-// at M = 8: 10.7 against 11.1).
+// x is staged in LDS from 4 rows on 257-384 tiles with >= 40 groups (5120
+// x 5120 at M = 4: 10.1 against 10.4; 5120 x 17408 at M = 4: 24.9 against
+// 25.3), from 7 rows above 1024 tiles (34816 x 5120 at M = 8: 45.9 against
+// 47.4) and from 11 rows on 385-1024 tiles (7168 x 5120 at M = 12: 12.5
+// against 12.9).
 Tiling choose_tiling(int M, int64_t N, int64_t K, bool allow_splitk) {
     Tiling t{};
     t.r = 1;
@@ -191,15 +194,18 @@ Tiling choose_tiling(int M, int64_t N, int64_t K, bool allow_splitk) {
     // at every M -- the two slices meet in one atomic exchange per output,
     // and the grid doubles
     const bool small_pair = ntiles <= 128 && G >= 20 && G <= 64;
+    // x staged in LDS already below 9 rows: from 4 rows on 257-384 tiles with
+    // >= 40 groups (O, down), from 7 rows above 1024 tiles (gate+up)
+    const bool lds_small_m = (M >= 4 && ntiles > 256 && ntiles <= 384 && G >= 40) ||
+                             (M >= 7 && ntiles > 1024);
     if (M == 1) {
         t.mfma = 0;
         t.kw = ntiles >= 256 && ntiles <= 1024 ? 2 : 4;
         t.depth = small_pair ? 2 : 4;
         t.xdirect = 1;
-    } else if ((M <= 8 && !(M > 6 && ntiles > 256 && ntiles <= 384 && G >= 40)) ||
-               (M <= 32 && G <= 8) ||
+    } else if ((M <= 8 && !lds_small_m) || (M <= 32 && G <= 8) ||
                (M <= 12 && G >= 10 && G <= 20 && ntiles > 256 && ntiles <= 512) ||
-               (M <= 32 && (ntiles <= 256 || (M <= 12 && ntiles > 384 && ntiles <= 1024 && G <= 64)))) {
+               (M <= 32 && (ntiles <= 256 || (M <= 10 && ntiles > 384 && ntiles <= 1024 && G <= 64)))) {
         t.mfma = 1;
         t.r = ntiles <= 256 || (ntiles > 512 && M <= 6) || G <= 20 ? 1 : 2;
         // rows of at most 8 groups (one GPU's O share under 8-way tensor

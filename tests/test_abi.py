@@ -238,14 +238,20 @@ def test_default_tiling():
 
 
 def test_default_waves_rule():
-    """M = 2-8, M <= 32 on weights of <= 256 tiles, and M = 9-12 on weights of
+    """M = 2-8 (2-3 on 257-384 tiles with >= 40 groups, 2-6 above 1024
+    tiles), M <= 32 on weights of <= 256 tiles, and M = 9-10 on weights of
     385-1024 tiles and <= 64 groups per row, read x directly in 256-thread
-    workgroups (one tile per wave on <= 256 tiles, two above); otherwise from
-    M = 9 x is staged in LDS for 512-thread workgroups: four K-waves when K
-    is not split and M <= 16 (or the weight has < 128 row blocks), else
-    two."""
-    for M in (1, 4, 6):
+    workgroups (one tile per wave on <= 256 tiles, two above); otherwise x
+    is staged in LDS for 512-thread workgroups: four K-waves when K is not
+    split and M <= 16 (or the weight has < 128 row blocks), else two."""
+    for M in (1, 2, 3):
         assert w12.w12_default_tiling(M, 5120, 17408).waves == 4
+    # from 4 rows on 257-384 tiles with >= 40 groups x is staged in LDS
+    for M in (4, 6):
+        t = w12.w12_default_tiling(M, 5120, 17408)
+        assert (t.waves, t.kw, t.x_direct, t.splitk) == (8, 2, 0, 3)
+        t = w12.w12_default_tiling(M, 5120, 5120)
+        assert (t.waves, t.kw, t.x_direct, t.splitk) == (8, 4, 0, 1)
     # 7-8 rows on 257-384 tiles with >= 40 groups stage x in LDS
     for M in (7, 8):
         assert w12.w12_default_tiling(M, 7168, 5120).waves == 4
@@ -265,11 +271,15 @@ def test_default_waves_rule():
     for M in (9, 16, 24, 32):
         t = w12.w12_default_tiling(M, 5120, 17408)
         assert (t.waves, t.kw, t.x_direct, t.splitk) == (16, 4, 0, 3)
-    assert w12.w12_default_tiling(8, 34816, 5120).waves == 4
+    # above 1024 tiles from 7 rows, on 385-1024 tiles from 11 rows
+    assert w12.w12_default_tiling(6, 34816, 5120).waves == 4
+    assert w12.w12_default_tiling(7, 34816, 5120).waves == 8
+    assert w12.w12_default_tiling(10, 7168, 5120).waves == 4
+    assert w12.w12_default_tiling(11, 7168, 5120).waves == 8
     for M in (9, 16, 24, 32):
         t = w12.w12_default_tiling(M, 34816, 5120)
         assert (t.waves, t.kw, t.x_direct, t.splitk) == (8, 4 if M <= 16 else 2, 0, 1)
-    for M in (9, 12):
+    for M in (9, 10):
         t = w12.w12_default_tiling(M, 7168, 5120)
         assert (t.waves, t.x_direct) == (4, 1)
         t = w12.w12_default_tiling(M, 5120, 5120)
@@ -305,12 +315,12 @@ def test_default_small_weights():
         assert w12.w12_default_tiling(M, 1024, 17408).splitk == 4
     # 257-512 tiles: two tiles per wave (at most 256 workgroups); above 512
     # tiles one again up to M = 6
-    assert w12.w12_default_tiling(4, 4112, 5120).r == 2
-    assert w12.w12_default_tiling(4, 4096, 5120).r == 1
+    assert w12.w12_default_tiling(3, 4112, 5120).r == 2
+    assert w12.w12_default_tiling(3, 4096, 5120).r == 1
     assert w12.w12_default_tiling(4, 8192, 5120).r == 2
     assert w12.w12_default_tiling(4, 8208, 5120).r == 1
     assert w12.w12_default_tiling(6, 34816, 5120).r == 1
-    assert w12.w12_default_tiling(7, 34816, 5120).r == 2
+    assert w12.w12_default_tiling(7, 16384, 5120).r == 2
 
 
 def test_default_large_m():
