@@ -18,14 +18,16 @@
 //     memory.  Lane L = 16 q + col holds row col of the tile and the 32
 //     weights k = 128 g + 32 b + 8 q + e; its 8-weight block b is ready as
 //     4 dwords of BF16 pairs after decode;
-//   * a workgroup (4 waves) owns R tiles per row-wave over one K slice
+//   * a workgroup (4, 8 or 16 waves) owns R tiles per row-wave over one K slice
 //     (grid y; the whole K unless K is split across workgroups); KW of its
 //     waves split the slice's groups (group g0 + i goes to K-wave i % KW)
 //     and add their partial sums through LDS in a fixed order;
-//   * with K split over S workgroups, each writes its slice's fp32 sums to a
+//   * with K split over S workgroups: S = 2 (up to 32 rows) publishes each
+//     output with one atomic exchange and the second arriver adds the two
+//     slices in slice order; S > 2 writes the slices' fp32 sums to a
 //     workspace and the last of a row block to finish (an atomic counter)
-//     adds the S slices in slice order and writes y -- so the result never
-//     depends on which workgroup finishes last, and no workgroup waits;
+//     adds them in slice order -- so the result never depends on which
+//     workgroup finishes last, and no workgroup waits for another;
 //   * each lane keeps D groups in flight in a register ring unrolled at
 //     compile time; every ring load is issued unconditionally (indices are
 //     clamped to valid memory), so the compiler waits only for the oldest
@@ -33,9 +35,10 @@
 //   * x lives in LDS (the columns of the workgroup's K slice).  If they fit
 //     they are loaded once, before the ring is primed, so the prologue
 //     barrier waits for x only.  Otherwise they are double-buffered in
-//     chunks of KC columns loaded one chunk ahead, one barrier per chunk,
-//     between ring windows.  In x-direct mode each ring slot carries its
-//     group's x values instead and there is no x barrier at all;
+//     chunks of KC columns loaded one chunk ahead (chunks 0 and 1 both
+//     before the ring is primed), one barrier per chunk, between ring
+//     windows.  In x-direct mode each ring slot carries its group's x values
+//     instead and there is no x barrier at all;
 // GEMV (M <= 8; the default at M = 1): v_dot2c_f32_bf16 into fp32, x[m]
 // read as a broadcast (all 16 lanes of a quarter read the same 16 bytes);
 // the 4 quarter sums of a row are added with a fixed xor butterfly.
