@@ -127,12 +127,14 @@ def test_workloads_sampled(oracle, name, M):
 
 
 @pytest.mark.parametrize("shape", [(896, 5120), (1536, 5120), (1024, 17408), (896, 2176),
-                                   (4352, 5120), (5120, 640)])
-@pytest.mark.parametrize("M", [2, 9, 16, 32])
+                                   (4352, 5120), (5120, 640), (5120, 2176)])
+@pytest.mark.parametrize("M", [2, 4, 9, 12, 16, 24, 32])
 def test_shard_shapes_default(oracle, shape, M):
     """One GPU's share of the QKV, gate+up, O and down weights under 8-way
     tensor parallelism and nearby small weights, with the default tilings
-    (one tile per wave and K split across workgroups on <= 256 tiles)."""
+    (one tile per wave and K split across workgroups on <= 256 tiles; x read
+    directly with two K-waves on short rows; x in LDS from 4 rows on the
+    gate+up share)."""
     P = prepared(shape)
     x = inputs.gaussian_bf16((M, shape[1]), 1.0, 13 * M + shape[0])
     _check(oracle, P, x, _sample_rows(P.N, seed=M), "shard %s M=%d" % (shape, M))
