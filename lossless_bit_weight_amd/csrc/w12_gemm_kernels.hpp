@@ -632,7 +632,7 @@ __host__ __device__ constexpr int kc_of(bool mfma, int rows, int KW, int D) {
             __syncthreads();                                                              \
             ++c;                                                                          \
             next_boundary += (L);                                                         \
-            xr.load(g, kbase + (int64_t)(c + 1 < (nchunks) ? c + 1 : c) * KC);            \
+            if (c + 1 < (nchunks)) xr.load(g, kbase + (int64_t)(c + 1) * KC);             \
         }                                                                                 \
     }
 
@@ -672,7 +672,7 @@ __host__ __device__ constexpr int kc_of(bool mfma, int rows, int KW, int D) {
                 store_next();                                                             \
                 __syncthreads();                                                          \
                 ++c;                                                                      \
-                xr.load(g, kbase + (int64_t)(c + 1 < (nchunks) ? c + 1 : c) * KC);        \
+                if (c + 1 < (nchunks)) xr.load(g, kbase + (int64_t)(c + 1) * KC);         \
             }                                                                             \
         }                                                                                 \
     }
