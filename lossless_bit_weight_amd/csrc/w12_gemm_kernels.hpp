@@ -50,6 +50,8 @@
 // for W = unpack(pack(W)) both return bitwise equal y.
 #pragma once
 
+#include <type_traits>
+
 #include "w12_decode.hpp"
 #include "w12_internal.hpp"
 
@@ -616,6 +618,26 @@ __host__ __device__ constexpr int kc_of(bool mfma, int rows, int KW, int D) {
     return mfma ? mfma_kc(rows, KW, D) : gemv_kc(rows, KW, D);
 }
 
+// Compile-time loops for the ring's tails: f(integral_constant<int, i>) for
+// i = I .. N - 1, and f(integral_constant<int, v>) for the runtime v in
+// [I, N) (nothing for any other v).
+template <int I, int N, class F>
+__device__ __forceinline__ void w12_static_for(F&& f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        w12_static_for<I + 1, N>(f);
+    }
+}
+template <int I, int N, class F>
+__device__ __forceinline__ void w12_select(int v, F&& f) {
+    if constexpr (I < N) {
+        if (v == I)
+            f(std::integral_constant<int, I>{});
+        else
+            w12_select<I + 1, N>(v, f);
+    }
+}
+
 // The main loop shared by both variants.  `fetch(j, ring[d], d)` loads wave
 // slice j (clamped to the wave's last slice, so it always issues the same
 // loads), `compute(ring[d], j, d)` consumes it, `xbuf` is the LDS chunk base.
@@ -651,8 +673,44 @@ __host__ __device__ constexpr int kc_of(bool mfma, int rows, int KW, int D) {
             }                                                                             \
         }                                                                                 \
         /* the last window refills only the groups that remain, so no load */            \
-        /* is left in flight after the loop; then the final partial window */            \
-        if (jb < (J)) {                                                                   \
+        /* is left in flight after the loop; then the final partial window. */           \
+        /* With D = 2 up to 32 rows each count of groups left (J - jb < 4) */           \
+        /* has a tail */                                                                  \
+        /* of its own in which every load is unconditional: with the loads */             \
+        /* predicated the compiler could not count them and waited for all of */          \
+        /* them -- the refill just issued included -- before each remaining */            \
+        /* group, a memory round trip at the end of every wave. */                        \
+        auto w12_tail = [&](auto rem_c) {                                                 \
+            constexpr int rem = decltype(rem_c)::value;                                   \
+            W12_CHUNK_STEP(CHUNKED, L, nchunks, xr, store_next)                           \
+            w12_static_for<0, (D)>([&](auto d_c) {                                        \
+                constexpr int d = decltype(d_c)::value;                                   \
+                if constexpr (d < rem) compute(ring[d], jb + d, d);                       \
+                if constexpr (d + (D) < rem) fetch(jb + d + (D), ring[d], d);             \
+                __builtin_amdgcn_sched_barrier(0);                                        \
+            });                                                                           \
+            if constexpr (rem > (D)) {                                                    \
+                jb += (D);                                                                \
+                W12_CHUNK_STEP(CHUNKED, L, nchunks, xr, store_next)                       \
+                w12_static_for<0, (D)>([&](auto d_c) {                                    \
+                    constexpr int d = decltype(d_c)::value;                               \
+                    if constexpr (d + (D) < rem) compute(ring[d], jb + d, d);             \
+                });                                                                       \
+            }                                                                             \
+            /* The tails end in different blocks, and where the sums are */              \
+            /* matrix-core results read right after the join the compiler did */           \
+            /* not always put the wait states such a read needs (measured: */              \
+            /* stale sums in the BF16 control at 16 rows, two K-waves, x direct). */       \
+            /* 24 wait states at the end of every tail cover any MFMA here. */            \
+            if constexpr (MFMA) {                                                         \
+                __builtin_amdgcn_sched_barrier(0);                                        \
+                asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");                              \
+                __builtin_amdgcn_sched_barrier(0);                                        \
+            }                                                                             \
+        };                                                                                \
+        if constexpr ((D) <= 2 && MR <= 32) {                                             \
+            w12_select<1, 2 * (D)>((J) - jb, w12_tail);                                   \
+        } else if (jb < (J)) {                                                            \
             W12_CHUNK_STEP(CHUNKED, L, nchunks, xr, store_next)                           \
             _Pragma("unroll") for (int d = 0; d < (D); ++d) {                             \
                 if (jb + d < (J)) compute(ring[d], jb + d, d);                            \
