@@ -454,3 +454,40 @@ def test_headline_configs_every_row(oracle, name, M):
     y_ref = oracle.gemm_w12_f64(x, p0, p1, p2, meta, P.N, nthreads=min(16, os.cpu_count() or 1))
     w_ref = oracle.unpack(p0, p1, p2, meta, P.N, P.K)
     assert_gemm_close(yh, y_ref, oracle.tolerance(x, w_ref), "%s M=%d every row" % (name, M))
+
+
+# Short rows (1-6 groups): every wave's groups fit the ring's last windows,
+# so each count of groups left takes its own tail of the main loop.
+SHORT_TILINGS = [(1, 1, 1, 2, 1), (1, 1, 2, 2, 1), (1, 1, 4, 2, 1), (1, 2, 2, 2, 1),
+                 (1, 1, 2, 2, 0), (1, 1, 4, 2, 0), (1, 1, 2, 2, 0, 1, 8), (1, 1, 4, 2, 0, 1, 16),
+                 (0, 1, 2, 4, 1), (0, 1, 4, 2, 1)]
+
+
+@pytest.mark.parametrize("tiling", SHORT_TILINGS, ids=lambda t: "x".join(map(str, t)))
+def test_short_rows_every_tail(oracle, tiling):
+    """K = 128 .. 768 (1 to 6 groups) with one, two and four K-waves: W12 and
+    BF16 bitwise equal and within the oracle tolerance.  (Regression: the
+    BF16 control with two K-waves and x read directly returned stale sums
+    when the wait states after its last MFMAs were missing.)"""
+    Ms = [1, 2, 4] if tiling[0] == 0 else [1, 2, 4, 16, 32]
+    for K in (128, 256, 384, 512, 768):
+        P = prepared((48, K))
+        rows = np.arange(P.N)
+        w_ref = P.ref_rows(oracle, rows)
+        for M in Ms:
+            what = "short rows %s K=%d M=%d" % (tiling, K, M)
+            print(what, flush=True)
+            if tiling[4] and not w12.x_direct_fits(M, tiling[1], tiling[3], tiling[0]):
+                continue
+            x = inputs.gaussian_bf16((M, K), 1.0, 7 * M + K)
+            xd = to_dev(x)
+            try:
+                y12 = w12.w12_gemm(xd, P.container("v1"), tiling=tiling)
+            except w12.W12Error as e:
+                assert e.status == -6, what
+                continue
+            y16 = w12.bf16_gemm(xd, P.w_tiled, tiling=tiling)
+            torch.cuda.synchronize()
+            y12h, y16h = y12.cpu().numpy(), y16.cpu().numpy()
+            assert np.array_equal(y12h.view(np.uint32), y16h.view(np.uint32)), what
+            assert_gemm_close(y12h, oracle.gemm_bf16_f64(x, w_ref), oracle.tolerance(x, w_ref), what)
