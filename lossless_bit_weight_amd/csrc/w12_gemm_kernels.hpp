@@ -321,11 +321,13 @@ __device__ __forceinline__ void exc_walk(int lane, int col, const uint8_t* area,
 // F::clamp_word(entry word 1) gives the BF16 clamp the planes hold for the
 // entry.  The entries walked are [beg, end) of the list (by default the
 // slice's blocks of `tile`).
+// With `first` the lane's entry of the first batch (entry beg + lane, when
+// it exists) is taken from that register pair instead of being loaded.
 template <class F, int XR, class Apply>
 __device__ __forceinline__ void exc_corrections(const GemmArgs& g, int64_t tile, int g0, int gn,
                                                 int lane, int col, uint8_t* area, int mb,
                                                 Apply apply, int64_t beg_in = -1,
-                                                int64_t end_in = -1) {
+                                                int64_t end_in = -1, const uint2* first = nullptr) {
     float* orig = reinterpret_cast<float*>(area + 256);
     float* clamp = reinterpret_cast<float*>(area + 512);
     uint16_t* xs = reinterpret_cast<uint16_t*>(area + 768);
@@ -345,8 +347,9 @@ __device__ __forceinline__ void exc_corrections(const GemmArgs& g, int64_t tile,
         float o = 0.f, cl = 0.f;
         int64_t k = 0;
         if (i < end) {
-            const uint32_t pos = g.exc_ent[2 * (int64_t)i];
-            const uint32_t val = g.exc_ent[2 * (int64_t)i + 1];
+            const bool pre = first != nullptr && base == beg;
+            const uint32_t pos = pre ? first->x : g.exc_ent[2 * (int64_t)i];
+            const uint32_t val = pre ? first->y : g.exc_ent[2 * (int64_t)i + 1];
             k = pos & 0xFFFFFFu;
             const int grp = (int)(k >> 7);
             if (grp >= g0 && grp < g0 + gn) {
@@ -822,22 +825,44 @@ __global__ __launch_bounds__(NW * 64 + (F::kExcWave && XD ? 64 : 0)) void gemm_k
 
     // Exception list walked after the main loop (no correction wave): the
     // entry range of each tile's blocks in this K slice is read here, before
-    // any other load, so the walk starts with the entries (one memory round
-    // trip fewer after the loop) and these loads are older than everything
-    // the ring's wait counts track.  Every wave loads (the address is
-    // uniform); without a list the loads read the first words of plane 0
-    // and the range stays empty.
+    // any other load, through the scalar cache (uniform addresses; these
+    // loads neither wait behind nor delay the vector loads), and once the
+    // ring is primed every wave loads the first 64 entries of each range,
+    // one per lane (exc_pre), so the walk after the loop starts with its
+    // entries in registers: one memory round trip fewer there, and the
+    // entry loads are older than every ring load the loop waits for.
+    // Without a list the offsets read the first words of plane 0 and the
+    // range stays empty.
     uint32_t exc_b[R], exc_e[R];
+    uint2 exc_pre[R];
     if constexpr (F::kHasExceptions && !(F::kExcWave && XD)) {
         const bool has = g.exc_off != nullptr;
-        const uint32_t* offp = has ? g.exc_off : reinterpret_cast<const uint32_t*>(g.p0);
+        const __attribute__((address_space(4))) uint32_t* off4 =
+            (const __attribute__((address_space(4))) uint32_t*)(has ? g.exc_off
+                                                                     : reinterpret_cast<const uint32_t*>(g.p0));
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const int64_t blk0 = has ? tload[r] * G + g0 : 0;
-            exc_b[r] = offp[blk0];
-            exc_e[r] = offp[has ? blk0 + gn : 0];
+            exc_b[r] = off4[blk0];
+            exc_e[r] = off4[has ? blk0 + gn : 0];
         }
     }
+    // The entry loads (after the ring is primed): a lane past the range
+    // reads its own tile's first plane-0 words instead (valid, and spread
+    // over the tiles rather than one hot word), so the load is issued
+    // unconditionally and the loop's wait counts stay exact.
+    auto exc_prefetch = [&]() {
+        if constexpr (F::kHasExceptions && !(F::kExcWave && XD)) {
+            const uint2* ent = reinterpret_cast<const uint2*>(g.exc_ent);
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const uint32_t i = exc_b[r] + (uint32_t)lane;
+                const uint2* p = i < exc_e[r] ? ent + i
+                                              : reinterpret_cast<const uint2*>(wbase[r].p0) + lane;
+                exc_pre[r] = *p;
+            }
+        }
+    };
 
     // The correction wave (exception list, x read directly): wave NW of the
     // workgroup walks the entries of every tile of the workgroup -- block
@@ -1106,11 +1131,13 @@ __global__ __launch_bounds__(NW * 64 + (F::kExcWave && XD ? 64 : 0)) void gemm_k
         xr.load(g, kbase + (int64_t)(nchunks > 1 ? 1 : 0) * KC);
 #pragma unroll
         for (int d = 0; d < D; ++d) fetch(d, ring[d], d);
+        exc_prefetch();
         x0.template store<FixedLayout<XLayout, KC / 8>>(lds);
     } else {
         if constexpr (!XD) xa.load(g, MR, kbase, units_per_row);
 #pragma unroll
         for (int d = 0; d < D; ++d) fetch(d, ring[d], d);
+        exc_prefetch();
         if constexpr (!XD) xa.template store<XLayout>(lds);
     }
     if constexpr (!XD) __syncthreads();
@@ -1182,7 +1209,7 @@ __global__ __launch_bounds__(NW * 64 + (F::kExcWave && XD ? 64 : 0)) void gemm_k
                                     const float xv = xs(16 * t + 4 * q + e);
                                     macc[r][mt][e] = fmaf(xv, orig, fmaf(-xv, clamp, macc[r][mt][e]));
                                 }
-                        }, exc_b[r], exc_e[r]);
+                        }, exc_b[r], exc_e[r], &exc_pre[r]);
                     }
                 }
             }
@@ -1305,7 +1332,7 @@ __global__ __launch_bounds__(NW * 64 + (F::kExcWave && XD ? 64 : 0)) void gemm_k
                             const float xv = xs(m);
                             gacc[r][m] = fmaf(xv, orig, fmaf(-xv, clamp, gacc[r][m]));
                         }
-                    }, exc_b[r], exc_e[r]);
+                    }, exc_b[r], exc_e[r], &exc_pre[r]);
                 }
             }
         }

@@ -248,3 +248,40 @@ def test_shared_workspace_mixed_containers(oracle):
         assert int(ws[:65536].count_nonzero()) == 0
         assert_gemm_close(y.cpu().numpy(), oracle.gemm_bf16_f64(x, ref_w),
                           oracle.tolerance(x, ref_w), "mixed %d %s" % (i, shape))
+
+
+# x staged in LDS (one to five chunks), every split mode: one slice, the
+# two-slice exchange, the counted finish of three or more
+STAGED_TILINGS = [(0, 1, 2, 2, 0), (0, 1, 4, 4, 0, 5), (1, 1, 1, 2, 0), (1, 1, 4, 2, 0, 2),
+                  (1, 1, 1, 2, 0, 1, 8), (1, 1, 4, 2, 0, 1, 8), (1, 1, 4, 2, 0, 2, 8),
+                  (1, 1, 2, 2, 0, 3, 8), (1, 1, 8, 2, 0, 1, 8)]
+
+
+@pytest.mark.parametrize("tiling", STAGED_TILINGS, ids=lambda t: str(t))
+def test_dense_lists_staged_x(oracle, tiling):
+    """Weights of unit scale (so that most groups are flagged and a tile's
+    slice holds hundreds of entries, past the 64 the correction wave loads
+    at once) and a sparse one, with x staged in LDS: the oracle's GEMM of
+    the raw weights within the tolerance, and the BF16 control on the same
+    weights with the same tiling within the same bound."""
+    for shape, sigma in (((96, 5120), 1.0), ((70, 2304), 0.02)):
+        N, K = shape
+        bits = _raw(shape, sigma, 5 * N + K)
+        wt, bad = _pack_exc(bits)
+        assert bad > 0
+        bt = w12.w12_bf16_tile(to_dev(bits))
+        for M in ([1, 3] if tiling[0] == 0 else [5, 16, 32]):
+            what = "dense exc gemm %s %s M=%d" % (shape, tiling, M)
+            print(what, flush=True)
+            x = inputs.gaussian_bf16((M, K), 1.0, 3 * M + K)
+            try:
+                y = _gemm(to_dev(x), wt, tiling)
+            except w12.W12Error as e:
+                assert e.status == -6, what
+                continue
+            yc = _control(to_dev(x), bt, tiling)
+            torch.cuda.synchronize()
+            ref = oracle.gemm_bf16_f64(x, bits)
+            tol = oracle.tolerance(x, bits)
+            assert_gemm_close(y.cpu().numpy(), ref, tol, what)
+            assert_gemm_close(yc.cpu().numpy(), ref, tol, what + " (control)")
