@@ -201,8 +201,11 @@ int w12_unpack(const void *p0, const void *p1, const void *p2,
  *   p0..meta: the container of an [N, K] weight as written by w12_pack.
  *   exc_offsets, exc_entries: its exception list (w12_exceptions) or both
  *            NULL; with a list the result is the GEMM of the original
- *            weights (within the fp32 tolerance; the corrections are added
- *            after the main loop).
+ *            weights (within the fp32 tolerance; each correction takes the
+ *            clamp back out and adds the original, so a one-hot x row
+ *            returns an original word exactly; applied by an extra wave
+ *            when x is read directly, inside the main loop when x is
+ *            staged in LDS, up to 32 rows, else after the main loop).
  *   y      : device output [M, N], row stride ldy elements (ldy >= N),
  *            BF16 bits (2-byte aligned) or fp32 (4-byte aligned) per y_type.
  * By default M = 1 runs a wavefront-reduction GEMV (v_dot2c_f32_bf16) and

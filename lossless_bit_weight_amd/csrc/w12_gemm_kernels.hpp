@@ -321,13 +321,14 @@ __device__ __forceinline__ void exc_walk(int lane, int col, const uint8_t* area,
 // F::clamp_word(entry word 1) gives the BF16 clamp the planes hold for the
 // entry.  The entries walked are [beg, end) of the list (by default the
 // slice's blocks of `tile`).
-// With `first` the lane's entry of the first batch (entry beg + lane, when
-// it exists) is taken from that register pair instead of being loaded.
+// With `use_first` the lane's entry of the first batch (entry beg + lane,
+// when it exists) is `first` instead of being loaded.
 template <class F, int XR, class Apply>
 __device__ __forceinline__ void exc_corrections(const GemmArgs& g, int64_t tile, int g0, int gn,
                                                 int lane, int col, uint8_t* area, int mb,
                                                 Apply apply, int64_t beg_in = -1,
-                                                int64_t end_in = -1, const uint2* first = nullptr) {
+                                                int64_t end_in = -1, bool use_first = false,
+                                                uint2 first = {0u, 0u}) {
     float* orig = reinterpret_cast<float*>(area + 256);
     float* clamp = reinterpret_cast<float*>(area + 512);
     uint16_t* xs = reinterpret_cast<uint16_t*>(area + 768);
@@ -347,9 +348,9 @@ __device__ __forceinline__ void exc_corrections(const GemmArgs& g, int64_t tile,
         float o = 0.f, cl = 0.f;
         int64_t k = 0;
         if (i < end) {
-            const bool pre = first != nullptr && base == beg;
-            const uint32_t pos = pre ? first->x : g.exc_ent[2 * (int64_t)i];
-            const uint32_t val = pre ? first->y : g.exc_ent[2 * (int64_t)i + 1];
+            const bool pre = use_first && base == beg;
+            const uint32_t pos = pre ? first.x : g.exc_ent[2 * (int64_t)i];
+            const uint32_t val = pre ? first.y : g.exc_ent[2 * (int64_t)i + 1];
             k = pos & 0xFFFFFFu;
             const int grp = (int)(k >> 7);
             if (grp >= g0 && grp < g0 + gn) {
@@ -643,7 +644,8 @@ __device__ __forceinline__ void w12_select(int v, F&& f) {
 
 // The main loop shared by both variants.  `fetch(j, ring[d], d)` loads wave
 // slice j (clamped to the wave's last slice, so it always issues the same
-// loads), `compute(ring[d], j, d)` consumes it, `xbuf` is the LDS chunk base.
+// loads), `compute(ring[d], j, d)` consumes it, `correct(j)` follows the
+// refill of its slot, `xbuf` is the LDS chunk base.
 // Ring slot d always holds slice jb + d, so the compiler sees straight-line
 // loads and waits exactly for the oldest slice.  The last window is peeled
 // off the loop and refills only the slices that remain: a load issued past
@@ -671,6 +673,7 @@ __device__ __forceinline__ void w12_select(int v, F&& f) {
             _Pragma("unroll") for (int d = 0; d < (D); ++d) {                             \
                 compute(ring[d], jb + d, d);                                              \
                 fetch(jb + d + (D), ring[d], d);                                          \
+                correct(jb + d);                                                          \
                 /* keep the next slot's arithmetic below this slot's loads */             \
                 __builtin_amdgcn_sched_barrier(0);                                        \
             }                                                                             \
@@ -690,6 +693,7 @@ __device__ __forceinline__ void w12_select(int v, F&& f) {
                 constexpr int d = decltype(d_c)::value;                                   \
                 if constexpr (d < rem) compute(ring[d], jb + d, d);                       \
                 if constexpr (d + (D) < rem) fetch(jb + d + (D), ring[d], d);             \
+                if constexpr (d < rem) correct(jb + d);                                   \
                 __builtin_amdgcn_sched_barrier(0);                                        \
             });                                                                           \
             if constexpr (rem > (D)) {                                                    \
@@ -697,7 +701,10 @@ __device__ __forceinline__ void w12_select(int v, F&& f) {
                 W12_CHUNK_STEP(CHUNKED, L, nchunks, xr, store_next)                       \
                 w12_static_for<0, (D)>([&](auto d_c) {                                    \
                     constexpr int d = decltype(d_c)::value;                               \
-                    if constexpr (d + (D) < rem) compute(ring[d], jb + d, d);             \
+                    if constexpr (d + (D) < rem) {                                        \
+                        compute(ring[d], jb + d, d);                                      \
+                        correct(jb + d);                                                  \
+                    }                                                                     \
                 });                                                                       \
             }                                                                             \
             /* The tails end in different blocks, and where the sums are */              \
@@ -718,12 +725,16 @@ __device__ __forceinline__ void w12_select(int v, F&& f) {
             _Pragma("unroll") for (int d = 0; d < (D); ++d) {                             \
                 if (jb + d < (J)) compute(ring[d], jb + d, d);                            \
                 if (jb + d + (D) < (J)) fetch(jb + d + (D), ring[d], d);                  \
+                if (jb + d < (J)) correct(jb + d);                                        \
                 __builtin_amdgcn_sched_barrier(0);                                        \
             }                                                                             \
             jb += (D);                                                                    \
             W12_CHUNK_STEP(CHUNKED, L, nchunks, xr, store_next)                           \
             _Pragma("unroll") for (int d = 0; d < (D); ++d) {                             \
-                if (jb + d < (J)) compute(ring[d], jb + d, d);                            \
+                if (jb + d < (J)) {                                                       \
+                    compute(ring[d], jb + d, d);                                          \
+                    correct(jb + d);                                                      \
+                }                                                                         \
             }                                                                             \
         }                                                                                 \
         /* Every thread stages its share of every x chunk, so a wave that ran */         \
@@ -851,6 +862,9 @@ __global__ __launch_bounds__(NW * 64 + (F::kExcWave && XD ? 64 : 0)) void gemm_k
     // reads its own tile's first plane-0 words instead (valid, and spread
     // over the tiles rather than one hot word), so the load is issued
     // unconditionally and the loop's wait counts stay exact.
+    // In-loop corrections: W12-v1 with a list (that fetch is only launched
+    // with one), MFMA, x staged in LDS, up to 32 x rows.
+    constexpr bool kInLoop = F::kExcWave && MFMA && !XD && MR <= 32;
     auto exc_prefetch = [&]() {
         if constexpr (F::kHasExceptions && !(F::kExcWave && XD)) {
             const uint2* ent = reinterpret_cast<const uint2*>(g.exc_ent);
@@ -860,6 +874,26 @@ __global__ __launch_bounds__(NW * 64 + (F::kExcWave && XD ? 64 : 0)) void gemm_k
                 const uint2* p = i < exc_e[r] ? ent + i
                                               : reinterpret_cast<const uint2*>(wbase[r].p0) + lane;
                 exc_pre[r] = *p;
+            }
+        }
+    };
+    // In-loop corrections (MFMA kernels with x staged in LDS and a list):
+    // the first 64 entries of each tile's slice (exc_pre, usually all of
+    // them) are applied inside the main loop, each by the lanes of its row
+    // right after the products of its group, with x read from the LDS copy;
+    // entries past the first 64 are walked after the loop.  exc_grp is each
+    // lane's entry's group (-1: none).  The entries are waited for once
+    // before the loop: a first use inside the loop made the compiler wait
+    // for them -- and for every load issued behind them -- on every pass.
+    int exc_grp[R];
+    auto exc_inloop_ready = [&]() {
+        if constexpr (kInLoop) {
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                uint32_t pos = exc_pre[r].x, val = exc_pre[r].y;
+                asm volatile("" : "+v"(pos), "+v"(val));
+                exc_pre[r] = make_uint2(pos, val);
+                exc_grp[r] = exc_b[r] + (uint32_t)lane < exc_e[r] ? (int)((pos & 0xFFFFFFu) >> 7) : -1;
             }
         }
     };
@@ -1116,6 +1150,46 @@ __global__ __launch_bounds__(NW * 64 + (F::kExcWave && XD ? 64 : 0)) void gemm_k
         }
     };
 
+    // Run after the refill of the group's ring slot has been issued (the
+    // corrections need neither the slot nor memory), so they do not delay it.
+    auto correct = [&](int j) {
+        // In-loop corrections of this group, in list order: for the lanes of
+        // the entry's row, acc = (acc - x * clamp) + x * original on the four
+        // rows of each 16-row tile they hold (a one-hot x row still returns
+        // the original word exactly).
+        if constexpr (kInLoop) {
+            {
+                const int grp = g0 + kw + j * KW;
+                const uint16_t* xb16 = reinterpret_cast<const uint16_t*>(lds + (CHUNKED ? (c & 1) * kBuf : 0));
+                const int64_t k0 = kbase + (CHUNKED ? (int64_t)c * KC : 0);
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    uint64_t mask = __ballot(exc_grp[r] == grp);
+                    while (mask != 0) {
+                        const int t = __ffsll((unsigned long long)mask) - 1;
+                        mask &= mask - 1;
+                        const uint32_t pos = (uint32_t)__builtin_amdgcn_readlane((int)exc_pre[r].x, t);
+                        const uint32_t val = (uint32_t)__builtin_amdgcn_readlane((int)exc_pre[r].y, t);
+                        if (col == (int)(pos >> 24)) {
+                            const int kr = (int)((int64_t)(pos & 0xFFFFFFu) - k0);
+                            const float o = bf16_to_f32(val & 0xFFFFu);
+                            const float cl = bf16_to_f32(F::clamp_word(val));
+#pragma unroll
+                            for (int mt = 0; mt < kMT; ++mt)
+#pragma unroll
+                                for (int e4 = 0; e4 < 4; ++e4) {
+                                    const int m = 16 * mt + 4 * q + e4;
+                                    const float xv = bf16_to_f32(
+                                        xb16[XLayout::phys(m, kr >> 3, units_per_row) * 8 + (kr & 7)]);
+                                    macc[r][mt][e4] = fmaf(xv, o, fmaf(-xv, cl, macc[r][mt][e4]));
+                                }
+                        }
+                    }
+                }
+            }
+        }
+    };
+
     // Prologue: x first, then the ring, so the barrier waits for x only.
     // Chunked: chunks 0 and 1 are both loaded before the ring is primed, so
     // that on entering the loop -- as after every chunk step -- the loads
@@ -1145,6 +1219,7 @@ __global__ __launch_bounds__(NW * 64 + (F::kExcWave && XD ? 64 : 0)) void gemm_k
     auto store_next = [&]() {
         xr.template store<FixedLayout<XLayout, KC / 8>>(lds + ((c + 1) & 1) * kBuf);
     };
+    exc_inloop_ready();
     W12_RING_LOOP(D, CHUNKED, J, L, nchunks, xr, store_next, fetch, compute)
 
     if constexpr (MFMA) {
@@ -1190,12 +1265,15 @@ __global__ __launch_bounds__(NW * 64 + (F::kExcWave && XD ? 64 : 0)) void gemm_k
             if (kw == 0 && g.exc_off != nullptr) {
                 // above 32 rows x is staged 16 rows at a time (the list is
                 // walked once per 16 rows): each output still takes its
-                // entries in list order
+                // entries in list order.  After in-loop corrections only the
+                // entries past each slice's first 64 are left.
                 constexpr int kXR = exc_rows(MFMA, MR);
                 uint8_t* area = reinterpret_cast<uint8_t*>(lds) + exc_base + nw * ExcStage<kXR>::kBytes;
 #pragma unroll
                 for (int r = 0; r < R; ++r) {
                     if (tile0 + r >= ntiles) continue;
+                    if (kInLoop && exc_e[r] - exc_b[r] <= 64u) continue;
+                    const bool rest = kInLoop;
 #pragma unroll
                     for (int mb = 0; mb < 16 * kMT; mb += kXR) {
                         if (mb >= g.M) break;
@@ -1209,7 +1287,7 @@ __global__ __launch_bounds__(NW * 64 + (F::kExcWave && XD ? 64 : 0)) void gemm_k
                                     const float xv = xs(16 * t + 4 * q + e);
                                     macc[r][mt][e] = fmaf(xv, orig, fmaf(-xv, clamp, macc[r][mt][e]));
                                 }
-                        }, exc_b[r], exc_e[r], &exc_pre[r]);
+                        }, rest ? exc_b[r] + 64 : exc_b[r], exc_e[r], !rest, exc_pre[r]);
                     }
                 }
             }
@@ -1332,7 +1410,7 @@ __global__ __launch_bounds__(NW * 64 + (F::kExcWave && XD ? 64 : 0)) void gemm_k
                             const float xv = xs(m);
                             gacc[r][m] = fmaf(xv, orig, fmaf(-xv, clamp, gacc[r][m]));
                         }
-                    }, exc_b[r], exc_e[r], &exc_pre[r]);
+                    }, exc_b[r], exc_e[r], true, exc_pre[r]);
                 }
             }
         }

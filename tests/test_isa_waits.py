@@ -7,8 +7,9 @@ Every kernel keeps D groups of weights in flight; the compiler's
 one memory round trip per window -- this happened to the BF16 control's
 LDS-staged kernels (the x chunk loaded after the ring was primed), which
 made the control slower than its W12 counterpart for a reason that has
-nothing to do with the weight format.  These tests pin exact waits for both
-fetches in the kernels the defaults use from M = 9 to 32."""
+nothing to do with the weight format.  These tests pin exact waits for the
+three fetches (W12, BF16, W12 with an exception list) in the kernels the
+defaults use from M = 9 to 32."""
 import os
 import re
 import shutil
@@ -32,7 +33,7 @@ def _asm(define: str, tmp_path) -> str:
 
 
 def _main_loop(asm: str, fetch: str, targs: str) -> list[str]:
-    """The loop with the most vector-memory loads in the kernel
+    """The loop with the most matrix-core instructions in the kernel
     gemm_kernel<fetch, targs...> (its main loop)."""
     name = "_ZN3w124kern11gemm_kernelINS0_%d%sE%sEEEvNS_8GemmArgsE" % (len(fetch), fetch, targs)
     i = asm.index(name + ":")
@@ -47,9 +48,9 @@ def _main_loop(asm: str, fetch: str, targs: str) -> list[str]:
         if head is None or head >= k:
             continue
         body = lines[head:k + 1]
-        loads = sum(1 for b in body if "global_load" in b)
-        if best is None or loads > best[0]:
-            best = (loads, body)
+        mfmas = sum(1 for b in body if "v_mfma" in b)
+        if best is None or mfmas > best[0]:
+            best = (mfmas, body)
     assert best is not None and best[0] > 0, name
     return best[1]
 
@@ -66,7 +67,7 @@ def mfma8_asm(tmp_path_factory):
     return _asm("W12_INST_MFMA8", tmp_path_factory.mktemp("isa"))
 
 
-@pytest.mark.parametrize("fetch", ["FetchW12", "FetchBF16"])
+@pytest.mark.parametrize("fetch", ["FetchW12", "FetchBF16", "FetchW12X"])
 @pytest.mark.parametrize("targs", MFMA8_CHUNKED)
 def test_chunked_loop_waits_exactly(mfma8_asm, fetch, targs):
     body = _main_loop(mfma8_asm, fetch, targs)
@@ -91,3 +92,19 @@ def test_chunked_loop_waits_exactly_16_waves(mfma16_asm, fetch, targs):
     waits = [l for l in body if "s_waitcnt" in l and "vmcnt" in l]
     assert waits, "no weight waits in the loop at all"
     assert not any(re.search(r"vmcnt\(0\)", w) for w in waits), (fetch, targs, waits)
+
+
+@pytest.mark.parametrize("targs", MFMA8_CHUNKED)
+def test_in_loop_corrections_wait_for_nothing(mfma8_asm, targs):
+    """With an exception list the LDS-staged kernels apply each group's
+    entries inside the main loop, reading them with v_readlane from
+    registers loaded in the prologue (the kernel's only lane reads).  They
+    are waited for once, before the loop; a wait on memory in front of
+    those reads would stall every pass."""
+    name = "_ZN3w124kern11gemm_kernelINS0_9FetchW12XE%sEEEvNS_8GemmArgsE" % targs
+    i = mfma8_asm.index(name + ":")
+    body = mfma8_asm[i:mfma8_asm.index(".Lfunc_end", i)].splitlines()
+    reads = [k for k, l in enumerate(body) if "v_readlane" in l]
+    assert reads, "no in-loop corrections found"
+    for k in reads:
+        assert not any("vmcnt" in l for l in body[max(0, k - 4):k]), (targs, body[max(0, k - 4):k + 1])
