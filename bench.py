@@ -86,7 +86,7 @@ def parse():
                          "share under 8-way tensor parallelism)")
     ap.add_argument("--exceptions-ms", type=str, default=None,
                     help="x rows for the raw (unprojected) weight with its exception list "
-                         "(default: 1,16 with the sweep, none with --no-sweep)")
+                         "(default: 1,4,8,16,32 with the sweep, none with --no-sweep)")
     ap.add_argument("--m", type=int, default=1, help="headline x rows (default 1)")
     ap.add_argument("--summarize-trace", nargs=2, metavar=("KERNEL_STATS_CSV", "VARIANT"),
                     help="print a markdown summary of a rocprofv3 --stats kernel table")
@@ -814,7 +814,7 @@ def main():
 
     exc = None
     exc_ms = args.exceptions_ms if args.exceptions_ms is not None else (
-        "" if args.no_sweep else "1,16")
+        "" if args.no_sweep else "1,4,8,16,32")
     exc_ms = [int(m) for m in exc_ms.split(",") if m]
     if exc_ms:
         exc = measure_exceptions(torch, w12, head_case, exc_ms, args.steps, args.warmup)

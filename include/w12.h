@@ -357,8 +357,9 @@ int bf16_gemm_ex(const uint16_t *x, int64_t M, int64_t ldx,
 /*
  * Name of the kernel variant the GEMMs launch for this shape (static string,
  * for reports and profiles), or NULL if the shape is rejected.  `is_w12`
- * selects the weight fetch (0 = BF16 control, 1 = W12-v1, 2 = W12-b),
- * `allow_splitk` the w12_gemm_ws default.
+ * selects the weight fetch (0 = BF16 control, 1 = W12-v1, 2 = W12-b, 3 =
+ * W12-v1 with an exception list, whose default can differ), `allow_splitk`
+ * the w12_gemm_ws default.
  */
 const char *w12_gemm_variant(int64_t M, int64_t N, int64_t K, int is_w12,
                              int allow_splitk);

@@ -238,6 +238,36 @@ static int check_workspace(const w12::Tiling& t, int64_t M, int64_t N, void* ws,
     return W12_OK;
 }
 
+// The default tiling of a W12-v1 GEMM whose container carries an exception
+// list.  The x-direct MFMA tilings run one tile per wave: their workgroup's
+// correction wave then has one tile's entries to prepare instead of two, and
+// finishes within the main loop (the summation order of every output is
+// unchanged).  From 6 rows the LDS-staged kernel, which applies the
+// corrections inside its main loop, is faster than the x-direct one with its
+// correction wave (raw QKV M = 8 13.1 against 14.2 us, gate+up M = 6 47.9
+// against 49.1), and so it is at any row count when K is split three ways or
+// more, with two K-waves (raw down M = 2, three slices: 26.0 against 31.4);
+// it is taken with the same split when it needs no more workspace, so a
+// workspace sized by w12_gemm_workspace_bytes still fits.
+static void list_tiling(w12::Tiling& t, int64_t M, int64_t N, int64_t K) {
+    if (!t.mfma || !t.xdirect) return;
+    w12::Tiling t2{};
+    t2.mfma = 1;
+    t2.r = 1;
+    t2.kw = t.splitk >= 3 ? 2 : 4;
+    t2.depth = 2;
+    t2.xdirect = 0;
+    t2.splitk = t.splitk;
+    t2.nw = 8;
+    w12::Tiling t1 = t;
+    t1.r = 1;
+    if ((M >= 6 || t.splitk >= 3) && w12::complete_tiling(t2, (int)M, N, K) &&
+        w12::workspace_bytes(t2, (int)M, N) <= w12::workspace_bytes(t, (int)M, N))
+        t = t2;
+    else if (t.r == 2 && w12::complete_tiling(t1, (int)M, N, K))
+        t = t1;
+}
+
 static int gemm_w12(int fetch, const uint16_t* x, int64_t M, int64_t ldx, const void* p0, const void* p1,
                     const void* p2, const uint8_t* meta, const uint32_t* exc_off,
                     const uint32_t* exc_ent, int64_t N, int64_t K, void* y,
@@ -249,16 +279,7 @@ static int gemm_w12(int fetch, const uint16_t* x, int64_t M, int64_t ldx, const 
     if (int rc = check_exceptions(exc_off, exc_ent, N, K)) return rc;
     w12::Tiling t;
     if (int rc = resolve_tiling(tiling, allow_splitk, M, N, K, &t)) return rc;
-    // With an exception list, the default x-direct MFMA tilings run one tile
-    // per wave: their workgroup's correction wave then has one tile's entries
-    // to prepare instead of two, and finishes within the main loop (the
-    // summation order of every output is unchanged).
-    if (tiling == nullptr && exc_off != nullptr && fetch == w12::kFetchW12 && t.mfma && t.xdirect &&
-        t.r == 2) {
-        w12::Tiling t1 = t;
-        t1.r = 1;
-        if (w12::complete_tiling(t1, (int)M, N, K)) t = t1;
-    }
+    if (tiling == nullptr && exc_off != nullptr && fetch == w12::kFetchW12) list_tiling(t, M, N, K);
     if (int rc = check_workspace(t, M, N, ws, ws_bytes)) return rc;
     w12::GemmArgs a = make_args(x, M, ldx, N, K, y, ldy, y_type);
     a.p0 = static_cast<const uint8_t*>(p0);
@@ -386,8 +407,11 @@ int w12_default_tiling(int64_t M, int64_t N, int64_t K, int allow_splitk, w12_ti
 
 const char* w12_gemm_variant(int64_t M, int64_t N, int64_t K, int is_w12, int allow_splitk) {
     if (check_weight_shape(N, K) != W12_OK || M < 1 || M > W12_MAX_M) return nullptr;
+    if (is_w12 < 0 || is_w12 > 3) return nullptr;
     const int fetch = is_w12 == 2 ? w12::kFetchW12B : is_w12 != 0 ? w12::kFetchW12 : w12::kFetchBF16;
-    return w12::tiling_name(w12::choose_tiling((int)M, N, K, allow_splitk != 0), fetch);
+    w12::Tiling t = w12::choose_tiling((int)M, N, K, allow_splitk != 0);
+    if (is_w12 == 3) list_tiling(t, M, N, K);
+    return w12::tiling_name(t, fetch);
 }
 
 }  // extern "C"

@@ -239,8 +239,9 @@ def w12_default_tiling(M: int, N: int, K: int, allow_splitk: bool = True) -> Til
 
 def w12_gemm_variant(M: int, N: int, K: int, is_w12: bool | int = True,
                      allow_splitk: bool = True) -> str | None:
-    """Variant name; is_w12: False/0 = BF16 control, True/1 = W12-v1, 2 = W12-b."""
-    fetch = 2 if (not isinstance(is_w12, bool) and int(is_w12) == 2) else int(bool(is_w12))
+    """Variant name; is_w12: False/0 = BF16 control, True/1 = W12-v1, 2 = W12-b,
+    3 = W12-v1 with an exception list."""
+    fetch = int(is_w12) if (not isinstance(is_w12, bool) and int(is_w12) in (2, 3)) else int(bool(is_w12))
     r = lib().w12_gemm_variant(int(M), int(N), int(K), fetch, int(bool(allow_splitk)))
     return None if r is None else r.decode()
 

@@ -1,6 +1,7 @@
 """The C-ABI library without a GPU: it loads, exports every function the
 header declares, and rejects bad arguments on the host before any launch."""
 import ctypes
+import re
 
 import pytest
 
@@ -127,6 +128,31 @@ def test_variant_selection():
     assert w12.w12_gemm_variant(65, 7168, 5120).startswith("w12_mfma_mt128_r1_kw1_d2_chunked_w8")
     assert w12.w12_gemm_variant(128, 896, 5120).startswith("w12_mfma_mt128_")
     assert w12.w12_gemm_variant(129, 5120, 17408) is None
+
+
+def test_variant_with_exception_list():
+    """With an exception list the x-direct MFMA defaults run one tile per
+    wave below 6 rows and give way to the LDS-staged kernel (corrections in
+    its main loop) from 6 rows, or with K split three ways or more, with the
+    same split; the GEMV at M = 1 and the LDS-staged defaults are
+    unchanged."""
+    V = w12.w12_gemm_variant
+    assert V(1, 7168, 5120, 3) == V(1, 7168, 5120)
+    assert V(2, 7168, 5120, 3) == "w12_mfma_mt16_r1_kw4_d2_xdirect"
+    assert V(4, 7168, 5120, 3) == "w12_mfma_mt16_r1_kw4_d2_xdirect"
+    assert V(6, 7168, 5120, 3) == "w12_mfma_mt16_r1_kw4_d2_chunked_w8"
+    assert V(8, 7168, 5120, 3) == "w12_mfma_mt16_r1_kw4_d2_chunked_w8"
+    assert V(6, 34816, 5120, 3) == "w12_mfma_mt16_r1_kw4_d2_chunked_w8"
+    assert V(2, 5120, 17408) == "w12_mfma_mt16_r2_kw4_d2_xdirect_s3"
+    assert V(2, 5120, 17408, 3) == "w12_mfma_mt16_r1_kw2_d2_chunked_w8_s3"
+    for M in (16, 32, 64):
+        assert V(M, 7168, 5120, 3) == V(M, 7168, 5120)
+    # the split (and so the workspace a default call needs) never changes
+    split = lambda name: re.search(r"_s(\d+)$", name).group(1) if re.search(r"_s(\d+)$", name) else "1"
+    for M in range(1, 33):
+        for N, K in ((7168, 5120), (896, 5120), (5120, 2176), (5120, 17408), (5120, 640)):
+            a, b = V(M, N, K), V(M, N, K, 3)
+            assert split(a) == split(b), (M, N, K, a, b)
     assert w12.w12_gemm_variant(1, 5120, 100) is None
 
 
