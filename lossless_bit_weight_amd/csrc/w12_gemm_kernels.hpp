@@ -48,6 +48,11 @@
 // permutation, so the four MFMAs of a group cover its 128 K exactly once.
 // The W12 and BF16 fetches feed identical operands in identical order, so
 // for W = unpack(pack(W)) both return bitwise equal y.
+// An exception list (the escape path that keeps every group lossless) adds,
+// for each listed weight, x * (original - clamp) as (acc - x * clamp) +
+// x * original, in list order: prepared by an extra wave in the x-direct
+// kernels, applied group by group inside the main loop in the LDS-staged
+// MFMA kernels up to 32 rows, walked after the loop elsewhere.
 #pragma once
 
 #include <type_traits>
@@ -404,9 +409,11 @@ __device__ __forceinline__ uint4 load_stream(const uint8_t* p) {
 
 struct FetchW12 {
     // kHasExceptions: the container may carry an exception list, whose
-    // corrections are added to the sums after the main loop.  kExcWave: in
-    // the kernels that read x directly, an extra wave of the workgroup
-    // prepares those corrections while the others stream the weights.
+    // corrections are added to the sums.  kExcWave (W12-v1 with a list): in
+    // the kernels that read x directly an extra wave of the workgroup
+    // prepares those corrections while the others stream the weights; the
+    // LDS-staged MFMA kernels up to 32 rows apply them inside the main loop;
+    // every other kernel walks the list after the main loop.
     static constexpr bool kHasExceptions = false;
     static constexpr bool kExcWave = false;
     static constexpr bool kHasMeta = true;
@@ -834,14 +841,16 @@ __global__ __launch_bounds__(NW * 64 + (F::kExcWave && XD ? 64 : 0)) void gemm_k
     for (int r = 0; r < R; ++r) wbase[r] = F::base(g, tload[r]);
     const int glast = g0 + gn - 1;
 
-    // Exception list walked after the main loop (no correction wave): the
-    // entry range of each tile's blocks in this K slice is read here, before
+    // Exception list applied in or after the main loop (no correction
+    // wave): the entry range of each tile's blocks in this K slice is read
+    // here, before
     // any other load, through the scalar cache (uniform addresses; these
     // loads neither wait behind nor delay the vector loads), and once the
     // ring is primed every wave loads the first 64 entries of each range,
-    // one per lane (exc_pre), so the walk after the loop starts with its
-    // entries in registers: one memory round trip fewer there, and the
-    // entry loads are older than every ring load the loop waits for.
+    // one per lane (exc_pre): the in-loop corrections take them from there,
+    // and the walk after the loop starts with its entries in registers (one
+    // memory round trip fewer); the entry loads are older than every ring
+    // load the loop waits for.
     // Without a list the offsets read the first words of plane 0 and the
     // range stays empty.
     uint32_t exc_b[R], exc_e[R];
