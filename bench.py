@@ -88,6 +88,9 @@ def parse():
                     help="x rows for the raw (unprojected) weight with its exception list "
                          "(default: 1,4,8,16,32 with the sweep, none with --no-sweep)")
     ap.add_argument("--m", type=int, default=1, help="headline x rows (default 1)")
+    ap.add_argument("--tiling", type=str, default="",
+                    help="headline tiling instead of the default: kind,r,kw,depth,x_direct"
+                         "[,splitk[,waves]] (kind 0 = GEMV, 1 = MFMA), for profiles of one variant")
     ap.add_argument("--summarize-trace", nargs=2, metavar=("KERNEL_STATS_CSV", "VARIANT"),
                     help="print a markdown summary of a rocprofv3 --stats kernel table")
     ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "VARIANT"),
@@ -191,24 +194,27 @@ def gemm_bytes(N, K, M, out_bytes, w_bytes):
     return w_bytes + 2 * M * K + out_bytes * M * N
 
 
-def measure(torch, w12, wl: Workload, M, steps, warmup, out_dtype, settle_s=0.05):
+def measure(torch, w12, wl: Workload, M, steps, warmup, out_dtype, settle_s=0.05, tiling=None):
+    """W12 and the BF16 control on the same tiling (the default, or `tiling`)."""
     x = torch.from_numpy(wl.case.activations(M).view(np.int16)).cuda()
     y = torch.empty((M, wl.N), dtype=out_dtype, device="cuda")
     out_b = 4 if out_dtype == torch.float32 else 2
     # one zero-filled split-K workspace for every launch (allocated outside
     # the graph; each launch leaves its counters at zero)
-    ws = torch.zeros(max(256, w12.w12_gemm_workspace_bytes(M, wl.N, wl.K)), dtype=torch.uint8,
+    ws = torch.zeros(max(256, w12.w12_gemm_workspace_bytes(M, wl.N, wl.K, tiling)), dtype=torch.uint8,
                      device="cuda")
-    l12 = [(lambda c=c: w12.w12_gemm(x, c, y=y, workspace=ws)) for c in wl.w12_copies]
-    l16 = [(lambda c=c: w12.bf16_gemm(x, c, y=y, workspace=ws)) for c in wl.bf16_copies]
+    l12 = [(lambda c=c: w12.w12_gemm(x, c, y=y, tiling=tiling, workspace=ws)) for c in wl.w12_copies]
+    l16 = [(lambda c=c: w12.bf16_gemm(x, c, y=y, tiling=tiling, workspace=ws)) for c in wl.bf16_copies]
     ms12, n12 = time_graph(torch, l12, steps, warmup, settle_s)
     ms16, n16 = time_graph(torch, l16, steps, warmup, settle_s)
     b12 = gemm_bytes(wl.N, wl.K, M, out_b, wl.w12_bytes)
     b16 = gemm_bytes(wl.N, wl.K, M, out_b, wl.bf16_bytes)
     return {
         "workload": wl.case.name, "M": M,
-        "w12_kernel": w12.w12_gemm_variant(M, wl.N, wl.K, 2 if wl.fmt == "b" else 1),
-        "bf16_kernel": w12.w12_gemm_variant(M, wl.N, wl.K, False),
+        "w12_kernel": (w12.w12_gemm_variant(M, wl.N, wl.K, 2 if wl.fmt == "b" else 1) if tiling is None
+                       else w12.w12_tiling_variant(M, wl.N, wl.K, tiling, 2 if wl.fmt == "b" else 1)),
+        "bf16_kernel": (w12.w12_gemm_variant(M, wl.N, wl.K, False) if tiling is None
+                        else w12.w12_tiling_variant(M, wl.N, wl.K, tiling, False)),
         "w12_us": ms12 * 1e3, "bf16_us": ms16 * 1e3,
         "w12_weight_gbps": wl.w12_bytes / (ms12 * 1e-3) / 1e9,
         "w12_bf16_equiv_gbps": wl.bf16_bytes / (ms12 * 1e-3) / 1e9,
@@ -715,7 +721,9 @@ def main():
     wl = Workload(head_case, torch, w12)
     print("headline workload ready (%s, raw unencodable groups %d)" % (head_case.name, wl.raw_bad),
           file=sys.stderr, flush=True)
-    head = measure(torch, w12, wl, head_m, args.steps, args.warmup, torch.float32, settle_s=0.5)
+    head_tiling = tuple(int(v) for v in args.tiling.split(",")) if args.tiling else None
+    head = measure(torch, w12, wl, head_m, args.steps, args.warmup, torch.float32, settle_s=0.5,
+                   tiling=head_tiling)
     rotation = len(wl.w12_copies)
     ceilings = {}
     ceilings[args.workload] = (read_ceiling(torch, w12, wl.w12_bytes, args.steps, args.warmup),

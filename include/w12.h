@@ -365,6 +365,15 @@ const char *w12_gemm_variant(int64_t M, int64_t N, int64_t K, int is_w12,
                              int allow_splitk);
 
 /*
+ * Name of the kernel variant an explicit tiling launches for this shape
+ * (the same names as w12_gemm_variant; static string), or NULL if the
+ * tiling or shape is rejected.  `is_w12` as above (0, 1 or 2).  For reports
+ * and profiles of a chosen tiling.
+ */
+const char *w12_tiling_variant(int64_t M, int64_t N, int64_t K,
+                               const w12_tiling_t *tiling, int is_w12);
+
+/*
  * w12_gemm_noalloc -- w12_gemm_ws for callers that cannot allocate device
  * memory (code under HIP graph capture, tight serving loops, harnesses that
  * forbid hipMalloc): the same operation, default tiling (K split over

@@ -405,6 +405,16 @@ int w12_default_tiling(int64_t M, int64_t N, int64_t K, int allow_splitk, w12_ti
     return W12_OK;
 }
 
+const char* w12_tiling_variant(int64_t M, int64_t N, int64_t K, const w12_tiling_t* tiling,
+                               int is_w12) {
+    if (tiling == nullptr || is_w12 < 0 || is_w12 > 2) return nullptr;
+    if (check_weight_shape(N, K) != W12_OK || M < 1 || M > W12_MAX_M) return nullptr;
+    w12::Tiling t;
+    if (resolve_tiling(tiling, true, M, N, K, &t) != W12_OK) return nullptr;
+    const int fetch = is_w12 == 2 ? w12::kFetchW12B : is_w12 != 0 ? w12::kFetchW12 : w12::kFetchBF16;
+    return w12::tiling_name(t, fetch);
+}
+
 const char* w12_gemm_variant(int64_t M, int64_t N, int64_t K, int is_w12, int allow_splitk) {
     if (check_weight_shape(N, K) != W12_OK || M < 1 || M > W12_MAX_M) return nullptr;
     if (is_w12 < 0 || is_w12 > 3) return nullptr;

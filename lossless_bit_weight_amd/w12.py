@@ -146,6 +146,8 @@ def lib() -> ctypes.CDLL:
     L.w12_read_probe.restype = i32
     L.w12_gemm_variant.argtypes = [i64, i64, i64, i32, i32]
     L.w12_gemm_variant.restype = ctypes.c_char_p
+    L.w12_tiling_variant.argtypes = [i64, i64, i64, ctypes.POINTER(Tiling), i32]
+    L.w12_tiling_variant.restype = ctypes.c_char_p
     # W12-b entry points: the W12-v1 signatures
     for name in ("pack", "unpack", "exceptions", "gemm", "gemm_ws", "gemm_ex"):
         fb, fv = getattr(L, "w12b_" + name), getattr(L, "w12_" + name)
@@ -243,6 +245,13 @@ def w12_gemm_variant(M: int, N: int, K: int, is_w12: bool | int = True,
     3 = W12-v1 with an exception list."""
     fetch = int(is_w12) if (not isinstance(is_w12, bool) and int(is_w12) in (2, 3)) else int(bool(is_w12))
     r = lib().w12_gemm_variant(int(M), int(N), int(K), fetch, int(bool(allow_splitk)))
+    return None if r is None else r.decode()
+
+
+def w12_tiling_variant(M: int, N: int, K: int, tiling, is_w12: bool | int = True) -> str | None:
+    """Variant name an explicit tiling launches (None if rejected)."""
+    fetch = 2 if (not isinstance(is_w12, bool) and int(is_w12) == 2) else int(bool(is_w12))
+    r = lib().w12_tiling_variant(int(M), int(N), int(K), _tiling_arg(tiling), fetch)
     return None if r is None else r.decode()
 
 

@@ -458,3 +458,17 @@ def test_noalloc_scratch_covers_the_workloads():
             assert need == 0 or need - 65536 <= 16 << 20, (N, K, M, need)
     assert w12.w12_gemm_workspace_bytes(128, 16384, 5120) - 65536 == 16 << 20   # fits exactly
     assert w12.w12_gemm_workspace_bytes(32, 64000, 15360) - 65536 > 16 << 20
+
+
+def test_tiling_variant_names():
+    """An explicit tiling's kernel name (for profiles of one variant): the
+    same scheme as the defaults, None for a tiling the library rejects."""
+    T = w12.w12_tiling_variant
+    assert T(4, 7168, 5120, (0, 1, 2, 4, 1)) == "w12_gemv_m4_r1_kw2_d4_xdirect"
+    assert T(4, 7168, 5120, (0, 1, 2, 4, 1), False) == "bf16_gemv_m4_r1_kw2_d4_xdirect"
+    assert T(4, 7168, 5120, (0, 1, 2, 4, 1), 2) == "w12b_gemv_m4_r1_kw2_d4_xdirect"
+    assert T(2, 7168, 5120, (1, 2, 4, 2, 1)) == w12.w12_gemm_variant(2, 7168, 5120)
+    assert T(16, 7168, 5120, (1, 1, 4, 2, 0, 1, 8)) == w12.w12_gemm_variant(16, 7168, 5120)
+    assert T(4, 7168, 5120, (0, 1, 2, 4, 1, 1, 8)) is None        # eight waves: MFMA only
+    assert T(9, 7168, 5120, (0, 1, 2, 4, 1)) is None              # GEMV up to 8 rows
+    assert T(4, 7168, 5000, (0, 1, 2, 4, 1)) is None              # K not a multiple of 128
