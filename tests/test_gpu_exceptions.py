@@ -285,3 +285,32 @@ def test_dense_lists_staged_x(oracle, tiling):
             tol = oracle.tolerance(x, bits)
             assert_gemm_close(y.cpu().numpy(), ref, tol, what)
             assert_gemm_close(yc.cpu().numpy(), ref, tol, what + " (control)")
+
+
+@pytest.mark.parametrize("M", [1, 4, 6, 8, 16, 32, 64])
+def test_raw_qkv_default_with_list(oracle, M):
+    """The full-size raw QKV weight (7168x5120, 11 174 listed weights) with
+    its exception list through the default tiling the benchmark times at each
+    row count -- the correction wave at M = 1-4, in-loop corrections from 6
+    rows (chosen because a list is present), the post-loop walk at 64 --
+    against the oracle's GEMM of the raw weights on sampled rows (the first
+    and last 64 and 384 more), and the BF16 control on the raw weights with
+    the same tiling within the same bound."""
+    bits = inputs.QKV.weights_raw()
+    wt, bad = _pack_exc(bits)
+    assert bad > 0
+    bt = w12.w12_bf16_tile(to_dev(bits))
+    rng = np.random.default_rng(M)
+    N, K = bits.shape
+    rows = np.array(sorted(set(range(64)) | set(range(N - 64, N)) |
+                           set(rng.choice(N, size=384, replace=False).tolist())))
+    x = inputs.QKV.activations(M)
+    what = "raw qkv default M=%d (%s)" % (M, w12.w12_gemm_variant(M, N, K, 3))
+    print(what, flush=True)
+    y = w12.w12_gemm(to_dev(x), wt)
+    yc = w12.bf16_gemm(to_dev(x), bt)
+    torch.cuda.synchronize()
+    ref = oracle.gemm_bf16_f64(x, bits[rows])
+    tol = oracle.tolerance(x, bits[rows])
+    assert_gemm_close(y.cpu().numpy()[:, rows], ref, tol, what)
+    assert_gemm_close(yc.cpu().numpy()[:, rows], ref, tol, what + " (control)")
