@@ -253,8 +253,10 @@ def test_shared_workspace_mixed_containers(oracle):
 # x staged in LDS (one to five chunks), every split mode: one slice, the
 # two-slice exchange, the counted finish of three or more
 STAGED_TILINGS = [(0, 1, 2, 2, 0), (0, 1, 4, 4, 0, 5), (1, 1, 1, 2, 0), (1, 1, 4, 2, 0, 2),
+                  (1, 2, 2, 2, 0), (1, 2, 4, 2, 0, 3), (1, 1, 2, 4, 0),
                   (1, 1, 1, 2, 0, 1, 8), (1, 1, 4, 2, 0, 1, 8), (1, 1, 4, 2, 0, 2, 8),
-                  (1, 1, 2, 2, 0, 3, 8), (1, 1, 8, 2, 0, 1, 8)]
+                  (1, 1, 2, 2, 0, 3, 8), (1, 1, 8, 2, 0, 1, 8), (1, 1, 4, 2, 0, 1, 16),
+                  (1, 1, 2, 2, 0, 3, 16)]
 
 
 @pytest.mark.parametrize("tiling", STAGED_TILINGS, ids=lambda t: str(t))
