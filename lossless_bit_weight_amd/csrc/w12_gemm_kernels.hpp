@@ -769,11 +769,34 @@ __host__ __device__ size_t lds_bytes(int gs) {
     const size_t m = x > red ? x : red;
     return (m + 15) / 16 * 16;
 }
-// With an exception list the owner waves also stage correction batches, in
-// an area after everything else (so it never meets x or the reductions).
+// With an exception list the owner waves also stage correction batches
+// after the main loop.
 template <bool MFMA, int MR, int KW, int NW>
 __host__ __device__ constexpr size_t exc_lds_bytes() {
     return (size_t)(NW / KW) * ExcStage<exc_rows(MFMA, MR)>::kBytes;
+}
+// Where those batches go: with x staged in LDS and several K-waves the walk
+// runs after the barrier that ends every read of x, so they reuse the x
+// buffers after the reduction partials when they fit there (a separate area
+// took the 32-row two-K-wave kernel past half the LDS, one workgroup per CU
+// instead of two); otherwise they go after everything else.  `extra` = the
+// LDS the launch must add for them.
+template <bool MFMA, int MR, int R, int KW, int D, bool CHUNKED, bool XD, int NW>
+__host__ __device__ size_t walk_base(int gs, size_t* extra) {
+    const size_t x = XD ? 0
+                     : CHUNKED ? 2 * (size_t)MR * kc_of(MFMA, MR, KW, D) * 2
+                               : (size_t)MR * gs * 128 * 2;
+    const size_t red = KW == 1 ? 0
+                       : MFMA ? (size_t)(KW - 1) * (NW / KW) * 64 * R * (MR / 16) * 16
+                              : (size_t)(KW - 1) * (NW / KW) * 16 * R * MR * 4;
+    const size_t redr = (red + 15) / 16 * 16;
+    const size_t need = exc_lds_bytes<MFMA, MR, KW, NW>();
+    if (!XD && KW > 1 && redr + need <= x) {
+        *extra = 0;
+        return redr;
+    }
+    *extra = need;
+    return lds_bytes<MFMA, MR, R, KW, D, CHUNKED, XD, NW>(gs);
 }
 // With a correction wave (F::kExcWave, x read directly): its one staging
 // area, then the two correction sums of every output of the workgroup's
@@ -817,8 +840,12 @@ __global__ __launch_bounds__(NW * 64 + (F::kExcWave && XD ? 64 : 0)) void gemm_k
     const int nw = wave / KW;
     const int64_t G = g.K / 128;
     const int64_t ntiles = (g.N + 15) / 16;
-    // start of the exception staging area (after the x buffers / reductions)
+    // the correction wave's area (after the x buffers / reductions) and the
+    // post-loop walk's (see walk_base)
     const size_t exc_base = lds_bytes<MFMA, MR, R, KW, D, CHUNKED, XD, NW>(g.gs);
+    size_t walk_extra;
+    const size_t walk_b = walk_base<MFMA, MR, R, KW, D, CHUNKED, XD, NW>(g.gs, &walk_extra);
+    (void)walk_extra;
     const int64_t tile0 = ((int64_t)blockIdx.x * kRowWaves + nw) * R;  // tile r: tile0 + r
 
     int64_t tload[R];  // tiles past the end are clamped for loading
@@ -1277,7 +1304,7 @@ __global__ __launch_bounds__(NW * 64 + (F::kExcWave && XD ? 64 : 0)) void gemm_k
                 // entries in list order.  After in-loop corrections only the
                 // entries past each slice's first 64 are left.
                 constexpr int kXR = exc_rows(MFMA, MR);
-                uint8_t* area = reinterpret_cast<uint8_t*>(lds) + exc_base + nw * ExcStage<kXR>::kBytes;
+                uint8_t* area = reinterpret_cast<uint8_t*>(lds) + walk_b + nw * ExcStage<kXR>::kBytes;
 #pragma unroll
                 for (int r = 0; r < R; ++r) {
                     if (tile0 + r >= ntiles) continue;
@@ -1408,7 +1435,7 @@ __global__ __launch_bounds__(NW * 64 + (F::kExcWave && XD ? 64 : 0)) void gemm_k
             }
         } else if constexpr (F::kHasExceptions) {
             if (kw == 0 && g.exc_off != nullptr) {
-                uint8_t* area = reinterpret_cast<uint8_t*>(lds) + exc_base + nw * ExcStage<MR>::kBytes;
+                uint8_t* area = reinterpret_cast<uint8_t*>(lds) + walk_b + nw * ExcStage<MR>::kBytes;
 #pragma unroll
                 for (int r = 0; r < R; ++r) {
                     if (tile0 + r >= ntiles) continue;
@@ -1467,8 +1494,11 @@ hipError_t launch_one(const GemmArgs& a, hipStream_t s) {
     constexpr bool kExcWave = F::kExcWave && XD;
     if (kExcWave)
         lds += excwave_lds_bytes<MR, R, KW, NW>();
-    else if (F::kHasExceptions && a.exc_off != nullptr)
-        lds += exc_lds_bytes<MFMA, MR, KW, NW>();
+    else if (F::kHasExceptions && a.exc_off != nullptr) {
+        size_t extra;
+        (void)walk_base<MFMA, MR, R, KW, D, CHUNKED, XD, NW>(a.gs, &extra);
+        lds += extra;
+    }
     hipLaunchKernelGGL((gemm_kernel<F, MFMA, MR, R, KW, D, CHUNKED, XD, NW>), grid,
                        dim3(NW * 64 + (kExcWave ? 64 : 0)), lds, s, a);
     return hipGetLastError();
