@@ -201,7 +201,10 @@ Tiling choose_tiling(int M, int64_t N, int64_t K, bool allow_splitk) {
     if (M == 1) {
         t.mfma = 0;
         t.kw = ntiles >= 256 && ntiles <= 1024 ? 2 : 4;
-        t.depth = small_pair ? 2 : 4;
+        // two groups in flight per wave above 1024 tiles: with 2 000+
+        // workgroups several share each CU and keep it fed (gate+up 41.7
+        // against 42.3 us with four)
+        t.depth = small_pair || ntiles > 1024 ? 2 : 4;
         t.xdirect = 1;
     } else if ((M <= 8 && !lds_small_m) || (M <= 32 && G <= 8) ||
                (M <= 12 && G >= 10 && G <= 20 && ntiles > 256 && ntiles <= 512) ||

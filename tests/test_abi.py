@@ -122,6 +122,8 @@ def test_variant_selection():
     assert w12.w12_gemm_variant(8, 7168, 5120).startswith("w12_mfma_mt16_")
     assert w12.w12_gemm_variant(9, 7168, 5120).startswith("w12_mfma_mt16_")
     assert w12.w12_gemm_variant(16, 34816, 5120).startswith("w12_mfma_mt16_")
+    assert w12.w12_gemm_variant(1, 34816, 5120) == "w12_gemv_m1_r1_kw4_d2_xdirect"
+    assert w12.w12_gemm_variant(1, 5120, 17408) == "w12_gemv_m1_r1_kw2_d4_xdirect"
     assert w12.w12_gemm_variant(17, 5120, 17408).startswith("w12_mfma_mt32_")
     assert w12.w12_gemm_variant(33, 5120, 17408).startswith("w12_mfma_mt64_r1_kw1_d2_chunked_w8_s6")
     assert w12.w12_gemm_variant(33, 2048, 5120).startswith("w12_mfma_mt64_r1_kw2_d2_chunked_w8")
